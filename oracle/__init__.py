@@ -1,0 +1,220 @@
+"""CPU oracle of MassAlloc Attention (MALA): ctypes wrapper of the fp64 C library.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the bench's
+CPU-baseline leg import this package.  The GPU operator must never route
+through it, and it imports nothing from the GPU package.
+
+Inputs are fp64 numpy arrays (the exact values of the rounded bf16/fp32
+inputs).  Layouts: prefill [B, H, L, d]; decode q [B, Hq, d] and caches
+[B, Hkv, Lcap, d].  Decision arrays are uint8, statistics fp64 (T is NaN for
+tiles not visited and for tau = 0).
+
+The arithmetic lives in mala_oracle.c, whose header lists the passages it
+follows and every reading of points the pages leave open.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from .build import build, lib_path
+
+_LIB = None
+_D = ctypes.POINTER(ctypes.c_double)
+_U8 = ctypes.POINTER(ctypes.c_uint8)
+_L = ctypes.POINTER(ctypes.c_long)
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        p = lib_path()
+        if not os.path.exists(p):
+            build()
+        lib = ctypes.CDLL(p)
+        lib.oracle_fwd_head.argtypes = [_D, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                        ctypes.c_int, ctypes.c_int, _L, ctypes.c_long, _U8, ctypes.c_double,
+                                        _D, _D, _U8, _D]
+        lib.oracle_bwd_head.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double,
+                                        ctypes.c_double, ctypes.c_int, ctypes.c_int, _L, ctypes.c_long, _L,
+                                        ctypes.c_long, _U8, ctypes.c_double, _D, _D, _D, _U8, _D]
+        lib.oracle_decode_group.argtypes = [_D, ctypes.c_int, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double,
+                                            ctypes.c_double, ctypes.c_long, ctypes.c_int, ctypes.c_int, _U8,
+                                            ctypes.c_double, _D, _D, _U8, _D, _D, _D, _D]
+        lib.oracle_decode_groups.argtypes = [ctypes.c_long, _D, ctypes.c_int, _D, _D, ctypes.c_long, ctypes.c_long,
+                                             ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_long,
+                                             ctypes.c_int, ctypes.c_int, _U8, ctypes.c_double, _D, _D, _U8, _D]
+        lib.oracle_omitted_head.argtypes = [_D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                            ctypes.c_int, _U8, _L, ctypes.c_long, _D, _D]
+        for f in ("oracle_fwd_head", "oracle_bwd_head", "oracle_decode_group", "oracle_decode_groups",
+                  "oracle_omitted_head"):
+            getattr(lib, f).restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def _p(a, t):
+    if a is None:
+        return None
+    return a.ctypes.data_as(t)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ids(x):
+    if x is None:
+        return None, 0
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int64).ravel()).astype(np.int_)
+    return a, len(a)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)
+
+
+def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
+    """MALA forward.  Returns (o, lse, keep, T); keep/T are [B, H, nqb, ntiles].
+
+    qblocks: optional iterable of query-block indices (same for every head);
+    rows of other blocks are left NaN.
+    replay: optional uint8 [B, H, nqb, ntiles] decisions adopted on tiles with
+    |T - 1| <= band.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, L, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    nqb, nt = -(-L // bq), -(-L // bk)
+    o = np.full((B, H, L, d), np.nan)
+    lse = np.full((B, H, L), np.nan)
+    keep = np.zeros((B, H, nqb, nt), dtype=np.uint8)
+    T = np.full((B, H, nqb, nt), np.nan)
+    ids, n = _ids(qblocks)
+    rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
+    for b in range(B):
+        for h in range(H):
+            rc = _lib().oracle_fwd_head(_p(q[b, h], _D), _p(k[b, h], _D), _p(v[b, h], _D), L, d, scale, float(tau),
+                                        bq, bk, _p(ids, _L), n, _p(None if rp is None else rp[b, h], _U8),
+                                        float(band), _p(o[b, h], _D), _p(lse[b, h], _D), _p(keep[b, h], _U8),
+                                        _p(T[b, h], _D))
+            _check(rc, "oracle_fwd_head")
+    return o, lse, keep, T
+
+
+def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None, ktiles=None):
+    """MALA backward against the given forward state (o, lse).
+
+    Returns (dq, dk, dv, keep, T).  qblocks / ktiles restrict which dq rows /
+    dk,dv rows are computed (others NaN).
+    """
+    q, k, v, o, lse, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(lse), _f64(do)
+    B, H, L, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    nqb, nt = -(-L // bq), -(-L // bk)
+    dq = np.full((B, H, L, d), np.nan)
+    dk = np.full((B, H, L, d), np.nan)
+    dv = np.full((B, H, L, d), np.nan)
+    keep = np.zeros((B, H, nqb, nt), dtype=np.uint8)
+    T = np.full((B, H, nqb, nt), np.nan)
+    qi, nq = _ids(qblocks)
+    ki, nk = _ids(ktiles)
+    rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
+    for b in range(B):
+        for h in range(H):
+            rc = _lib().oracle_bwd_head(_p(q[b, h], _D), _p(k[b, h], _D), _p(v[b, h], _D), _p(o[b, h], _D),
+                                        _p(lse[b, h], _D), _p(do[b, h], _D), L, d, scale, float(tau), bq, bk,
+                                        _p(qi, _L), nq, _p(ki, _L), nk, _p(None if rp is None else rp[b, h], _U8),
+                                        float(band), _p(dq[b, h], _D), _p(dk[b, h], _D), _p(dv[b, h], _D),
+                                        _p(keep[b, h], _U8), _p(T[b, h], _D))
+            _check(rc, "oracle_bwd_head")
+    return dq, dk, dv, keep, T
+
+
+def decode_shapes(Lk, split_keys, bk):
+    return -(-Lk // split_keys), -(-split_keys // bk)
+
+
+def decode(q, kc, vc, Lk, tau, split_keys, bk, scale=None, rows_per_vote=None, replay=None, band=1e-4,
+           units=None):
+    """Split-KV MALA decode.  q [B, Hq, d]; kc, vc [B, Hkv, Lcap, d].
+
+    Returns (o [B, Hq, d], lse [B, Hq], keep, T) with keep/T of shape
+    [B, Hkv, G/rows_per_vote, nsplit, tps].  units: optional list of (b, g)
+    pairs to compute (others left NaN / 0).
+    """
+    q = _f64(q)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[1]
+    G = Hq // Hkv
+    R = G if rows_per_vote is None else int(rows_per_vote)
+    scale = default_scale(d) if scale is None else float(scale)
+    nsplit, tps = decode_shapes(Lk, split_keys, bk)
+    o = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    keep = np.zeros((B, Hkv, G // R, nsplit, tps), dtype=np.uint8)
+    T = np.full((B, Hkv, G // R, nsplit, tps), np.nan)
+    units = [(b, g) for b in range(B) for g in range(Hkv)] if units is None else list(units)
+    n = len(units)
+    qs = np.stack([q[b, g * G:(g + 1) * G] for b, g in units])
+    ks = np.stack([_f64(kc[b, g, :Lk]) for b, g in units])
+    vs = np.stack([_f64(vc[b, g, :Lk]) for b, g in units])
+    ou = np.zeros((n, G, d))
+    lu = np.zeros((n, G))
+    kb = np.zeros((n, G // R, nsplit, tps), dtype=np.uint8)
+    Tb = np.full((n, G // R, nsplit, tps), np.nan)
+    rp = None
+    if replay is not None:
+        rp = np.ascontiguousarray(np.stack([replay[b, g] for b, g in units]), dtype=np.uint8)
+    rc = _lib().oracle_decode_groups(n, _p(qs, _D), G, _p(ks, _D), _p(vs, _D), Lk * d, Lk, d, scale, float(tau),
+                                     split_keys, bk, R, _p(rp, _U8), float(band), _p(ou, _D), _p(lu, _D),
+                                     _p(kb, _U8), _p(Tb, _D))
+    _check(rc, "oracle_decode_groups")
+    for u, (b, g) in enumerate(units):
+        o[b, g * G:(g + 1) * G] = ou[u]
+        lse[b, g * G:(g + 1) * G] = lu[u]
+        keep[b, g] = kb[u]
+        T[b, g] = Tb[u]
+    return o, lse, keep, T
+
+
+def decode_group_partials(q, k, v, Lk, tau, split_keys, bk, scale=None, rows_per_vote=None):
+    """One KV group (q [G, d], k/v [Lk, d]); also returns the per-partition
+    states (m [G, nsplit], l [G, nsplit], acc [G, nsplit, d])."""
+    q, k, v = _f64(q), _f64(k[:Lk]), _f64(v[:Lk])
+    G, d = q.shape
+    R = G if rows_per_vote is None else int(rows_per_vote)
+    scale = default_scale(d) if scale is None else float(scale)
+    nsplit, tps = decode_shapes(Lk, split_keys, bk)
+    o = np.zeros((G, d)); lse = np.zeros(G)
+    keep = np.zeros((G // R, nsplit, tps), dtype=np.uint8); T = np.full((G // R, nsplit, tps), np.nan)
+    pm = np.zeros((G, nsplit)); pl = np.zeros((G, nsplit)); pa = np.zeros((G, nsplit, d))
+    rc = _lib().oracle_decode_group(_p(q, _D), G, _p(k, _D), _p(v, _D), Lk, d, scale, float(tau), split_keys, bk,
+                                    R, None, 0.0, _p(o, _D), _p(lse, _D), _p(keep, _U8), _p(T, _D),
+                                    _p(pm, _D), _p(pl, _D), _p(pa, _D))
+    _check(rc, "oracle_decode_group")
+    return o, lse, keep, T, pm, pl, pa
+
+
+def omitted(q, k, keep, bq, bk, scale=None, qblocks=None):
+    """Per-row omitted dense mass and kept slots for forward decisions `keep`.
+    Returns (omitted [B, H, L], slots [B, H, L]) (NaN outside computed blocks)."""
+    q, k = _f64(q), _f64(k)
+    B, H, L, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    om = np.full((B, H, L), np.nan)
+    sl = np.full((B, H, L), np.nan)
+    ids, n = _ids(qblocks)
+    kp = np.ascontiguousarray(keep, dtype=np.uint8)
+    for b in range(B):
+        for h in range(H):
+            rc = _lib().oracle_omitted_head(_p(q[b, h], _D), _p(k[b, h], _D), L, d, scale, bq, bk,
+                                            _p(kp[b, h], _U8), _p(ids, _L), n, _p(om[b, h], _D), _p(sl[b, h], _D))
+            _check(rc, "oracle_omitted_head")
+    return om, sl

@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle against facts fixed independently of it.
+
+Each test names the fact it checks.  Passages are cited from "MassAlloc
+Attention: Let Attention Allocate Its Own Compute" (agihunt.info digest) by
+paragraph topic.  Inputs are small seeded instances of the named workloads so
+the whole file runs in well under a minute on CPU.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import dense
+from synth import WORKLOADS, prefill_inputs, decode_inputs, to_f64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _prefill(name, L=None, heads=None, family="planted"):
+    w = WORKLOADS[name]
+    x = prefill_inputs(w, family=family, L=L, heads=heads)
+    H = len(heads) if heads is not None else w.H
+    hs = list(heads) if heads is not None else list(range(w.H))
+    return w, [to_f64(x[n][:, hs], w.dtype) for n in ("q", "k", "v", "do")]
+
+
+def _legal(L, bq, bk):
+    nqb, nt = -(-L // bq), -(-L // bk)
+    return np.array([[t * bk <= min(b * bq + bq, L) - 1 for t in range(nt)] for b in range(nqb)])
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return _prefill("tiny")
+
+
+@pytest.fixture(scope="module")
+def small_bf16():
+    # 8K-workload recipe, shortened to a ragged length (not a multiple of 128 or 64)
+    return _prefill("mw8k", L=1000, heads=[0, 2, 5])
+
+
+# ---------------------------------------------------------------- worked examples
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLDEN, "worked_examples.json")))["cases"],
+                         ids=lambda c: c["name"])
+def test_worked_example(case):
+    """Hand-derived decisions (tests/golden/worked_examples.md); O and lse are the
+    closed-form softmax over the hand-derived kept keys."""
+    q = np.array(case["q"], float).reshape(1, 1, -1, 1)
+    k = np.array(case["k"], float).reshape(1, 1, -1, 1)
+    v = np.array(case["v"], float).reshape(1, 1, -1, 1)
+    o, lse, keep, T = oracle.fwd(q, k, v, case["tau"], case["bq"], case["bk"], scale=case["scale"])
+    exp_keep = np.array(case["keep"], np.uint8)
+    assert (keep[0, 0] == exp_keep).all()
+    for i, kk in enumerate(case["kept_keys"]):
+        s = np.array([case["q"][i] * case["k"][j] for j in kk])
+        z = sum(math.exp(x) for x in s)
+        o_exp = sum(math.exp(x) * case["v"][j] for x, j in zip(s, kk)) / z
+        assert abs(o[0, 0, i, 0] - o_exp) <= 1e-12 * abs(o_exp)
+        assert abs(lse[0, 0, i] - math.log(z)) <= 1e-12
+
+
+def test_worked_example_distant_row3_closed_form():
+    """Row 3 of the first worked example, written out: O = (40e^2 + 10e^3)/(e^2 + e^3)."""
+    q = np.ones((1, 1, 4, 1)); k = np.array([3.0, -3.0, 0.5, 2.0]).reshape(1, 1, 4, 1)
+    v = np.array([10.0, 20.0, 30.0, 40.0]).reshape(1, 1, 4, 1)
+    o, lse, keep, _ = oracle.fwd(q, k, v, 1.0, 1, 1, scale=1.0)
+    e2, e3 = math.exp(2), math.exp(3)
+    assert abs(o[0, 0, 3, 0] - (40 * e2 + 10 * e3) / (e2 + e3)) < 1e-12
+    assert abs(lse[0, 0, 3] - math.log(e2 + e3)) < 1e-12
+
+
+# ---------------------------------------------------------------- P1: tau = 0 is full attention
+def test_tau0_fwd_equals_dense_tiny(tiny):
+    """Savings paragraph: as tau -> 0 both passes recover full attention."""
+    w, (q, k, v, do) = tiny
+    o, lse, keep, _ = oracle.fwd(q, k, v, 0.0, w.bq, w.bk)
+    od, ld = dense.fwd(q, k, v, 1 / math.sqrt(w.d))
+    assert np.abs(o - od).max() <= 1e-12 * np.abs(od).max()
+    assert np.abs(lse - ld).max() <= 1e-12 * np.abs(ld).max()
+    assert keep[0, 0][_legal(w.L, w.bq, w.bk)].all()
+
+
+def test_tau0_fwd_equals_dense_bf16_ragged(small_bf16):
+    w, (q, k, v, do) = small_bf16
+    o, lse, _, _ = oracle.fwd(q, k, v, 0.0, 128, 64)
+    od, ld = dense.fwd(q, k, v, 1 / math.sqrt(w.d))
+    assert np.abs(o - od).max() <= 1e-12 * np.abs(od).max()
+    assert np.abs(lse - ld).max() <= 1e-12 * np.abs(ld).max()
+
+
+# ---------------------------------------------------------------- P2: tau = 0 backward is the exact gradient
+def test_dense_gradient_matches_finite_differences():
+    """The dense analytic gradient (the tau=0 target) against central differences
+    of the scalar loss sum(dO * O) on a 2-head, 64-token instance."""
+    rng = np.random.default_rng(7)
+    L, d = 64, 16
+    scale = 1 / math.sqrt(d)
+    for h in range(2):
+        q, k, v, do = (rng.standard_normal((L, d)) for _ in range(4))
+        dq, dk, dv = dense.bwd_head(q, k, v, do, scale)
+
+        def loss(q_, k_, v_):
+            return float((dense.fwd_head(q_, k_, v_, scale)[0] * do).sum())
+
+        eps = 1e-6
+        for arr, grad, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+            for (i, c) in [(0, 0), (17, 3), (40, 9), (63, 15), (5, 1)]:
+                a = [q.copy(), k.copy(), v.copy()]
+                a[which][i, c] += eps
+                lp = loss(*a)
+                a[which][i, c] -= 2 * eps
+                lm = loss(*a)
+                fd = (lp - lm) / (2 * eps)
+                assert abs(fd - grad[i, c]) <= 1e-6 * max(1.0, abs(fd)), (which, i, c, fd, grad[i, c])
+
+
+def test_tau0_bwd_equals_dense_gradient(tiny, small_bf16):
+    for w, (q, k, v, do) in (tiny, small_bf16):
+        bq, bk = (w.bq, w.bk) if w.dtype == "f32" else (128, 64)
+        o, lse, _, _ = oracle.fwd(q, k, v, 0.0, bq, bk)
+        dq, dk, dv, keep, _ = oracle.bwd(q, k, v, o, lse, do, 0.0, bq, bk)
+        g = dense.bwd(q, k, v, do, 1 / math.sqrt(w.d))
+        for a, b in zip((dq, dk, dv), g):
+            assert np.abs(a - b).max() <= 1e-11 * np.abs(b).max()
+        assert keep[0, 0][_legal(q.shape[2], bq, bk)].all()
+
+
+# ---------------------------------------------------------------- P3: no empty row
+@pytest.mark.parametrize("tau", [0.5, 1.0, 4.0, 64.0, math.inf])
+def test_no_empty_row(small_bf16, tau):
+    """Forward paragraph: the first legal tile is always kept, so no row is empty."""
+    w, (q, k, v, do) = small_bf16
+    o, lse, keep, T = oracle.fwd(q, k, v, tau, 128, 64)
+    assert np.isfinite(lse).all() and np.isfinite(o).all()
+
+
+# ---------------------------------------------------------------- P4: nesting
+@pytest.mark.parametrize("tau", [0.5, 1.0, 2.0, 16.0])
+def test_backward_support_nested_in_forward(small_bf16, tau):
+    """Backward paragraph: testing against the final normalizer can only shrink the
+    ratios, so every forward-skipped tile is skipped in backward too."""
+    w, (q, k, v, do) = small_bf16
+    o, lse, kf, _ = oracle.fwd(q, k, v, tau, 128, 64)
+    _, _, _, kb, _ = oracle.bwd(q, k, v, o, lse, do, tau, 128, 64)
+    assert (kb <= kf).all()
+    if tau >= 2.0:
+        assert kb.sum() < kf.sum()   # the inclusion is strict somewhere on these inputs
+
+
+# ---------------------------------------------------------------- P5: omitted-mass bound
+@pytest.mark.parametrize("tau", [0.25, 1.0, 8.0, 1000.0])
+def test_omitted_mass_below_bound(tau):
+    """Limits paragraph: per-row omitted mass stays below tau/(1+tau); checked by
+    brute force against the dense softmax on inputs where many tiles skip."""
+    w, (q, k, v, do) = _prefill("mw8k", L=700, heads=[2, 6, 9])
+    o, lse, keep, _ = oracle.fwd(q, k, v, tau, 128, 64)
+    worst = 0.0
+    for h in range(q.shape[1]):
+        P = dense.probs_head(q[0, h], k[0, h], 1 / math.sqrt(w.d))
+        L = q.shape[2]
+        mask = np.zeros((L, L), bool)
+        for i in range(L):
+            for t in range(-(-L // 64)):
+                if keep[0, h, i // 128, t]:
+                    mask[i, t * 64:(t + 1) * 64] = True
+        om = (P * ~mask).sum(axis=1)
+        assert (om < tau / (1 + tau)).all()
+        worst = max(worst, om.max())
+    if tau >= 8.0:
+        assert worst > 1e-3   # the bound is exercised, not vacuous
+
+
+# ---------------------------------------------------------------- P6: tau = +inf keeps only forced tiles
+def test_tau_inf_forced_tiles_only(small_bf16):
+    """Forward keeps exactly the tiles visited while some row is still empty (for
+    128x64 tiles: the two diagonal-side tiles 2b+1 and 2b); the output is dense
+    attention restricted to those keys.  Backward has no forced keep: all zero."""
+    w, (q, k, v, do) = small_bf16
+    L = q.shape[2]
+    o, lse, keep, _ = oracle.fwd(q, k, v, math.inf, 128, 64)
+    nqb, nt = keep.shape[2:]
+    exp = np.zeros((nqb, nt), np.uint8)
+    for b in range(nqb):
+        jmax = (min(b * 128 + 128, L) - 1) // 64
+        exp[b, jmax] = 1
+        if b * 128 < jmax * 64:   # rows b*128 .. see nothing in the last tile
+            exp[b, jmax - 1] = 1
+    for h in range(q.shape[1]):
+        assert (keep[0, h] == exp).all()
+        mask = np.zeros((L, L), bool)
+        for i in range(L):
+            for t in range(nt):
+                if exp[i // 128, t]:
+                    mask[i, t * 64:(t + 1) * 64] = True
+        od, ld = dense.fwd_head(q[0, h], k[0, h], v[0, h], 1 / math.sqrt(w.d), key_mask=mask)
+        assert np.abs(o[0, h] - od).max() <= 1e-12 * np.abs(od).max()
+        assert np.abs(lse[0, h] - ld).max() <= 1e-12
+    dq, dk, dv, kb, _ = oracle.bwd(q, k, v, o, lse, do, math.inf, 128, 64)
+    assert kb.sum() == 0
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
+
+
+# ---------------------------------------------------------------- P10: kept-set restricted dense
+@pytest.mark.parametrize("tau", [1.0, 4.0])
+def test_fwd_output_is_dense_over_kept_keys(small_bf16, tau):
+    """The online update is exact on the kept set: O_i and lse_i equal softmax
+    attention of row i over the keys of its block's kept tiles."""
+    w, (q, k, v, do) = small_bf16
+    L = q.shape[2]
+    o, lse, keep, _ = oracle.fwd(q, k, v, tau, 128, 64)
+    for h in range(q.shape[1]):
+        mask = np.zeros((L, L), bool)
+        for i in range(L):
+            for t in range(keep.shape[3]):
+                if keep[0, h, i // 128, t]:
+                    mask[i, t * 64:(t + 1) * 64] = True
+        od, ld = dense.fwd_head(q[0, h], k[0, h], v[0, h], 1 / math.sqrt(w.d), key_mask=mask)
+        assert np.abs(o[0, h] - od).max() <= 1e-12 * np.abs(od).max()
+        assert np.abs(lse[0, h] - ld).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- P7: decision brute force
+@pytest.mark.parametrize("tau", [1.0, 4.0, 16.0])
+def test_decisions_by_direct_sums(tau):
+    """Every tile's statistic recomputed without online rescaling: for each row the
+    running normalizer is the plain sum of exp(s) over keys of previously kept
+    tiles, T = max over voting rows of max_j exp(s_ij)/Z_i * Lq_i/tau."""
+    w, (q, k, v, do) = _prefill("mw8k", L=520, heads=[2, 5])
+    bq, bk = 128, 64
+    o, lse, keep, T = oracle.fwd(q, k, v, tau, bq, bk)
+    L = q.shape[2]
+    scale = 1 / math.sqrt(w.d)
+    flips = 0
+    for h in range(q.shape[1]):
+        S = scale * q[0, h] @ k[0, h].T
+        for b in range(keep.shape[2]):
+            rows = range(b * bq, min(b * bq + bq, L))
+            Z = {i: 0.0 for i in rows}
+            jmax = (max(rows)) // bk
+            for t in range(jmax, -1, -1):
+                cols = range(t * bk, min(t * bk + bk, L))
+                Tt = 0.0
+                for i in rows:
+                    vis = [j for j in cols if j <= i]
+                    if not vis:
+                        continue
+                    if Z[i] == 0.0:
+                        Tt = math.inf
+                        continue
+                    r = max(math.exp(S[i, j]) for j in vis) / Z[i]
+                    Tt = max(Tt, r * (i + 1) / tau)
+                kp = Tt >= 1.0
+                assert kp == bool(keep[0, h, b, t]), (h, b, t, Tt)
+                if math.isfinite(Tt):
+                    assert abs(Tt - T[0, h, b, t]) <= 1e-9 * Tt
+                if kp:
+                    for i in rows:
+                        Z[i] += sum(math.exp(S[i, j]) for j in cols if j <= i)
+                flips += not kp
+    assert flips > 0
+
+
+# ---------------------------------------------------------------- P9: log-domain form of the test
+@pytest.mark.parametrize("tau", [0.5, 1.0, 4.0])
+def test_log_domain_test_gives_same_decisions(tau):
+    """The GPU kernels test rowmax_i >= m_i + ln(l_i) + ln(tau) - ln(Lq_i) instead
+    of the ratio form.  Both forms, run side by side in fp64 on the same running
+    state, agree on every tile of these inputs (they differ only on exact ties)."""
+    w, (q, k, v, do) = _prefill("mw8k", L=384, heads=[2])
+    bq, bk = 128, 64
+    _, _, keep, _ = oracle.fwd(q, k, v, tau, bq, bk)
+    S = q[0, 0] @ k[0, 0].T / math.sqrt(w.d)
+    L = S.shape[0]
+    for b in range(keep.shape[2]):
+        rows = list(range(b * bq, min(b * bq + bq, L)))
+        m = {i: -math.inf for i in rows}
+        lsum = {i: 0.0 for i in rows}
+        for t in range((rows[-1]) // bk, -1, -1):
+            kp_log = False
+            for i in rows:
+                vis = [j for j in range(t * bk, min(t * bk + bk, L)) if j <= i]
+                if not vis:
+                    continue
+                if lsum[i] == 0.0:
+                    kp_log = True
+                    continue
+                thr = m[i] + math.log(lsum[i]) + math.log(tau) - math.log(i + 1)
+                kp_log |= max(S[i, j] for j in vis) >= thr
+            assert kp_log == bool(keep[0, 0, b, t])
+            if kp_log:
+                for i in rows:
+                    vis = [j for j in range(t * bk, min(t * bk + bk, L)) if j <= i]
+                    if not vis:
+                        continue
+                    mn = max(m[i], max(S[i, j] for j in vis))
+                    lsum[i] = lsum[i] * math.exp(m[i] - mn) + sum(math.exp(S[i, j] - mn) for j in vis)
+                    m[i] = mn
+
+
+# ---------------------------------------------------------------- replay mode
+def test_replay_band_only_overrides_near_threshold(small_bf16):
+    """Replay adopts foreign decisions only where |T - 1| <= band: flipping every
+    decision outside the band changes nothing."""
+    w, (q, k, v, do) = small_bf16
+    o, lse, keep, T = oracle.fwd(q, k, v, 1.0, 128, 64)
+    o2, lse2, keep2, T2 = oracle.fwd(q, k, v, 1.0, 128, 64, replay=1 - keep, band=1e-4)
+    near = np.isfinite(T) & (np.abs(T - 1) <= 1e-4)
+    assert (keep2[~near] == keep[~near]).all()
+    o3, _, keep3, T3 = oracle.fwd(q, k, v, 1.0, 128, 64, replay=1 - keep, band=np.inf)
+    finite = np.isfinite(T3)
+    assert (keep3[finite] != keep[finite]).any()
+
+
+# ---------------------------------------------------------------- P8: decode
+def _decode_small(Lk=1000):
+    w = WORKLOADS["decode128k"]
+    x = decode_inputs(w, Lk=Lk, batches=[0])
+    return w, to_f64(x["q"][:1], w.dtype), to_f64(x["k"][:1], w.dtype), to_f64(x["v"][:1], w.dtype)
+
+
+def test_decode_tau0_is_dense_single_query():
+    w, q, kc, vc = _decode_small(1000)
+    o, lse, keep, _ = oracle.decode(q, kc, vc, 1000, 0.0, 256, 64)
+    G = w.group
+    for h in range(w.H):
+        g = h // G
+        s = kc[0, g] @ q[0, h] / math.sqrt(w.d)
+        p = np.exp(s - s.max())
+        assert np.abs(o[0, h] - p @ vc[0, g] / p.sum()).max() <= 1e-12 * np.abs(o[0, h]).max()
+        assert abs(lse[0, h] - (s.max() + math.log(p.sum()))) <= 1e-12
+
+
+def test_decode_split_independence_at_tau0():
+    w, q, kc, vc = _decode_small(1000)
+    o1, l1, _, _ = oracle.decode(q, kc, vc, 1000, 0.0, 128, 64)
+    o2, l2, _, _ = oracle.decode(q, kc, vc, 1000, 0.0, 4096, 64)
+    assert np.abs(o1 - o2).max() <= 1e-12 * np.abs(o2).max()
+    assert np.abs(l1 - l2).max() <= 1e-12
+
+
+@pytest.mark.parametrize("tau", [1.0, 8.0])
+def test_decode_one_split_one_row_equals_forward_row(tau):
+    """With a single partition and a one-row vote, decode of the query at
+    position Lk-1 is the forward pass of that row with a one-row block."""
+    w, q, kc, vc = _decode_small(777)
+    Lk = 777
+    o, lse, keep, T = oracle.decode(q, kc, vc, Lk, tau, 4096, 64, rows_per_vote=1)
+    for h in (0, 5, 30):
+        g = h // w.group
+        qq = np.zeros((1, 1, Lk, w.d))
+        qq[0, 0, Lk - 1] = q[0, h]
+        kk = kc[0, g, :Lk][None, None]
+        vv = vc[0, g, :Lk][None, None]
+        of, lf, kf, Tf = oracle.fwd(qq, kk, vv, tau, 1, 64, qblocks=[Lk - 1])
+        assert np.abs(o[0, h] - of[0, 0, Lk - 1]).max() <= 1e-12 * np.abs(of[0, 0, Lk - 1]).max()
+        assert abs(lse[0, h] - lf[0, 0, Lk - 1]) <= 1e-12
+        nt = -(-Lk // 64)
+        assert (keep[0, g, h % w.group, 0, :nt] == kf[0, 0, Lk - 1, :nt]).all()
+
+
+@pytest.mark.parametrize("tau", [1.0, 16.0])
+def test_decode_is_dense_over_kept_keys_and_bounded(tau):
+    """The exact merge of partition states makes decode output the softmax over
+    the union of kept tiles; per partition the omitted mass obeys the bound."""
+    w, q, kc, vc = _decode_small(1500)
+    Lk, S, bk = 1500, 512, 64
+    o, lse, keep, T = oracle.decode(q, kc, vc, Lk, tau, S, bk)
+    G = w.group
+    nsplit, tps = oracle.decode_shapes(Lk, S, bk)
+    skipped_any = False
+    for h in range(w.H):
+        g = h // G
+        s = kc[0, g, :Lk] @ q[0, h] / math.sqrt(w.d)
+        mask = np.zeros(Lk, bool)
+        for p in range(nsplit):
+            for t in range(tps):
+                if keep[0, g, 0, p, t]:
+                    mask[p * S + t * bk: min(p * S + (t + 1) * bk, (p + 1) * S, Lk)] = True
+        skipped_any |= not mask.all()
+        e = np.exp(s[mask] - s[mask].max())
+        assert np.abs(o[0, h] - e @ vc[0, g, :Lk][mask] / e.sum()).max() <= 1e-12 * np.abs(o[0, h]).max()
+        P = np.exp(s - s.max()); P /= P.sum()
+        assert P[~mask].sum() < tau / (1 + tau)
+        # each partition's first visited tile is kept
+        for p in range(nsplit):
+            nt = -(-(min((p + 1) * S, Lk) - p * S) // bk)
+            assert keep[0, g, 0, p, nt - 1] == 1
+    if tau >= 16.0:
+        assert skipped_any
+
+
+def test_invalid_tau_rejected():
+    q = np.zeros((1, 1, 4, 2))
+    for bad in (-1.0, float("nan")):
+        with pytest.raises(RuntimeError):
+            oracle.fwd(q, q, q, bad, 2, 2)
