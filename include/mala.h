@@ -1,0 +1,172 @@
+/*
+ * mala.h -- C ABI of libmala.so: MassAlloc Attention (MALA) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * MALA is causal softmax attention that still scores every legal causal tile
+ * (QK) but gates the post-score work of each tile on the tile's normalized
+ * contribution.  Source: "MassAlloc Attention: Let Attention Allocate Its Own
+ * Compute", digest page at agihunt.info (arXiv 2609.32712).  Its paragraphs
+ * are cited by topic:
+ *   threshold paragraph  -- the per-tile test of the largest per-key
+ *                           contribution ratio against tau/Lq, Lq = number of
+ *                           causally visible keys of the query row;
+ *   forward paragraph    -- test against the running online-softmax
+ *                           normalizer, block vote, diagonal-to-early visit
+ *                           order, first legal tile always kept, lse written;
+ *   backward paragraph   -- test against the final log-normalizer, nested
+ *                           support, no stored mask;
+ *   savings paragraph    -- what a skipped tile saves; tau -> 0 gives full
+ *                           attention; no attention matrix or mask stored.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are DEVICE pointers to densely packed row-major arrays; the
+ *    library allocates nothing, keeps no pointer after returning and never
+ *    synchronizes the device.  The caller owns every buffer (including the
+ *    workspace) and must keep it alive until the work queued on `stream` has
+ *    finished.
+ *  - `stream` is a hipStream_t (NULL: the default stream).  All work is queued
+ *    on it in order; calls are asynchronous.
+ *  - Element type `dtype`: MALA_BF16 tensors hold bfloat16 values, MALA_F32
+ *    tensors hold float.  lse and statistics are always float / int32.
+ *    Arithmetic is fp32 (bf16 MFMA products accumulated in fp32).
+ *  - Scores are s_ij = scale * <q_i, k_j>; scale <= 0 selects 1/sqrt(d).
+ *    lse is the natural-log normalizer: lse_i = ln sum_{kept j} exp(s_ij).
+ *  - tau >= 0 (finite or +inf).  tau = 0 selects the ungated instantiation
+ *    (full causal attention, every legal tile kept).  tau = +inf keeps only
+ *    the tiles forward must keep (those visited while a row is still empty)
+ *    and nothing in backward.
+ *  - Errors: every argument is validated before anything is queued; on error
+ *    nothing is queued, the status is returned and mala_last_error() (per
+ *    thread) describes it.  A HIP launch failure returns MALA_ERR_HIP.
+ *  - Thread safety: calls may be made concurrently from several host threads.
+ *
+ * Supported shapes (anything else returns MALA_ERR_UNSUPPORTED)
+ *  - prefill (fwd/bwd): H == Hkv; L >= 1 (ragged L allowed);
+ *      MALA_BF16 with d = 128 and tile {128, 64};
+ *      MALA_F32  with d = 64  and tile {64, 64}.
+ *  - decode: Hq % Hkv == 0 with G = Hq/Hkv <= 8; MALA_BF16, d = 128, bk = 64,
+ *      split_keys a positive multiple of bk.
+ */
+#ifndef MALA_H
+#define MALA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MALA_OK = 0,
+    MALA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, tau < 0 or NaN, short workspace */
+    MALA_ERR_UNSUPPORTED = -2, /* valid request outside the supported shapes listed above           */
+    MALA_ERR_HIP = -3          /* a HIP runtime call or kernel launch failed                         */
+} mala_status;
+
+typedef enum { MALA_BF16 = 0, MALA_F32 = 1 } mala_dtype;
+
+/* Tile shape: bq query rows (one vote block) by bk keys. */
+typedef struct {
+    int bq;
+    int bk;
+} mala_tile;
+
+/*
+ * Optional per-call statistics; every pointer may be NULL (not written).
+ * Prefill (fwd or bwd), nqb = ceil(L/bq), ntiles = ceil(L/bk),
+ * words = ceil(ntiles/32):
+ *   kept      int32 [B, H, nqb]         tiles kept per query block
+ *   legal     int32 [B, H, nqb]         legal (tested) tiles per query block
+ *   keep_bits uint32 [B, H, nqb, words] bit (t % 32) of word t/32 = tile t kept
+ * Decode, nsplit = ceil(Lk/split_keys), tps = split_keys/bk, words = ceil(tps/32):
+ *   kept, legal int32 [B, Hkv, nsplit];  keep_bits uint32 [B, Hkv, nsplit, words],
+ *   bit t = tile t of the partition (tile 0 starts at the partition start).
+ *   keep_bits_dkdv uint32 [B, H, nqb, words], mala_bwd only: the decisions as
+ *             taken by the dK/dV pass (the dQ pass writes keep_bits); the two
+ *             passes recompute the same scores and must agree bit for bit.
+ * These are debug/measurement outputs: the library never reads them back and
+ * backward does not consume anything forward wrote here.
+ */
+typedef struct {
+    int32_t* kept;
+    int32_t* legal;
+    uint32_t* keep_bits;
+    uint32_t* keep_bits_dkdv;
+} mala_stats;
+
+/*
+ * mala_fwd -- gated forward (forward paragraph, threshold paragraph).
+ *
+ * q, k, v: [B, H, L, d].  o: [B, H, L, d] (same dtype).  lse: float [B, H, L].
+ * For each query block of bq rows, key tiles t = jmax .. 0 (diagonal first)
+ * are scored; row i of the block votes to keep tile t iff its running state
+ * is empty or max_j exp(s_ij - m_i)/l_i >= tau/(i+1) over its visible keys
+ * (m_i, l_i: running max and normalizer before the tile); the tile is kept
+ * for the whole block iff any row votes keep; only kept tiles load V and
+ * update (m, l, acc).  o = acc/l, lse = m + ln l.
+ */
+mala_status mala_fwd(const void* q, const void* k, const void* v,
+                     int B, int H, int Hkv, int L, int d, mala_dtype dtype,
+                     float tau, mala_tile tile, float scale,
+                     void* o, float* lse, mala_stats* stats, void* stream);
+
+/* Workspace bytes mala_bwd needs for these sizes (0 for invalid sizes). */
+size_t mala_bwd_workspace_size(int B, int H, int L, int d, mala_dtype dtype, mala_tile tile);
+
+/*
+ * mala_bwd -- gated backward (backward paragraph).
+ *
+ * Inputs q, k, v, o, dout: [B, H, L, d]; lse: float [B, H, L] -- o and lse
+ * exactly as mala_fwd wrote them (the ordinary attention state; no mask).
+ * Outputs dq, dk, dv: [B, H, L, d], fully overwritten.
+ * With P_ij = exp(s_ij - lse_i), a tile (query block, key tile) is kept iff
+ * some row has a visible key with P_ij >= tau/(i+1) (no forced keep).  Kept
+ * tiles contribute dV += P^T dO, dS = P o (dO V^T - D) with
+ * D_i = sum_c dO_ic O_ic, dQ += scale dS K, dK += scale dS^T Q; skipped tiles
+ * contribute nothing.  tile must equal the forward's.
+ * workspace: device buffer of at least mala_bwd_workspace_size(...) bytes,
+ * 256-byte aligned, contents ignored on entry.
+ */
+mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, int B, int H, int Hkv, int L, int d, mala_dtype dtype,
+                     float tau, mala_tile tile, float scale,
+                     void* dq, void* dk, void* dv, mala_stats* stats,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mala_decode needs for these sizes (0 for invalid sizes). */
+size_t mala_decode_workspace_size(int B, int Hq, int Hkv, int Lk, int d, int split_keys);
+
+/*
+ * mala_decode -- one new query token per sequence against a KV cache, with
+ * the same test (threshold paragraph: one tau for training and decoding).
+ *
+ * q: [B, Hq, d] (query at position Lk-1).  kcache, vcache: [B, Hkv, Lcap, d];
+ * rows 0 .. Lk-1 are valid (row Lk-1 holds the new token).  o: [B, Hq, d];
+ * lse: float [B, Hq] or NULL.  Query head h uses KV head h / (Hq/Hkv).
+ * Split-KV: keys are cut into partitions [p*split_keys, min((p+1)*split_keys, Lk));
+ * each partition is cut into bk-key tiles from its start and visited last tile
+ * first with its own running state (so its first visited tile is kept); the
+ * G = Hq/Hkv query heads of a KV group vote together (the rows that share one
+ * K/V tile); Lq = Lk.  Partition states are merged exactly.
+ * workspace: at least mala_decode_workspace_size(...) bytes, 256-byte aligned.
+ */
+mala_status mala_decode(const void* q, const void* kcache, const void* vcache,
+                        int B, int Hq, int Hkv, int Lk, int Lcap, int d, mala_dtype dtype,
+                        float tau, int split_keys, int bk, float scale,
+                        void* o, float* lse, mala_stats* stats,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* mala_status_string(mala_status status);
+/* Message of the last failing call on this host thread ("" if none). */
+const char* mala_last_error(void);
+/* ABI version (major * 100 + minor). */
+int mala_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MALA_H */

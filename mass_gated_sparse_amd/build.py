@@ -1,0 +1,36 @@
+"""Builds libmala.so (all HIP kernels + the C ABI) for gfx950 with hipcc, in-tree."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = ["mala_api.hip", "mala_fwd.hip", "mala_bwd.hip", "mala_decode.hip", "mala_simple.hip"]
+ARCH = "gfx950"
+# -packed-fp32-ops: no packed fp32 VALU instructions are generated.
+HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def lib_path() -> str:
+    return os.path.join(HERE, "libmala.so")
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    out = lib_path()
+    tmp = out + ".tmp"
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc, *HIPCC_FLAGS, "-shared", *srcs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msg = "\n".join(line for line in (r.stdout + r.stderr).splitlines() if noise not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
+    if verbose and msg.strip():
+        print(msg)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,197 @@
+// C ABI of libmala.so: argument validation, workspace layout and dispatch.
+// The operator's definition and the contract of every entry point are in
+// include/mala.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mala.h"
+#include "mala_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mala_status fail(mala_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+mala_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MALA_OK;
+    return fail(MALA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// tau >= 0 (possibly +inf); NaN and negatives rejected.
+bool tau_ok(float tau) { return tau >= 0.f; }
+
+float eff_scale(float scale, int d) { return scale > 0.f ? scale : 1.f / sqrtf(float(d)); }
+
+float log2_tau_of(float tau) { return isinf(tau) ? INFINITY : log2f(tau); }
+
+// Supported prefill instantiations.
+bool prefill_supported(mala_dtype dt, int d, mala_tile t) {
+    if (dt == MALA_BF16) return d == 128 && t.bq == 128 && t.bk == 64;
+    if (dt == MALA_F32) return d == 64 && t.bq == 64 && t.bk == 64;
+    return false;
+}
+
+mala_status check_prefill(const void* q, const void* k, const void* v, int B, int H, int Hkv, int L, int d,
+                          mala_dtype dt, float tau, mala_tile tile) {
+    if (!q || !k || !v) return fail(MALA_ERR_INVALID_ARG, "null input pointer");
+    if (B <= 0 || H <= 0 || Hkv <= 0 || L <= 0 || d <= 0)
+        return fail(MALA_ERR_INVALID_ARG, "sizes must be positive (B=%d H=%d Hkv=%d L=%d d=%d)", B, H, Hkv, L, d);
+    if (tile.bq <= 0 || tile.bk <= 0) return fail(MALA_ERR_INVALID_ARG, "tile sizes must be positive");
+    if (!tau_ok(tau)) return fail(MALA_ERR_INVALID_ARG, "tau must be >= 0 (got %f)", double(tau));
+    if (dt != MALA_BF16 && dt != MALA_F32) return fail(MALA_ERR_INVALID_ARG, "unknown dtype %d", int(dt));
+    if (H != Hkv) return fail(MALA_ERR_UNSUPPORTED, "prefill needs H == Hkv (got %d, %d)", H, Hkv);
+    if (!prefill_supported(dt, d, tile))
+        return fail(MALA_ERR_UNSUPPORTED, "unsupported prefill instantiation dtype=%d d=%d tile=%dx%d", int(dt), d,
+                    tile.bq, tile.bk);
+    if ((long)B * H * L * d >= (1L << 40)) return fail(MALA_ERR_UNSUPPORTED, "tensor too large");
+    return MALA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mala_version(void) { return 100; }
+
+const char* mala_status_string(mala_status s) {
+    switch (s) {
+        case MALA_OK: return "ok";
+        case MALA_ERR_INVALID_ARG: return "invalid argument";
+        case MALA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MALA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* mala_last_error(void) { return g_err; }
+
+mala_status mala_fwd(const void* q, const void* k, const void* v, int B, int H, int Hkv, int L, int d,
+                     mala_dtype dtype, float tau, mala_tile tile, float scale, void* o, float* lse,
+                     mala_stats* stats, void* stream) {
+    g_err[0] = 0;
+    mala_status st = check_prefill(q, k, v, B, H, Hkv, L, d, dtype, tau, tile);
+    if (st) return st;
+    if (!o || !lse) return fail(MALA_ERR_INVALID_ARG, "null output pointer");
+    mala::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.L = L; a.d = d;
+    a.nqb = int(cdiv(L, tile.bq));
+    a.ntiles = int(cdiv(L, tile.bk));
+    a.words = int(cdiv(a.ntiles, 32));
+    const float sc = eff_scale(scale, d);
+    a.scale_log2 = sc * mala::kLog2e;
+    a.log2_tau = log2_tau_of(tau);
+    a.gated = tau != 0.f;
+    if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = dtype == MALA_BF16 ? mala::launch_fwd_bf16(a, s) : mala::launch_simple_fwd_f32(a, s);
+    return hip_status(e, "mala_fwd launch");
+}
+
+size_t mala_bwd_workspace_size(int B, int H, int L, int d, mala_dtype dtype, mala_tile tile) {
+    (void)d; (void)dtype; (void)tile;
+    if (B <= 0 || H <= 0 || L <= 0) return 0;
+    return 3 * align256(size_t(B) * H * L * sizeof(float));
+}
+
+mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     int B, int H, int Hkv, int L, int d, mala_dtype dtype, float tau, mala_tile tile, float scale,
+                     void* dq, void* dk, void* dv, mala_stats* stats, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    g_err[0] = 0;
+    mala_status st = check_prefill(q, k, v, B, H, Hkv, L, d, dtype, tau, tile);
+    if (st) return st;
+    if (!o || !lse || !dout) return fail(MALA_ERR_INVALID_ARG, "null forward-state or dout pointer");
+    if (!dq || !dk || !dv) return fail(MALA_ERR_INVALID_ARG, "null gradient pointer");
+    const size_t need = mala_bwd_workspace_size(B, H, L, d, dtype, tile);
+    if (!workspace || workspace_bytes < need)
+        return fail(MALA_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(MALA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    mala::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    const size_t rows = size_t(B) * H * L;
+    char* ws = static_cast<char*>(workspace);
+    a.Dv = reinterpret_cast<float*>(ws);
+    a.lse2 = reinterpret_cast<float*>(ws + align256(rows * 4));
+    a.thr = reinterpret_cast<float*>(ws + 2 * align256(rows * 4));
+    a.B = B; a.H = H; a.L = L; a.d = d;
+    a.nqb = int(cdiv(L, tile.bq));
+    a.ntiles = int(cdiv(L, tile.bk));
+    a.words = int(cdiv(a.ntiles, 32));
+    a.scale = eff_scale(scale, d);
+    a.scale_log2 = a.scale * mala::kLog2e;
+    a.log2_tau = log2_tau_of(tau);
+    a.gated = tau != 0.f;
+    a.f32 = dtype == MALA_F32;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (stats) {
+        a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits;
+        a.aux_bits = stats->keep_bits_dkdv;
+        if (a.aux_bits) {  // the dK/dV pass ORs its decisions in
+            hipError_t e0 = hipMemsetAsync(a.aux_bits, 0, size_t(B) * H * a.nqb * a.words * sizeof(uint32_t), s);
+            if (e0 != hipSuccess) return hip_status(e0, "mala_bwd stats clear");
+        }
+    }
+    hipError_t e = mala::launch_bwd_prep(a, s);
+    if (e != hipSuccess) return hip_status(e, "mala_bwd prep launch");
+    e = a.f32 ? mala::launch_simple_bwd_f32(a, s) : mala::launch_bwd_bf16(a, s);
+    return hip_status(e, "mala_bwd launch");
+}
+
+size_t mala_decode_workspace_size(int B, int Hq, int Hkv, int Lk, int d, int split_keys) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || d <= 0 || split_keys <= 0) return 0;
+    const long nsplit = cdiv(Lk, split_keys);
+    return align256(size_t(B) * Hq * nsplit * (d + 2) * sizeof(float));
+}
+
+mala_status mala_decode(const void* q, const void* kcache, const void* vcache, int B, int Hq, int Hkv, int Lk,
+                        int Lcap, int d, mala_dtype dtype, float tau, int split_keys, int bk, float scale, void* o,
+                        float* lse, mala_stats* stats, void* workspace, size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q || !kcache || !vcache || !o) return fail(MALA_ERR_INVALID_ARG, "null pointer");
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || d <= 0 || split_keys <= 0 || bk <= 0)
+        return fail(MALA_ERR_INVALID_ARG, "sizes must be positive");
+    if (Lcap < Lk) return fail(MALA_ERR_INVALID_ARG, "Lcap (%d) < Lk (%d)", Lcap, Lk);
+    if (!tau_ok(tau)) return fail(MALA_ERR_INVALID_ARG, "tau must be >= 0 (got %f)", double(tau));
+    if (dtype != MALA_BF16 && dtype != MALA_F32) return fail(MALA_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
+    if (Hq % Hkv) return fail(MALA_ERR_INVALID_ARG, "Hq (%d) not a multiple of Hkv (%d)", Hq, Hkv);
+    const int G = Hq / Hkv;
+    if (dtype != MALA_BF16 || d != 128 || bk != 64 || G > 8 || split_keys % bk)
+        return fail(MALA_ERR_UNSUPPORTED, "unsupported decode instantiation dtype=%d d=%d bk=%d G=%d split=%d",
+                    int(dtype), d, bk, G, split_keys);
+    const size_t need = mala_decode_workspace_size(B, Hq, Hkv, Lk, d, split_keys);
+    if (!workspace || workspace_bytes < need)
+        return fail(MALA_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(MALA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+    mala::DecArgs a{};
+    a.q = q; a.kc = kcache; a.vc = vcache; a.o = o; a.lse = lse;
+    a.part = static_cast<float*>(workspace);
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.Lk = Lk; a.Lcap = Lcap; a.d = d;
+    a.split_keys = split_keys; a.bk = bk;
+    a.nsplit = int(cdiv(Lk, split_keys));
+    a.tps = split_keys / bk;
+    a.words = int(cdiv(a.tps, 32));
+    const float sc = eff_scale(scale, d);
+    a.scale_log2 = sc * mala::kLog2e;
+    a.log2_tau = log2_tau_of(tau);
+    a.log2_lq = log2f(float(Lk));
+    a.gated = tau != 0.f;
+    if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; }
+    return hip_status(mala::launch_decode_bf16(a, reinterpret_cast<hipStream_t>(stream)), "mala_decode launch");
+}
+
+}  // extern "C"

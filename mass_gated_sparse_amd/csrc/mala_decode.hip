@@ -1,0 +1,277 @@
+// MALA split-KV decode, bf16 KV cache, head dim 128, 64-key tiles.
+//
+// Source: "MassAlloc Attention: Let Attention Allocate Its Own Compute"
+// (agihunt.info digest).  Threshold paragraph: the same tau and the same
+// per-tile test serve decoding; Lq of the new token is the number of cached
+// keys it sees (Lk).  Forward paragraph: tiles are visited from the most
+// recent keys back with a running normalizer and the first visited tile is
+// kept.  Savings and limitations paragraphs: the KV cache is read in full for
+// QK; a skipped tile saves its V read, so decode is bound by cache traffic.
+//
+// One workgroup (4 waves) per (sequence, KV head, partition).  The G query
+// heads sharing the KV head are the rows of the vote: they share every K/V
+// tile load, so a skipped tile really saves the V bytes.  The kernel is
+// HBM-bound: K tiles are prefetched one tile ahead into registers; V is read
+// only for kept tiles.
+//
+// Thread mapping.  Scores: thread t handles key t/4 of the tile and a
+// 32-element quarter of d (four 16-byte loads), bf16 dot2 products in fp32,
+// summed over the 4 quarters with lane shuffles.  PV: thread t handles an
+// 8-element d chunk (t%16) of keys 16*wave + 4*i + (t/16)%4, i = 0..3; its
+// fp32 accumulators are summed over the 16 key subsets once per partition.
+// Partial states (m2 = running max of s*log2(e), l, acc[d]) are written per
+// (sequence, query head, partition) and merged exactly by the combine kernel.
+#include <float.h>
+
+#include "mala_kernels.hpp"
+
+namespace mala {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int G, bool GATED, bool STATS>
+__global__ __launch_bounds__(256) void decode_split_bf16_d128(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    float* __restrict__ part, int Hq, int Hkv, int Lk, int Lcap, int split_keys, int nsplit, int tps, int words,
+    float scale_log2, float log2_tau, float log2_lq, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
+    uint32_t* __restrict__ bits) {
+    constexpr int D = 128, BK = 64;
+    __shared__ int vote_sm[2][4];
+    __shared__ float wmax_sm[4][G];
+    __shared__ float wsum_sm[4][G];
+    __shared__ float p_sm[G][BK];
+    __shared__ float red_sm[G][16][D + 4];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int p = blockIdx.x;
+    const int bg = blockIdx.y;  // b * Hkv + g
+    const int b = bg / Hkv, g = bg % Hkv;
+    const long kvbase = long(bg) * Lcap * D;
+    const int k0 = p * split_keys;
+    const int k1 = min(k0 + split_keys, Lk);
+    const int nt = (k1 - k0 + BK - 1) / BK;
+
+    // score mapping
+    const int skey = tid >> 2, quarter = tid & 3;
+    uint32_t qr[G][16];
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+        const bf16_t* qrow = q + (long(b) * Hq + g * G + r) * D + 32 * quarter;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
+            qr[r][4 * c + 0] = x[0]; qr[r][4 * c + 1] = x[1]; qr[r][4 * c + 2] = x[2]; qr[r][4 * c + 3] = x[3];
+        }
+    }
+    // PV mapping
+    const int dch = tid & 15, ksub = (tid >> 4) & 3;
+    float acc[G][8];
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
+    float m2[G], lsum[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) { m2[r] = -INFINITY; lsum[r] = 0.f; }
+
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    u32x4 kr[4];
+    auto load_k = [&](int t) {
+        const int key = k0 + t * BK + skey;
+        const bf16_t* src = kc + kvbase + long(key) * D + 32 * quarter;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kr[c] = key < k1 ? *reinterpret_cast<const u32x4*>(src + 8 * c) : z4;
+    };
+
+    int nkept = 0;
+    uint32_t word = 0;
+    if (STATS && bits && tid == 0)
+        for (int w = ((nt - 1) >> 5) + 1; w < words; ++w) bits[(long(bg) * nsplit + p) * words + w] = 0u;
+
+    load_k(nt - 1);
+    for (int t = nt - 1; t >= 0; --t) {
+        const int par = t & 1;
+        u32x4 kcur[4] = {kr[0], kr[1], kr[2], kr[3]};
+        if (t > 0) load_k(t - 1);
+        const int key = k0 + t * BK + skey;
+        const bool kvalid = key < k1;
+        float s[G];
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            float a = 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                a = dot2(qr[r][4 * c + 0], kcur[c][0], a);
+                a = dot2(qr[r][4 * c + 1], kcur[c][1], a);
+                a = dot2(qr[r][4 * c + 2], kcur[c][2], a);
+                a = dot2(qr[r][4 * c + 3], kcur[c][3], a);
+            }
+            a += __shfl_xor(a, 1, 64);
+            a += __shfl_xor(a, 2, 64);
+            s[r] = kvalid ? a : -INFINITY;
+        }
+
+        bool keep = true;
+        if (GATED) {
+            bool vote = false;
+#pragma unroll
+            for (int r = 0; r < G; ++r) {
+                const float thr = (lsum[r] == 0.f) ? -FLT_MAX
+                                                   : (m2[r] + fast_log2(lsum[r]) + log2_tau - log2_lq) / scale_log2;
+                vote |= s[r] >= thr;
+            }
+            const bool wv = wave_any(vote);
+            if (lane == 0) vote_sm[par][wave] = wv ? 1 : 0;
+            __syncthreads();
+            keep = (vote_sm[par][0] | vote_sm[par][1] | vote_sm[par][2] | vote_sm[par][3]) != 0;
+        }
+        if (STATS && tid == 0) {
+            nkept += keep;
+            if (keep) word |= 1u << (t & 31);
+            if (bits && (t & 31) == 0) {
+                bits[(long(bg) * nsplit + p) * words + (t >> 5)] = word;
+                word = 0;
+            }
+        }
+        if (!keep) continue;
+
+        // V loads for this tile (consumed after the normalizer update)
+        u32x4 vr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int vk = k0 + t * BK + 16 * wave + 4 * i + ksub;
+            vr[i] = vk < k1 ? *reinterpret_cast<const u32x4*>(vc + kvbase + long(vk) * D + 8 * dch) : z4;
+        }
+        // running max over the tile's 64 keys, per row
+        float mx[G];
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            float x = s[r];
+#pragma unroll
+            for (int m = 4; m <= 32; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+            mx[r] = x;
+        }
+        if (lane == 0)
+#pragma unroll
+            for (int r = 0; r < G; ++r) wmax_sm[wave][r] = mx[r];
+        __syncthreads();
+        float mref[G], alpha[G];
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            const float tm = fmaxf(fmaxf(wmax_sm[0][r], wmax_sm[1][r]), fmaxf(wmax_sm[2][r], wmax_sm[3][r]));
+            const float mn = fmaxf(m2[r], tm * scale_log2);
+            mref[r] = mn;  // finite: every tile holds at least one valid key
+            alpha[r] = fast_exp2(m2[r] - mn);
+            m2[r] = mn;
+            const float pv = fast_exp2(fmaf(s[r], scale_log2, -mn));  // -inf (invalid key) gives 0
+            float ps = (quarter == 0) ? pv : 0.f;
+#pragma unroll
+            for (int m = 4; m <= 32; m <<= 1) ps += __shfl_xor(ps, m, 64);
+            if (quarter == 0) p_sm[r][skey] = pv;
+            if (lane == 0) wsum_sm[wave][r] = ps;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            lsum[r] = lsum[r] * alpha[r] + ((wsum_sm[0][r] + wsum_sm[1][r]) + (wsum_sm[2][r] + wsum_sm[3][r]));
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[r][c] *= alpha[r];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kk = 16 * wave + 4 * i + ksub;
+            float vf[8];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                vf[2 * c] = __uint_as_float(vr[i][c] << 16);
+                vf[2 * c + 1] = __uint_as_float(vr[i][c] & 0xffff0000u);
+            }
+#pragma unroll
+            for (int r = 0; r < G; ++r) {
+                const float pw = p_sm[r][kk];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(pw, vf[c], acc[r][c]);
+            }
+        }
+        (void)mref;
+        __syncthreads();  // p_sm / wmax_sm / wsum_sm are rewritten by the next kept tile
+    }
+
+    // sum the 16 key subsets of every d chunk, write the partial state
+#pragma unroll
+    for (int r = 0; r < G; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) red_sm[r][4 * wave + ksub][8 * dch + c] = acc[r][c];
+    __syncthreads();
+    for (int e = tid; e < G * D; e += 256) {
+        const int r = e / D, dd = e % D;
+        float x = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x += red_sm[r][u][dd];
+        float* dst = part + ((long(b) * Hq + g * G + r) * nsplit + p) * (D + 2);
+        dst[2 + dd] = x;
+        if (dd == 0) { dst[0] = m2[r]; dst[1] = lsum[r]; }
+    }
+    if (STATS && tid == 0) {
+        if (kept) kept[long(bg) * nsplit + p] = nkept;
+        if (legal) legal[long(bg) * nsplit + p] = nt;
+    }
+}
+
+// Exact merge of the partition states of every (sequence, query head).
+__global__ __launch_bounds__(128) void decode_combine_d128(const float* __restrict__ part, bf16_t* __restrict__ o,
+                                                           float* __restrict__ lse, int nsplit) {
+    constexpr int D = 128;
+    const long bh = blockIdx.x;
+    const int dd = threadIdx.x;
+    const float* src = part + bh * nsplit * (D + 2);
+    float M = -INFINITY;
+    for (int p = 0; p < nsplit; ++p) M = fmaxf(M, src[p * (D + 2)]);
+    float lam = 0.f, x = 0.f;
+    for (int p = 0; p < nsplit; ++p) {
+        const float w = fast_exp2(src[p * (D + 2)] - M);
+        lam = fmaf(src[p * (D + 2) + 1], w, lam);
+        x = fmaf(src[p * (D + 2) + 2 + dd], w, x);
+    }
+    o[bh * D + dd] = f32_to_bf16(x / lam);
+    if (lse && dd == 0) lse[bh] = (M + fast_log2(lam)) * kLn2;
+}
+
+template <int G>
+static void launch_decode_g(const DecArgs& a, hipStream_t s) {
+    dim3 grid(a.nsplit, a.B * a.Hkv), block(256);
+    const bool st = a.kept || a.legal || a.bits;
+#define MALA_DEC_LAUNCH(GT, ST)                                                                                    \
+    hipLaunchKernelGGL((decode_split_bf16_d128<G, GT, ST>), grid, block, 0, s, (const bf16_t*)a.q,                \
+                       (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.part, a.Hq, a.Hkv, a.Lk, a.Lcap, a.split_keys, \
+                       a.nsplit, a.tps, a.words, a.scale_log2, a.log2_tau, a.log2_lq, a.kept, a.legal, a.bits)
+    if (a.gated) {
+        if (st) MALA_DEC_LAUNCH(true, true);
+        else MALA_DEC_LAUNCH(true, false);
+    } else {
+        if (st) MALA_DEC_LAUNCH(false, true);
+        else MALA_DEC_LAUNCH(false, false);
+    }
+#undef MALA_DEC_LAUNCH
+}
+
+hipError_t launch_decode_bf16(const DecArgs& a, hipStream_t s) {
+    switch (a.G) {
+        case 1: launch_decode_g<1>(a, s); break;
+        case 2: launch_decode_g<2>(a, s); break;
+        case 4: launch_decode_g<4>(a, s); break;
+        case 8: launch_decode_g<8>(a, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_combine_d128, dim3(a.B * a.Hq), dim3(128), 0, s, a.part, (bf16_t*)a.o, a.lse,
+                       a.nsplit);
+    return hipGetLastError();
+}
+
+}  // namespace mala

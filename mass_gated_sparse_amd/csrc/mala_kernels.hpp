@@ -1,0 +1,59 @@
+// Launch descriptors shared by the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mala_device.hpp"
+
+namespace mala {
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void* o;
+    float* lse;
+    int B, H, L, d;
+    int nqb, ntiles, words;
+    float scale_log2;  // scale * log2(e)
+    float log2_tau;    // log2(tau); +inf for tau = +inf
+    bool gated;        // false for tau = 0
+    int32_t *kept, *legal;
+    uint32_t* bits;
+};
+
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float* lse;
+    void *dq, *dk, *dv;
+    float *Dv, *lse2, *thr;  // per-row workspace arrays [B, H, L]
+    int B, H, L, d;
+    int nqb, ntiles, words;
+    float scale, scale_log2, log2_tau;
+    bool gated, f32;
+    int32_t *kept, *legal;
+    uint32_t *bits, *aux_bits;  // aux_bits: decisions as seen by the dK/dV kernel (debug)
+};
+
+struct DecArgs {
+    const void *q, *kc, *vc;
+    void* o;
+    float* lse;
+    float* part;  // [B, Hq, nsplit, d + 2] fp32 partial states (m2, l, acc[d])
+    int B, Hq, Hkv, G, Lk, Lcap, d;
+    int split_keys, bk, nsplit, tps, words;
+    float scale_log2, log2_tau, log2_lq;
+    bool gated;
+    int32_t *kept, *legal;
+    uint32_t* bits;
+};
+
+hipError_t launch_simple_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t s);
+hipError_t launch_simple_bwd_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecArgs& a, hipStream_t s);
+
+}  // namespace mala

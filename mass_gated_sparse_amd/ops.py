@@ -1,0 +1,155 @@
+"""PyTorch-facing wrappers of the MALA C ABI (forward, backward, decode).
+
+Tensors must be contiguous CUDA (HIP) tensors of dtype bfloat16 or float32.
+Outputs and workspaces are allocated with torch (device memory plumbing);
+the work itself is queued by libmala.so on torch's current stream.
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import MALA_BF16, MALA_F32, Stats, Tile
+
+DEFAULT_TILE = {torch.bfloat16: (128, 64), torch.float32: (64, 64)}
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return MALA_BF16
+    if t.dtype == torch.float32:
+        return MALA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("MALA tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("MALA tensors must be contiguous")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def prefill_stats_buffers(B, H, L, tile, device, dkdv=False):
+    bq, bk = tile
+    nqb, nt = -(-L // bq), -(-L // bk)
+    words = -(-nt // 32)
+    st = {"kept": torch.zeros(B, H, nqb, dtype=torch.int32, device=device),
+          "legal": torch.zeros(B, H, nqb, dtype=torch.int32, device=device),
+          "keep_bits": torch.zeros(B, H, nqb, words, dtype=torch.int32, device=device)}
+    if dkdv:
+        st["keep_bits_dkdv"] = torch.zeros(B, H, nqb, words, dtype=torch.int32, device=device)
+    return st
+
+
+def _stats_struct(st):
+    if st is None:
+        return None
+    return ctypes.byref(Stats(*(ctypes.c_void_p(st[n].data_ptr()) if n in st else None
+                                for n in ("kept", "legal", "keep_bits", "keep_bits_dkdv"))))
+
+
+def fwd_into(q, k, v, o, lse, tau, tile=None, scale=0.0, stats=None, stream=None):
+    """Queue mala_fwd writing into preallocated o [B,H,L,d] and lse [B,H,L] (fp32)."""
+    B, H, L, d = q.shape
+    tile = tile or DEFAULT_TILE[q.dtype]
+    rc = _lib.load().mala_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, k.shape[1], L, d, _dt(q), float(tau), Tile(*tile),
+                              float(scale), _ptr(o), _ptr(lse), _stats_struct(stats), _stream(stream))
+    _lib.check("mala_fwd", rc)
+
+
+def fwd(q, k, v, tau, tile=None, scale=0.0, stats=False):
+    """MALA forward.  Returns (o, lse) or (o, lse, stats dict)."""
+    _check_dev(q, k, v)
+    B, H, L, d = q.shape
+    tile = tile or DEFAULT_TILE[q.dtype]
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device)
+    st = prefill_stats_buffers(B, H, L, tile, q.device) if stats else None
+    fwd_into(q, k, v, o, lse, tau, tile, scale, st)
+    return (o, lse, st) if stats else (o, lse)
+
+
+def bwd_workspace(q, tile=None):
+    B, H, L, d = q.shape
+    tile = tile or DEFAULT_TILE[q.dtype]
+    n = _lib.load().mala_bwd_workspace_size(B, H, L, d, _dt(q), Tile(*tile))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile=None, scale=0.0, stats=None, stream=None):
+    B, H, L, d = q.shape
+    tile = tile or DEFAULT_TILE[q.dtype]
+    rc = _lib.load().mala_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), B, H, k.shape[1], L, d,
+                              _dt(q), float(tau), Tile(*tile), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                              _stats_struct(stats), _ptr(ws), ws.numel(), _stream(stream))
+    _lib.check("mala_bwd", rc)
+
+
+def bwd(q, k, v, o, lse, do, tau, tile=None, scale=0.0, stats=False):
+    """MALA backward against forward state (o, lse).  Returns (dq, dk, dv[, stats])."""
+    _check_dev(q, k, v, o, lse, do)
+    B, H, L, d = q.shape
+    tile = tile or DEFAULT_TILE[q.dtype]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = bwd_workspace(q, tile)
+    st = prefill_stats_buffers(B, H, L, tile, q.device, dkdv=True) if stats else None
+    bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile, scale, st)
+    return (dq, dk, dv, st) if stats else (dq, dk, dv)
+
+
+def decode_stats_buffers(B, Hkv, Lk, split_keys, bk, device):
+    nsplit = -(-Lk // split_keys)
+    words = -(-(split_keys // bk) // 32)
+    return {"kept": torch.zeros(B, Hkv, nsplit, dtype=torch.int32, device=device),
+            "legal": torch.zeros(B, Hkv, nsplit, dtype=torch.int32, device=device),
+            "keep_bits": torch.zeros(B, Hkv, nsplit, words, dtype=torch.int32, device=device)}
+
+
+def decode_workspace(B, Hq, Hkv, Lk, d, split_keys, device):
+    n = _lib.load().mala_decode_workspace_size(B, Hq, Hkv, Lk, d, split_keys)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys=4096, bk=64, scale=0.0, stats=None, stream=None):
+    B, Hq, d = q.shape
+    _, Hkv, Lcap, _ = kc.shape
+    rc = _lib.load().mala_decode(_ptr(q), _ptr(kc), _ptr(vc), B, Hq, Hkv, int(Lk), Lcap, d, _dt(q), float(tau),
+                                 int(split_keys), int(bk), float(scale), _ptr(o), _ptr(lse), _stats_struct(stats),
+                                 _ptr(ws), ws.numel(), _stream(stream))
+    _lib.check("mala_decode", rc)
+
+
+def decode(q, kc, vc, Lk, tau, split_keys=4096, bk=64, scale=0.0, stats=False):
+    """Split-KV MALA decode.  q [B,Hq,d], caches [B,Hkv,Lcap,d].  Returns (o, lse[, stats])."""
+    _check_dev(q, kc, vc)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[1]
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    ws = decode_workspace(B, Hq, Hkv, Lk, d, split_keys, q.device)
+    st = decode_stats_buffers(B, Hkv, Lk, split_keys, bk, q.device) if stats else None
+    decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys, bk, scale, st)
+    return (o, lse, st) if stats else (o, lse)
+
+
+def bits_to_keep(bits, ntiles):
+    """Unpack int32 keep-bit words [..., words] to a uint8 array [..., ntiles] (numpy)."""
+    import numpy as np
+    b = bits.cpu().numpy().astype(np.uint32)
+    idx = np.arange(ntiles)
+    return ((b[..., idx // 32] >> (idx % 32).astype(np.uint32)) & 1).astype(np.uint8)
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

@@ -84,6 +84,15 @@ def _normal_rows(w: Workload, tensor: int, b: int, h: int, n: int) -> np.ndarray
     return _rng(w.seed, tensor, b, h).standard_normal((n, w.d))
 
 
+def _sink(kf: np.ndarray) -> np.ndarray:
+    """Mean of the first four keys (of all keys when fewer exist)."""
+    n = min(4, kf.shape[0])
+    acc = kf[0].copy()
+    for r in range(1, n):
+        acc = acc + kf[r]
+    return acc / n
+
+
 def planted_query(w: Workload, b: int, h: int, kf: np.ndarray, positions: np.ndarray) -> np.ndarray:
     """fp64 planted queries for query head h at the given positions.
 
@@ -99,7 +108,7 @@ def planted_query(w: Workload, b: int, h: int, kf: np.ndarray, positions: np.nda
     ridx = _rng(w.seed, _RIDX, b, h).integers(0, hi, size=(n, 4))
     c = sharpness(w, b, h)
     i = positions.astype(np.int64)
-    sink = (kf[0] + kf[1] + kf[2] + kf[3]) / 4.0
+    sink = _sink(kf)
     local = kf[np.maximum(i - delta[i], 0)]
     r = ridx[i]
     retr = (kf[r[:, 0]] + kf[r[:, 1]] + kf[r[:, 2]] + kf[r[:, 3]]) / 4.0
@@ -113,7 +122,7 @@ def _decode_query(w: Workload, b: int, h: int, kf: np.ndarray, i: int) -> np.nda
     delta = int(_rng(w.seed, _DELTA, b, h).integers(0, 32))
     ridx = _rng(w.seed, _RIDX, b, h).integers(0, i + 1, size=4)
     c = sharpness(w, b, h)
-    return c * (0.3 * z + 2.0 * (kf[0] + kf[1] + kf[2] + kf[3]) / 4.0 + 1.5 * kf[max(i - delta, 0)] + 2.5 * (kf[ridx[0]] + kf[ridx[1]] + kf[ridx[2]] + kf[ridx[3]]) / 4.0)
+    return c * (0.3 * z + 2.0 * _sink(kf) + 1.5 * kf[max(i - delta, 0)] + 2.5 * (kf[ridx[0]] + kf[ridx[1]] + kf[ridx[2]] + kf[ridx[3]]) / 4.0)
 
 
 def prefill_inputs(w: Workload, family: str = "planted", L: int = None, heads=None):

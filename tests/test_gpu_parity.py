@@ -1,0 +1,168 @@
+"""GPU parity: libmala.so (through its C ABI) against the fp64 CPU oracle.
+
+Inputs are seeded instances of the named workloads (synth); the oracle runs
+on exactly the values the GPU received.  Forward/decode decisions must match
+tile for tile outside the |T-1| <= 1e-4 band (the oracle replays the GPU's
+decisions inside it); backward decisions must match tile for tile given the
+GPU's own O and lse; O within rel-L2 5e-3, gradients within 1e-2.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS, prefill_inputs, decode_inputs, to_f64
+from tests.parity import (BAND, TOL_GRAD, TOL_O, bf16_to_f64, decision_report, legal_mask, rel_l2)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _dev_tensors(x, dtype, names):
+    out = []
+    for n in names:
+        a = x[n]
+        if dtype == "bf16":
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(a)
+        out.append(t.cuda().contiguous())
+    return out
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mass_gated_sparse_amd import ops as _ops
+    return _ops
+
+
+def _prefill_case(name, L, heads, family="planted"):
+    w = WORKLOADS[name]
+    x = prefill_inputs(w, family=family, L=L, heads=heads)
+    for n in x:
+        x[n] = np.ascontiguousarray(x[n][:, list(heads)])
+    return w, x
+
+
+def _check_fwd(ops, w, x, tau, bq, bk):
+    q, k, v = _dev_tensors(x, w.dtype, ("q", "k", "v"))
+    o, lse, st = ops.fwd(q, k, v, tau, tile=(bq, bk), stats=True)
+    torch.cuda.synchronize()
+    B, H, L, d = q.shape
+    nt = -(-L // bk)
+    gk = ops.bits_to_keep(st["keep_bits"], nt)
+    qf, kf, vf = (to_f64(x[n], w.dtype) for n in ("q", "k", "v"))
+    oo, ol, ok, oT = oracle.fwd(qf, kf, vf, tau, bq, bk, replay=gk, band=BAND)
+    legal = legal_mask(L, bq, bk)
+    bad, near, near_list = decision_report(gk, ok, oT, legal)
+    assert bad == 0, f"forward decisions differ outside the band on {bad} tiles"
+    kept = st["kept"].cpu().numpy()
+    assert (kept == (gk * legal).sum(-1)).all()
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)[None, None, :]).all()
+    e_o = rel_l2(bf16_to_f64(o), oo)
+    e_l = float(np.abs(lse.cpu().numpy() - ol).max())
+    assert e_o <= TOL_O, e_o
+    assert e_l <= 1e-3, e_l
+    return dict(o=o, lse=lse, keep=gk, T=oT, near=near, err_o=e_o, legal=legal)
+
+
+@pytest.mark.parametrize("tau", [0.0, 1.0, 4.0, 16.0, math.inf])
+def test_fwd_f32_tiny(ops, tau):
+    w, x = _prefill_case("tiny", None, range(2))
+    r = _check_fwd(ops, w, x, tau, 64, 64)
+    assert r["err_o"] < 1e-5
+
+
+@pytest.mark.parametrize("L,heads", [(1000, (0, 2, 5)), (2048, (1, 3, 6, 9))])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 4.0, math.inf])
+def test_fwd_bf16(ops, L, heads, tau):
+    w, x = _prefill_case("mw8k", L, heads)
+    r = _check_fwd(ops, w, x, tau, 128, 64)
+    if tau == 4.0:
+        assert (r["keep"][..., r["legal"]] == 0).any()  # gating exercised
+
+
+def _check_bwd(ops, w, x, tau, bq, bk):
+    q, k, v, do = _dev_tensors(x, w.dtype, ("q", "k", "v", "do"))
+    o, lse = ops.fwd(q, k, v, tau, tile=(bq, bk))
+    dq, dk, dv, st = ops.bwd(q, k, v, o, lse, do, tau, tile=(bq, bk), stats=True)
+    torch.cuda.synchronize()
+    B, H, L, d = q.shape
+    nt = -(-L // bk)
+    gk = ops.bits_to_keep(st["keep_bits"], nt)
+    gk2 = ops.bits_to_keep(st["keep_bits_dkdv"], nt)
+    legal = legal_mask(L, bq, bk)
+    assert (gk[..., legal] == gk2[..., legal]).all(), "dQ and dK/dV passes disagree"
+    qf, kf, vf, dof = (to_f64(x[n], w.dtype) for n in ("q", "k", "v", "do"))
+    of, lf = bf16_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    gq, gkk, gv, ok, oT = oracle.bwd(qf, kf, vf, of, lf, dof, tau, bq, bk, replay=gk, band=BAND)
+    bad, near, near_list = decision_report(gk, ok, oT, legal)
+    assert bad == 0, f"backward decisions differ on {bad} tiles"
+    assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+    errs = [rel_l2(bf16_to_f64(a), b) for a, b in ((dq, gq), (dk, gkk), (dv, gv))]
+    if tau == math.inf:
+        assert all(float(t.abs().max()) == 0.0 for t in (dq, dk, dv))
+    else:
+        assert max(errs) <= TOL_GRAD, errs
+    return dict(keep=gk, errs=errs, near=near)
+
+
+@pytest.mark.parametrize("tau", [0.0, 1.0, 16.0, math.inf])
+def test_bwd_f32_tiny(ops, tau):
+    w, x = _prefill_case("tiny", None, range(2))
+    r = _check_bwd(ops, w, x, tau, 64, 64)
+    if tau not in (math.inf,):
+        assert max(r["errs"]) < 1e-5
+
+
+@pytest.mark.parametrize("L,heads", [(1000, (0, 2, 5)), (2048, (1, 3))])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 4.0, math.inf])
+def test_bwd_bf16(ops, L, heads, tau):
+    w, x = _prefill_case("mw8k", L, heads)
+    _check_bwd(ops, w, x, tau, 128, 64)
+
+
+def _decode_case(Lk, batches, Lcap=None):
+    w = WORKLOADS["decode128k"]
+    x = decode_inputs(w, Lk=Lk, Lcap=Lcap, batches=batches)
+    for n in x:
+        x[n] = np.ascontiguousarray(x[n][list(batches)])
+    return w, x
+
+
+@pytest.mark.parametrize("Lk,split,Lcap", [(3000, 1024, None), (4097, 4096, 4200), (64, 4096, None), (1, 64, 100)])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 16.0, math.inf])
+def test_decode_bf16(ops, Lk, split, Lcap, tau):
+    w, x = _decode_case(Lk, (0, 1), Lcap)
+    q, kc, vc = _dev_tensors(x, "bf16", ("q", "k", "v"))
+    o, lse, st = ops.decode(q, kc, vc, Lk, tau, split_keys=split, bk=64, stats=True)
+    torch.cuda.synchronize()
+    tps = split // 64
+    gk = ops.bits_to_keep(st["keep_bits"], tps)  # [B, Hkv, nsplit, tps]
+    qf, kf, vf = (to_f64(x[n], "bf16") for n in ("q", "k", "v"))
+    oo, ol, ok, oT = oracle.decode(qf, kf, vf, Lk, tau, split, 64, replay=gk[:, :, None], band=BAND)
+    nsplit = -(-Lk // split)
+    legal = np.zeros((nsplit, tps), bool)
+    for p in range(nsplit):
+        legal[p, : -(-(min((p + 1) * split, Lk) - p * split) // 64)] = True
+    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal)
+    assert bad == 0
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+    assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
+    assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+
+
+def test_invalid_arguments_rejected(ops):
+    from mass_gated_sparse_amd._lib import MalaError
+    q = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(MalaError):
+        ops.fwd(q, q, q, -1.0)
+    with pytest.raises(MalaError):
+        ops.fwd(q, q, q, float("nan"))
+    q64 = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(MalaError) as e:
+        ops.fwd(q64, q64, q64, 1.0)
+    assert e.value.status == -2
