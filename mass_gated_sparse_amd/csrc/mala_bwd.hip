@@ -1,11 +1,470 @@
-// MALA backward, bf16 inputs, head dim 128 (MFMA kernels).
+// MALA backward, bf16 inputs, head dim 128, 128x64 tiles, on gfx950 MFMA.
+//
+// Source: "MassAlloc Attention: Let Attention Allocate Its Own Compute"
+// (agihunt.info digest).  Backward paragraph: backward tests every legal tile
+// against the FINAL log-normalizer written by forward (no stored mask, no
+// replay of partial sums); the kept set is nested in forward's.  Motivation
+// paragraph: backward post-score work is probability reconstruction plus dP,
+// dS, dQ, dK and dV -- all of it is skipped for a skipped tile.
+//
+// Per tile (query block of 128 rows, key tile of 64 keys) the tile is kept
+// iff some row i has a visible key j with s_ij - lse_i >= ln(tau) - ln(i+1),
+// i.e. P_ij >= tau/Lq_i.  With thr_i = (lse_i*log2e + log2 tau - log2(i+1)) /
+// (scale*log2e), computed once per row by bwd_prep, that is raw <q_i,k_j> >=
+// thr_i.  Kept tiles:  P = exp(s - lse), dP = dO V^T, dS = P (dP - D),
+// dV += P^T dO, dK += scale dS^T Q, dQ += scale dS K.
+//
+// Two kernels share the work and take the SAME decisions without exchanging
+// any mask:
+//   dQ pass   -- one workgroup per query block (4 waves x 32 rows), scores
+//                S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K, B = Q);
+//   dK/dV pass -- one workgroup per 128 keys (4 waves x 32 keys, i.e. two
+//                key tiles), scores S = Q K^T with the same instruction and
+//                the same k-step order (A = Q, B = K).
+// MFMA computes each output element as the same ordered sum over k whichever
+// operand holds which matrix, so both passes see bit-identical raw scores and
+// compare them with the same per-row threshold.
+//
+// Transposed operands (K^T for dQ, Q^T and dO^T for dK/dV) are read from the
+// row-major LDS tiles with ds_read_b64_tr_b16: within each 16-lane group the
+// 16 lanes read a 16x4 block M (one 8-byte row each) and lane i receives
+// M[i/4 + 4e][i%4], e = 0..3 -- four consecutive rows at one column.
+#include <float.h>
+
 #include "mala_kernels.hpp"
 
 namespace mala {
 
+namespace bwdk {
+constexpr int BQ = 128, BK = 64, D = 128;
+// row-major 128-element bf16 rows (256 B) with 16-byte chunks XOR-swizzled by row
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+// byte offset of element (row, d) in a swizzled tile
+__device__ __forceinline__ int swz_el(int row, int d) { return swz(row, d >> 3) + ((d & 7) << 1); }
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ u32x2 tr16(const uint8_t* lds_base, int byte_off) {
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    lds_bf16x4* p = (lds_bf16x4*)((lds_u8*)const_cast<uint8_t*>(lds_base) + byte_off);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
+}
+
+// A-operand (8 rows r0+{0..3}, r0+8+{0..3} at column d = 32db + lane%32) of a
+// "transposed" product, read from a swizzled row-major tile.  r0 is the base
+// row for the calling lane's half (callers pass rowbase + 4*hl).
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int rowbase, int db, int lane) {
+    const int g = lane >> 4, i = lane & 15, a = i & 3, es = i >> 2;
+    const int hl = g >> 1, dh = g & 1;
+    const int d = 32 * db + 16 * dh + 4 * a;
+    const int r = rowbase + 4 * hl + es;
+    const u32x2 lo = tr16(tile, swz_el(r, d));
+    const u32x2 hi = tr16(tile, swz_el(r + 8, d));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+}  // namespace bwdk
+
+// ------------------------------------------------------------------------- dQ
+template <bool GATED, bool STATS>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
+    const float* __restrict__ thr, bf16_t* __restrict__ dq, int BH, int L, int nqb, int words, float scale,
+    float scale_log2, int32_t* __restrict__ kept, int32_t* __restrict__ legal, uint32_t* __restrict__ bits) {
+    using namespace bwdk;
+    __shared__ __attribute__((aligned(16))) uint8_t ksm2[2][BK * 256];  // K tile t in ksm2[t & 1]
+    __shared__ __attribute__((aligned(16))) uint8_t vsm[BK * 256];
+    __shared__ int vote_sm[4];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
+    const int qb = nqb - 1 - int(blockIdx.x) / BH;
+    const int bh = int(blockIdx.x) % BH;
+    const long hoff = long(bh) * L * D;
+    const bf16_t* kh = k + hoff;
+    const bf16_t* vh = v + hoff;
+    const int row = qb * BQ + wave * 32 + j;
+    const bool rvalid = row < L;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    u32x4 qf[8], of[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        qf[s] = rvalid ? *reinterpret_cast<const u32x4*>(q + hoff + long(row) * D + 16 * s + 8 * hl) : z4;
+        of[s] = rvalid ? *reinterpret_cast<const u32x4*>(dout + hoff + long(row) * D + 16 * s + 8 * hl) : z4;
+    }
+    const float th = rvalid ? thr[long(bh) * L + row] : INFINITY;
+    const float l2 = rvalid ? lse2[long(bh) * L + row] : INFINITY;
+    const float Di = rvalid ? Dv[long(bh) * L + row] : 0.f;
+
+    f32x16 gacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gacc[db][r] = 0.f;
+    const int jmax = (min(qb * BQ + BQ, L) - 1) / BK;
+
+    u32x4 kreg[4];
+    auto load_k = [&](int t) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int jg = t * BK + it * 16 + (tid >> 4);
+            kreg[it] = (jg < L) ? *reinterpret_cast<const u32x4*>(kh + long(jg) * D + (tid & 15) * 8) : z4;
+        }
+    };
+
+    int nkept = 0;
+    uint32_t word = 0;
+    if (STATS && bits && tid == 0)
+        for (int w = (jmax >> 5) + 1; w < words; ++w) bits[(long(bh) * nqb + qb) * words + w] = 0u;
+
+    auto store_k = [&](uint8_t* dst) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) *reinterpret_cast<u32x4*>(dst + swz(it * 16 + (tid >> 4), tid & 15)) = kreg[it];
+    };
+
+    load_k(jmax);
+    store_k(ksm2[jmax & 1]);
+    __syncthreads();
+
+    for (int t = jmax; t >= 0; --t) {
+        uint8_t* ksm = ksm2[t & 1];
+        if (t > 0) load_k(t - 1);
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(ksm + swz(32 * kb + j, 2 * s + hl));
+                sacc[kb] = mfma32(a, qf[s], sacc[kb]);
+            }
+        }
+        const bool diag = t >= 2 * qb;
+        bool keep = true;
+        if (GATED) {
+            bool vote = false;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t * BK + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    const bool vis = !diag || (key <= row && key < L);
+                    vote |= vis && sacc[kb][r] >= th;
+                }
+            const bool wv = wave_any(vote);
+            if (lane == 0) vote_sm[wave] = wv ? 1 : 0;
+        }
+        // Every wave has finished the previous iteration, so the other K buffer
+        // and the V buffer are free again.
+        __syncthreads();
+        if (GATED) keep = (vote_sm[0] | vote_sm[1] | vote_sm[2] | vote_sm[3]) != 0;
+        if (t > 0) store_k(ksm2[(t - 1) & 1]);
+        if (keep) {
+            // V tile (row-major, swizzled) for dP^T = V dO^T
+            u32x4 vreg[4];
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int jg = t * BK + it * 16 + (tid >> 4);
+                vreg[it] = (jg < L) ? *reinterpret_cast<const u32x4*>(vh + long(jg) * D + (tid & 15) * 8) : z4;
+            }
+            // P = exp(s - lse) (zero on invisible entries)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t * BK + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    const bool vis = !diag || (key <= row && key < L);
+                    sacc[kb][r] = vis ? fast_exp2(fmaf(sacc[kb][r], scale_log2, -l2)) : 0.f;
+                }
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                *reinterpret_cast<u32x4*>(vsm + swz(it * 16 + (tid >> 4), tid & 15)) = vreg[it];
+            __syncthreads();  // V tile and the next K tile are visible
+            // dP^T (keys x rows) = V dO^T
+            f32x16 pacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pacc[kb][r] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(vsm + swz(32 * kb + j, 2 * s + hl));
+                    pacc[kb] = mfma32(a, of[s], pacc[kb]);
+                }
+            }
+            // dS^T = P^T (dP^T - D) as bf16 B operands
+            u32x4 dsf[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r0 = 8 * hf + 2 * e;
+                        dsf[kb][hf][e] = pack_bf16x2(sacc[kb][r0] * (pacc[kb][r0] - Di),
+                                                     sacc[kb][r0 + 1] * (pacc[kb][r0 + 1] - Di));
+                    }
+            // dQ^T (d x rows) += K^T dS^T ; K^T read transposed from the K tile
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const u32x4 a = tr_operand(ksm, 32 * kb + 16 * hf, db, lane);
+                        gacc[db] = mfma32(a, dsf[kb][hf], gacc[db]);
+                    }
+        }
+        if (STATS && tid == 0) {
+            nkept += keep;
+            if (keep) word |= 1u << (t & 31);
+            if (bits && (t & 31) == 0) {
+                bits[(long(bh) * nqb + qb) * words + (t >> 5)] = word;
+                word = 0;
+            }
+        }
+        if (!keep) __syncthreads();  // the next K tile is visible
+    }
+    if (rvalid) {
+        bf16_t* grow = dq + hoff + long(row) * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 w;
+                w[0] = pack_bf16x2(gacc[db][4 * g + 0] * scale, gacc[db][4 * g + 1] * scale);
+                w[1] = pack_bf16x2(gacc[db][4 * g + 2] * scale, gacc[db][4 * g + 3] * scale);
+                *reinterpret_cast<u32x2*>(grow + 32 * db + 8 * g + 4 * hl) = w;
+            }
+    }
+    if (STATS && tid == 0) {
+        if (kept) kept[long(bh) * nqb + qb] = nkept;
+        if (legal) legal[long(bh) * nqb + qb] = jmax + 1;
+    }
+}
+
+// ---------------------------------------------------------------------- dK/dV
+template <bool GATED>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
+    const float* __restrict__ thr, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BH, int L, int nqb,
+    int ncol, int words, float scale, float scale_log2, uint32_t* __restrict__ aux_bits) {
+    using namespace bwdk;
+    __shared__ __attribute__((aligned(16))) uint8_t qsm[BQ * 256];
+    __shared__ __attribute__((aligned(16))) uint8_t osm[BQ * 256];
+    __shared__ __attribute__((aligned(16))) float thr_sm[BQ];
+    __shared__ __attribute__((aligned(16))) float l2_sm[BQ];
+    __shared__ __attribute__((aligned(16))) float d_sm[BQ];
+    __shared__ int vote_sm[4];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
+    const int c = int(blockIdx.x) / BH;  // 128-key column; longest (c = 0) first
+    const int bh = int(blockIdx.x) % BH;
+    const long hoff = long(bh) * L * D;
+    const int key = 128 * c + 32 * wave + j;
+    const bool kvalid = key < L;
+    const int tw = 2 * c + (wave >> 1);       // this wave's key tile
+    const bool tile_exists = tw * BK < L;
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    // K and V of this wave's 32 keys as B operands (lane = key, 8 contiguous d)
+    u32x4 kf[8], vf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(k + hoff + long(key) * D + 16 * s + 8 * hl) : z4;
+        vf[s] = kvalid ? *reinterpret_cast<const u32x4*>(v + hoff + long(key) * D + 16 * s + 8 * hl) : z4;
+    }
+    f32x16 dvacc[4], dkacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dvacc[db][r] = 0.f; dkacc[db][r] = 0.f; }
+
+    for (int qb = c; qb < nqb; ++qb) {
+        const int r0 = qb * BQ;
+        __syncthreads();  // previous block's LDS reads are done
+        // Q and dO tiles (row-major, swizzled) and per-row state
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int rr = it * 16 + (tid >> 4);
+            const bool ok = r0 + rr < L;
+            const long go = hoff + long(r0 + rr) * D + (tid & 15) * 8;
+            const u32x4 xq = ok ? *reinterpret_cast<const u32x4*>(q + go) : z4;
+            const u32x4 xo = ok ? *reinterpret_cast<const u32x4*>(dout + go) : z4;
+            *reinterpret_cast<u32x4*>(qsm + swz(rr, tid & 15)) = xq;
+            *reinterpret_cast<u32x4*>(osm + swz(rr, tid & 15)) = xo;
+        }
+        if (tid < BQ) {
+            const bool ok = r0 + tid < L;
+            const long ri = long(bh) * L + r0 + tid;
+            thr_sm[tid] = ok ? thr[ri] : INFINITY;
+            l2_sm[tid] = ok ? lse2[ri] : INFINITY;
+            d_sm[tid] = ok ? Dv[ri] : 0.f;
+        }
+        __syncthreads();
+
+        // S (rows x keys) = Q K^T: 4 row blocks of 32, 8 k-steps
+        f32x16 sacc[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(qsm + swz(32 * rb + j, 2 * s + hl));
+                sacc[rb] = mfma32(a, kf[s], sacc[rb]);
+            }
+        }
+        const bool diag = qb == c;
+        bool keep = tile_exists;
+        if (GATED) {
+            bool vote = false;
+            if (tile_exists) {
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int rl = 32 * rb + 8 * g + 4 * hl;  // 4 consecutive rows
+                        const f32x4 th = *reinterpret_cast<const f32x4*>(thr_sm + rl);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            const int rowg = r0 + rl + x;
+                            const bool vis = kvalid && (!diag || key <= rowg);
+                            vote |= vis && sacc[rb][4 * g + x] >= th[x];
+                        }
+                    }
+            }
+            const bool wv = wave_any(vote);
+            if (lane == 0) vote_sm[wave] = wv ? 1 : 0;
+            __syncthreads();
+            const int pair = wave >> 1;
+            keep = tile_exists && (vote_sm[2 * pair] | vote_sm[2 * pair + 1]) != 0;
+        }
+        if (aux_bits && keep && (wave & 1) == 0 && lane == 0)
+            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (tw >> 5)], 1u << (tw & 31));
+        if (!keep) continue;
+
+        // P = exp(s - lse) (zero where invisible)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int rl = 32 * rb + 8 * g + 4 * hl;
+                const f32x4 lz = *reinterpret_cast<const f32x4*>(l2_sm + rl);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int rowg = r0 + rl + x;
+                    const bool vis = kvalid && (!diag || key <= rowg);
+                    sacc[rb][4 * g + x] = vis ? fast_exp2(fmaf(sacc[rb][4 * g + x], scale_log2, -lz[x])) : 0.f;
+                }
+            }
+        // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
+        {
+            u32x4 pf[4][2];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pf[rb][hf][e] = pack_bf16x2(sacc[rb][8 * hf + 2 * e], sacc[rb][8 * hf + 2 * e + 1]);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const u32x4 a = tr_operand(osm, 32 * rb + 16 * hf, db, lane);
+                        dvacc[db] = mfma32(a, pf[rb][hf], dvacc[db]);
+                    }
+        }
+        // dP (rows x keys) = dO V^T ; dS = P (dP - D)
+        u32x4 dsf[4][2];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            f32x16 pacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(osm + swz(32 * rb + j, 2 * s + hl));
+                pacc = mfma32(a, vf[s], pacc);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(d_sm + 32 * rb + 8 * g + 4 * hl);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) pacc[4 * g + x] = sacc[rb][4 * g + x] * (pacc[4 * g + x] - dd[x]);
+            }
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dsf[rb][hf][e] = pack_bf16x2(pacc[8 * hf + 2 * e], pacc[8 * hf + 2 * e + 1]);
+        }
+        // dK^T (d x keys) += Q^T dS
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const u32x4 a = tr_operand(qsm, 32 * rb + 16 * hf, db, lane);
+                    dkacc[db] = mfma32(a, dsf[rb][hf], dkacc[db]);
+                }
+    }
+
+    // accumulators hold dK^T, dV^T: lane = key, register r of block db = d 32db + 8(r/4) + 4hl + r%4
+    if (kvalid) {
+        bf16_t* krow = dk + hoff + long(key) * D;
+        bf16_t* vrow = dv + hoff + long(key) * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                u32x2 wk, wv;
+                wk[0] = pack_bf16x2(dkacc[db][4 * g + 0] * scale, dkacc[db][4 * g + 1] * scale);
+                wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale);
+                wv[0] = pack_bf16x2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
+                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+                *reinterpret_cast<u32x2*>(krow + 32 * db + 8 * g + 4 * hl) = wk;
+                *reinterpret_cast<u32x2*>(vrow + 32 * db + 8 * g + 4 * hl) = wv;
+            }
+    }
+    (void)ncol;
+}
+
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
-    (void)a; (void)s;
-    return hipErrorNotSupported;
+    const int BH = a.B * a.H;
+    const int ncol = (a.L + 127) / 128;
+    dim3 g1(unsigned(ncol) * unsigned(BH)), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
+    const bool st = a.kept || a.legal || a.bits;
+    if (a.gated)
+        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<true>), g1, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
+                           (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dk,
+                           (bf16_t*)a.dv, BH, a.L, a.nqb, ncol, a.words, a.scale, a.scale_log2, a.aux_bits);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<false>), g1, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
+                           (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dk,
+                           (bf16_t*)a.dv, BH, a.L, a.nqb, ncol, a.words, a.scale, a.scale_log2, a.aux_bits);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+#define MALA_DQ_LAUNCH(G, S)                                                                                  \
+    hipLaunchKernelGGL((bwd_dq_bf16_d128<G, S>), g2, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,       \
+                       (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dq, BH, a.L, \
+                       a.nqb, a.words, a.scale, a.scale_log2, a.kept, a.legal, a.bits)
+    if (a.gated) {
+        if (st) MALA_DQ_LAUNCH(true, true);
+        else MALA_DQ_LAUNCH(true, false);
+    } else {
+        if (st) MALA_DQ_LAUNCH(false, true);
+        else MALA_DQ_LAUNCH(false, false);
+    }
+#undef MALA_DQ_LAUNCH
+    return hipGetLastError();
 }
 
 }  // namespace mala
