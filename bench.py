@@ -1,0 +1,309 @@
+"""Bench of the MALA hot path on one MI355X.
+
+One step = forward + backward of the 128K training shape (B=1, H=4 of a
+32-head layer, L=131072, d=128, bf16, 128x64 tiles) followed by split-KV
+decode of the 128K decode shape (B=16, 32 query / 8 KV heads, Lk=131073,
+split 4096, 64-key tiles), all at the same tau (default 1).  Inputs are the
+seeded planted-structure synthetic inputs, resident in HBM before timing.
+
+Printed: one JSON line.  `value` is dense-equivalent TFLOP/s of the whole
+step (FlashAttention causal convention: fwd 2*B*H*L^2*d, bwd 2.5x fwd,
+decode 4*B*Hq*Lk*d) at tau; the same library at tau=0 (full attention) is
+timed beside it.  `roofline` covers the kernel that takes most of the step;
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dev_bf16(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def legal_tiles(L, bq, bk):
+    nqb = -(-L // bq)
+    return sum((min(b * bq + bq, L) - 1) // bk + 1 for b in range(nqb))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--tau", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison run")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 32K tau sweep")
+    ap.add_argument("--cpu-sample-blocks", type=int, default=0,
+                    help="query blocks in the CPU-oracle sample (0: one per OpenMP thread, at most 16)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = 1 << 28  # 256 Mi bf16 elements = 512 MiB read + 512 MiB written
+        a = torch.empty(n, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 3}))
+        return
+
+    from mass_gated_sparse_amd import ops
+    from synth import WORKLOADS, decode_inputs, prefill_inputs
+
+    wx, wd = WORKLOADS["train128k"], WORKLOADS["decode128k"]
+    t0 = time.time()
+    xp = prefill_inputs(wx)
+    q, k, v, do = (dev_bf16(torch, xp[n]) for n in ("q", "k", "v", "do"))
+    log(f"prefill inputs {q.shape} ready in {time.time() - t0:.1f}s")
+    t0 = time.time()
+    xd = decode_inputs(wd, threads=16)
+    qd, kc, vc = (dev_bf16(torch, xd[n]) for n in ("q", "k", "v"))
+    xd0 = {"q": xd["q"][:1].copy(), "k": xd["k"][:1, :2].copy(), "v": xd["v"][:1, :2].copy()}
+    del xd
+    log(f"decode inputs {tuple(kc.shape)} ready in {time.time() - t0:.1f}s")
+
+    B, H, L, d = q.shape
+    Bd, Hq, Lk = wd.B, wd.H, wd.L
+    split = wd.split_keys
+    tile = (wx.bq, wx.bk)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_b = ops.bwd_workspace(q, tile)
+    od = torch.empty_like(qd)
+    lsed = torch.empty(Bd, Hq, dtype=torch.float32, device="cuda")
+    ws_d = ops.decode_workspace(Bd, Hq, wd.Hkv, Lk, d, split, qd.device)
+
+    # ---- kept-tile statistics (untimed; stats-enabled launches)
+    def stats_pass(tau):
+        st = ops.prefill_stats_buffers(B, H, L, tile, q.device, dkdv=False)
+        ops.fwd_into(q, k, v, o, lse, tau, tile, stats=st)
+        fk = int(st["kept"].sum())
+        stb = ops.prefill_stats_buffers(B, H, L, tile, q.device, dkdv=False)
+        ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws_b, tile, stats=stb)
+        bk_ = int(stb["kept"].sum())
+        std = ops.decode_stats_buffers(Bd, wd.Hkv, Lk, split, wd.bk, qd.device)
+        ops.decode_into(qd, kc, vc, Lk, od, lsed, tau, ws_d, split, wd.bk, stats=std)
+        dkp, dlg = int(std["kept"].sum()), int(std["legal"].sum())
+        torch.cuda.synchronize()
+        return fk, bk_, dkp, dlg
+
+    n_legal = B * H * legal_tiles(L, *tile)
+
+    # ---- timed steps
+    def run(tau, steps, warmup):
+        ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)] for n in ("fwd", "bwd", "dec")}
+        for _ in range(warmup):
+            ops.fwd_into(q, k, v, o, lse, tau, tile)
+            ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws_b, tile)
+            ops.decode_into(qd, kc, vc, Lk, od, lsed, tau, ws_d, split, wd.bk)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            ev["fwd"][2 * i].record()
+            ops.fwd_into(q, k, v, o, lse, tau, tile)
+            ev["fwd"][2 * i + 1].record()
+            ev["bwd"][2 * i].record()
+            ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws_b, tile)
+            ev["bwd"][2 * i + 1].record()
+            ev["dec"][2 * i].record()
+            ops.decode_into(qd, kc, vc, Lk, od, lsed, tau, ws_d, split, wd.bk)
+            ev["dec"][2 * i + 1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t_start) * 1e3 / steps
+        ms = {n: float(np.mean([ev[n][2 * i].elapsed_time(ev[n][2 * i + 1]) for i in range(steps)])) for n in ev}
+        return wall, ms
+
+    dense_fwd = 2.0 * B * H * L * L * d
+    dense_bwd = 2.5 * dense_fwd
+    dense_dec = 4.0 * Bd * Hq * Lk * d
+    dense_step = dense_fwd + dense_bwd + dense_dec
+
+    fk, bk_, dkp, dlg = stats_pass(args.tau)
+    log(f"tau={args.tau}: fwd kept {fk}/{n_legal}, bwd kept {bk_}/{n_legal}, decode kept {dkp}/{dlg}")
+    wall, ms = run(args.tau, args.steps, args.warmup)
+    log(f"tau={args.tau}: step {wall:.2f} ms  fwd {ms['fwd']:.2f}  bwd {ms['bwd']:.2f}  decode {ms['dec']:.3f}")
+    out_tau0 = None
+    if not args.no_tau0 and args.tau != 0.0:
+        wall0, ms0 = run(0.0, args.steps, args.warmup)
+        log(f"tau=0: step {wall0:.2f} ms  fwd {ms0['fwd']:.2f}  bwd {ms0['bwd']:.2f}  decode {ms0['dec']:.3f}")
+        out_tau0 = {"ms_per_step": wall0, "fwd_ms": ms0["fwd"], "bwd_ms": ms0["bwd"], "decode_ms": ms0["dec"],
+                    "speedup_fwd": ms0["fwd"] / ms["fwd"], "speedup_bwd": ms0["bwd"] / ms["bwd"],
+                    "speedup_decode": ms0["dec"] / ms["dec"], "speedup_step": wall0 / wall}
+
+    # ---- roofline of the forward kernel (one kernel per mala_fwd call, timed live)
+    tile_flop = 2.0 * tile[0] * tile[1] * d
+    fwd_alg_flop = tile_flop * (n_legal + fk)  # QK on every legal tile, PV on kept tiles
+    fwd_tflops = fwd_alg_flop / (ms["fwd"] * 1e-3) / 1e12
+    roofline = {"kernel": "fwd_bf16_d128 (mala_fwd)", "bound": "mfma", "achieved": fwd_tflops,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": fwd_tflops / PEAK_BF16_TFLOPS,
+                "traffic": None,
+                "per_unit": f"2*{tile[0]}*{tile[1]}*{d} FLOP per legal tile (QK) + same per kept tile (PV)",
+                "units_per_launch": {"legal_tiles": n_legal, "kept_tiles": fk}}
+    dec_bytes = Bd * wd.Hkv * Lk * d * 2 * (1.0 + dkp / dlg)  # K always, V of kept tiles
+    decode_roof = {"bound": "hbm", "achieved": dec_bytes / (ms["dec"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                   "unit": "GB/s", "frac": dec_bytes / (ms["dec"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                   "per_unit": "256 B of K per key always + 256 B of V per key of a kept tile"}
+
+    sweep = None if args.no_sweep else sweep32k(torch, ops, args.steps, args.warmup)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        nb = args.cpu_sample_blocks or min(16, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+        cpu = cpu_baseline(wx, wd, xp, xd0, nb, args.tau)
+        log(f"cpu baseline took {time.time() - t0:.1f}s")
+
+    res = {
+        "metric": "fwd/bwd/decode ms + dense-equiv TFLOP/s at 128K, tau=1 vs tau=0; % tiles kept",
+        "value": dense_step / (wall * 1e-3) / 1e12,
+        "unit": "TFLOP/s (dense-equivalent, fwd+bwd+decode step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded planted sink+local+retrieval inputs)",
+        "config": {"workload": "train128k fwd+bwd (B1 H4 L131072 d128, 128x64 tiles) + decode128k "
+                               "(B16 Hq32 Hkv8 Lk131073 d128, split 4096, 64-key tiles)",
+                   "tau": args.tau, "global_batch": B, "seq_len": L, "parallelism": "none (one GPU's 4-head share)"},
+        "fwd_ms": ms["fwd"], "bwd_ms": ms["bwd"], "decode_ms": ms["dec"],
+        "fwd_dense_tflops": dense_fwd / (ms["fwd"] * 1e-3) / 1e12,
+        "bwd_dense_tflops": dense_bwd / (ms["bwd"] * 1e-3) / 1e12,
+        "decode_dense_tflops": dense_dec / (ms["dec"] * 1e-3) / 1e12,
+        "kept_frac": {"fwd": fk / n_legal, "bwd": bk_ / n_legal, "decode": dkp / dlg},
+        "tau0": out_tau0,
+        "roofline": roofline,
+        "decode_roofline": decode_roof,
+        "sweep32k": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+def sweep32k(torch, ops, steps, warmup):
+    """32K tau sweep (B1 H8 L32768 d128 bf16): fwd/bwd ms, dense-equivalent
+    TFLOP/s and kept-tile fractions at tau in {0, 0.5, 1, 2}, for the planted
+    and the diffuse input families."""
+    from synth import WORKLOADS, prefill_inputs
+    w = WORKLOADS["sweep32k"]
+    tile = (w.bq, w.bk)
+    out = {}
+    for family in ("planted", "diffuse"):
+        x = prefill_inputs(w, family=family)
+        q, k, v, do = (dev_bf16(torch, x[n]) for n in ("q", "k", "v", "do"))
+        del x
+        B, H, L, d = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = ops.bwd_workspace(q, tile)
+        n_legal = B * H * legal_tiles(L, *tile)
+        dense_fwd = 2.0 * B * H * L * L * d
+        res = {}
+        for tau in w.taus:
+            st = ops.prefill_stats_buffers(B, H, L, tile, q.device)
+            ops.fwd_into(q, k, v, o, lse, tau, tile, stats=st)
+            stb = ops.prefill_stats_buffers(B, H, L, tile, q.device)
+            ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile, stats=stb)
+            torch.cuda.synchronize()
+            fk, bk_ = int(st["kept"].sum()), int(stb["kept"].sum())
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            for _ in range(warmup):
+                ops.fwd_into(q, k, v, o, lse, tau, tile)
+                ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
+            tf = tb = 0.0
+            for _ in range(steps):
+                ev[0].record()
+                ops.fwd_into(q, k, v, o, lse, tau, tile)
+                ev[1].record()
+                ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
+                ev[2].record()
+                torch.cuda.synchronize()
+                tf += ev[0].elapsed_time(ev[1])
+                tb += ev[1].elapsed_time(ev[2])
+            tf, tb = tf / steps, tb / steps
+            res[str(tau)] = {"fwd_ms": tf, "bwd_ms": tb, "fwd_dense_tflops": dense_fwd / tf / 1e9,
+                             "bwd_dense_tflops": 2.5 * dense_fwd / tb / 1e9,
+                             "kept_fwd": fk / n_legal, "kept_bwd": bk_ / n_legal}
+        for tau in w.taus:
+            if tau != 0.0:
+                r = res[str(tau)]
+                r["speedup_fwd_vs_tau0"] = res["0.0"]["fwd_ms"] / r["fwd_ms"]
+                r["speedup_bwd_vs_tau0"] = res["0.0"]["bwd_ms"] / r["bwd_ms"]
+        out[family] = res
+        log(f"sweep32k {family}: " + ", ".join(f"tau={t}: fwd {r['fwd_ms']:.2f} bwd {r['bwd_ms']:.2f} "
+                                              f"kept {r['kept_fwd']:.3f}/{r['kept_bwd']:.3f}" for t, r in res.items()))
+        del q, k, v, do, o, dq, dk, dv
+    return out
+
+
+def cpu_baseline(wx, wd, xp, xd0, nblocks, tau):
+    """fp64 CPU oracle on a bounded sample of the same step.
+
+    Sample: head 0 of the 128K prefill, rows of its last `nblocks` query
+    blocks (full-length rows): forward of those rows, dQ of those rows, dK/dV
+    of the 2*nblocks key tiles whose contributing rows all lie in that range;
+    plus decode of two (sequence, KV head) units of the decode shape.  FLOPs
+    are the dense-equivalent work the oracle executes on the sample (every
+    legal (row, key) pair counted as kept): 4d per pair forward, 6d per pair
+    in the dQ pass (S, dP, dQ), 8d per pair in the dK/dV pass (S, dP, dK,
+    dV), 4d per (row, key) in decode."""
+    import oracle
+    from synth import to_f64
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    L, d, bq, bk = wx.L, wx.d, wx.bq, wx.bk
+    nqb = -(-L // bq)
+    qbs = list(range(nqb - nblocks, nqb))
+    r0 = qbs[0] * bq
+    kts = list(range(r0 // bk, -(-L // bk)))
+    qf, kf, vf, dof = (to_f64(xp[n][:, :1], "bf16") for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    o, lse, keep, _ = oracle.fwd(qf, kf, vf, tau, bq, bk, qblocks=qbs)
+    oracle.bwd(qf, kf, vf, np.nan_to_num(o), np.nan_to_num(lse), dof, tau, bq, bk, qblocks=qbs, ktiles=kts)
+    t_pre = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    oracle.decode(to_f64(xd0["q"], "bf16"), xd0["k"], xd0["v"], wd.L, tau, wd.split_keys, wd.bk,
+                  units=[(0, 0), (0, 1)])
+    t_dec = time.perf_counter() - t1
+    pairs_rows = sum(i + 1 for i in range(r0, L))
+    pairs_keys = sum(L - j for j in range(kts[0] * bk, L))
+    flops = 4.0 * d * pairs_rows + 6.0 * d * pairs_rows + 8.0 * d * pairs_keys + 2 * wd.group * 4.0 * wd.L * d
+    total = t_pre + t_dec
+    return {"value": flops / total / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": threads,
+            "kind": "oracle", "seconds": round(total, 2),
+            "sample": f"head 0 of train128k, last {nblocks} query blocks (rows {r0}..{L - 1}): fwd, dQ of those "
+                      f"rows, dK/dV of key tiles {kts[0]}..{kts[-1]}; decode128k units (b0,g0),(b0,g1); "
+                      f"tau={tau}; dense-equivalent FLOPs executed by the oracle"}
+
+
+if __name__ == "__main__":
+    main()

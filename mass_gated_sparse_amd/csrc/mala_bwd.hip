@@ -37,8 +37,14 @@ namespace mala {
 
 namespace bwdk {
 constexpr int BQ = 128, BK = 64, D = 128;
-// row-major 128-element bf16 rows (256 B) with 16-byte chunks XOR-swizzled by row
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+// Row-major 128-element bf16 rows (256 B) with 16-byte chunks XOR-swizzled by
+// a permutation of the row's low 4 bits (its two 2-bit fields swapped).  It is
+// conflict-free for both access patterns used here: 16 consecutive rows at one
+// chunk (MFMA operand reads, tile stores) hit 16 distinct chunks, and the
+// transposed reads -- 8 consecutive rows x 4 consecutive chunks -- hit every
+// chunk exactly twice.
+__device__ __forceinline__ int rowkey(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + ((chunk ^ rowkey(row)) << 4); }
 // byte offset of element (row, d) in a swizzled tile
 __device__ __forceinline__ int swz_el(int row, int d) { return swz(row, d >> 3) + ((d & 7) << 1); }
 
@@ -246,6 +252,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 }
 
 // ---------------------------------------------------------------------- dK/dV
+// One workgroup per 128 keys.  The Q and dO tiles of successive query blocks
+// are double-buffered in LDS: while block qb is being computed from one
+// buffer, block qb+1 streams into the other with direct global->LDS loads
+// (no registers involved).  Rows past L are read clamped to row L-1 and are
+// masked out of every vote and every product (P = 0 there).
 template <bool GATED>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -253,12 +264,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
     const float* __restrict__ thr, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BH, int L, int nqb,
     int ncol, int words, float scale, float scale_log2, uint32_t* __restrict__ aux_bits) {
     using namespace bwdk;
-    __shared__ __attribute__((aligned(16))) uint8_t qsm[BQ * 256];
-    __shared__ __attribute__((aligned(16))) uint8_t osm[BQ * 256];
-    __shared__ __attribute__((aligned(16))) float thr_sm[BQ];
-    __shared__ __attribute__((aligned(16))) float l2_sm[BQ];
-    __shared__ __attribute__((aligned(16))) float d_sm[BQ];
-    __shared__ int vote_sm[4];
+    __shared__ __attribute__((aligned(1024))) uint8_t qsA[BQ * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t osA[BQ * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t qsB[BQ * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t osB[BQ * 256];
+    __shared__ __attribute__((aligned(16))) float stA[3][BQ];  // thr, lse2, D of the block's rows
+    __shared__ __attribute__((aligned(16))) float stB[3][BQ];
+    __shared__ int vote_sm[2][4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     const int c = int(blockIdx.x) / BH;  // 128-key column; longest (c = 0) first
@@ -266,9 +278,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
     const long hoff = long(bh) * L * D;
     const int key = 128 * c + 32 * wave + j;
     const bool kvalid = key < L;
-    const int tw = 2 * c + (wave >> 1);       // this wave's key tile
+    const int tw = 2 * c + (wave >> 1);  // this wave's key tile
     const bool tile_exists = tw * BK < L;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
+    (void)ncol;
 
     // K and V of this wave's 32 keys as B operands (lane = key, 8 contiguous d)
     u32x4 kf[8], vf[8];
@@ -283,29 +296,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dvacc[db][r] = 0.f; dkacc[db][r] = 0.f; }
 
-    for (int qb = c; qb < nqb; ++qb) {
-        const int r0 = qb * BQ;
-        __syncthreads();  // previous block's LDS reads are done
-        // Q and dO tiles (row-major, swizzled) and per-row state
+    typedef __attribute__((address_space(3))) void lds_void;
+    // Direct loads of one 128x128 tile: 32 segments of 4 rows (1 KiB); wave w
+    // issues segments 8w..8w+7; lane l of a segment fills physical chunk l%16
+    // of row l/16, i.e. it reads the logical chunk that the swizzle puts there.
+    auto tile_async = [&](const bf16_t* g, uint8_t* dst, int r0) {
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
-            const int rr = it * 16 + (tid >> 4);
-            const bool ok = r0 + rr < L;
-            const long go = hoff + long(r0 + rr) * D + (tid & 15) * 8;
-            const u32x4 xq = ok ? *reinterpret_cast<const u32x4*>(q + go) : z4;
-            const u32x4 xo = ok ? *reinterpret_cast<const u32x4*>(dout + go) : z4;
-            *reinterpret_cast<u32x4*>(qsm + swz(rr, tid & 15)) = xq;
-            *reinterpret_cast<u32x4*>(osm + swz(rr, tid & 15)) = xo;
+            const int seg = wave * 8 + it;
+            const int row = 4 * seg + (lane >> 4);
+            const int chunk = (lane & 15) ^ rowkey(row);
+            const int grow = min(r0 + row, L - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(g + hoff + long(grow) * D + chunk * 8),
+                                             (lds_void*)(dst + seg * 1024), 16, 0, 0);
         }
+    };
+    // Per-row state of a block: loaded raw (row index clamped) into registers
+    // before the tile prefetch is issued, written to LDS (with the padding-row
+    // defaults) only at the end of the iteration, so waiting for these loads
+    // never waits for the prefetch.
+    float stv[3];
+    int st_row = 0;
+    auto stats_load = [&](int r0) {
+        st_row = r0 + (tid & (BQ - 1));
+        const long ri = long(bh) * L + min(st_row, L - 1);
+        stv[0] = thr[ri];
+        stv[1] = lse2[ri];
+        stv[2] = Dv[ri];
+    };
+    auto stats_store = [&](float (*st)[BQ]) {
         if (tid < BQ) {
-            const bool ok = r0 + tid < L;
-            const long ri = long(bh) * L + r0 + tid;
-            thr_sm[tid] = ok ? thr[ri] : INFINITY;
-            l2_sm[tid] = ok ? lse2[ri] : INFINITY;
-            d_sm[tid] = ok ? Dv[ri] : 0.f;
+            const bool ok = st_row < L;
+            st[0][tid] = ok ? stv[0] : INFINITY;
+            st[1][tid] = ok ? stv[1] : INFINITY;
+            st[2][tid] = ok ? stv[2] : 0.f;
         }
-        __syncthreads();
+    };
 
+    // one query block: compute from (qs, os, st) while the next block streams into (qn, on, sn)
+    auto block = [&](int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ], uint8_t* qn,
+                     uint8_t* on, float (*sn)[BQ]) {
+        const int r0 = qb * BQ;
+        const bool more = qb + 1 < nqb;
+        if (more) {
+            stats_load(r0 + BQ);
+            tile_async(q, qn, r0 + BQ);
+            tile_async(dout, on, r0 + BQ);
+        }
         // S (rows x keys) = Q K^T: 4 row blocks of 32, 8 k-steps
         f32x16 sacc[4];
 #pragma unroll
@@ -314,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
             for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(qsm + swz(32 * rb + j, 2 * s + hl));
+                const u32x4 a = *reinterpret_cast<const u32x4*>(qs + swz(32 * rb + j, 2 * s + hl));
                 sacc[rb] = mfma32(a, kf[s], sacc[rb]);
             }
         }
@@ -328,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int rl = 32 * rb + 8 * g + 4 * hl;  // 4 consecutive rows
-                        const f32x4 th = *reinterpret_cast<const f32x4*>(thr_sm + rl);
+                        const f32x4 th = *reinterpret_cast<const f32x4*>(&st[0][rl]);
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
                             const int rowg = r0 + rl + x;
@@ -338,83 +375,100 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
                     }
             }
             const bool wv = wave_any(vote);
-            if (lane == 0) vote_sm[wave] = wv ? 1 : 0;
-            __syncthreads();
+            const int par = qb & 1;
+            if (lane == 0) vote_sm[par][wave] = wv ? 1 : 0;
+            lds_barrier();  // the next block's prefetch stays in flight
             const int pair = wave >> 1;
-            keep = tile_exists && (vote_sm[2 * pair] | vote_sm[2 * pair + 1]) != 0;
+            keep = tile_exists && (vote_sm[par][2 * pair] | vote_sm[par][2 * pair + 1]) != 0;
         }
         if (aux_bits && keep && (wave & 1) == 0 && lane == 0)
             atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (tw >> 5)], 1u << (tw & 31));
-        if (!keep) continue;
-
-        // P = exp(s - lse) (zero where invisible)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int rl = 32 * rb + 8 * g + 4 * hl;
-                const f32x4 lz = *reinterpret_cast<const f32x4*>(l2_sm + rl);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int rowg = r0 + rl + x;
-                    const bool vis = kvalid && (!diag || key <= rowg);
-                    sacc[rb][4 * g + x] = vis ? fast_exp2(fmaf(sacc[rb][4 * g + x], scale_log2, -lz[x])) : 0.f;
-                }
-            }
-        // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
-        {
-            u32x4 pf[4][2];
+        if (keep) {
+            // P = exp(s - lse) (zero where invisible; lse2 = +inf on rows past L)
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int rl = 32 * rb + 8 * g + 4 * hl;
+                    const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[1][rl]);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int rowg = r0 + rl + x;
+                        const bool vis = kvalid && (!diag || key <= rowg);
+                        sacc[rb][4 * g + x] = vis ? fast_exp2(fmaf(sacc[rb][4 * g + x], scale_log2, -lz[x])) : 0.f;
+                    }
+                }
+            // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
+            {
+                u32x4 pf[4][2];
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            pf[rb][hf][e] = pack_bf16x2(sacc[rb][8 * hf + 2 * e], sacc[rb][8 * hf + 2 * e + 1]);
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+                            const u32x4 a = tr_operand(os, 32 * rb + 16 * hf, db, lane);
+                            dvacc[db] = mfma32(a, pf[rb][hf], dvacc[db]);
+                        }
+            }
+            // dP (rows x keys) = dO V^T ; dS = P (dP - D)
+            u32x4 dsf[4][2];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                f32x16 pacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(os + swz(32 * rb + j, 2 * s + hl));
+                    pacc = mfma32(a, vf[s], pacc);
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[2][32 * rb + 8 * g + 4 * hl]);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) pacc[4 * g + x] = sacc[rb][4 * g + x] * (pacc[4 * g + x] - dd[x]);
+                }
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        pf[rb][hf][e] = pack_bf16x2(sacc[rb][8 * hf + 2 * e], sacc[rb][8 * hf + 2 * e + 1]);
+                        dsf[rb][hf][e] = pack_bf16x2(pacc[8 * hf + 2 * e], pacc[8 * hf + 2 * e + 1]);
+            }
+            // dK^T (d x keys) += Q^T dS
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
-                        const u32x4 a = tr_operand(osm, 32 * rb + 16 * hf, db, lane);
-                        dvacc[db] = mfma32(a, pf[rb][hf], dvacc[db]);
+                        const u32x4 a = tr_operand(qs, 32 * rb + 16 * hf, db, lane);
+                        dkacc[db] = mfma32(a, dsf[rb][hf], dkacc[db]);
                     }
         }
-        // dP (rows x keys) = dO V^T ; dS = P (dP - D)
-        u32x4 dsf[4][2];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            f32x16 pacc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(osm + swz(32 * rb + j, 2 * s + hl));
-                pacc = mfma32(a, vf[s], pacc);
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(d_sm + 32 * rb + 8 * g + 4 * hl);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) pacc[4 * g + x] = sacc[rb][4 * g + x] * (pacc[4 * g + x] - dd[x]);
-            }
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dsf[rb][hf][e] = pack_bf16x2(pacc[8 * hf + 2 * e], pacc[8 * hf + 2 * e + 1]);
-        }
-        // dK^T (d x keys) += Q^T dS
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const u32x4 a = tr_operand(qsm, 32 * rb + 16 * hf, db, lane);
-                    dkacc[db] = mfma32(a, dsf[rb][hf], dkacc[db]);
-                }
+        if (more) stats_store(sn);
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's direct loads into the next buffer have landed
+        __syncthreads();                // next buffer complete; every wave is done with this one
+    };
+
+    // prologue: first block into buffer A
+    tile_async(q, qsA, c * BQ);
+    tile_async(dout, osA, c * BQ);
+    stats_load(c * BQ);
+    stats_store(stA);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int qb = c; qb < nqb; ++qb) {
+        const bool odd = (qb - c) & 1;
+        block(qb, odd ? qsB : qsA, odd ? osB : osA, odd ? stB : stA, odd ? qsA : qsB, odd ? osA : osB,
+              odd ? stA : stB);
     }
 
     // accumulators hold dK^T, dV^T: lane = key, register r of block db = d 32db + 8(r/4) + 4hl + r%4
@@ -434,7 +488,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
                 *reinterpret_cast<u32x2*>(vrow + 32 * db + 8 * g + 4 * hl) = wv;
             }
     }
-    (void)ncol;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {

@@ -52,4 +52,11 @@ __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations,
+// then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// global loads (vmcnt), so direct global->LDS prefetches stay in flight across
+// it.  The memory clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace mala

@@ -15,6 +15,7 @@ follows and every reading of points the pages leave open.
 import ctypes
 import math
 import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -80,6 +81,18 @@ def default_scale(d):
     return 1.0 / math.sqrt(d)
 
 
+def _per_head(B, H, fn):
+    """Run fn(b, h) for every head; heads run side by side (the C calls
+    release the GIL; each call is independent)."""
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+    if len(jobs) == 1:
+        fn(*jobs[0])
+        return
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        for f in [ex.submit(fn, b, h) for b, h in jobs]:
+            f.result()
+
+
 def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     """MALA forward.  Returns (o, lse, keep, T); keep/T are [B, H, nqb, ntiles].
 
@@ -98,13 +111,15 @@ def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     T = np.full((B, H, nqb, nt), np.nan)
     ids, n = _ids(qblocks)
     rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
-    for b in range(B):
-        for h in range(H):
-            rc = _lib().oracle_fwd_head(_p(q[b, h], _D), _p(k[b, h], _D), _p(v[b, h], _D), L, d, scale, float(tau),
-                                        bq, bk, _p(ids, _L), n, _p(None if rp is None else rp[b, h], _U8),
-                                        float(band), _p(o[b, h], _D), _p(lse[b, h], _D), _p(keep[b, h], _U8),
-                                        _p(T[b, h], _D))
-            _check(rc, "oracle_fwd_head")
+
+    def one(b, h):
+        rc = _lib().oracle_fwd_head(_p(q[b, h], _D), _p(k[b, h], _D), _p(v[b, h], _D), L, d, scale, float(tau),
+                                    bq, bk, _p(ids, _L), n, _p(None if rp is None else rp[b, h], _U8),
+                                    float(band), _p(o[b, h], _D), _p(lse[b, h], _D), _p(keep[b, h], _U8),
+                                    _p(T[b, h], _D))
+        _check(rc, "oracle_fwd_head")
+
+    _per_head(B, H, one)
     return o, lse, keep, T
 
 
@@ -126,14 +141,16 @@ def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qb
     qi, nq = _ids(qblocks)
     ki, nk = _ids(ktiles)
     rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
-    for b in range(B):
-        for h in range(H):
-            rc = _lib().oracle_bwd_head(_p(q[b, h], _D), _p(k[b, h], _D), _p(v[b, h], _D), _p(o[b, h], _D),
-                                        _p(lse[b, h], _D), _p(do[b, h], _D), L, d, scale, float(tau), bq, bk,
-                                        _p(qi, _L), nq, _p(ki, _L), nk, _p(None if rp is None else rp[b, h], _U8),
-                                        float(band), _p(dq[b, h], _D), _p(dk[b, h], _D), _p(dv[b, h], _D),
-                                        _p(keep[b, h], _U8), _p(T[b, h], _D))
-            _check(rc, "oracle_bwd_head")
+
+    def one(b, h):
+        rc = _lib().oracle_bwd_head(_p(q[b, h], _D), _p(k[b, h], _D), _p(v[b, h], _D), _p(o[b, h], _D),
+                                    _p(lse[b, h], _D), _p(do[b, h], _D), L, d, scale, float(tau), bq, bk,
+                                    _p(qi, _L), nq, _p(ki, _L), nk, _p(None if rp is None else rp[b, h], _U8),
+                                    float(band), _p(dq[b, h], _D), _p(dk[b, h], _D), _p(dv[b, h], _D),
+                                    _p(keep[b, h], _U8), _p(T[b, h], _D))
+        _check(rc, "oracle_bwd_head")
+
+    _per_head(B, H, one)
     return dq, dk, dv, keep, T
 
 
@@ -212,9 +229,11 @@ def omitted(q, k, keep, bq, bk, scale=None, qblocks=None):
     sl = np.full((B, H, L), np.nan)
     ids, n = _ids(qblocks)
     kp = np.ascontiguousarray(keep, dtype=np.uint8)
-    for b in range(B):
-        for h in range(H):
-            rc = _lib().oracle_omitted_head(_p(q[b, h], _D), _p(k[b, h], _D), L, d, scale, bq, bk,
-                                            _p(kp[b, h], _U8), _p(ids, _L), n, _p(om[b, h], _D), _p(sl[b, h], _D))
-            _check(rc, "oracle_omitted_head")
+
+    def one(b, h):
+        rc = _lib().oracle_omitted_head(_p(q[b, h], _D), _p(k[b, h], _D), L, d, scale, bq, bk,
+                                        _p(kp[b, h], _U8), _p(ids, _L), n, _p(om[b, h], _D), _p(sl[b, h], _D))
+        _check(rc, "oracle_omitted_head")
+
+    _per_head(B, H, one)
     return om, sl

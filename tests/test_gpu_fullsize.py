@@ -1,0 +1,128 @@
+"""GPU parity at the full workload sizes, on sampled outputs.
+
+The GPU runs the whole workload exactly as the bench launches it; the oracle
+recomputes sampled query blocks (forward decisions, O, lse, dQ), sampled key
+tiles (dK, dV) and sampled decode groups one by one -- every MALA decision of a
+query block depends on that block's rows only, so a sampled block is checked
+exactly, not approximately.  Same rules as the small-size parity tests.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS, decode_inputs, prefill_inputs, to_f64
+from tests.parity import BAND, TOL_GRAD, TOL_O, bf16_to_f64, decision_report, legal_mask, rel_l2
+
+torch = pytest.importorskip("torch")
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mass_gated_sparse_amd import ops as _ops
+    return _ops
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _rows(blocks, bq, L):
+    return np.concatenate([np.arange(b * bq, min(b * bq + bq, L)) for b in blocks])
+
+
+def _prefill_full(ops, name, tau, qblocks, ktiles, family="planted"):
+    w = WORKLOADS[name]
+    x = prefill_inputs(w, family=family)
+    q, k, v, do = (_dev(x[n]) for n in ("q", "k", "v", "do"))
+    bq, bk = w.bq, w.bk
+    o, lse, st = ops.fwd(q, k, v, tau, tile=(bq, bk), stats=True)
+    dq, dk, dv, stb = ops.bwd(q, k, v, o, lse, do, tau, tile=(bq, bk), stats=True)
+    torch.cuda.synchronize()
+    B, H, L, d = q.shape
+    nt = -(-L // bk)
+    legal = legal_mask(L, bq, bk)
+    gk = ops.bits_to_keep(st["keep_bits"], nt)
+    gkb = ops.bits_to_keep(stb["keep_bits"], nt)
+    gkb2 = ops.bits_to_keep(stb["keep_bits_dkdv"], nt)
+    assert (gkb[..., legal] == gkb2[..., legal]).all()
+    qf, kf, vf, dof = (to_f64(x[n], w.dtype) for n in ("q", "k", "v", "do"))
+    # forward, sampled query blocks
+    oo, ol, ok, oT = oracle.fwd(qf, kf, vf, tau, bq, bk, replay=gk, band=BAND, qblocks=qblocks)
+    sel = np.zeros_like(legal)
+    sel[list(qblocks)] = legal[list(qblocks)]
+    bad, near, _ = decision_report(gk, ok, oT, sel)
+    assert bad == 0, f"{name} tau={tau}: {bad} forward decisions differ"
+    rows = _rows(qblocks, bq, L)
+    of = bf16_to_f64(o)
+    assert rel_l2(of[:, :, rows], oo[:, :, rows]) <= TOL_O
+    assert np.abs(lse.cpu().numpy()[:, :, rows] - ol[:, :, rows]).max() <= 1e-3
+    # backward against the GPU's own forward state, sampled blocks and key tiles
+    lf = lse.cpu().numpy().astype(np.float64)
+    gq, gkk, gv, okb, oTb = oracle.bwd(qf, kf, vf, of, lf, dof, tau, bq, bk, replay=gkb, band=BAND,
+                                       qblocks=qblocks, ktiles=ktiles)
+    selb = np.zeros_like(legal)
+    selb[list(qblocks)] = legal[list(qblocks)]
+    for t in ktiles:
+        selb[:, t] |= legal[:, t]
+    bad, near_b, _ = decision_report(gkb, okb, oTb, selb)
+    assert bad == 0, f"{name} tau={tau}: {bad} backward decisions differ"
+    krows = _rows(ktiles, bk, L)
+    e = [rel_l2(bf16_to_f64(dq)[:, :, rows], gq[:, :, rows]),
+         rel_l2(bf16_to_f64(dk)[:, :, krows], gkk[:, :, krows]),
+         rel_l2(bf16_to_f64(dv)[:, :, krows], gv[:, :, krows])]
+    assert max(e) <= TOL_GRAD, e
+    return legal, gk, gkb
+
+
+@pytest.mark.parametrize("tau", [1.0])
+def test_train128k_full(ops, tau):
+    legal, gk, gkb = _prefill_full(ops, "train128k", tau, qblocks=(0, 1, 300, 1023), ktiles=(0, 1, 1500, 2046, 2047))
+    # backward paragraph: backward support is nested in forward's.  Both GPU
+    # decisions are fp32, so a tile exactly at the threshold could flip; allow
+    # at most a handful of such tiles over all 4.2M legal tiles.
+    viol = int(((gkb == 1) & (gk == 0) & legal).sum())
+    assert viol <= 4, viol
+
+
+@pytest.mark.parametrize("tau,family", [(0.5, "planted"), (2.0, "planted"), (1.0, "diffuse")])
+def test_sweep32k_full(ops, tau, family):
+    _prefill_full(ops, "sweep32k", tau, qblocks=(0, 77, 255), ktiles=(0, 300, 510, 511), family=family)
+
+
+def test_mw8k_full(ops):
+    legal, gk, gkb = _prefill_full(ops, "mw8k", 1.0, qblocks=(0, 5, 40, 63), ktiles=(0, 64, 126, 127))
+    kept = gk[..., legal].mean()
+    assert 0.0 < kept < 1.0
+
+
+@pytest.mark.parametrize("tau", [1.0, 0.0])
+def test_decode128k_full(ops, tau):
+    w = WORKLOADS["decode128k"]
+    x = decode_inputs(w, threads=16)
+    q, kc, vc = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse, st = ops.decode(q, kc, vc, w.L, tau, split_keys=w.split_keys, bk=w.bk, stats=True)
+    torch.cuda.synchronize()
+    tps = w.split_keys // w.bk
+    gk = ops.bits_to_keep(st["keep_bits"], tps)
+    nsplit = -(-w.L // w.split_keys)
+    legal = np.zeros((nsplit, tps), bool)
+    for p in range(nsplit):
+        legal[p, : -(-(min((p + 1) * w.split_keys, w.L) - p * w.split_keys) // w.bk)] = True
+    og, lg = bf16_to_f64(o), lse.cpu().numpy()
+    for b, g in [(0, 0), (7, 3), (15, 7)]:
+        hs = slice(g * w.group, (g + 1) * w.group)
+        qs = to_f64(x["q"][b:b + 1, hs], "bf16")
+        ks = to_f64(x["k"][b:b + 1, g:g + 1], "bf16")
+        vs = to_f64(x["v"][b:b + 1, g:g + 1], "bf16")
+        oo, ol, ok, oT = oracle.decode(qs, ks, vs, w.L, tau, w.split_keys, w.bk,
+                                       replay=gk[b:b + 1, g:g + 1, None], band=BAND)
+        bad, near, _ = decision_report(gk[b, g], ok[0, 0, 0], oT[0, 0, 0], legal)
+        assert bad == 0
+        assert rel_l2(og[b, hs], oo[0]) <= TOL_O
+        assert np.abs(lg[b, hs] - ol[0]).max() <= 1e-3
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
