@@ -52,6 +52,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the 32K tau sweep")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0,
                     help="query blocks in the CPU-oracle sample (0: one per OpenMP thread, at most 16)")
+    ap.add_argument("--micro", action="store_true",
+                    help="only run the ceiling microbenchmarks (MFMA, LDS, transposed LDS, HBM)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter calibration)")
     args = ap.parse_args()
@@ -65,6 +67,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+
+    if args.micro:
+        print(json.dumps(micro(torch)))
+        return
 
     if args.copy_calibration:
         n = 1 << 28  # 256 Mi bf16 elements = 512 MiB read + 512 MiB written
@@ -206,6 +212,49 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
+
+
+def micro(torch):
+    """Measured ceilings on this GPU: dense bf16 MFMA (32x32x16, 8 independent
+    chains per wave), LDS read bandwidth (16-byte reads, conflict-free) and the
+    transposing 8-byte LDS reads, HBM streaming reads (8 GiB)."""
+    import ctypes
+    from mass_gated_sparse_amd.build import ubench_path
+    lib = ctypes.CDLL(ubench_path())
+    vp = ctypes.c_void_p
+    dev = torch.cuda.get_device_properties(0)
+    cus = dev.multi_processor_count
+    st = vp(torch.cuda.current_stream().cuda_stream)
+    out = torch.empty(1 << 22, dtype=torch.int32, device="cuda")
+    seed = torch.randint(0, 1 << 16, (256,), dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
+    res = {"cus": cus}
+    blocks = cus * 8
+    it = 2000
+    t = timed(lambda: lib.ubench_mfma(vp(seed.data_ptr()), vp(out.data_ptr()), blocks, it, st))
+    res["mfma_bf16_tflops"] = blocks * 4 * it * 8 * 32768 / t / 1e12
+    it = 4000
+    t = timed(lambda: lib.ubench_lds(vp(out.data_ptr()), cus * 2, it, st))
+    res["lds_read_bytes_per_clk_per_cu_at_2p4ghz"] = cus * 2 * 4 * it * 8 * 1024 / t / cus / 2.4e9
+    res["lds_read_tbs"] = cus * 2 * 4 * it * 8 * 1024 / t / 1e12
+    t = timed(lambda: lib.ubench_lds_tr(vp(out.data_ptr()), cus * 2, it, st))
+    res["lds_tr_read_bytes_per_clk_per_cu_at_2p4ghz"] = cus * 2 * 4 * it * 4 * 1024 / t / cus / 2.4e9
+    n16 = (8 << 30) // 16
+    buf = torch.empty(n16 * 4, dtype=torch.int32, device="cuda").fill_(1)
+    t = timed(lambda: lib.ubench_hbm(vp(buf.data_ptr()), ctypes.c_long(n16), vp(out.data_ptr()), cus * 16, st))
+    res["hbm_read_gbs"] = n16 * 16 / t / 1e9
+    return res
 
 
 def sweep32k(torch, ops, steps, warmup):

@@ -15,11 +15,13 @@ def lib_path() -> str:
     return os.path.join(HERE, "libmala.so")
 
 
-def build(verbose: bool = False) -> str:
+def ubench_path() -> str:
+    return os.path.join(HERE, "libmala_ubench.so")
+
+
+def _hipcc(srcs, out, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    out = lib_path()
     tmp = out + ".tmp"
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
     cmd = [hipcc, *HIPCC_FLAGS, "-shared", *srcs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -30,6 +32,17 @@ def build(verbose: bool = False) -> str:
         print(msg)
     os.replace(tmp, out)
     return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libmala.so (the operator) and libmala_ubench.so (ceiling
+    microbenchmarks used by bench.py --micro) side by side."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(2) as ex:
+        f1 = ex.submit(_hipcc, [os.path.join(CSRC, s) for s in SOURCES], lib_path(), verbose)
+        f2 = ex.submit(_hipcc, [os.path.join(CSRC, "mala_ubench.hip")], ubench_path(), verbose)
+        f2.result()
+        return f1.result()
 
 
 if __name__ == "__main__":

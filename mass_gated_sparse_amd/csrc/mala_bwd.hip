@@ -37,38 +37,6 @@ namespace mala {
 
 namespace bwdk {
 constexpr int BQ = 128, BK = 64, D = 128;
-// Row-major 128-element bf16 rows (256 B) with 16-byte chunks XOR-swizzled by
-// a permutation of the row's low 4 bits (its two 2-bit fields swapped).  It is
-// conflict-free for both access patterns used here: 16 consecutive rows at one
-// chunk (MFMA operand reads, tile stores) hit 16 distinct chunks, and the
-// transposed reads -- 8 consecutive rows x 4 consecutive chunks -- hit every
-// chunk exactly twice.
-__device__ __forceinline__ int rowkey(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + ((chunk ^ rowkey(row)) << 4); }
-// byte offset of element (row, d) in a swizzled tile
-__device__ __forceinline__ int swz_el(int row, int d) { return swz(row, d >> 3) + ((d & 7) << 1); }
-
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-__device__ __forceinline__ u32x2 tr16(const uint8_t* lds_base, int byte_off) {
-    typedef __attribute__((address_space(3))) uint8_t lds_u8;
-    lds_bf16x4* p = (lds_bf16x4*)((lds_u8*)const_cast<uint8_t*>(lds_base) + byte_off);
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
-}
-
-// A-operand (8 rows r0+{0..3}, r0+8+{0..3} at column d = 32db + lane%32) of a
-// "transposed" product, read from a swizzled row-major tile.  r0 is the base
-// row for the calling lane's half (callers pass rowbase + 4*hl).
-__device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int rowbase, int db, int lane) {
-    const int g = lane >> 4, i = lane & 15, a = i & 3, es = i >> 2;
-    const int hl = g >> 1, dh = g & 1;
-    const int d = 32 * db + 16 * dh + 4 * a;
-    const int r = rowbase + 4 * hl + es;
-    const u32x2 lo = tr16(tile, swz_el(r, d));
-    const u32x2 hi = tr16(tile, swz_el(r + 8, d));
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
 }  // namespace bwdk
 
 // ------------------------------------------------------------------------- dQ
@@ -296,7 +264,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dvacc[db][r] = 0.f; dkacc[db][r] = 0.f; }
 
-    typedef __attribute__((address_space(3))) void lds_void;
     // Direct loads of one 128x128 tile: 32 segments of 4 rows (1 KiB); wave w
     // issues segments 8w..8w+7; lane l of a segment fills physical chunk l%16
     // of row l/16, i.e. it reads the logical chunk that the swizzle puts there.

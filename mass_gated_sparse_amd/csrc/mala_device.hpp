@@ -17,18 +17,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u) return bf16_t((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return bf16_t(u >> 16);
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+
+// Two fp32 -> packed bf16x2 (lo in bits 0..15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 x = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
 }
 
-// Two fp32 -> packed bf16x2 (lo in bits 0..15).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
-}
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return bf16_t(pack_bf16x2(f, 0.f) & 0xffffu); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -58,5 +58,102 @@ __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 // it.  The memory clobber keeps the compiler from moving memory accesses
 // across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------- LDS tiles
+// Tiles of 128-element bf16 rows (256 B per row) are kept row-major in LDS
+// with their 16-byte chunks XOR-swizzled by a permutation of the row's low 4
+// bits (the two 2-bit fields swapped).  Conflict-free for both patterns used:
+// 16 consecutive rows at one chunk (MFMA operand reads, tile stores) hit 16
+// distinct chunks, and the transposed reads below -- 8 consecutive rows x 4
+// consecutive chunks -- hit every chunk exactly twice.
+__device__ __forceinline__ int rowkey(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + ((chunk ^ rowkey(row)) << 4); }
+__device__ __forceinline__ int swz_el(int row, int d) { return swz(row, d >> 3) + ((d & 7) << 1); }
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ds_read_b64_tr_b16: within each 16-lane group the lanes read a 16x4 block
+// M of 16-bit elements (one 8-byte row per lane) and lane i receives
+// M[i/4 + 4e][i%4], e = 0..3.
+__device__ __forceinline__ u32x2 tr16(const uint8_t* lds_base, int byte_off) {
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    lds_bf16x4* p = (lds_bf16x4*)((lds_u8*)const_cast<uint8_t*>(lds_base) + byte_off);
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p));
+}
+
+// LDS pointer from a 32-bit LDS byte address.
+__device__ __forceinline__ const uint8_t* lds_ptr(uint32_t addr) {
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    return (const uint8_t*)(lds_u8*)(uintptr_t)addr;
+}
+
+// Per-lane byte offsets of the transposed operand reads of tr_operand within
+// a tile (rowbase 0): [db][0] for rows 4hl + {0..3}, [db][1] for rows
+// 8 + 4hl + {0..3}.  Adding 256*rowbase (rowbase a multiple of 16) gives the
+// offsets for other row bases, because the swizzle depends on row % 16 only.
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[4][2]) {
+    const int g = lane >> 4, i = lane & 15, a = i & 3, es = i >> 2;
+    const int hl = g >> 1, dh = g & 1;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int d = 32 * db + 16 * dh + 4 * a;
+        off[db][0] = swz_el(4 * hl + es, d);
+        off[db][1] = swz_el(8 + 4 * hl + es, d);
+    }
+}
+
+// tr_operand with precomputed offsets: base = LDS address of the tile plus
+// 256 * rowbase.
+__device__ __forceinline__ u32x4 tr_operand_at(uint32_t base, const int (&off)[2]) {
+    const u32x2 lo = tr16(lds_ptr(base), off[0]);
+    const u32x2 hi = tr16(lds_ptr(base), off[1]);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// A operand of a 32x32x16 product whose contraction runs over the ROWS of a
+// swizzled tile: lane l gets column d = 32*db + l%32 at rows
+// rowbase + 4*(l/32) + {0..3} and rowbase + 8 + 4*(l/32) + {0..3} -- the row
+// order of registers 8*hf .. 8*hf+7 of a 32x32 accumulator block.
+__device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int rowbase, int db, int lane) {
+    const int g = lane >> 4, i = lane & 15, a = i & 3, es = i >> 2;
+    const int hl = g >> 1, dh = g & 1;
+    const int d = 32 * db + 16 * dh + 4 * a;
+    const int r = rowbase + 4 * hl + es;
+    const u32x2 lo = tr16(tile, swz_el(r, d));
+    const u32x2 hi = tr16(tile, swz_el(r + 8, d));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// One direct global->LDS load: every lane reads 16 bytes at `gaddr`; lane l's
+// bytes land at LDS byte address lds_addr + 16*l (lds_addr must be the same in
+// all lanes).  The data goes to LDS, not to registers, and completion is
+// tracked by the callers with explicit s_waitcnt vmcnt(N) before the barrier
+// that publishes the tile.  Written as asm rather than with
+// __builtin_amdgcn_global_load_lds because the compiler cannot tell which LDS
+// bytes such a load writes and then waits for every outstanding load before
+// each later LDS access, which would serialize the prefetch.  The asm has no
+// register outputs (nothing can be overwritten late); it clobbers M0.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_addr) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((lds_void*)const_cast<void*>(p)));
+}
+
+// Direct global->LDS copy of rows [row0, row0 + nrows) of a 128-wide bf16
+// matrix into a swizzled tile, nrows/4 segments of 1 KiB: segment s holds
+// rows 4s..4s+3; lane l of the issuing wave fills physical chunk l%16 of row
+// 4s + l/16.  Rows at or past `rows_valid` read row rows_valid-1 instead
+// (callers mask them).  Each call issues one 16-byte load per lane.
+__device__ __forceinline__ void dma_segment(const bf16_t* g, long row0, int rows_valid, uint8_t* tile, int seg,
+                                            int lane) {
+    const int row = 4 * seg + (lane >> 4);
+    const int chunk = (lane & 15) ^ rowkey(row);
+    const int rr = min(row, rows_valid - 1);
+    dma16(g + (row0 + rr) * 128 + chunk * 8, __builtin_amdgcn_readfirstlane(lds_addr_of(tile + seg * 1024)));
+}
 
 }  // namespace mala

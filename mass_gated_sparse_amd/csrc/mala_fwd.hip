@@ -11,23 +11,30 @@
 //
 // Work decomposition.  One workgroup (4 waves) owns one 128-row query block =
 // one vote block.  Wave w owns rows 32w..32w+31.  Scores are computed
-// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane l then holds
-// query row l%32 and 16 keys per 32-key block, so every per-row operation
-// (test, max, exp, rescale) is lane-local and the whole test is one compare
-// per score plus a wave ballot and a 4-way OR through LDS.  The output is also
-// kept transposed, O^T += V^T P^T, so the online-softmax rescale stays
-// lane-local; P^T comes straight from the score registers (converted to bf16)
-// and V is written transposed into LDS when (and only when) a tile is kept.
+// transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
+// B = Q held in registers): lane l then holds query row l%32 and 16 keys per
+// 32-key block, so every per-row operation (test, max, exp, rescale) is
+// lane-local and the whole test is one compare per score plus a wave ballot
+// and a 4-way OR through LDS.  The output is kept transposed as well,
+// O^T += V^T P^T: P^T comes straight from the score registers (as bf16) and
+// V^T is read from the row-major V tile with transposing LDS reads.
 //
+// Pipeline.  Tiles flow through three overlapped stages.  While tile t is
+// tested, the scores of tile t-1 are computed and the PV product of tile t+1
+// is accumulated:
+//   * K tiles arrive by direct global->LDS loads one tile ahead (two slots);
+//   * the running statistics (m, l) of a kept tile are updated right after its
+//     vote -- they need no V -- so the next vote never waits for V;
+//   * V of a kept tile is requested right after its vote and consumed one
+//     iteration later: O += P_{t+1} V_{t+1} (in the frame of m after tile t+1),
+//     then O *= exp2(m_{t+1} - m_t).  This is the same recurrence as the
+//     undelayed update, applied in the same order.
+// Per iteration: one barrier (vote exchange, next K visible), plus one when
+// the previous tile was kept (its V visible).
 // The test runs in the raw dot-product domain: with c = scale*log2(e) and the
 // running state kept as m2 = max s*log2(e) and l, row i keeps the tile iff
 // max_j <q_i,k_j> >= (m2 + log2 l + log2 tau - log2 Lq_i) / c,
 // i.e. exp(max_j s_ij - m)/l >= tau/Lq_i.  An empty row (l = 0) keeps.
-//
-// LDS: K tile 64x128 bf16 (16 KiB, 16-byte chunks XOR-swizzled by key so the
-// 32-key MFMA operand reads are conflict-free), V^T 128x64 bf16 with rows
-// padded to 136 B (17 KiB).  The next K tile is prefetched into registers
-// while the current one is scored.
 #include <float.h>
 
 #include "mala_kernels.hpp"
@@ -36,8 +43,6 @@ namespace mala {
 
 namespace fwdk {
 constexpr int BQ = 128, BK = 64, D = 128;
-constexpr int VT = 136;  // bytes per V^T row in LDS
-__device__ __forceinline__ int kswz(int key, int chunk) { return key * 256 + ((chunk ^ (key & 15)) << 4); }
 }  // namespace fwdk
 
 template <bool GATED, bool STATS>
@@ -47,27 +52,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
                                                         float scale_log2, float log2_tau, int32_t* __restrict__ kept,
                                                         int32_t* __restrict__ legal, uint32_t* __restrict__ bits) {
     using namespace fwdk;
-    __shared__ __attribute__((aligned(16))) uint8_t ksm[BK * 256];
-    __shared__ __attribute__((aligned(16))) uint8_t vsm[D * VT];
-    __shared__ int vote_sm[4];
+    __shared__ __attribute__((aligned(1024))) uint8_t kslot[2][BK * 256];  // K tile t in kslot[t & 1]
+    __shared__ __attribute__((aligned(1024))) uint8_t vslot[2][BK * 256];  // V tile t in vslot[t & 1]
+    __shared__ int vote_sm[2][4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     const int qb = nqb - 1 - int(blockIdx.x) / BH;  // longest query blocks first
     const int bh = int(blockIdx.x) % BH;
     const long hoff = long(bh) * L * D;
-    const bf16_t* qh = q + hoff;
     const bf16_t* kh = k + hoff;
     const bf16_t* vh = v + hoff;
     const int row = qb * BQ + wave * 32 + j;
     const bool rvalid = row < L;
     const u32x4 z4 = {0u, 0u, 0u, 0u};
-    const u32x2 z2 = {0u, 0u};
 
     // Q as the B operand of S^T = K Q^T: step s holds q[row][16s + 8hl .. +8].
     u32x4 qf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-        qf[s] = rvalid ? *reinterpret_cast<const u32x4*>(qh + long(row) * D + 16 * s + 8 * hl) : z4;
+        qf[s] = rvalid ? *reinterpret_cast<const u32x4*>(q + hoff + long(row) * D + 16 * s + 8 * hl) : z4;
 
     f32x16 oacc[4];
 #pragma unroll
@@ -76,21 +79,57 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m2 = -INFINITY, lsum = 0.f;
     const float log2_lq = fast_log2(float(row + 1));
+    const float inv_scale_log2 = 1.f / scale_log2;
     const int jmax = (min(qb * BQ + BQ, L) - 1) / BK;
 
-    // K tile loader: thread loads keys it*16 + tid/16 (it = 0..3), chunk tid%16.
-    u32x4 kreg[4];
-    auto load_k = [&](int t) {
+    // 64-key tile t -> 16 segments of 4 rows; wave w issues segments 4w..4w+3,
+    // one 16-byte load per lane each.  Per-lane source offsets (row and the
+    // swizzled chunk) are fixed; rows past L are clamped on the last tile only.
+    int gofs[4];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int jg = t * BK + it * 16 + (tid >> 4);
-            kreg[it] = (jg < L) ? *reinterpret_cast<const u32x4*>(kh + long(jg) * D + (tid & 15) * 8) : z4;
+    for (int it = 0; it < 4; ++it) {
+        const int rt = 4 * it + (lane >> 4);  // row within the segment group of this wave, mod 16
+        gofs[it] = (16 * wave + rt) * D + (((lane & 15) ^ rowkey(rt)) << 3);
+    }
+    auto tile_dma = [&](const bf16_t* g, uint8_t* dst, int t) {
+        const bf16_t* gt = g + long(t) * BK * D;
+        const uint32_t la = lds_addr_of(dst) + 4096 * wave;
+        if ((t + 1) * BK <= L) {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) dma16(gt + gofs[it], __builtin_amdgcn_readfirstlane(la + 1024 * it));
+        } else {
+#pragma unroll
+            for (int it = 0; it < 4; ++it) dma_segment(g, long(t) * BK, L - t * BK, dst, 4 * wave + it, lane);
         }
     };
-    auto store_k = [&]() {
+    int koff[8];  // K operand of step s: row j, chunk 2s + hl
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-            *reinterpret_cast<u32x4*>(ksm + kswz(it * 16 + (tid >> 4), tid & 15)) = kreg[it];
+    for (int s = 0; s < 8; ++s) koff[s] = swz(j, 2 * s + hl);
+    int voff[4][2];
+    tr_offsets(lane, voff);
+    auto scores = [&](const uint8_t* kt, f32x16* sacc) {
+        const uint32_t kb0 = lds_addr_of(kt);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(kb0 + 8192 * kb) + koff[s]);
+                sacc[kb] = mfma32(a, qf[s], sacc[kb]);
+            }
+        }
+    };
+    // O^T (d x rows) += V^T (d x keys) P^T (keys x rows)
+    auto pv = [&](const uint8_t* vt, const u32x4 (*pf)[2]) {
+        const uint32_t vb = lds_addr_of(vt);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    oacc[db] = mfma32(tr_operand_at(vb + 256 * (32 * kb + 16 * hf), voff[db]), pf[kb][hf], oacc[db]);
     };
 
     int nkept = 0;
@@ -98,79 +137,66 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     if (STATS && bits && tid == 0)
         for (int w = (jmax >> 5) + 1; w < words; ++w) bits[(long(bh) * nqb + qb) * words + w] = 0u;
 
-    load_k(jmax);
-    store_k();
-    __syncthreads();
+    // prologue: scores of tile jmax; K(jmax-1) requested
+    tile_dma(kh, kslot[jmax & 1], jmax);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    lds_barrier();
+    if (jmax >= 1) tile_dma(kh, kslot[(jmax - 1) & 1], jmax - 1);
+    f32x16 sc[2], sn[2];      // scores of the tile being tested / of the next tile
+    scores(kslot[jmax & 1], sc);
 
+    u32x4 ppend[2][2];        // P of the previous kept tile (bf16), waiting for its V
+    bool pend = false;        // previous tile kept (its V in flight)
     for (int t = jmax; t >= 0; --t) {
-        if (t > 0) load_k(t - 1);  // prefetch the next tile while this one is scored
-
-        // ---- scores S^T (keys x rows) of tile t: 2 blocks of 32 keys, 8 k-steps over d
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(ksm + kswz(32 * kb + j, 2 * s + hl));
-                sacc[kb] = mfma32(a, qf[s], sacc[kb]);
-            }
-        }
-        // causal mask on the tiles that reach the diagonal (key > row invisible)
+        // causal mask on the tiles that reach the diagonal: register r of key
+        // block kb holds key t*64 + 32kb + 8(r/4) + 4hl + r%4, invisible when > row
         if (t >= 2 * qb) {
+            const int lim = row - t * BK - 4 * hl;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = t * BK + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if (key > row) sacc[kb][r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
         }
-
         // ---- test + block vote
-        bool keep = true;
         if (GATED) {
             float thr_raw;
-            if (!rvalid) thr_raw = INFINITY;               // padding rows never vote
-            else if (lsum == 0.f) thr_raw = -FLT_MAX;      // empty row: any visible key keeps
-            else thr_raw = (m2 + fast_log2(lsum) + log2_tau - log2_lq) / scale_log2;
+            if (!rvalid) thr_raw = INFINITY;           // padding rows never vote
+            else if (lsum == 0.f) thr_raw = -FLT_MAX;  // empty row: any visible key keeps
+            else thr_raw = (m2 + fast_log2(lsum) + log2_tau - log2_lq) * inv_scale_log2;
             bool vote = false;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) vote |= sacc[kb][r] >= thr_raw;
+                for (int r = 0; r < 16; ++r) vote |= sc[kb][r] >= thr_raw;
             const bool wv = wave_any(vote);
-            if (lane == 0) vote_sm[wave] = wv ? 1 : 0;
-            __syncthreads();  // votes visible; all waves are done reading this K tile
-            keep = (vote_sm[0] | vote_sm[1] | vote_sm[2] | vote_sm[3]) != 0;
-        } else {
-            __syncthreads();
+            if (lane == 0) vote_sm[t & 1][wave] = wv ? 1 : 0;
         }
+        // K(t-1) has landed once at most the V loads of tile t+1 are outstanding
+        // (with statistics on, thread 0 also has keep-bit stores in flight)
+        if (pend && !STATS) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+        else __builtin_amdgcn_s_waitcnt(0x0f70);
+        lds_barrier();  // votes, K(t-1) visible; every wave is done with kslot[t & 1]
+        // The vote flags are read first and used after the K prefetch is issued.
+        int vflags = 1;
+        if (GATED) vflags = vote_sm[t & 1][0] | vote_sm[t & 1][1] | vote_sm[t & 1][2] | vote_sm[t & 1][3];
+        if (t >= 2) tile_dma(kh, kslot[t & 1], t - 2);  // K(t-2) into the slot K(t) used
+        const bool keep = vflags != 0;
 
+        // Next tile's scores in both branches: alone for a skipped tile, and in
+        // one block with this tile's statistics for a kept one, so the
+        // exp/max/sum work interleaves with the MFMAs.  (At t = 0 the "next"
+        // scores read a stale slot and are never used.)
+        float alpha = 1.f;
         if (keep) {
-            // V tile loads (consumed after the softmax update below).
-            // 16 units of 4 keys x 32 d; unit u = (2*wave + hl) + 8*it.
-            u32x2 vr[2][4];
-            int vdg[2], vkg[2];
-#pragma unroll
-            for (int it = 0; it < 2; ++it) {
-                const int u = (2 * wave + hl) + 8 * it;
-                vdg[it] = 8 * (u & 3) + (j & 7);    // d = 4*vdg .. +3
-                vkg[it] = 4 * (u >> 2) + (j >> 3);  // keys 4*vkg .. +3
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = t * BK + 4 * vkg[it] + i;
-                    vr[it][i] = key < L ? *reinterpret_cast<const u32x2*>(vh + long(key) * D + 4 * vdg[it]) : z2;
-                }
-            }
-
-            // online softmax update of this row (lane-local; the two lane halves share a row)
+            tile_dma(vh, vslot[t & 1], t);  // V only for kept tiles
+            scores(kslot[(t - 1) & 1], sn);
+            // statistics (no V needed); P_t = exp2(s*c - m) kept in place
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
             const float mn = fmaxf(m2, mx * scale_log2);
             const float mref = (mn == -INFINITY) ? 0.f : mn;
@@ -179,62 +205,44 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(fmaf(sacc[kb][r], scale_log2, -mref));
-                    sacc[kb][r] = p;
+                    const float p = fast_exp2(fmaf(sc[kb][r], scale_log2, -mref));
+                    sc[kb][r] = p;
                     lpart += p;
                 }
             lpart += shfl_xor_f(lpart, 32);
-            const float alpha = fast_exp2(m2 - mref);
+            alpha = fast_exp2(m2 - mref);
             lsum = lsum * alpha + lpart;
             m2 = mn;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        } else {
+            scores(kslot[(t - 1) & 1], sn);
+        }
 
-            // P^T as B operands: step (kb, half) holds score registers 8*half .. 8*half+7
-            u32x4 pf[2][2];
+        // PV of the previous kept tile (in its own frame), then this tile's rescale
+        if (pend) {
+            if (STATS) __builtin_amdgcn_s_waitcnt(0x0f70);
+            else if (keep && t >= 2) __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): K(t-2), V(t) may fly
+            else if (keep || t >= 2) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+            else __builtin_amdgcn_s_waitcnt(0x0f70);
+            lds_barrier();  // V(t+1) visible
+            pv(vslot[(t + 1) & 1], ppend);
+        }
+        if (keep) {
+            if (__ballot(alpha != 1.f) != 0ull) {  // skipped when no row's max moved (exact)
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+            // P^T as B operands: step (kb, hf) holds score registers 8*hf .. 8*hf+7
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        pf[kb][hf][e] = pack_bf16x2(sacc[kb][8 * hf + 2 * e], sacc[kb][8 * hf + 2 * e + 1]);
-
-            // V -> V^T in LDS: 4x4 (key x d) blocks transposed in registers
-#pragma unroll
-            for (int it = 0; it < 2; ++it) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int sh = (e & 1) * 16;
-                    uint32_t x0, x1, x2, x3;
-                    if (e < 2) { x0 = vr[it][0][0]; x1 = vr[it][1][0]; x2 = vr[it][2][0]; x3 = vr[it][3][0]; }
-                    else       { x0 = vr[it][0][1]; x1 = vr[it][1][1]; x2 = vr[it][2][1]; x3 = vr[it][3][1]; }
-                    u32x2 w;
-                    w[0] = ((x0 >> sh) & 0xffffu) | (((x1 >> sh) & 0xffffu) << 16);
-                    w[1] = ((x2 >> sh) & 0xffffu) | (((x3 >> sh) & 0xffffu) << 16);
-                    *reinterpret_cast<u32x2*>(vsm + (4 * vdg[it] + e) * VT + 8 * vkg[it]) = w;
-                }
-            }
-            __syncthreads();  // V^T ready
-
-            // O^T (d x rows) += V^T (d x keys) P^T (keys x rows)
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const uint8_t* vrow = vsm + (32 * db + j) * VT;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const int key0 = 32 * kb + 16 * hf + 4 * hl;
-                        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 2 * key0);
-                        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 2 * (key0 + 8));
-                        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                        oacc[db] = mfma32(a, pf[kb][hf], oacc[db]);
-                    }
-            }
+                        ppend[kb][hf][e] = pack_bf16x2(sc[kb][8 * hf + 2 * e], sc[kb][8 * hf + 2 * e + 1]);
         }
+        pend = keep;
 
         if (STATS && tid == 0) {
             nkept += keep;
@@ -244,8 +252,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
                 word = 0;
             }
         }
-        if (t > 0) store_k();
-        __syncthreads();  // next K tile in LDS; V^T reads of this tile done
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sc[kb] = sn[kb];
+    }
+    if (pend) {  // PV of the last kept tile (tile 0)
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        lds_barrier();
+        pv(vslot[0], ppend);
     }
 
     // ---- epilogue: O = acc / l (bf16), lse = ln(sum) in natural log
