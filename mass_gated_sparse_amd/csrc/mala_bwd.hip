@@ -40,6 +40,12 @@ constexpr int BQ = 128, BK = 64, D = 128;
 }  // namespace bwdk
 
 // ------------------------------------------------------------------------- dQ
+// One workgroup per query block (4 waves x 32 rows), key tiles from the
+// diagonal back.  Backward thresholds depend only on the final lse, so the
+// vote of a tile never waits for another tile's post-score work: while tile t
+// is finished (its V in flight), the scores and the vote of tile t-1 are
+// computed.  K tiles stream into a three-slot LDS ring two tiles ahead by
+// direct global->LDS loads; V is requested right after a keep decision.
 template <bool GATED, bool STATS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -47,9 +53,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const float* __restrict__ thr, bf16_t* __restrict__ dq, int BH, int L, int nqb, int words, float scale,
     float scale_log2, int32_t* __restrict__ kept, int32_t* __restrict__ legal, uint32_t* __restrict__ bits) {
     using namespace bwdk;
-    __shared__ __attribute__((aligned(16))) uint8_t ksm2[2][BK * 256];  // K tile t in ksm2[t & 1]
-    __shared__ __attribute__((aligned(16))) uint8_t vsm[BK * 256];
-    __shared__ int vote_sm[4];
+    __shared__ __attribute__((aligned(1024))) uint8_t kring[3][BK * 256];  // K tile t in kring[t % 3]
+    __shared__ __attribute__((aligned(1024))) uint8_t vtile[BK * 256];
+    __shared__ int vote_sm[2][4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     const int qb = nqb - 1 - int(blockIdx.x) / BH;
@@ -78,13 +84,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
         for (int r = 0; r < 16; ++r) gacc[db][r] = 0.f;
     const int jmax = (min(qb * BQ + BQ, L) - 1) / BK;
 
-    u32x4 kreg[4];
-    auto load_k = [&](int t) {
+    // 64-row tile t -> 16 segments of 4 rows; wave w issues segments 4w..4w+3:
+    // row 16w + 4it + l/16 of the tile, physical chunk l%16 (rows past L clamped).
+    const int drow = 16 * wave + (lane >> 4);
+    const int dchk = (lane & 15) << 3;
+    auto tile_dma = [&](const bf16_t* g, uint8_t* dst, int t) {
+        const uint32_t la = lds_addr_of(dst) + 4096 * wave;
+        const int rmax = L - 1 - t * BK;
+        const bf16_t* gt = g + long(t) * BK * D;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int jg = t * BK + it * 16 + (tid >> 4);
-            kreg[it] = (jg < L) ? *reinterpret_cast<const u32x4*>(kh + long(jg) * D + (tid & 15) * 8) : z4;
+            const int r = drow + 4 * it;
+            dma16(gt + min(r, rmax) * D + (dchk ^ (rowkey(r) << 3)), __builtin_amdgcn_readfirstlane(la + 1024 * it));
         }
+    };
+    int koff[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) koff[s] = swz(j, 2 * s + hl);
+    int troff[4][2];
+    tr_offsets(lane, troff);
+
+    // S^T (keys x rows) of a tile: A = K rows from LDS, B = Q (registers)
+    auto scores = [&](const uint8_t* kt, f32x16* sacc) {
+        const uint32_t kb0 = lds_addr_of(kt);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(kb0 + 8192 * kb) + koff[s]);
+                sacc[kb] = mfma32(a, qf[s], sacc[kb]);
+            }
+        }
+    };
+    // visibility (causal, in range) of register r of key block kb on tile t
+    auto visible = [&](int t, int kb, int r) {
+        const int key = t * BK + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+        return t < 2 * qb || (key <= row && key < L);
+    };
+    auto vote_of = [&](int t, const f32x16* sacc) {
+        bool vote = false;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) vote |= visible(t, kb, r) && sacc[kb][r] >= th;
+        return wave_any(vote);
     };
 
     int nkept = 0;
@@ -92,84 +137,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     if (STATS && bits && tid == 0)
         for (int w = (jmax >> 5) + 1; w < words; ++w) bits[(long(bh) * nqb + qb) * words + w] = 0u;
 
-    auto store_k = [&](uint8_t* dst) {
-#pragma unroll
-        for (int it = 0; it < 4; ++it) *reinterpret_cast<u32x4*>(dst + swz(it * 16 + (tid >> 4), tid & 15)) = kreg[it];
-    };
-
-    load_k(jmax);
-    store_k(ksm2[jmax & 1]);
-    __syncthreads();
+    // prologue: K(jmax) (and K(jmax-1)) requested; scores + vote of tile jmax
+    tile_dma(kh, kring[jmax % 3], jmax);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    lds_barrier();
+    if (jmax >= 1) tile_dma(kh, kring[(jmax - 1) % 3], jmax - 1);
+    f32x16 sc[2];  // scores of the tile being voted on
+    scores(kring[jmax % 3], sc);
+    if (GATED) {
+        const bool wv = vote_of(jmax, sc);
+        if (lane == 0) vote_sm[jmax & 1][wave] = wv ? 1 : 0;
+    }
 
     for (int t = jmax; t >= 0; --t) {
-        uint8_t* ksm = ksm2[t & 1];
-        if (t > 0) load_k(t - 1);
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(ksm + swz(32 * kb + j, 2 * s + hl));
-                sacc[kb] = mfma32(a, qf[s], sacc[kb]);
-            }
-        }
-        const bool diag = t >= 2 * qb;
-        bool keep = true;
-        if (GATED) {
-            bool vote = false;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = t * BK + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    const bool vis = !diag || (key <= row && key < L);
-                    vote |= vis && sacc[kb][r] >= th;
-                }
-            const bool wv = wave_any(vote);
-            if (lane == 0) vote_sm[wave] = wv ? 1 : 0;
-        }
-        // Every wave has finished the previous iteration, so the other K buffer
-        // and the V buffer are free again.
-        __syncthreads();
-        if (GATED) keep = (vote_sm[0] | vote_sm[1] | vote_sm[2] | vote_sm[3]) != 0;
-        if (t > 0) store_k(ksm2[(t - 1) & 1]);
+        // Everything issued in the previous iteration has landed: K(t-1) (and
+        // the V tile that iteration consumed).
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        lds_barrier();  // vote flags of tile t and K(t-1) visible; previous V reads done
+        int vflags = 1;
+        if (GATED) vflags = vote_sm[t & 1][0] | vote_sm[t & 1][1] | vote_sm[t & 1][2] | vote_sm[t & 1][3];
+        const bool keep = vflags != 0;
+        if (keep) tile_dma(vh, vtile, t);
+        if (t >= 2) tile_dma(kh, kring[(t - 2) % 3], t - 2);
+        // P = exp(s - lse) (zero on invisible entries) as bf16 B operands; step
+        // (kb, hf) holds score registers 8hf .. 8hf+7 of key block kb
+        u32x4 pk[2][2];
         if (keep) {
-            // V tile (row-major, swizzled) for dP^T = V dO^T
-            u32x4 vreg[4];
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int jg = t * BK + it * 16 + (tid >> 4);
-                vreg[it] = (jg < L) ? *reinterpret_cast<const u32x4*>(vh + long(jg) * D + (tid & 15) * 8) : z4;
-            }
-            // P = exp(s - lse) (zero on invisible entries)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = t * BK + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    const bool vis = !diag || (key <= row && key < L);
-                    sacc[kb][r] = vis ? fast_exp2(fmaf(sacc[kb][r], scale_log2, -l2)) : 0.f;
-                }
-#pragma unroll
-            for (int it = 0; it < 4; ++it)
-                *reinterpret_cast<u32x4*>(vsm + swz(it * 16 + (tid >> 4), tid & 15)) = vreg[it];
-            __syncthreads();  // V tile and the next K tile are visible
-            // dP^T (keys x rows) = V dO^T
-            f32x16 pacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) pacc[kb][r] = 0.f;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(vsm + swz(32 * kb + j, 2 * s + hl));
-                    pacc[kb] = mfma32(a, of[s], pacc[kb]);
-                }
-            }
-            // dS^T = P^T (dP^T - D) as bf16 B operands
-            u32x4 dsf[2][2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -177,19 +170,64 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r0 = 8 * hf + 2 * e;
-                        dsf[kb][hf][e] = pack_bf16x2(sacc[kb][r0] * (pacc[kb][r0] - Di),
-                                                     sacc[kb][r0 + 1] * (pacc[kb][r0 + 1] - Di));
+                        const float p0 = visible(t, kb, r0) ? fast_exp2(fmaf(sc[kb][r0], scale_log2, -l2)) : 0.f;
+                        const float p1 =
+                            visible(t, kb, r0 + 1) ? fast_exp2(fmaf(sc[kb][r0 + 1], scale_log2, -l2)) : 0.f;
+                        pk[kb][hf][e] = pack_bf16x2(p0, p1);
                     }
-            // dQ^T (d x rows) += K^T dS^T ; K^T read transposed from the K tile
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // scores and vote of the next tile while V(t) is in flight
+        if (t >= 1) {
+            scores(kring[(t - 1) % 3], sc);
+            if (GATED) {
+                const bool wv = vote_of(t - 1, sc);
+                if (lane == 0) vote_sm[(t - 1) & 1][wave] = wv ? 1 : 0;
+            }
+        }
+        if (keep) {
+            // V(t) was issued just before K(t-2); wait for both (this kernel may
+            // also have register-spill traffic in flight, so no partial counts)
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+            lds_barrier();  // V(t) visible
+            __builtin_amdgcn_sched_barrier(0);
+            // dP^T (keys x rows) = V dO^T
+            f32x16 pacc[2];
+            const uint32_t vb0 = lds_addr_of(vtile);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) pacc[kb][r] = 0.f;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(vb0 + 8192 * kb) + koff[s]);
+                    pacc[kb] = mfma32(a, of[s], pacc[kb]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // dS^T = P^T (dP^T - D), P taken from its bf16 operand copy, in place
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r0 = 8 * hf + 2 * e;
+                        const uint32_t w = pk[kb][hf][e];
+                        pk[kb][hf][e] = pack_bf16x2(__uint_as_float(w << 16) * (pacc[kb][r0] - Di),
+                                                    __uint_as_float(w & 0xffff0000u) * (pacc[kb][r0 + 1] - Di));
+                    }
+            __builtin_amdgcn_sched_barrier(0);
+            // dQ^T (d x rows) += K^T dS^T ; K^T read transposed from tile t's slot
+            const uint32_t kt0 = lds_addr_of(kring[t % 3]);
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const u32x4 a = tr_operand(ksm, 32 * kb + 16 * hf, db, lane);
-                        gacc[db] = mfma32(a, dsf[kb][hf], gacc[db]);
-                    }
+                    for (int hf = 0; hf < 2; ++hf)
+                        gacc[db] = mfma32(tr_operand_at(kt0 + 256 * (32 * kb + 16 * hf), troff[db]), pk[kb][hf],
+                                          gacc[db]);
         }
         if (STATS && tid == 0) {
             nkept += keep;
@@ -199,7 +237,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
                 word = 0;
             }
         }
-        if (!keep) __syncthreads();  // the next K tile is visible
     }
     if (rvalid) {
         bf16_t* grow = dq + hoff + long(row) * D;
@@ -267,17 +304,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
     // Direct loads of one 128x128 tile: 32 segments of 4 rows (1 KiB); wave w
     // issues segments 8w..8w+7; lane l of a segment fills physical chunk l%16
     // of row l/16, i.e. it reads the logical chunk that the swizzle puts there.
-    auto tile_async = [&](const bf16_t* g, uint8_t* dst, int r0) {
+    // Per-lane source offsets are fixed; rows past L are clamped on the last
+    // block only.  Completion is awaited explicitly at the end of the block.
+    int gofs[8];
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int seg = wave * 8 + it;
-            const int row = 4 * seg + (lane >> 4);
-            const int chunk = (lane & 15) ^ rowkey(row);
-            const int grow = min(r0 + row, L - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(g + hoff + long(grow) * D + chunk * 8),
-                                             (lds_void*)(dst + seg * 1024), 16, 0, 0);
+    for (int it = 0; it < 8; ++it) {
+        const int rt = 4 * it + (lane >> 4);
+        gofs[it] = (32 * wave + rt) * D + (((lane & 15) ^ rowkey(rt)) << 3);
+    }
+    auto tile_async = [&](const bf16_t* g, uint8_t* dst, int r0) {
+        const uint32_t la = lds_addr_of(dst) + 8192 * wave;
+        if (r0 + BQ <= L) {
+            const bf16_t* gt = g + hoff + long(r0) * D;
+#pragma unroll
+            for (int it = 0; it < 8; ++it) dma16(gt + gofs[it], __builtin_amdgcn_readfirstlane(la + 1024 * it));
+        } else {
+#pragma unroll
+            for (int it = 0; it < 8; ++it) dma_segment(g + hoff, r0, L - r0, dst, 8 * wave + it, lane);
         }
     };
+    int qoff[8];  // normal (row-major) operand reads: row j of a 32-row block, chunk 2s + hl
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qoff[s] = swz(j, 2 * s + hl);
+    int troff[4][2];
+    tr_offsets(lane, troff);
     // Per-row state of a block: loaded raw (row index clamped) into registers
     // before the tile prefetch is issued, written to LDS (with the padding-row
     // defaults) only at the end of the iteration, so waiting for these loads
@@ -318,10 +368,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
             for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(qs + swz(32 * rb + j, 2 * s + hl));
+                const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(lds_addr_of(qs) + 8192 * rb) + qoff[s]);
                 sacc[rb] = mfma32(a, kf[s], sacc[rb]);
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
         const bool diag = qb == c;
         bool keep = tile_exists;
         if (GATED) {
@@ -351,41 +402,39 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
         if (aux_bits && keep && (wave & 1) == 0 && lane == 0)
             atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (tw >> 5)], 1u << (tw & 31));
         if (keep) {
-            // P = exp(s - lse) (zero where invisible; lse2 = +inf on rows past L)
+            // P = exp(s - lse) (zero where invisible; lse2 = +inf on rows past L),
+            // kept only as bf16 B operands: step (rb, hf) holds rows
+            // 32rb + 16hf + 8(e/4) + 4hl + e%4 of this lane's key.
+            u32x4 pf[4][2];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int rl = 32 * rb + 8 * g + 4 * hl;
                     const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[1][rl]);
+                    float p[4];
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
                         const int rowg = r0 + rl + x;
                         const bool vis = kvalid && (!diag || key <= rowg);
-                        sacc[rb][4 * g + x] = vis ? fast_exp2(fmaf(sacc[rb][4 * g + x], scale_log2, -lz[x])) : 0.f;
+                        p[x] = vis ? fast_exp2(fmaf(sacc[rb][4 * g + x], scale_log2, -lz[x])) : 0.f;
                     }
+                    pf[rb][g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
+                    pf[rb][g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
                 }
+            __builtin_amdgcn_sched_barrier(0);
             // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
-            {
-                u32x4 pf[4][2];
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            pf[rb][hf][e] = pack_bf16x2(sacc[rb][8 * hf + 2 * e], sacc[rb][8 * hf + 2 * e + 1]);
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                        for (int hf = 0; hf < 2; ++hf) {
-                            const u32x4 a = tr_operand(os, 32 * rb + 16 * hf, db, lane);
-                            dvacc[db] = mfma32(a, pf[rb][hf], dvacc[db]);
-                        }
-            }
-            // dP (rows x keys) = dO V^T ; dS = P (dP - D)
+                    for (int hf = 0; hf < 2; ++hf) {
+                        const u32x4 a = tr_operand_at(lds_addr_of(os) + 256 * (32 * rb + 16 * hf), troff[db]);
+                        dvacc[db] = mfma32(a, pf[rb][hf], dvacc[db]);
+                    }
+            __builtin_amdgcn_sched_barrier(0);
+            // dP (rows x keys) = dO V^T ; dS = P (dP - D), P taken from its bf16 operand copy
             u32x4 dsf[4][2];
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb) {
@@ -394,21 +443,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
                 for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(os + swz(32 * rb + j, 2 * s + hl));
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(lds_addr_of(os) + 8192 * rb) + qoff[s]);
                     pacc = mfma32(a, vf[s], pacc);
                 }
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[2][32 * rb + 8 * g + 4 * hl]);
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) pacc[4 * g + x] = sacc[rb][4 * g + x] * (pacc[4 * g + x] - dd[x]);
+                    const uint32_t w0 = pf[rb][g >> 1][2 * (g & 1)], w1 = pf[rb][g >> 1][2 * (g & 1) + 1];
+                    const float p0 = __uint_as_float(w0 << 16), p1 = __uint_as_float(w0 & 0xffff0000u);
+                    const float p2 = __uint_as_float(w1 << 16), p3 = __uint_as_float(w1 & 0xffff0000u);
+                    dsf[rb][g >> 1][2 * (g & 1)] =
+                        pack_bf16x2(p0 * (pacc[4 * g + 0] - dd[0]), p1 * (pacc[4 * g + 1] - dd[1]));
+                    dsf[rb][g >> 1][2 * (g & 1) + 1] =
+                        pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
                 }
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        dsf[rb][hf][e] = pack_bf16x2(pacc[8 * hf + 2 * e], pacc[8 * hf + 2 * e + 1]);
             }
+            __builtin_amdgcn_sched_barrier(0);
             // dK^T (d x keys) += Q^T dS
 #pragma unroll
             for (int db = 0; db < 4; ++db)
@@ -416,13 +466,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
                 for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
-                        const u32x4 a = tr_operand(qs, 32 * rb + 16 * hf, db, lane);
+                        const u32x4 a = tr_operand_at(lds_addr_of(qs) + 256 * (32 * rb + 16 * hf), troff[db]);
                         dkacc[db] = mfma32(a, dsf[rb][hf], dkacc[db]);
                     }
         }
         if (more) stats_store(sn);
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's direct loads into the next buffer have landed
-        __syncthreads();                // next buffer complete; every wave is done with this one
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffer landed
+        lds_barrier();                       // next buffer complete; every wave is done with this one
     };
 
     // prologue: first block into buffer A
@@ -430,8 +480,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
     tile_async(dout, osA, c * BQ);
     stats_load(c * BQ);
     stats_store(stA);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    lds_barrier();
     for (int qb = c; qb < nqb; ++qb) {
         const bool odd = (qb - c) & 1;
         block(qb, odd ? qsB : qsA, odd ? osB : osA, odd ? stB : stA, odd ? qsA : qsB, odd ? osA : osB,
