@@ -126,28 +126,27 @@ def main():
 
     n_legal = B * H * legal_tiles(L, *tile)
 
-    # ---- timed steps
+    # ---- timed steps: each kernel is bracketed by events that the library
+    # records on the stream it launches on (mala_stats.events)
     def run(tau, steps, warmup):
-        ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)] for n in ("fwd", "bwd", "dec")}
         for _ in range(warmup):
             ops.fwd_into(q, k, v, o, lse, tau, tile)
             ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws_b, tile)
             ops.decode_into(qd, kc, vc, Lk, od, lsed, tau, ws_d, split, wd.bk)
         torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(steps)]
         t_start = time.perf_counter()
-        for i in range(steps):
-            ev["fwd"][2 * i].record()
-            ops.fwd_into(q, k, v, o, lse, tau, tile)
-            ev["fwd"][2 * i + 1].record()
-            ev["bwd"][2 * i].record()
-            ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws_b, tile)
-            ev["bwd"][2 * i + 1].record()
-            ev["dec"][2 * i].record()
-            ops.decode_into(qd, kc, vc, Lk, od, lsed, tau, ws_d, split, wd.bk)
-            ev["dec"][2 * i + 1].record()
+        for e in evs:
+            ops.fwd_into(q, k, v, o, lse, tau, tile, stats={"events": e[0:2]})
+            ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws_b, tile, stats={"events": e[2:6]})
+            ops.decode_into(qd, kc, vc, Lk, od, lsed, tau, ws_d, split, wd.bk, stats={"events": e[6:8]})
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t_start) * 1e3 / steps
-        ms = {n: float(np.mean([ev[n][2 * i].elapsed_time(ev[n][2 * i + 1]) for i in range(steps)])) for n in ev}
+
+        def avg(a, b):
+            return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+        ms = {"fwd": avg(0, 1), "bwd": avg(2, 5), "bwd_prep": avg(2, 3), "dkdv": avg(3, 4), "dq": avg(4, 5),
+              "dec": avg(6, 7)}
         return wall, ms
 
     dense_fwd = 2.0 * B * H * L * L * d
@@ -158,28 +157,42 @@ def main():
     fk, bk_, dkp, dlg = stats_pass(args.tau)
     log(f"tau={args.tau}: fwd kept {fk}/{n_legal}, bwd kept {bk_}/{n_legal}, decode kept {dkp}/{dlg}")
     wall, ms = run(args.tau, args.steps, args.warmup)
-    log(f"tau={args.tau}: step {wall:.2f} ms  fwd {ms['fwd']:.2f}  bwd {ms['bwd']:.2f}  decode {ms['dec']:.3f}")
+    log(f"tau={args.tau}: step {wall:.2f} ms  fwd {ms['fwd']:.2f}  bwd {ms['bwd']:.2f} (dK/dV {ms['dkdv']:.2f}, "
+        f"dQ {ms['dq']:.2f})  decode {ms['dec']:.3f}")
     out_tau0 = None
     if not args.no_tau0 and args.tau != 0.0:
         wall0, ms0 = run(0.0, args.steps, args.warmup)
-        log(f"tau=0: step {wall0:.2f} ms  fwd {ms0['fwd']:.2f}  bwd {ms0['bwd']:.2f}  decode {ms0['dec']:.3f}")
+        log(f"tau=0: step {wall0:.2f} ms  fwd {ms0['fwd']:.2f}  bwd {ms0['bwd']:.2f} (dK/dV {ms0['dkdv']:.2f}, "
+            f"dQ {ms0['dq']:.2f})  decode {ms0['dec']:.3f}")
         out_tau0 = {"ms_per_step": wall0, "fwd_ms": ms0["fwd"], "bwd_ms": ms0["bwd"], "decode_ms": ms0["dec"],
+                    "dkdv_ms": ms0["dkdv"], "dq_ms": ms0["dq"],
                     "speedup_fwd": ms0["fwd"] / ms["fwd"], "speedup_bwd": ms0["bwd"] / ms["bwd"],
                     "speedup_decode": ms0["dec"] / ms["dec"], "speedup_step": wall0 / wall}
 
-    # ---- roofline of the forward kernel (one kernel per mala_fwd call, timed live)
+    # ---- rooflines: algorithmic work per launch / live average launch duration
     tile_flop = 2.0 * tile[0] * tile[1] * d
-    fwd_alg_flop = tile_flop * (n_legal + fk)  # QK on every legal tile, PV on kept tiles
-    fwd_tflops = fwd_alg_flop / (ms["fwd"] * 1e-3) / 1e12
-    roofline = {"kernel": "fwd_bf16_d128 (mala_fwd)", "bound": "mfma", "achieved": fwd_tflops,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": fwd_tflops / PEAK_BF16_TFLOPS,
-                "traffic": None,
-                "per_unit": f"2*{tile[0]}*{tile[1]}*{d} FLOP per legal tile (QK) + same per kept tile (PV)",
-                "units_per_launch": {"legal_tiles": n_legal, "kept_tiles": fk}}
-    dec_bytes = Bd * wd.Hkv * Lk * d * 2 * (1.0 + dkp / dlg)  # K always, V of kept tiles
-    decode_roof = {"bound": "hbm", "achieved": dec_bytes / (ms["dec"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                   "unit": "GB/s", "frac": dec_bytes / (ms["dec"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                   "per_unit": "256 B of K per key always + 256 B of V per key of a kept tile"}
+    per_tile = f"2*{tile[0]}*{tile[1]}*{d} FLOP per tile product"
+    traffic = load_traffic()
+    kern = {
+        "fwd_bf16_d128": (ms["fwd"], tile_flop * (n_legal + fk), "mfma",
+                          f"QK on every legal tile + PV on each kept tile; {per_tile}"),
+        "bwd_dkdv_bf16_d128": (ms["dkdv"], tile_flop * (n_legal + 3 * bk_), "mfma",
+                               f"S on every legal tile + dV, dP, dK on each kept tile; {per_tile}"),
+        "bwd_dq_bf16_d128": (ms["dq"], tile_flop * (n_legal + 2 * bk_), "mfma",
+                             f"S on every legal tile + dP, dQ on each kept tile; {per_tile}"),
+        "decode_split_bf16_d128": (ms["dec"], Bd * wd.Hkv * Lk * d * 2 * (1.0 + dkp / dlg), "hbm",
+                                   "256 B of K per cached key always + 256 B of V per key of a kept tile"),
+    }
+    rooflines = {}
+    for name, (t_ms, work, bound, per_unit) in kern.items():
+        if bound == "mfma":
+            ach, peak, unit = work / (t_ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = work / (t_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        rooflines[name] = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+                           "traffic": traffic.get(name), "kernel": name, "ms": t_ms,
+                           "work_per_launch": work, "per_unit": per_unit}
+    roofline = rooflines[max(rooflines, key=lambda n: rooflines[n]["ms"])]
 
     sweep = None if args.no_sweep else sweep32k(torch, ops, args.steps, args.warmup)
 
@@ -201,17 +214,40 @@ def main():
                                "(B16 Hq32 Hkv8 Lk131073 d128, split 4096, 64-key tiles)",
                    "tau": args.tau, "global_batch": B, "seq_len": L, "parallelism": "none (one GPU's 4-head share)"},
         "fwd_ms": ms["fwd"], "bwd_ms": ms["bwd"], "decode_ms": ms["dec"],
+        "bwd_kernels_ms": {"prep": ms["bwd_prep"], "dkdv": ms["dkdv"], "dq": ms["dq"]},
         "fwd_dense_tflops": dense_fwd / (ms["fwd"] * 1e-3) / 1e12,
         "bwd_dense_tflops": dense_bwd / (ms["bwd"] * 1e-3) / 1e12,
         "decode_dense_tflops": dense_dec / (ms["dec"] * 1e-3) / 1e12,
         "kept_frac": {"fwd": fk / n_legal, "bwd": bk_ / n_legal, "decode": dkp / dlg},
         "tau0": out_tau0,
         "roofline": roofline,
-        "decode_roofline": decode_roof,
+        "kernel_rooflines": rooflines,
         "sweep32k": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
+
+
+def load_traffic():
+    """Measured HBM bytes per launch of each kernel, from the committed counter
+    summary profiles/hbm_traffic.json (FETCH_SIZE + WRITE_SIZE scaled by the
+    copy-kernel calibration).  An entry is used only while the sha1 of the
+    kernel's source file equals the one recorded with the counters; once the
+    kernel has changed its traffic is unknown (None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        rec = json.load(f)
+    out = {}
+    for name, r in rec.get("kernels", {}).items():
+        src = os.path.join(ROOT, r["source"])
+        if os.path.exists(src):
+            with open(src, "rb") as f:
+                if hashlib.sha1(f.read()).hexdigest() == r["source_sha1"]:
+                    out[name] = r["bytes_per_launch"]
+    return out
 
 
 def micro(torch):

@@ -86,6 +86,12 @@ typedef struct {
  *   keep_bits_dkdv uint32 [B, H, nqb, words], mala_bwd only: the decisions as
  *             taken by the dK/dV pass (the dQ pass writes keep_bits); the two
  *             passes recompute the same scores and must agree bit for bit.
+ *   events    up to 4 hipEvent_t handles (NULL entries skipped), recorded on
+ *             `stream` around the call's kernels: mala_fwd and mala_decode
+ *             record events[0] before and events[1] after their kernels;
+ *             mala_bwd records events[0] before the row-state kernel,
+ *             events[1] before the dK/dV pass, events[2] before the dQ pass and
+ *             events[3] after it.  For per-kernel timing by the caller.
  * These are debug/measurement outputs: the library never reads them back and
  * backward does not consume anything forward wrote here.
  */
@@ -94,6 +100,7 @@ typedef struct {
     int32_t* legal;
     uint32_t* keep_bits;
     uint32_t* keep_bits_dkdv;
+    void* events[4];
 } mala_stats;
 
 /*

@@ -97,7 +97,10 @@ mala_status mala_fwd(const void* q, const void* k, const void* v, int B, int H, 
     a.gated = tau != 0.f;
     if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = dtype == MALA_BF16 ? mala::launch_fwd_bf16(a, s) : mala::launch_simple_fwd_f32(a, s);
+    hipEvent_t e0 = stats ? (hipEvent_t)stats->events[0] : nullptr, e1 = stats ? (hipEvent_t)stats->events[1] : nullptr;
+    hipError_t e = mala::mark(e0, s);
+    if (e == hipSuccess) e = dtype == MALA_BF16 ? mala::launch_fwd_bf16(a, s) : mala::launch_simple_fwd_f32(a, s);
+    if (e == hipSuccess) e = mala::mark(e1, s);
     return hip_status(e, "mala_fwd launch");
 }
 
@@ -141,12 +144,14 @@ mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o,
     if (stats) {
         a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits;
         a.aux_bits = stats->keep_bits_dkdv;
+        for (int i = 0; i < 4; ++i) a.ev[i] = (hipEvent_t)stats->events[i];
         if (a.aux_bits) {  // the dK/dV pass ORs its decisions in
             hipError_t e0 = hipMemsetAsync(a.aux_bits, 0, size_t(B) * H * a.nqb * a.words * sizeof(uint32_t), s);
             if (e0 != hipSuccess) return hip_status(e0, "mala_bwd stats clear");
         }
     }
-    hipError_t e = mala::launch_bwd_prep(a, s);
+    hipError_t e = mala::mark(a.ev[0], s);
+    if (e == hipSuccess) e = mala::launch_bwd_prep(a, s);
     if (e != hipSuccess) return hip_status(e, "mala_bwd prep launch");
     e = a.f32 ? mala::launch_simple_bwd_f32(a, s) : mala::launch_bwd_bf16(a, s);
     return hip_status(e, "mala_bwd launch");
@@ -191,7 +196,12 @@ mala_status mala_decode(const void* q, const void* kcache, const void* vcache, i
     a.log2_lq = log2f(float(Lk));
     a.gated = tau != 0.f;
     if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; }
-    return hip_status(mala::launch_decode_bf16(a, reinterpret_cast<hipStream_t>(stream)), "mala_decode launch");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipEvent_t e0 = stats ? (hipEvent_t)stats->events[0] : nullptr, e1 = stats ? (hipEvent_t)stats->events[1] : nullptr;
+    hipError_t e = mala::mark(e0, s);
+    if (e == hipSuccess) e = mala::launch_decode_bf16(a, s);
+    if (e == hipSuccess) e = mala::mark(e1, s);
+    return hip_status(e, "mala_decode launch");
 }
 
 }  // extern "C"

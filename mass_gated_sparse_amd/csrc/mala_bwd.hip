@@ -512,6 +512,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     const int ncol = (a.L + 127) / 128;
     dim3 g1(unsigned(ncol) * unsigned(BH)), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
     const bool st = a.kept || a.legal || a.bits;
+    hipError_t e = mark(a.ev[1], s);
+    if (e != hipSuccess) return e;
     if (a.gated)
         hipLaunchKernelGGL((bwd_dkdv_bf16_d128<true>), g1, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
                            (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dk,
@@ -520,7 +522,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((bwd_dkdv_bf16_d128<false>), g1, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
                            (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dk,
                            (bf16_t*)a.dv, BH, a.L, a.nqb, ncol, a.words, a.scale, a.scale_log2, a.aux_bits);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(a.ev[2], s);
     if (e != hipSuccess) return e;
 #define MALA_DQ_LAUNCH(G, S)                                                                                  \
     hipLaunchKernelGGL((bwd_dq_bf16_d128<G, S>), g2, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,       \
@@ -534,7 +537,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
         else MALA_DQ_LAUNCH(false, false);
     }
 #undef MALA_DQ_LAUNCH
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(a.ev[3], s);
+    return e;
 }
 
 }  // namespace mala

@@ -34,6 +34,7 @@ struct BwdArgs {
     bool gated, f32;
     int32_t *kept, *legal;
     uint32_t *bits, *aux_bits;  // aux_bits: decisions as seen by the dK/dV kernel (debug)
+    hipEvent_t ev[4];           // optional timing events (see mala_stats)
 };
 
 struct DecArgs {
@@ -48,6 +49,9 @@ struct DecArgs {
     int32_t *kept, *legal;
     uint32_t* bits;
 };
+
+// Records e on s when e is non-null.
+inline hipError_t mark(hipEvent_t e, hipStream_t s) { return e ? hipEventRecord(e, s) : hipSuccess; }
 
 hipError_t launch_simple_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t s);

@@ -337,11 +337,14 @@ hipError_t launch_simple_bwd_f32(const BwdArgs& a, hipStream_t s) {
     constexpr int BQ = 64, BK = 64, D = 64;
     dim3 g1(a.ntiles, a.B * a.H), b1(BK);
     dim3 g2(a.nqb, a.B * a.H), b2(BQ);
+    hipError_t e = mark(a.ev[1], s);
+    if (e != hipSuccess) return e;
     if (a.gated) {
         hipLaunchKernelGGL((simple_bwd_dkdv_f32<BQ, BK, D, true>), g1, b1, 0, s, (const float*)a.q,
                            (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.Dv, a.lse2, a.thr,
                            (float*)a.dk, (float*)a.dv, a.L, a.nqb, a.ntiles, a.scale, a.scale_log2, a.aux_bits,
                            a.words);
+        e = mark(a.ev[2], s);
         hipLaunchKernelGGL((simple_bwd_dq_f32<BQ, BK, D, true>), g2, b2, 0, s, (const float*)a.q,
                            (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.Dv, a.lse2, a.thr,
                            (float*)a.dq, a.L, a.nqb, a.scale, a.scale_log2, a.kept, a.legal, a.bits, a.words);
@@ -350,11 +353,14 @@ hipError_t launch_simple_bwd_f32(const BwdArgs& a, hipStream_t s) {
                            (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.Dv, a.lse2, a.thr,
                            (float*)a.dk, (float*)a.dv, a.L, a.nqb, a.ntiles, a.scale, a.scale_log2, a.aux_bits,
                            a.words);
+        e = mark(a.ev[2], s);
         hipLaunchKernelGGL((simple_bwd_dq_f32<BQ, BK, D, false>), g2, b2, 0, s, (const float*)a.q,
                            (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.Dv, a.lse2, a.thr,
                            (float*)a.dq, a.L, a.nqb, a.scale, a.scale_log2, a.kept, a.legal, a.bits, a.words);
     }
-    return hipGetLastError();
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) e = mark(a.ev[3], s);
+    return e;
 }
 
 }  // namespace mala

@@ -53,10 +53,19 @@ def prefill_stats_buffers(B, H, L, tile, device, dkdv=False):
 
 
 def _stats_struct(st):
+    """Stats dict -> mala_stats.  Tensors under kept/legal/keep_bits/keep_bits_dkdv;
+    optional "events": up to 4 torch.cuda.Event(enable_timing=True), recorded by
+    the library around its kernels (see include/mala.h)."""
     if st is None:
         return None
-    return ctypes.byref(Stats(*(ctypes.c_void_p(st[n].data_ptr()) if n in st else None
-                                for n in ("kept", "legal", "keep_bits", "keep_bits_dkdv"))))
+    s = Stats(*(ctypes.c_void_p(st[n].data_ptr()) if n in st else None
+                for n in ("kept", "legal", "keep_bits", "keep_bits_dkdv")))
+    for i, ev in enumerate(st.get("events", ())):
+        if ev is not None:
+            if not ev.cuda_event:
+                ev.record()  # torch creates the underlying event lazily
+            s.events[i] = ev.cuda_event
+    return ctypes.byref(s)
 
 
 def fwd_into(q, k, v, o, lse, tau, tile=None, scale=0.0, stats=None, stream=None):

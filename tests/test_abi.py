@@ -1,0 +1,169 @@
+"""Host-side checks of the C ABI in include/mala.h (no GPU needed).
+
+The library must load, export every function the header declares, and reject
+bad arguments on the host before any HIP call: every call below fails
+validation, so the dummy pointers handed in are never dereferenced and no
+kernel is launched.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mala.h")
+
+OK, INVALID, UNSUPPORTED, HIPERR = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return sorted(set(re.findall(r"\b(mala_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mass_gated_sparse_amd import _lib
+    from mass_gated_sparse_amd.build import lib_path
+    if not os.path.exists(lib_path()):
+        pytest.fail("libmala.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_declares_the_documented_entry_points():
+    fns = declared_functions()
+    for name in ("mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size", "mala_decode_workspace_size",
+                 "mala_status_string", "mala_last_error", "mala_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from mass_gated_sparse_amd import _lib
+    raw = ctypes.CDLL(lib._name)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, missing
+    assert sorted(_lib.EXPORTS) == declared_functions()
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mala_version() == 100
+    assert lib.mala_status_string(OK) == b"ok"
+    assert lib.mala_status_string(INVALID) == b"invalid argument"
+    assert lib.mala_status_string(UNSUPPORTED) == b"unsupported configuration"
+    assert lib.mala_status_string(HIPERR) == b"HIP runtime error"
+    assert lib.mala_status_string(7) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    from mass_gated_sparse_amd._lib import MALA_BF16, Tile
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for B, H, L in [(1, 4, 131072), (2, 3, 1000), (1, 1, 1)]:
+        assert lib.mala_bwd_workspace_size(B, H, L, 128, MALA_BF16, Tile(128, 64)) == 3 * a256(B * H * L * 4)
+    assert lib.mala_bwd_workspace_size(0, 4, 10, 128, MALA_BF16, Tile(128, 64)) == 0
+    for B, Hq, Hkv, Lk, d, split in [(16, 32, 8, 131073, 128, 4096), (1, 4, 1, 2500, 128, 1024), (3, 8, 2, 64, 128, 64)]:
+        nsplit = math.ceil(Lk / split)
+        assert lib.mala_decode_workspace_size(B, Hq, Hkv, Lk, d, split) == a256(B * Hq * nsplit * (d + 2) * 4)
+    assert lib.mala_decode_workspace_size(1, 4, 1, 0, 128, 4096) == 0
+
+
+P = ctypes.c_void_p(1 << 20)  # dummy, never dereferenced (validation fails first)
+ALIGNED_WS = ctypes.c_void_p(1 << 20)
+MISALIGNED_WS = ctypes.c_void_p((1 << 20) + 16)
+
+
+def fwd(lib, q=P, B=1, H=2, Hkv=2, L=256, d=128, dt=0, tau=1.0, tile=(128, 64), o=P, lse=P):
+    from mass_gated_sparse_amd._lib import Tile
+    return lib.mala_fwd(q, P, P, B, H, Hkv, L, d, dt, tau, Tile(*tile), 0.0, o, lse, None, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    ({"q": None}, INVALID, "null input"),
+    ({"o": None}, INVALID, "null output"),
+    ({"L": 0}, INVALID, "positive"),
+    ({"B": -1}, INVALID, "positive"),
+    ({"tau": -0.5}, INVALID, "tau"),
+    ({"tau": float("nan")}, INVALID, "tau"),
+    ({"dt": 5}, INVALID, "dtype"),
+    ({"tile": (0, 64)}, INVALID, "tile"),
+    ({"Hkv": 1}, UNSUPPORTED, "H == Hkv"),
+    ({"d": 64}, UNSUPPORTED, "instantiation"),
+    ({"tile": (64, 64)}, UNSUPPORTED, "instantiation"),
+    ({"dt": 1}, UNSUPPORTED, "instantiation"),  # f32 path is d=64 only
+    ({"B": 1 << 12, "H": 1 << 12, "Hkv": 1 << 12, "L": 1 << 10}, UNSUPPORTED, "too large"),
+])
+def test_fwd_rejects(lib, kw, status, msg):
+    assert fwd(lib, **kw) == status
+    assert msg in lib.mala_last_error().decode()
+
+
+def bwd(lib, ws=ALIGNED_WS, ws_bytes=1 << 30, dq=P, dout=P, tau=1.0, d=128):
+    from mass_gated_sparse_amd._lib import Tile
+    return lib.mala_bwd(P, P, P, P, P, dout, 1, 2, 2, 256, d, 0, tau, Tile(128, 64), 0.0, dq, P, P, None,
+                        ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    ({"dout": None}, INVALID, "dout"),
+    ({"dq": None}, INVALID, "gradient"),
+    ({"ws": None}, INVALID, "workspace too small"),
+    ({"ws_bytes": 100}, INVALID, "workspace too small"),
+    ({"ws": MISALIGNED_WS}, INVALID, "aligned"),
+    ({"tau": -1.0}, INVALID, "tau"),
+    ({"d": 96}, UNSUPPORTED, "instantiation"),
+])
+def test_bwd_rejects(lib, kw, status, msg):
+    assert bwd(lib, **kw) == status
+    assert msg in lib.mala_last_error().decode()
+
+
+def dec(lib, q=P, B=2, Hq=8, Hkv=2, Lk=5000, Lcap=8192, d=128, dt=0, tau=1.0, split=4096, bk=64,
+        ws=ALIGNED_WS, ws_bytes=1 << 30):
+    return lib.mala_decode(q, P, P, B, Hq, Hkv, Lk, Lcap, d, dt, tau, split, bk, 0.0, P, P, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    ({"q": None}, INVALID, "null"),
+    ({"Lk": 0}, INVALID, "positive"),
+    ({"Lcap": 4000}, INVALID, "Lcap"),
+    ({"tau": -2.0}, INVALID, "tau"),
+    ({"Hq": 6, "Hkv": 4}, INVALID, "multiple"),
+    ({"dt": 3}, INVALID, "dtype"),
+    ({"dt": 1}, UNSUPPORTED, "instantiation"),
+    ({"d": 64}, UNSUPPORTED, "instantiation"),
+    ({"bk": 32}, UNSUPPORTED, "instantiation"),
+    ({"Hq": 32, "Hkv": 2}, UNSUPPORTED, "instantiation"),  # group of 16 > 8
+    ({"split": 4000}, UNSUPPORTED, "instantiation"),      # not a multiple of 64
+    ({"ws_bytes": 64}, INVALID, "workspace too small"),
+    ({"ws": MISALIGNED_WS}, INVALID, "aligned"),
+])
+def test_decode_rejects(lib, kw, status, msg):
+    assert dec(lib, **kw) == status
+    assert msg in lib.mala_last_error().decode()
+
+
+def test_error_is_cleared_by_next_call(lib):
+    assert fwd(lib, q=None) == INVALID
+    assert lib.mala_last_error() != b""
+    assert dec(lib, Lk=0) == INVALID
+    assert b"positive" in lib.mala_last_error()
+
+
+def test_python_wrappers_reject_host_tensors():
+    import torch
+    from mass_gated_sparse_amd import ops
+    x = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        ops.fwd(x, x, x, 1.0)
+    with pytest.raises(ValueError, match="GPU"):
+        ops.decode(x[0], x, x, 128, 1.0)
+
+
+def test_python_error_carries_library_message(lib):
+    from mass_gated_sparse_amd import _lib
+    assert fwd(lib, tau=-1.0) == INVALID
+    with pytest.raises(_lib.MalaError, match="tau must be >= 0"):
+        _lib.check("mala_fwd", INVALID)
