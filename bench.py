@@ -51,12 +51,19 @@ def main():
     ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison run")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 32K tau sweep")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0,
-                    help="query blocks in the CPU-oracle sample (0: one per OpenMP thread, at most 16)")
+                    help="query blocks in the CPU-oracle sample (0: three per OpenMP thread, at most 48)")
     ap.add_argument("--micro", action="store_true",
                     help="only run the ceiling microbenchmarks (MFMA, LDS, transposed LDS, HBM)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter calibration)")
+    ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="no GPU: turn rocprofv3 csv output dirs (kernel trace of this bench; FETCH_SIZE and "
+                         "WRITE_SIZE passes of a short bench run; the same two passes of --copy-calibration) "
+                         "into profiles/*.md and profiles/hbm_traffic.json")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -199,7 +206,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
-        nb = args.cpu_sample_blocks or min(16, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+        nb = args.cpu_sample_blocks or 3 * min(16, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
         cpu = cpu_baseline(wx, wd, xp, xd0, nb, args.tau)
         log(f"cpu baseline took {time.time() - t0:.1f}s")
 
@@ -228,13 +235,115 @@ def main():
     print(json.dumps(res))
 
 
-def load_traffic():
-    """Measured HBM bytes per launch of each kernel, from the committed counter
-    summary profiles/hbm_traffic.json (FETCH_SIZE + WRITE_SIZE scaled by the
-    copy-kernel calibration).  An entry is used only while the sha1 of the
-    kernel's source file equals the one recorded with the counters; once the
-    kernel has changed its traffic is unknown (None)."""
+# kernel -> (instantiation timed by the bench at tau > 0, source files it is built from)
+PROFILED = {
+    "fwd_bf16_d128": ("fwd_bf16_d128<true, false>", ["mala_fwd.hip"]),
+    "bwd_dkdv_bf16_d128": ("bwd_dkdv_bf16_d128<true>", ["mala_bwd.hip"]),
+    "bwd_dq_bf16_d128": ("bwd_dq_bf16_d128<true, false>", ["mala_bwd.hip"]),
+    "decode_split_bf16_d128": ("decode_split_bf16_d128<4, true, false>", ["mala_decode.hip"]),
+}
+COMMON_SOURCES = ["mala_device.hpp", "mala_kernels.hpp"]
+CSRC = "mass_gated_sparse_amd/csrc"
+
+
+def sources_sha1(files):
     import hashlib
+    h = hashlib.sha1()
+    for f in files + COMMON_SOURCES:
+        with open(os.path.join(ROOT, CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _counter_per_dispatch(d, counter):
+    """{kernel name: [value per dispatch]} from a rocprofv3 --pmc csv dir (values summed over
+    the counter's instances within a dispatch)."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (_, name), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    # kernel-time summary of the bench command
+    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    lines = ["# Kernel time: bench.py, 128K training step + 128K decode", "",
+             "Command (from the repository root, on one MI355X):", "",
+             "    cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --kernel-trace --stats "
+             "--output-format csv -d <dir> -o run -- python3 bench.py --steps 3 --warmup 1 --no-sweep "
+             "--no-cpu-baseline", "",
+             "Runs at tau=1 and tau=0 (stats passes, warmup and timed steps all included).", "",
+             "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    with open(os.path.join(prof, "kernel_trace_train128k_decode128k.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    # HBM traffic: counters scaled by what they read for a copy of known size
+    cal = {}
+    for cdir, counter in ((cfetch_dir, "FETCH_SIZE"), (cwrite_dir, "WRITE_SIZE")):
+        vals = _counter_per_dispatch(cdir, counter)
+        big = max((v for vs in vals.values() for v in vs))
+        cal[counter] = (1 << 29) / (big * 1024.0)  # 512 MiB read and written per copy launch
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    rec = {"unit": "bytes per launch", "calibration": {
+        "copy_bytes": 1 << 29, "fetch_factor": cal["FETCH_SIZE"], "write_factor": cal["WRITE_SIZE"],
+        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
+                   "python3 bench.py --copy-calibration"},
+        "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- python3 "
+                   "bench.py --steps 1 --warmup 0 --no-tau0 --no-sweep --no-cpu-baseline",
+        "kernels": {}}
+    md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)", "",
+          f"Commands: `{rec['command']}`; calibration: `{rec['calibration']['command']}` "
+          "(torch copy of 512 MiB bf16).", "",
+          f"Calibration factors (bytes per counter KiB / 1024): fetch {cal['FETCH_SIZE']:.4f}, "
+          f"write {cal['WRITE_SIZE']:.4f}.", "",
+          "| kernel | dispatches | FETCH KiB | WRITE KiB | scaled GB per launch |", "|---|---:|---:|---:|---:|"]
+    for kname, (inst, srcs) in PROFILED.items():
+        fv = [v for n, vs in fetch.items() if inst in n for v in vs]
+        wv = [v for n, vs in write.items() if inst in n for v in vs]
+        if not fv or not wv:
+            continue
+        fk, wk = float(np.mean(fv)), float(np.mean(wv))
+        b = fk * 1024 * cal["FETCH_SIZE"] + wk * 1024 * cal["WRITE_SIZE"]
+        rec["kernels"][kname] = {"instantiation": inst, "dispatches": len(fv), "fetch_kib": fk, "write_kib": wk,
+                                 "bytes_per_launch": b, "sources": [f"{CSRC}/{x}" for x in srcs + COMMON_SOURCES],
+                                 "sources_sha1": sources_sha1(srcs)}
+        md.append(f"| `{inst}` | {len(fv)} | {fk:.0f} | {wk:.0f} | {b / 1e9:.3f} |")
+    with open(os.path.join(prof, "hbm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(os.path.join(prof, "hbm_traffic_train128k_decode128k.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(rec["kernels"], indent=1))
+
+
+def load_traffic():
+    """Measured HBM bytes per launch of each kernel from profiles/hbm_traffic.json.
+    An entry is used only while the sha1 of the kernel's sources still equals
+    the one recorded with the counters: once a kernel has changed, its traffic
+    is unknown (None)."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return {}
@@ -242,11 +351,8 @@ def load_traffic():
         rec = json.load(f)
     out = {}
     for name, r in rec.get("kernels", {}).items():
-        src = os.path.join(ROOT, r["source"])
-        if os.path.exists(src):
-            with open(src, "rb") as f:
-                if hashlib.sha1(f.read()).hexdigest() == r["source_sha1"]:
-                    out[name] = r["bytes_per_launch"]
+        if name in PROFILED and sources_sha1(PROFILED[name][1]) == r["sources_sha1"]:
+            out[name] = r["bytes_per_launch"]
     return out
 
 
