@@ -7,8 +7,12 @@ CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["mala_api.hip", "mala_fwd.hip", "mala_bwd.hip", "mala_decode.hip", "mala_simple.hip"]
 ARCH = "gfx950"
 # -packed-fp32-ops: no packed fp32 VALU instructions are generated.
+# -amdgpu-mfma-vgpr-form: MFMA results go to arch VGPRs first; kernels that
+#   run one wave per SIMD then keep long-lived operands in AGPRs without the
+#   per-iteration AGPR<->VGPR copies and scratch spills the default form gives.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def lib_path() -> str:

@@ -31,6 +31,8 @@
 // M[i/4 + 4e][i%4], e = 0..3 -- four consecutive rows at one column.
 #include <float.h>
 
+#include <type_traits>
+
 #include "mala_kernels.hpp"
 
 namespace mala {
@@ -350,9 +352,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
         }
     };
 
-    // one query block: compute from (qs, os, st) while the next block streams into (qn, on, sn)
-    auto block = [&](int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ], uint8_t* qn,
-                     uint8_t* on, float (*sn)[BQ]) {
+    // one query block: compute from (qs, os, st) while the next block streams
+    // into (qn, on, sn).  Only the diagonal block (qb == c) needs visibility
+    // masks: it is the only block with keys past some row, and the only block
+    // of the last column, whose keys may run past L.  Elsewhere every key is
+    // visible to every row.
+    auto block = [&](auto diag_tag, int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ],
+                     uint8_t* qn, uint8_t* on, float (*sn)[BQ]) {
+        constexpr bool diag = decltype(diag_tag)::value;
         const int r0 = qb * BQ;
         const bool more = qb + 1 < nqb;
         if (more) {
@@ -373,7 +380,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        const bool diag = qb == c;
         bool keep = tile_exists;
         if (GATED) {
             bool vote = false;
@@ -386,8 +392,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
                         const f32x4 th = *reinterpret_cast<const f32x4*>(&st[0][rl]);
 #pragma unroll
                         for (int x = 0; x < 4; ++x) {
-                            const int rowg = r0 + rl + x;
-                            const bool vis = kvalid && (!diag || key <= rowg);
+                            const bool vis = !diag || (kvalid && key <= r0 + rl + x);
                             vote |= vis && sacc[rb][4 * g + x] >= th[x];
                         }
                     }
@@ -415,8 +420,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
                     float p[4];
 #pragma unroll
                     for (int x = 0; x < 4; ++x) {
-                        const int rowg = r0 + rl + x;
-                        const bool vis = kvalid && (!diag || key <= rowg);
+                        // keys past L only reach their own (unstored) dK/dV rows: no mask needed
+                        const bool vis = !diag || key <= r0 + rl + x;
                         p[x] = vis ? fast_exp2(fmaf(sacc[rb][4 * g + x], scale_log2, -lz[x])) : 0.f;
                     }
                     pf[rb][g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
@@ -482,10 +487,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
     stats_store(stA);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     lds_barrier();
-    for (int qb = c; qb < nqb; ++qb) {
-        const bool odd = (qb - c) & 1;
-        block(qb, odd ? qsB : qsA, odd ? osB : osA, odd ? stB : stA, odd ? qsA : qsB, odd ? osA : osB,
-              odd ? stA : stB);
+    // diagonal block from buffer A, then pairs of blocks B->A, A->B with static buffers
+    block(std::true_type{}, c, qsA, osA, stA, qsB, osB, stB);
+    for (int qb = c + 1; qb < nqb; qb += 2) {
+        block(std::false_type{}, qb, qsB, osB, stB, qsA, osA, stA);
+        if (qb + 1 < nqb) block(std::false_type{}, qb + 1, qsA, osA, stA, qsB, osB, stB);
     }
 
     // accumulators hold dK^T, dV^T: lane = key, register r of block db = d 32db + 8(r/4) + 4hl + r%4
