@@ -259,44 +259,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 }
 
 // ---------------------------------------------------------------------- dK/dV
-// One workgroup per 128 keys.  The Q and dO tiles of successive query blocks
-// are double-buffered in LDS: while block qb is being computed from one
-// buffer, block qb+1 streams into the other with direct global->LDS loads
-// (no registers involved).  Rows past L are read clamped to row L-1 and are
-// masked out of every vote and every product (P = 0 there).
+// One workgroup of 8 waves per 64-key tile, i.e. per vote column: a skipped
+// (query block, key tile) pair skips the whole workgroup's post-score work.
+// Wave w owns keys 32(w&1) .. +31 of the tile and rows 32(w>>1) .. +31 of
+// every query block, so two waves share each SIMD.  K of the wave's keys is
+// held in registers (B operand of S = Q K^T); the V tile sits in LDS (B
+// operand of dP = dO V^T).  The Q and dO tiles of successive query blocks are
+// double-buffered in LDS: while block qb is computed from one buffer, block
+// qb+1 streams into the other with direct global->LDS loads.  Each wave
+// accumulates dK^T and dV^T over its own 32 rows of every block; the four
+// row quarters are summed through LDS at the end.  Rows past L are read
+// clamped to row L-1 and are masked out of every vote and product (their
+// thr and lse are +inf, so P = 0 there).
 template <bool GATED>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
     const float* __restrict__ thr, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BH, int L, int nqb,
-    int ncol, int words, float scale, float scale_log2, uint32_t* __restrict__ aux_bits) {
+    int words, float scale, float scale_log2, uint32_t* __restrict__ aux_bits) {
     using namespace bwdk;
-    __shared__ __attribute__((aligned(1024))) uint8_t qsA[BQ * 256];
-    __shared__ __attribute__((aligned(1024))) uint8_t osA[BQ * 256];
-    __shared__ __attribute__((aligned(1024))) uint8_t qsB[BQ * 256];
-    __shared__ __attribute__((aligned(1024))) uint8_t osB[BQ * 256];
+    // buf[0..3]: Q and dO tiles of two query blocks (A: buf[0], buf[1]; B:
+    // buf[2], buf[3]); reused at the end for the cross-wave reduction.
+    __shared__ __attribute__((aligned(1024))) uint8_t buf[4][BQ * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t vtile[BK * 256];
     __shared__ __attribute__((aligned(16))) float stA[3][BQ];  // thr, lse2, D of the block's rows
     __shared__ __attribute__((aligned(16))) float stB[3][BQ];
-    __shared__ int vote_sm[2][4];
+    __shared__ __attribute__((aligned(16))) int vote_sm[2][8];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
-    const int c = int(blockIdx.x) / BH;  // 128-key column; longest (c = 0) first
+    const int kb = wave & 1, rq = wave >> 1;
+    const int t = int(blockIdx.x) / BH;  // 64-key tile; longest (t = 0) first
     const int bh = int(blockIdx.x) % BH;
     const long hoff = long(bh) * L * D;
-    const int key = 128 * c + 32 * wave + j;
+    const int key = t * BK + 32 * kb + j;
     const bool kvalid = key < L;
-    const int tw = 2 * c + (wave >> 1);  // this wave's key tile
-    const bool tile_exists = tw * BK < L;
+    const int qb0 = (t * BK) / BQ;  // first query block that sees the tile (its diagonal block)
     const u32x4 z4 = {0u, 0u, 0u, 0u};
-    (void)ncol;
+    uint8_t* qsA = buf[0];
+    uint8_t* osA = buf[1];
+    uint8_t* qsB = buf[2];
+    uint8_t* osB = buf[3];
 
-    // K and V of this wave's 32 keys as B operands (lane = key, 8 contiguous d)
-    u32x4 kf[8], vf[8];
+    // K of this wave's 32 keys as B operands (lane = key, 8 contiguous d)
+    u32x4 kf[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < 8; ++s)
         kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(k + hoff + long(key) * D + 16 * s + 8 * hl) : z4;
-        vf[s] = kvalid ? *reinterpret_cast<const u32x4*>(v + hoff + long(key) * D + 16 * s + 8 * hl) : z4;
-    }
     f32x16 dvacc[4], dkacc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -304,44 +312,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
         for (int r = 0; r < 16; ++r) { dvacc[db][r] = 0.f; dkacc[db][r] = 0.f; }
 
     // Direct loads of one 128x128 tile: 32 segments of 4 rows (1 KiB); wave w
-    // issues segments 8w..8w+7; lane l of a segment fills physical chunk l%16
-    // of row l/16, i.e. it reads the logical chunk that the swizzle puts there.
-    // Per-lane source offsets are fixed; rows past L are clamped on the last
-    // block only.  Completion is awaited explicitly at the end of the block.
-    int gofs[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int rt = 4 * it + (lane >> 4);
-        gofs[it] = (32 * wave + rt) * D + (((lane & 15) ^ rowkey(rt)) << 3);
-    }
+    // issues segments 4w..4w+3 (rows 16w .. 16w+15); lane l of a segment fills
+    // physical chunk l%16 of row l/16, i.e. it reads the logical chunk that the
+    // swizzle puts there.  Rows past L read row L-1 instead (masked later).
     auto tile_async = [&](const bf16_t* g, uint8_t* dst, int r0) {
-        const uint32_t la = lds_addr_of(dst) + 8192 * wave;
-        if (r0 + BQ <= L) {
-            const bf16_t* gt = g + hoff + long(r0) * D;
+        const uint32_t la = lds_addr_of(dst) + 4096 * wave;
+        const bf16_t* gb = g + hoff + long(r0) * D;  // wave-uniform
+        const int lim = L - 1 - r0;
 #pragma unroll
-            for (int it = 0; it < 8; ++it) dma16(gt + gofs[it], __builtin_amdgcn_readfirstlane(la + 1024 * it));
-        } else {
-#pragma unroll
-            for (int it = 0; it < 8; ++it) dma_segment(g + hoff, r0, L - r0, dst, 8 * wave + it, lane);
+        for (int it = 0; it < 4; ++it) {
+            const int rt = 16 * wave + 4 * it + (lane >> 4);
+            const uint32_t off = uint32_t(min(rt, lim) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
+            dma16s(gb, off, __builtin_amdgcn_readfirstlane(la + 1024 * it));
         }
     };
-    int qoff[8];  // normal (row-major) operand reads: row j of a 32-row block, chunk 2s + hl
+    // Operand read offsets within a Q or dO tile, this wave's row quarter
+    // folded in: normal (row-major) reads of row 32rq + j, chunk 2s + hl, and
+    // the transposed reads of tr_operand_at (rowbase 32rq).
+    int qoff[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qoff[s] = swz(j, 2 * s + hl);
+    for (int s = 0; s < 8; ++s) qoff[s] = swz(j, 2 * s + hl) + 8192 * rq;
     int troff[4][2];
     tr_offsets(lane, troff);
-    // Per-row state of a block: loaded raw (row index clamped) into registers
-    // before the tile prefetch is issued, written to LDS (with the padding-row
-    // defaults) only at the end of the iteration, so waiting for these loads
-    // never waits for the prefetch.
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        troff[db][0] += 8192 * rq;
+        troff[db][1] += 8192 * rq;
+    }
+    // Per-row state of a block, held by threads 0..127: loaded raw (row index
+    // clamped) into registers before the tile prefetch is issued, written to
+    // LDS (with the padding-row defaults) only at the end of the block, so
+    // waiting for these loads never waits for the prefetch.
     float stv[3];
     int st_row = 0;
     auto stats_load = [&](int r0) {
-        st_row = r0 + (tid & (BQ - 1));
-        const long ri = long(bh) * L + min(st_row, L - 1);
-        stv[0] = thr[ri];
-        stv[1] = lse2[ri];
-        stv[2] = Dv[ri];
+        if (tid < BQ) {
+            st_row = r0 + tid;
+            const long ri = long(bh) * L + min(st_row, L - 1);
+            stv[0] = thr[ri];
+            stv[1] = lse2[ri];
+            stv[2] = Dv[ri];
+        }
     };
     auto stats_store = [&](float (*st)[BQ]) {
         if (tid < BQ) {
@@ -351,11 +362,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
             st[2][tid] = ok ? stv[2] : 0.f;
         }
     };
+    // this wave's 32 keys of V, addressed with the Q-tile offsets
+    const uint32_t va = lds_addr_of(vtile) + 8192 * kb - 8192 * rq;
 
-    // one query block: compute from (qs, os, st) while the next block streams
-    // into (qn, on, sn).  Only the diagonal block (qb == c) needs visibility
+    // One query block: compute from (qs, os, st) while the next block streams
+    // into (qn, on, sn).  Only the diagonal block (qb == qb0) needs visibility
     // masks: it is the only block with keys past some row, and the only block
-    // of the last column, whose keys may run past L.  Elsewhere every key is
+    // of the last tiles, whose keys may run past L.  Elsewhere every key is
     // visible to every row.
     auto block = [&](auto diag_tag, int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ],
                      uint8_t* qn, uint8_t* on, float (*sn)[BQ]) {
@@ -367,167 +380,172 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_d128(
             tile_async(q, qn, r0 + BQ);
             tile_async(dout, on, r0 + BQ);
         }
-        // S (rows x keys) = Q K^T: 4 row blocks of 32, 8 k-steps
-        f32x16 sacc[4];
+        const uint32_t qa = lds_addr_of(qs), oa = lds_addr_of(os);
+        // S (32 rows x 32 keys) = Q K^T; register r holds row 32rq + 8(r/4) + 4hl + r%4, key j
+        f32x16 sacc;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[rb][r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(lds_addr_of(qs) + 8192 * rb) + qoff[s]);
-                sacc[rb] = mfma32(a, kf[s], sacc[rb]);
-            }
-        }
+        for (int s = 0; s < 8; ++s) sacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(qa) + qoff[s]), kf[s], sacc);
         __builtin_amdgcn_sched_barrier(0);
-        bool keep = tile_exists;
+        bool keep = true;
         if (GATED) {
             bool vote = false;
-            if (tile_exists) {
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
+            for (int g = 0; g < 4; ++g) {
+                const int rl = 32 * rq + 8 * g + 4 * hl;  // 4 consecutive rows
+                const f32x4 th = *reinterpret_cast<const f32x4*>(&st[0][rl]);
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int rl = 32 * rb + 8 * g + 4 * hl;  // 4 consecutive rows
-                        const f32x4 th = *reinterpret_cast<const f32x4*>(&st[0][rl]);
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            const bool vis = !diag || (kvalid && key <= r0 + rl + x);
-                            vote |= vis && sacc[rb][4 * g + x] >= th[x];
-                        }
-                    }
+                for (int x = 0; x < 4; ++x) {
+                    const bool vis = !diag || (kvalid && key <= r0 + rl + x);
+                    vote |= vis && sacc[4 * g + x] >= th[x];
+                }
             }
             const bool wv = wave_any(vote);
             const int par = qb & 1;
             if (lane == 0) vote_sm[par][wave] = wv ? 1 : 0;
             lds_barrier();  // the next block's prefetch stays in flight
-            const int pair = wave >> 1;
-            keep = tile_exists && (vote_sm[par][2 * pair] | vote_sm[par][2 * pair + 1]) != 0;
+            const u32x4 va0 = *reinterpret_cast<const u32x4*>(&vote_sm[par][0]);
+            const u32x4 va1 = *reinterpret_cast<const u32x4*>(&vote_sm[par][4]);
+            keep = ((va0[0] | va0[1] | va0[2] | va0[3]) | (va1[0] | va1[1] | va1[2] | va1[3])) != 0u;
         }
-        if (aux_bits && keep && (wave & 1) == 0 && lane == 0)
-            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (tw >> 5)], 1u << (tw & 31));
+        if (aux_bits && keep && tid == 0)
+            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (t >> 5)], 1u << (t & 31));
         if (keep) {
             // P = exp(s - lse) (zero where invisible; lse2 = +inf on rows past L),
-            // kept only as bf16 B operands: step (rb, hf) holds rows
-            // 32rb + 16hf + 8(e/4) + 4hl + e%4 of this lane's key.
-            u32x4 pf[4][2];
+            // kept only as bf16 B operands: step hf holds registers 8hf .. 8hf+7.
+            u32x4 pf[2];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+            for (int g = 0; g < 4; ++g) {
+                const int rl = 32 * rq + 8 * g + 4 * hl;
+                const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[1][rl]);
+                float p[4];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int rl = 32 * rb + 8 * g + 4 * hl;
-                    const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[1][rl]);
-                    float p[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        // keys past L only reach their own (unstored) dK/dV rows: no mask needed
-                        const bool vis = !diag || key <= r0 + rl + x;
-                        p[x] = vis ? fast_exp2(fmaf(sacc[rb][4 * g + x], scale_log2, -lz[x])) : 0.f;
-                    }
-                    pf[rb][g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
-                    pf[rb][g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
+                for (int x = 0; x < 4; ++x) {
+                    // keys past L only reach their own (unstored) dK/dV rows: no mask needed
+                    const bool vis = !diag || key <= r0 + rl + x;
+                    p[x] = vis ? fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[x])) : 0.f;
                 }
+                pf[g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
+                pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
+            }
             __builtin_amdgcn_sched_barrier(0);
             // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const u32x4 a = tr_operand_at(lds_addr_of(os) + 256 * (32 * rb + 16 * hf), troff[db]);
-                        dvacc[db] = mfma32(a, pf[rb][hf], dvacc[db]);
-                    }
+                for (int hf = 0; hf < 2; ++hf)
+                    dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
             __builtin_amdgcn_sched_barrier(0);
-            // dP (rows x keys) = dO V^T ; dS = P (dP - D), P taken from its bf16 operand copy
-            u32x4 dsf[4][2];
+            // dP (32 rows x 32 keys) = dO V^T ; dS = P (dP - D), P taken from its bf16 operand copy
+            f32x16 pacc;
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                f32x16 pacc;
+            for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+            for (int s = 0; s < 8; ++s)
+                pacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(oa) + qoff[s]),
+                              *reinterpret_cast<const u32x4*>(lds_ptr(va) + qoff[s]), pacc);
+            u32x4 dsf[2];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(lds_addr_of(os) + 8192 * rb) + qoff[s]);
-                    pacc = mfma32(a, vf[s], pacc);
-                }
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[2][32 * rb + 8 * g + 4 * hl]);
-                    const uint32_t w0 = pf[rb][g >> 1][2 * (g & 1)], w1 = pf[rb][g >> 1][2 * (g & 1) + 1];
-                    const float p0 = __uint_as_float(w0 << 16), p1 = __uint_as_float(w0 & 0xffff0000u);
-                    const float p2 = __uint_as_float(w1 << 16), p3 = __uint_as_float(w1 & 0xffff0000u);
-                    dsf[rb][g >> 1][2 * (g & 1)] =
-                        pack_bf16x2(p0 * (pacc[4 * g + 0] - dd[0]), p1 * (pacc[4 * g + 1] - dd[1]));
-                    dsf[rb][g >> 1][2 * (g & 1) + 1] =
-                        pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
-                }
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[2][32 * rq + 8 * g + 4 * hl]);
+                const uint32_t w0 = pf[g >> 1][2 * (g & 1)], w1 = pf[g >> 1][2 * (g & 1) + 1];
+                const float p0 = __uint_as_float(w0 << 16), p1 = __uint_as_float(w0 & 0xffff0000u);
+                const float p2 = __uint_as_float(w1 << 16), p3 = __uint_as_float(w1 & 0xffff0000u);
+                dsf[g >> 1][2 * (g & 1)] = pack_bf16x2(p0 * (pacc[4 * g + 0] - dd[0]), p1 * (pacc[4 * g + 1] - dd[1]));
+                dsf[g >> 1][2 * (g & 1) + 1] =
+                    pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
             }
             __builtin_amdgcn_sched_barrier(0);
             // dK^T (d x keys) += Q^T dS
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        const u32x4 a = tr_operand_at(lds_addr_of(qs) + 256 * (32 * rb + 16 * hf), troff[db]);
-                        dkacc[db] = mfma32(a, dsf[rb][hf], dkacc[db]);
-                    }
+                for (int hf = 0; hf < 2; ++hf)
+                    dkacc[db] = mfma32(tr_operand_at(qa + 256 * (16 * hf), troff[db]), dsf[hf], dkacc[db]);
         }
         if (more) stats_store(sn);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffer landed
         lds_barrier();                       // next buffer complete; every wave is done with this one
     };
 
-    // prologue: first block into buffer A
-    tile_async(q, qsA, c * BQ);
-    tile_async(dout, osA, c * BQ);
-    stats_load(c * BQ);
-    stats_store(stA);
+    // prologue: V tile, first block into buffer A
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {  // V tile: segments 2w, 2w+1 (rows 8w .. 8w+7)
+        const int rt = 8 * wave + 4 * it + (lane >> 4);
+        const uint32_t off = uint32_t(min(rt, L - 1 - t * BK) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
+        dma16s(v + hoff + long(t) * BK * D, off, __builtin_amdgcn_readfirstlane(lds_addr_of(vtile) + 2048 * wave + 1024 * it));
+    }
+    tile_async(q, qsA, qb0 * BQ);
+    tile_async(dout, osA, qb0 * BQ);
+    stats_load(qb0 * BQ);
     __builtin_amdgcn_s_waitcnt(0x0f70);
+    stats_store(stA);
     lds_barrier();
-    // diagonal block from buffer A, then pairs of blocks B->A, A->B with static buffers
-    block(std::true_type{}, c, qsA, osA, stA, qsB, osB, stB);
-    for (int qb = c + 1; qb < nqb; qb += 2) {
-        block(std::false_type{}, qb, qsB, osB, stB, qsA, osA, stA);
-        if (qb + 1 < nqb) block(std::false_type{}, qb + 1, qsA, osA, stA, qsB, osB, stB);
+    // diagonal block from buffer A, then alternate B, A, ...  (buffer chosen at
+    // run time so that the operand addresses stay two registers per buffer)
+    block(std::true_type{}, qb0, qsA, osA, stA, qsB, osB, stB);
+    for (int qb = qb0 + 1; qb < nqb; ++qb) {
+        const bool odd = (qb - qb0) & 1;
+        block(std::false_type{}, qb, odd ? qsB : qsA, odd ? osB : osA, odd ? stB : stA, odd ? qsA : qsB,
+              odd ? osA : osB, odd ? stA : stB);
     }
 
-    // accumulators hold dK^T, dV^T: lane = key, register r of block db = d 32db + 8(r/4) + 4hl + r%4
-    if (kvalid) {
-        bf16_t* krow = dk + hoff + long(key) * D;
-        bf16_t* vrow = dv + hoff + long(key) * D;
+    // Sum the four row quarters.  Accumulators hold dK^T, dV^T: lane = key,
+    // register 4g + x of block db = d 32db + 8g + 4hl + x.  Wave w stores its
+    // 16 (db, g) groups as float4 at red[(16w + 4db + g) * 64 + lane]; output
+    // group gi = (kb, 4db + g, lane) sums waves kb, kb + 2, kb + 4, kb + 6.
+    f32x4* red = reinterpret_cast<f32x4*>(&buf[0][0]);
+    auto reduce_store = [&](const f32x16* acc, bf16_t* out, float mul) {
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 wk, wv;
-                wk[0] = pack_bf16x2(dkacc[db][4 * g + 0] * scale, dkacc[db][4 * g + 1] * scale);
-                wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * scale, dkacc[db][4 * g + 3] * scale);
-                wv[0] = pack_bf16x2(dvacc[db][4 * g + 0], dvacc[db][4 * g + 1]);
-                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
-                *reinterpret_cast<u32x2*>(krow + 32 * db + 8 * g + 4 * hl) = wk;
-                *reinterpret_cast<u32x2*>(vrow + 32 * db + 8 * g + 4 * hl) = wv;
+            for (int g = 0; g < 4; ++g)
+                red[(16 * wave + 4 * db + g) * 64 + lane] =
+                    f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gi = tid + 512 * i;
+            const int l = gi & 63, dbg = (gi >> 6) & 15, kh = gi >> 10;
+            f32x4 sum = red[(16 * kh + dbg) * 64 + l];
+#pragma unroll
+            for (int rr = 1; rr < 4; ++rr) {
+                const f32x4 x = red[(16 * (kh + 2 * rr) + dbg) * 64 + l];
+                sum[0] += x[0];
+                sum[1] += x[1];
+                sum[2] += x[2];
+                sum[3] += x[3];
             }
-    }
+            const int kk = t * BK + 32 * kh + (l & 31);
+            if (kk < L) {
+                u32x2 w;
+                w[0] = pack_bf16x2(sum[0] * mul, sum[1] * mul);
+                w[1] = pack_bf16x2(sum[2] * mul, sum[3] * mul);
+                const int d0 = 32 * (dbg >> 2) + 8 * (dbg & 3) + 4 * (l >> 5);
+                *reinterpret_cast<u32x2*>(out + hoff + long(kk) * D + d0) = w;
+            }
+        }
+        lds_barrier();
+    };
+    reduce_store(dkacc, dk, scale);
+    reduce_store(dvacc, dv, 1.f);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     const int BH = a.B * a.H;
-    const int ncol = (a.L + 127) / 128;
-    dim3 g1(unsigned(ncol) * unsigned(BH)), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
+    dim3 g1(unsigned(a.ntiles) * unsigned(BH)), b1(512), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
     const bool st = a.kept || a.legal || a.bits;
     hipError_t e = mark(a.ev[1], s);
     if (e != hipSuccess) return e;
     if (a.gated)
-        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<true>), g1, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
+        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<true>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
                            (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dk,
-                           (bf16_t*)a.dv, BH, a.L, a.nqb, ncol, a.words, a.scale, a.scale_log2, a.aux_bits);
+                           (bf16_t*)a.dv, BH, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.aux_bits);
     else
-        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<false>), g1, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
+        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<false>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
                            (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dk,
-                           (bf16_t*)a.dv, BH, a.L, a.nqb, ncol, a.words, a.scale, a.scale_log2, a.aux_bits);
+                           (bf16_t*)a.dv, BH, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.aux_bits);
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(a.ev[2], s);
     if (e != hipSuccess) return e;

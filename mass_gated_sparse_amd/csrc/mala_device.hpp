@@ -139,6 +139,13 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_addr) : "memory", "m0");
 }
 
+// Same load with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset (the saddr form): one VGPR of address per lane instead of two.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
     return uint32_t(reinterpret_cast<uintptr_t>((lds_void*)const_cast<void*>(p)));
 }
