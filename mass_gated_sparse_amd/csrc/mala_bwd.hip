@@ -48,6 +48,8 @@ constexpr int BQ = 128, BK = 64, D = 128;
 // is finished (its V in flight), the scores and the vote of tile t-1 are
 // computed.  K tiles stream into a three-slot LDS ring two tiles ahead by
 // direct global->LDS loads; V is requested right after a keep decision.
+// Only the tiles at or past 2qb (the diagonal pair) need visibility masks;
+// they are peeled off the loop as compile-time variants.
 template <bool GATED, bool STATS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const float* __restrict__ thr, bf16_t* __restrict__ dq, int BH, int L, int nqb, int words, float scale,
     float scale_log2, int32_t* __restrict__ kept, int32_t* __restrict__ legal, uint32_t* __restrict__ bits) {
     using namespace bwdk;
-    __shared__ __attribute__((aligned(1024))) uint8_t kring[3][BK * 256];  // K tile t in kring[t % 3]
+    __shared__ __attribute__((aligned(1024))) uint8_t kring[3][BK * 256];
     __shared__ __attribute__((aligned(1024))) uint8_t vtile[BK * 256];
     __shared__ int vote_sm[2][4];
 
@@ -67,13 +69,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const bf16_t* vh = v + hoff;
     const int row = qb * BQ + wave * 32 + j;
     const bool rvalid = row < L;
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
 
+    // Q and dO rows as B operands; rows past L read row L-1 (their P is 0:
+    // thr and lse are +inf there)
     u32x4 qf[8], of[8];
+    const long rowc = min(row, L - 1);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-        qf[s] = rvalid ? *reinterpret_cast<const u32x4*>(q + hoff + long(row) * D + 16 * s + 8 * hl) : z4;
-        of[s] = rvalid ? *reinterpret_cast<const u32x4*>(dout + hoff + long(row) * D + 16 * s + 8 * hl) : z4;
+        qf[s] = *reinterpret_cast<const u32x4*>(q + hoff + rowc * D + 16 * s + 8 * hl);
+        of[s] = *reinterpret_cast<const u32x4*>(dout + hoff + rowc * D + 16 * s + 8 * hl);
     }
     const float th = rvalid ? thr[long(bh) * L + row] : INFINITY;
     const float l2 = rvalid ? lse2[long(bh) * L + row] : INFINITY;
@@ -85,19 +89,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 #pragma unroll
         for (int r = 0; r < 16; ++r) gacc[db][r] = 0.f;
     const int jmax = (min(qb * BQ + BQ, L) - 1) / BK;
+    const int tdiag = 2 * qb;  // tiles t >= tdiag reach the diagonal
 
     // 64-row tile t -> 16 segments of 4 rows; wave w issues segments 4w..4w+3:
     // row 16w + 4it + l/16 of the tile, physical chunk l%16 (rows past L clamped).
-    const int drow = 16 * wave + (lane >> 4);
-    const int dchk = (lane & 15) << 3;
-    auto tile_dma = [&](const bf16_t* g, uint8_t* dst, int t) {
-        const uint32_t la = lds_addr_of(dst) + 4096 * wave;
+    auto tile_dma = [&](const bf16_t* g, uint32_t la, int t) {
+        la += 4096 * wave;
         const int rmax = L - 1 - t * BK;
-        const bf16_t* gt = g + long(t) * BK * D;
+        const bf16_t* gt = g + long(t) * BK * D;  // wave-uniform
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int r = drow + 4 * it;
-            dma16(gt + min(r, rmax) * D + (dchk ^ (rowkey(r) << 3)), __builtin_amdgcn_readfirstlane(la + 1024 * it));
+            const int r = 16 * wave + 4 * it + (lane >> 4);
+            const uint32_t off = uint32_t(min(r, rmax) * D + (((lane & 15) ^ rowkey(r)) << 3)) * 2u;
+            dma16s(gt, off, __builtin_amdgcn_readfirstlane(la + 1024 * it));
         }
     };
     int koff[8];
@@ -107,8 +111,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     tr_offsets(lane, troff);
 
     // S^T (keys x rows) of a tile: A = K rows from LDS, B = Q (registers)
-    auto scores = [&](const uint8_t* kt, f32x16* sacc) {
-        const uint32_t kb0 = lds_addr_of(kt);
+    auto scores = [&](uint32_t kb0, f32x16* sacc) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -120,17 +123,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
             }
         }
     };
-    // visibility (causal, in range) of register r of key block kb on tile t
-    auto visible = [&](int t, int kb, int r) {
-        const int key = t * BK + 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-        return t < 2 * qb || (key <= row && key < L);
+    // Scores of a tile at or past tdiag: keys past the row or past L become
+    // -inf, so they neither vote nor carry probability.  Register r of key
+    // block kb holds key t*64 + 32kb + 8(r/4) + 4hl + r%4.  Every key of a
+    // tile below tdiag is visible to every row of the block.
+    auto mask_diag = [&](int t, f32x16* sacc) {
+        const int lim = min(row, L - 1) - t * BK - 4 * hl;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[kb][r] = -INFINITY;
     };
-    auto vote_of = [&](int t, const f32x16* sacc) {
+    auto vote_of = [&](const f32x16* sacc) {
         bool vote = false;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) vote |= visible(t, kb, r) && sacc[kb][r] >= th;
+            for (int r = 0; r < 16; ++r) vote |= sacc[kb][r] >= th;
         return wave_any(vote);
     };
 
@@ -139,28 +149,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     if (STATS && bits && tid == 0)
         for (int w = (jmax >> 5) + 1; w < words; ++w) bits[(long(bh) * nqb + qb) * words + w] = 0u;
 
+    // K ring: ks0 holds tile t, ks1 tile t-1, ks2 is free (tile t-2 goes there)
+    uint32_t ks0 = lds_addr_of(kring[0]), ks1 = lds_addr_of(kring[1]), ks2 = lds_addr_of(kring[2]);
+    const uint32_t vta = lds_addr_of(vtile);
+
     // prologue: K(jmax) (and K(jmax-1)) requested; scores + vote of tile jmax
-    tile_dma(kh, kring[jmax % 3], jmax);
+    tile_dma(kh, ks0, jmax);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     lds_barrier();
-    if (jmax >= 1) tile_dma(kh, kring[(jmax - 1) % 3], jmax - 1);
+    if (jmax >= 1) tile_dma(kh, ks1, jmax - 1);
     f32x16 sc[2];  // scores of the tile being voted on
-    scores(kring[jmax % 3], sc);
+    scores(ks0, sc);
+    mask_diag(jmax, sc);
     if (GATED) {
-        const bool wv = vote_of(jmax, sc);
+        const bool wv = vote_of(sc);
         if (lane == 0) vote_sm[jmax & 1][wave] = wv ? 1 : 0;
     }
 
-    for (int t = jmax; t >= 0; --t) {
-        // Everything issued in the previous iteration has landed: K(t-1) (and
-        // the V tile that iteration consumed).
+    auto step = [&](auto diag_next, int t) {
+        // Everything issued in the previous step has landed: K(t-1) (and the
+        // V tile that step consumed).
         __builtin_amdgcn_s_waitcnt(0x0f70);
-        lds_barrier();  // vote flags of tile t and K(t-1) visible; previous V reads done
+        lds_barrier();  // vote flags of tile t and K(t-1) visible; previous V and K(t+1) reads done
         int vflags = 1;
         if (GATED) vflags = vote_sm[t & 1][0] | vote_sm[t & 1][1] | vote_sm[t & 1][2] | vote_sm[t & 1][3];
         const bool keep = vflags != 0;
-        if (keep) tile_dma(vh, vtile, t);
-        if (t >= 2) tile_dma(kh, kring[(t - 2) % 3], t - 2);
+        if (keep) tile_dma(vh, vta, t);
+        if (t >= 2) tile_dma(kh, ks2, t - 2);
         // P = exp(s - lse) (zero on invisible entries) as bf16 B operands; step
         // (kb, hf) holds score registers 8hf .. 8hf+7 of key block kb
         u32x4 pk[2][2];
@@ -172,64 +187,55 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r0 = 8 * hf + 2 * e;
-                        const float p0 = visible(t, kb, r0) ? fast_exp2(fmaf(sc[kb][r0], scale_log2, -l2)) : 0.f;
-                        const float p1 =
-                            visible(t, kb, r0 + 1) ? fast_exp2(fmaf(sc[kb][r0 + 1], scale_log2, -l2)) : 0.f;
-                        pk[kb][hf][e] = pack_bf16x2(p0, p1);
+                        pk[kb][hf][e] = pack_bf16x2(fast_exp2(fmaf(sc[kb][r0], scale_log2, -l2)),
+                                                    fast_exp2(fmaf(sc[kb][r0 + 1], scale_log2, -l2)));
                     }
         }
         __builtin_amdgcn_sched_barrier(0);
         // scores and vote of the next tile while V(t) is in flight
         if (t >= 1) {
-            scores(kring[(t - 1) % 3], sc);
+            scores(ks1, sc);
+            if (decltype(diag_next)::value) mask_diag(t - 1, sc);
             if (GATED) {
-                const bool wv = vote_of(t - 1, sc);
+                const bool wv = vote_of(sc);
                 if (lane == 0) vote_sm[(t - 1) & 1][wave] = wv ? 1 : 0;
             }
         }
         if (keep) {
-            // V(t) was issued just before K(t-2); wait for both (this kernel may
-            // also have register-spill traffic in flight, so no partial counts)
+            // V(t) was issued just before K(t-2); wait for both
             __builtin_amdgcn_s_waitcnt(0x0f70);
             lds_barrier();  // V(t) visible
             __builtin_amdgcn_sched_barrier(0);
-            // dP^T (keys x rows) = V dO^T
-            f32x16 pacc[2];
-            const uint32_t vb0 = lds_addr_of(vtile);
+            // per 32-key half kb: dP^T (keys x rows) = V dO^T; dS^T = P^T (dP^T - D)
+            // (P from its bf16 operand copy, in place); dQ^T (d x rows) += K^T dS^T
+            // with K^T read transposed from tile t's slot
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
+                f32x16 pacc;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) pacc[kb][r] = 0.f;
+                for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(vb0 + 8192 * kb) + koff[s]);
-                    pacc[kb] = mfma32(a, of[s], pacc[kb]);
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(vta + 8192 * kb) + koff[s]);
+                    pacc = mfma32(a, of[s], pacc);
                 }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // dS^T = P^T (dP^T - D), P taken from its bf16 operand copy, in place
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r0 = 8 * hf + 2 * e;
                         const uint32_t w = pk[kb][hf][e];
-                        pk[kb][hf][e] = pack_bf16x2(__uint_as_float(w << 16) * (pacc[kb][r0] - Di),
-                                                    __uint_as_float(w & 0xffff0000u) * (pacc[kb][r0 + 1] - Di));
+                        pk[kb][hf][e] = pack_bf16x2(__uint_as_float(w << 16) * (pacc[r0] - Di),
+                                                    __uint_as_float(w & 0xffff0000u) * (pacc[r0 + 1] - Di));
                     }
-            __builtin_amdgcn_sched_barrier(0);
-            // dQ^T (d x rows) += K^T dS^T ; K^T read transposed from tile t's slot
-            const uint32_t kt0 = lds_addr_of(kring[t % 3]);
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int db = 0; db < 4; ++db)
 #pragma unroll
                     for (int hf = 0; hf < 2; ++hf)
-                        gacc[db] = mfma32(tr_operand_at(kt0 + 256 * (32 * kb + 16 * hf), troff[db]), pk[kb][hf],
+                        gacc[db] = mfma32(tr_operand_at(ks0 + 256 * (32 * kb + 16 * hf), troff[db]), pk[kb][hf],
                                           gacc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if (STATS && tid == 0) {
             nkept += keep;
@@ -239,7 +245,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
                 word = 0;
             }
         }
-    }
+        const uint32_t done = ks0;
+        ks0 = ks1;
+        ks1 = ks2;
+        ks2 = done;
+    };
+
+    // the tile after t needs masks iff t - 1 >= tdiag (at most one step)
+    int t = jmax;
+    for (; t - 1 >= tdiag; --t) step(std::true_type{}, t);
+    for (; t >= 0; --t) step(std::false_type{}, t);
+
     if (rvalid) {
         bf16_t* grow = dq + hoff + long(row) * D;
 #pragma unroll
