@@ -64,13 +64,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     const bf16_t* vh = v + hoff;
     const int row = qb * BQ + wave * 32 + j;
     const bool rvalid = row < L;
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
 
     // Q as the B operand of S^T = K Q^T: step s holds q[row][16s + 8hl .. +8].
+    // Rows past L read row L-1; they never vote and are never stored.
     u32x4 qf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-        qf[s] = rvalid ? *reinterpret_cast<const u32x4*>(q + hoff + long(row) * D + 16 * s + 8 * hl) : z4;
+        qf[s] = *reinterpret_cast<const u32x4*>(q + hoff + long(min(row, L - 1)) * D + 16 * s + 8 * hl);
 
     f32x16 oacc[4];
 #pragma unroll
@@ -82,24 +82,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     const float inv_scale_log2 = 1.f / scale_log2;
     const int jmax = (min(qb * BQ + BQ, L) - 1) / BK;
 
-    // 64-key tile t -> 16 segments of 4 rows; wave w issues segments 4w..4w+3,
-    // one 16-byte load per lane each.  Per-lane source offsets (row and the
-    // swizzled chunk) are fixed; rows past L are clamped on the last tile only.
-    int gofs[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int rt = 4 * it + (lane >> 4);  // row within the segment group of this wave, mod 16
-        gofs[it] = (16 * wave + rt) * D + (((lane & 15) ^ rowkey(rt)) << 3);
-    }
     auto tile_dma = [&](const bf16_t* g, uint8_t* dst, int t) {
-        const bf16_t* gt = g + long(t) * BK * D;
         const uint32_t la = lds_addr_of(dst) + 4096 * wave;
-        if ((t + 1) * BK <= L) {
+        const int rmax = L - 1 - t * BK;
+        const bf16_t* gt = g + long(t) * BK * D;  // wave-uniform
 #pragma unroll
-            for (int it = 0; it < 4; ++it) dma16(gt + gofs[it], __builtin_amdgcn_readfirstlane(la + 1024 * it));
-        } else {
-#pragma unroll
-            for (int it = 0; it < 4; ++it) dma_segment(g, long(t) * BK, L - t * BK, dst, 4 * wave + it, lane);
+        for (int it = 0; it < 4; ++it) {
+            const int r = 16 * wave + 4 * it + (lane >> 4);
+            const uint32_t off = uint32_t(min(r, rmax) * D + (((lane & 15) ^ rowkey(r)) << 3)) * 2u;
+            dma16s(gt, off, __builtin_amdgcn_readfirstlane(la + 1024 * it));
         }
     };
     int koff[8];  // K operand of step s: row j, chunk 2s + hl
@@ -159,17 +150,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
                     if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
         }
         // ---- test + block vote
+        // lane-local row maximum: the vote needs it, a kept tile's statistics too
+        float mx = sc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
         if (GATED) {
             float thr_raw;
             if (!rvalid) thr_raw = INFINITY;           // padding rows never vote
             else if (lsum == 0.f) thr_raw = -FLT_MAX;  // empty row: any visible key keeps
             else thr_raw = (m2 + fast_log2(lsum) + log2_tau - log2_lq) * inv_scale_log2;
-            bool vote = false;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) vote |= sc[kb][r] >= thr_raw;
-            const bool wv = wave_any(vote);
+            const bool wv = wave_any(mx >= thr_raw);
             if (lane == 0) vote_sm[t & 1][wave] = wv ? 1 : 0;
         }
         // K(t-1) has landed once at most the V loads of tile t+1 are outstanding
@@ -192,11 +184,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
             tile_dma(vh, vslot[t & 1], t);  // V only for kept tiles
             scores(kslot[(t - 1) & 1], sn);
             // statistics (no V needed); P_t = exp2(s*c - m) kept in place
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
             const float mn = fmaxf(m2, mx * scale_log2);
             const float mref = (mn == -INFINITY) ? 0.f : mn;
