@@ -37,6 +37,8 @@
 // i.e. exp(max_j s_ij - m)/l >= tau/Lq_i.  An empty row (l = 0) keeps.
 #include <float.h>
 
+#include <type_traits>
+
 #include "mala_kernels.hpp"
 
 namespace mala {
@@ -128,17 +130,31 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     if (STATS && bits && tid == 0)
         for (int w = (jmax >> 5) + 1; w < words; ++w) bits[(long(bh) * nqb + qb) * words + w] = 0u;
 
-    // prologue: scores of tile jmax; K(jmax-1) requested
+    // prologue: K(jmax) and K(jmax-1) visible; scores of tile jmax; then
+    // K(jmax-2) requested into the slot K(jmax) used
     tile_dma(kh, kslot[jmax & 1], jmax);
+    if (jmax >= 1) tile_dma(kh, kslot[(jmax - 1) & 1], jmax - 1);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     lds_barrier();
-    if (jmax >= 1) tile_dma(kh, kslot[(jmax - 1) & 1], jmax - 1);
-    f32x16 sc[2], sn[2];      // scores of the tile being tested / of the next tile
+    f32x16 sc[2], sn[2];  // scores of the tile being tested / of the next tile
     scores(kslot[jmax & 1], sc);
+    if (jmax >= 2) {
+        lds_barrier();  // every wave is done with K(jmax)
+        tile_dma(kh, kslot[jmax & 1], jmax - 2);
+    }
 
-    u32x4 ppend[2][2];        // P of the previous kept tile (bf16), waiting for its V
-    bool pend = false;        // previous tile kept (its V in flight)
-    for (int t = jmax; t >= 0; --t) {
+    u32x4 ppend[2][2];  // P of the previous kept tile (bf16), waiting for its V
+    bool pend = false;  // previous tile kept (its V in flight)
+    // Per tile t, one barrier.  Before it: the vote of t and the scores of t-1
+    // (K(t-1) has been visible since the previous barrier), so the MFMAs hide
+    // the vote exchange.  After it: the K(t-3) and V(t) requests (each has a
+    // whole step to land), this tile's statistics, the PV of the previous kept
+    // tile t+1 and this tile's rescale.
+    // One step per tile; the tile parity P = t & 1 is a compile-time constant,
+    // so every LDS slot address is a constant (it folds into the instructions'
+    // offset fields) and the score registers are renamed, not copied.
+    auto step = [&](auto par_tag, int t) {
+        constexpr int P = decltype(par_tag)::value;
         // causal mask on the tiles that reach the diagonal: register r of key
         // block kb holds key t*64 + 32kb + 8(r/4) + 4hl + r%4, invisible when > row
         if (t >= 2 * qb) {
@@ -162,27 +178,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
             else if (lsum == 0.f) thr_raw = -FLT_MAX;  // empty row: any visible key keeps
             else thr_raw = (m2 + fast_log2(lsum) + log2_tau - log2_lq) * inv_scale_log2;
             const bool wv = wave_any(mx >= thr_raw);
-            if (lane == 0) vote_sm[t & 1][wave] = wv ? 1 : 0;
+            if (lane == 0) vote_sm[P][wave] = wv ? 1 : 0;
         }
-        // K(t-1) has landed once at most the V loads of tile t+1 are outstanding
-        // (with statistics on, thread 0 also has keep-bit stores in flight)
-        if (pend && !STATS) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
-        else __builtin_amdgcn_s_waitcnt(0x0f70);
-        lds_barrier();  // votes, K(t-1) visible; every wave is done with kslot[t & 1]
-        // The vote flags are read first and used after the K prefetch is issued.
+        if (t >= 1) scores(kslot[1 - P], sn);
+        // K(t-2) and V(t+1), requested in the previous step, have landed (with
+        // statistics on, thread 0 also waits for its keep-bit stores)
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        lds_barrier();  // votes, K(t-2), V(t+1) visible; every wave is done with kslot[1 - P]
         int vflags = 1;
-        if (GATED) vflags = vote_sm[t & 1][0] | vote_sm[t & 1][1] | vote_sm[t & 1][2] | vote_sm[t & 1][3];
-        if (t >= 2) tile_dma(kh, kslot[t & 1], t - 2);  // K(t-2) into the slot K(t) used
+        if (GATED) vflags = vote_sm[P][0] | vote_sm[P][1] | vote_sm[P][2] | vote_sm[P][3];
         const bool keep = vflags != 0;
+        if (t >= 3) tile_dma(kh, kslot[1 - P], t - 3);  // K(t-3) into the slot K(t-1) used
+        if (keep) tile_dma(vh, vslot[P], t);              // V only for kept tiles
 
-        // Next tile's scores in both branches: alone for a skipped tile, and in
-        // one block with this tile's statistics for a kept one, so the
-        // exp/max/sum work interleaves with the MFMAs.  (At t = 0 the "next"
-        // scores read a stale slot and are never used.)
         float alpha = 1.f;
         if (keep) {
-            tile_dma(vh, vslot[t & 1], t);  // V only for kept tiles
-            scores(kslot[(t - 1) & 1], sn);
             // statistics (no V needed); P_t = exp2(s*c - m) kept in place
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
             const float mn = fmaxf(m2, mx * scale_log2);
@@ -200,19 +210,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
             alpha = fast_exp2(m2 - mref);
             lsum = lsum * alpha + lpart;
             m2 = mn;
-        } else {
-            scores(kslot[(t - 1) & 1], sn);
         }
-
         // PV of the previous kept tile (in its own frame), then this tile's rescale
-        if (pend) {
-            if (STATS) __builtin_amdgcn_s_waitcnt(0x0f70);
-            else if (keep && t >= 2) __builtin_amdgcn_s_waitcnt(0x0f78);  // vmcnt(8): K(t-2), V(t) may fly
-            else if (keep || t >= 2) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
-            else __builtin_amdgcn_s_waitcnt(0x0f70);
-            lds_barrier();  // V(t+1) visible
-            pv(vslot[(t + 1) & 1], ppend);
-        }
+        if (pend) pv(vslot[1 - P], ppend);
         if (keep) {
             if (__ballot(alpha != 1.f) != 0ull) {  // skipped when no row's max moved (exact)
 #pragma unroll
@@ -241,6 +241,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) sc[kb] = sn[kb];
+    };
+    using Even = std::integral_constant<int, 0>;
+    using Odd = std::integral_constant<int, 1>;
+    int t = jmax;
+    if (t & 1) step(Odd{}, t--);
+    for (; t >= 0; t -= 2) {
+        step(Even{}, t);
+        if (t >= 2) step(Odd{}, t - 1);
     }
     if (pend) {  // PV of the last kept tile (tile 0)
         __builtin_amdgcn_s_waitcnt(0x0f70);
