@@ -149,24 +149,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     if (STATS && bits && tid == 0)
         for (int w = (jmax >> 5) + 1; w < words; ++w) bits[(long(bh) * nqb + qb) * words + w] = 0u;
 
-    // K ring: ks0 holds tile t, ks1 tile t-1, ks2 is free (tile t-2 goes there)
-    uint32_t ks0 = lds_addr_of(kring[0]), ks1 = lds_addr_of(kring[1]), ks2 = lds_addr_of(kring[2]);
+    // K ring: tile t lives in kring[t % 3]
     const uint32_t vta = lds_addr_of(vtile);
 
     // prologue: K(jmax) (and K(jmax-1)) requested; scores + vote of tile jmax
-    tile_dma(kh, ks0, jmax);
+    tile_dma(kh, lds_addr_of(kring[jmax % 3]), jmax);
     __builtin_amdgcn_s_waitcnt(0x0f70);
     lds_barrier();
-    if (jmax >= 1) tile_dma(kh, ks1, jmax - 1);
+    if (jmax >= 1) tile_dma(kh, lds_addr_of(kring[(jmax + 2) % 3]), jmax - 1);
     f32x16 sc[2];  // scores of the tile being voted on
-    scores(ks0, sc);
+    scores(lds_addr_of(kring[jmax % 3]), sc);
     mask_diag(jmax, sc);
     if (GATED) {
         const bool wv = vote_of(sc);
         if (lane == 0) vote_sm[jmax & 1][wave] = wv ? 1 : 0;
     }
 
-    auto step = [&](auto diag_next, int t) {
+    // One step per tile; R = t % 3 is a compile-time constant, so the ring slot
+    // addresses are constants (they fold into the instructions' offset fields).
+    auto step = [&](auto res_tag, int t) {
+        constexpr int R = decltype(res_tag)::value;
+        const uint32_t ks0 = lds_addr_of(kring[R]);            // tile t
+        const uint32_t ks1 = lds_addr_of(kring[(R + 2) % 3]);  // tile t-1
+        const uint32_t ks2 = lds_addr_of(kring[(R + 1) % 3]);  // free: tile t-2 goes there
         // Everything issued in the previous step has landed: K(t-1) (and the
         // V tile that step consumed).
         __builtin_amdgcn_s_waitcnt(0x0f70);
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
         // scores and vote of the next tile while V(t) is in flight
         if (t >= 1) {
             scores(ks1, sc);
-            if (decltype(diag_next)::value) mask_diag(t - 1, sc);
+            if (t - 1 >= tdiag) mask_diag(t - 1, sc);
             if (GATED) {
                 const bool wv = vote_of(sc);
                 if (lane == 0) vote_sm[(t - 1) & 1][wave] = wv ? 1 : 0;
@@ -245,16 +250,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
                 word = 0;
             }
         }
-        const uint32_t done = ks0;
-        ks0 = ks1;
-        ks1 = ks2;
-        ks2 = done;
     };
 
-    // the tile after t needs masks iff t - 1 >= tdiag (at most one step)
+    using R0 = std::integral_constant<int, 0>;
+    using R1 = std::integral_constant<int, 1>;
+    using R2 = std::integral_constant<int, 2>;
     int t = jmax;
-    for (; t - 1 >= tdiag; --t) step(std::true_type{}, t);
-    for (; t >= 0; --t) step(std::false_type{}, t);
+    if (t % 3 == 1) step(R1{}, t--);  // peel down to a tile with t % 3 == 2
+    if (t % 3 == 0) step(R0{}, t--);
+    for (; t >= 2; t -= 3) {
+        step(R2{}, t);
+        step(R1{}, t - 1);
+        step(R0{}, t - 2);
+    }
 
     if (rvalid) {
         bf16_t* grow = dq + hoff + long(row) * D;
