@@ -411,45 +411,53 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(qa) + qoff[s]), kf[s], sacc);
+        if (diag) {  // keys past the row -> -inf: they neither vote nor carry probability
+            const int lim = key - r0 - 32 * rq - 4 * hl;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) < lim) sacc[r] = -INFINITY;
+        }
         __builtin_amdgcn_sched_barrier(0);
-        bool keep = true;
         if (GATED) {
             bool vote = false;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int rl = 32 * rq + 8 * g + 4 * hl;  // 4 consecutive rows
-                const f32x4 th = *reinterpret_cast<const f32x4*>(&st[0][rl]);
+                const f32x4 th = *reinterpret_cast<const f32x4*>(&st[0][32 * rq + 8 * g + 4 * hl]);
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const bool vis = !diag || (kvalid && key <= r0 + rl + x);
-                    vote |= vis && sacc[4 * g + x] >= th[x];
-                }
+                for (int x = 0; x < 4; ++x) vote |= sacc[4 * g + x] >= th[x];
             }
             const bool wv = wave_any(vote);
-            const int par = qb & 1;
-            if (lane == 0) vote_sm[par][wave] = wv ? 1 : 0;
+            if (lane == 0) vote_sm[qb & 1][wave] = wv ? 1 : 0;
+        }
+        // dP (32 rows x 32 keys) = dO V^T: issued before the vote barrier so
+        // that the MFMAs cover the exchange (wasted work on a skipped block)
+        f32x16 pacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            pacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(oa) + qoff[s]),
+                          *reinterpret_cast<const u32x4*>(lds_ptr(va) + qoff[s]), pacc);
+        bool keep = true;
+        if (GATED) {
             lds_barrier();  // the next block's prefetch stays in flight
-            const u32x4 va0 = *reinterpret_cast<const u32x4*>(&vote_sm[par][0]);
-            const u32x4 va1 = *reinterpret_cast<const u32x4*>(&vote_sm[par][4]);
+            const u32x4 va0 = *reinterpret_cast<const u32x4*>(&vote_sm[qb & 1][0]);
+            const u32x4 va1 = *reinterpret_cast<const u32x4*>(&vote_sm[qb & 1][4]);
             keep = ((va0[0] | va0[1] | va0[2] | va0[3]) | (va1[0] | va1[1] | va1[2] | va1[3])) != 0u;
         }
+        __builtin_amdgcn_sched_barrier(0);
         if (aux_bits && keep && tid == 0)
             atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (t >> 5)], 1u << (t & 31));
         if (keep) {
-            // P = exp(s - lse) (zero where invisible; lse2 = +inf on rows past L),
+            // P = exp(s - lse) (zero where masked; lse2 = +inf on rows past L),
             // kept only as bf16 B operands: step hf holds registers 8hf .. 8hf+7.
             u32x4 pf[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int rl = 32 * rq + 8 * g + 4 * hl;
-                const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[1][rl]);
+                const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[1][32 * rq + 8 * g + 4 * hl]);
                 float p[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    // keys past L only reach their own (unstored) dK/dV rows: no mask needed
-                    const bool vis = !diag || key <= r0 + rl + x;
-                    p[x] = vis ? fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[x])) : 0.f;
-                }
+                for (int x = 0; x < 4; ++x) p[x] = fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[x]));
                 pf[g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
                 pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
             }
@@ -460,15 +468,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
                     dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
-            __builtin_amdgcn_sched_barrier(0);
-            // dP (32 rows x 32 keys) = dO V^T ; dS = P (dP - D), P taken from its bf16 operand copy
-            f32x16 pacc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                pacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(oa) + qoff[s]),
-                              *reinterpret_cast<const u32x4*>(lds_ptr(va) + qoff[s]), pacc);
+            // dS = P (dP - D), P taken from its bf16 operand copy
             u32x4 dsf[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
