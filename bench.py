@@ -152,7 +152,7 @@ def main():
 
         def avg(a, b):
             return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
-        ms = {"fwd": avg(0, 1), "bwd": avg(2, 5), "bwd_prep": avg(2, 3), "dkdv": avg(3, 4), "dq": avg(4, 5),
+        ms = {"fwd": avg(0, 1), "bwd": avg(2, 5), "bwd_prep": avg(2, 3), "dq": avg(3, 4), "dkdv": avg(4, 5),
               "dec": avg(6, 7)}
         return wall, ms
 

@@ -83,15 +83,16 @@ typedef struct {
  * Decode, nsplit = ceil(Lk/split_keys), tps = split_keys/bk, words = ceil(tps/32):
  *   kept, legal int32 [B, Hkv, nsplit];  keep_bits uint32 [B, Hkv, nsplit, words],
  *   bit t = tile t of the partition (tile 0 starts at the partition start).
- *   keep_bits_dkdv uint32 [B, H, nqb, words], mala_bwd only: the decisions as
- *             taken by the dK/dV pass (the dQ pass writes keep_bits); the two
- *             passes recompute the same scores and must agree bit for bit.
+ *   keep_bits_dkdv uint32 [B, H, nqb, words], mala_bwd only: the tiles the
+ *             dK/dV pass actually processed (the dQ pass writes keep_bits and
+ *             hands the same decisions to the dK/dV pass); the two must agree
+ *             bit for bit.
  *   events    up to 4 hipEvent_t handles (NULL entries skipped), recorded on
  *             `stream` around the call's kernels: mala_fwd and mala_decode
  *             record events[0] before and events[1] after their kernels;
  *             mala_bwd records events[0] before the row-state kernel,
- *             events[1] before the dK/dV pass, events[2] before the dQ pass and
- *             events[3] after it.  For per-kernel timing by the caller.
+ *             events[1] before the dQ pass, events[2] before the dK/dV pass
+ *             and events[3] after it.  For per-kernel timing by the caller.
  * These are debug/measurement outputs: the library never reads them back and
  * backward does not consume anything forward wrote here.
  */
@@ -134,7 +135,10 @@ size_t mala_bwd_workspace_size(int B, int H, int L, int d, mala_dtype dtype, mal
  * D_i = sum_c dO_ic O_ic, dQ += scale dS K, dK += scale dS^T Q; skipped tiles
  * contribute nothing.  tile must equal the forward's.
  * workspace: device buffer of at least mala_bwd_workspace_size(...) bytes,
- * 256-byte aligned, contents ignored on entry.
+ * 256-byte aligned, contents ignored on entry.  It holds three per-row fp32
+ * arrays [B, H, L] (D, base-2 lse, threshold) and the decision bits
+ * [B, H, nqb, ceil(ntiles/32)] that the dQ pass hands to the dK/dV pass within
+ * this call (nothing is kept between calls).
  */
 mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dout, int B, int H, int Hkv, int L, int d, mala_dtype dtype,

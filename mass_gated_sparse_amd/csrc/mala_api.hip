@@ -105,9 +105,11 @@ mala_status mala_fwd(const void* q, const void* k, const void* v, int B, int H, 
 }
 
 size_t mala_bwd_workspace_size(int B, int H, int L, int d, mala_dtype dtype, mala_tile tile) {
-    (void)d; (void)dtype; (void)tile;
-    if (B <= 0 || H <= 0 || L <= 0) return 0;
-    return 3 * align256(size_t(B) * H * L * sizeof(float));
+    (void)d; (void)dtype;
+    if (B <= 0 || H <= 0 || L <= 0 || tile.bq <= 0 || tile.bk <= 0) return 0;
+    const size_t words = cdiv(cdiv(L, tile.bk), 32);
+    return 3 * align256(size_t(B) * H * L * sizeof(float)) +
+           align256(size_t(B) * H * cdiv(L, tile.bq) * words * sizeof(uint32_t));
 }
 
 mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
@@ -131,6 +133,7 @@ mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o,
     a.Dv = reinterpret_cast<float*>(ws);
     a.lse2 = reinterpret_cast<float*>(ws + align256(rows * 4));
     a.thr = reinterpret_cast<float*>(ws + 2 * align256(rows * 4));
+    a.dbits = reinterpret_cast<uint32_t*>(ws + 3 * align256(rows * 4));
     a.B = B; a.H = H; a.L = L; a.d = d;
     a.nqb = int(cdiv(L, tile.bq));
     a.ntiles = int(cdiv(L, tile.bk));
@@ -145,7 +148,7 @@ mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o,
         a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits;
         a.aux_bits = stats->keep_bits_dkdv;
         for (int i = 0; i < 4; ++i) a.ev[i] = (hipEvent_t)stats->events[i];
-        if (a.aux_bits) {  // the dK/dV pass ORs its decisions in
+        if (a.aux_bits) {  // the dK/dV pass ORs in the blocks it visits
             hipError_t e0 = hipMemsetAsync(a.aux_bits, 0, size_t(B) * H * a.nqb * a.words * sizeof(uint32_t), s);
             if (e0 != hipSuccess) return hip_status(e0, "mala_bwd stats clear");
         }

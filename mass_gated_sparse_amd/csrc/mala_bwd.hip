@@ -14,16 +14,15 @@
 // thr_i.  Kept tiles:  P = exp(s - lse), dP = dO V^T, dS = P (dP - D),
 // dV += P^T dO, dK += scale dS^T Q, dQ += scale dS K.
 //
-// Two kernels share the work and take the SAME decisions without exchanging
-// any mask:
+// Two kernels share the work:
 //   dQ pass   -- one workgroup per query block (4 waves x 32 rows), scores
 //                S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K, B = Q);
-//   dK/dV pass -- one workgroup per 128 keys (4 waves x 32 keys, i.e. two
-//                key tiles), scores S = Q K^T with the same instruction and
-//                the same k-step order (A = Q, B = K).
-// MFMA computes each output element as the same ordered sum over k whichever
-// operand holds which matrix, so both passes see bit-identical raw scores and
-// compare them with the same per-row threshold.
+//                it tests every legal tile and writes the decision bits into
+//                the backward's workspace;
+//   dK/dV pass -- one workgroup per 64-key tile (8 waves), runs second and
+//                visits only the query blocks those bits keep.
+// No mask passes from forward to backward: the bits are made and consumed
+// inside one mala_bwd call, from the final lse.
 //
 // Transposed operands (K^T for dQ, Q^T and dO^T for dK/dV) are read from the
 // row-major LDS tiles with ds_read_b64_tr_b16: within each 16-lane group the
@@ -55,15 +54,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
     const float* __restrict__ thr, bf16_t* __restrict__ dq, int BH, int L, int nqb, int words, float scale,
-    float scale_log2, int32_t* __restrict__ kept, int32_t* __restrict__ legal, uint32_t* __restrict__ bits) {
+    float scale_log2, int32_t* __restrict__ kept, int32_t* __restrict__ legal, uint32_t* __restrict__ bits,
+    uint32_t* __restrict__ dbits) {
     using namespace bwdk;
     __shared__ __attribute__((aligned(1024))) uint8_t kring[3][BK * 256];
     __shared__ __attribute__((aligned(1024))) uint8_t vtile[BK * 256];
     __shared__ int vote_sm[2][4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
-    const int qb = nqb - 1 - int(blockIdx.x) / BH;
-    const int bh = int(blockIdx.x) % BH;
+    int qrank, bh;
+    balanced_item(int(blockIdx.x), BH, max(1, nqb / 32), qrank, bh);
+    const int qb = nqb - 1 - qrank;  // longest query blocks first
     const long hoff = long(bh) * L * D;
     const bf16_t* kh = k + hoff;
     const bf16_t* vh = v + hoff;
@@ -242,11 +243,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (STATS && tid == 0) {
+        // decisions: handed to the dK/dV pass (dbits), and to the caller's stats
+        if ((GATED || STATS) && tid == 0) {
             nkept += keep;
             if (keep) word |= 1u << (t & 31);
-            if (bits && (t & 31) == 0) {
-                bits[(long(bh) * nqb + qb) * words + (t >> 5)] = word;
+            if ((t & 31) == 0) {
+                const long wi = (long(bh) * nqb + qb) * words + (t >> 5);
+                if (GATED) dbits[wi] = word;
+                if (STATS && bits) bits[wi] = word;
                 word = 0;
             }
         }
@@ -283,46 +287,46 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 }
 
 // ---------------------------------------------------------------------- dK/dV
-// One workgroup of 8 waves per 64-key tile, i.e. per vote column: a skipped
-// (query block, key tile) pair skips the whole workgroup's post-score work.
-// Wave w owns keys 32(w&1) .. +31 of the tile and rows 32(w>>1) .. +31 of
-// every query block, so two waves share each SIMD.  K of the wave's keys is
-// held in registers (B operand of S = Q K^T); the V tile sits in LDS (B
-// operand of dP = dO V^T).  The Q and dO tiles of successive query blocks are
-// double-buffered in LDS: while block qb is computed from one buffer, block
-// qb+1 streams into the other with direct global->LDS loads.  Each wave
-// accumulates dK^T and dV^T over its own 32 rows of every block; the four
-// row quarters are summed through LDS at the end.  Rows past L are read
-// clamped to row L-1 and are masked out of every vote and product (their
-// thr and lse are +inf, so P = 0 there).
+// One workgroup of 8 waves per 64-key tile: wave w owns keys 32(w&1) .. +31
+// of the tile and rows 32(w>>1) .. +31 of every query block, so two waves
+// share each SIMD.  K of the wave's keys is held in registers (B operand of
+// S = Q K^T); the V tile sits in LDS (B operand of dP = dO V^T).
+//
+// Decisions.  The dQ pass runs first and tests every tile against the final
+// lse; its decision bits reach this pass through the backward's workspace.
+// This pass visits only the kept query blocks of its key tile: a skipped
+// block costs no Q/dO load, no S and no post-score work, and both passes use
+// the same decisions by construction.
+//
+// The Q and dO tiles of successive kept query blocks are double-buffered in
+// LDS: while one block is computed, the next streams into the other buffer
+// with direct global->LDS loads.  Each wave accumulates dK^T and dV^T over
+// its own 32 rows of every block; the four row quarters are summed through
+// LDS at the end.  Rows past L are read clamped to row L-1; their lse is
+// +inf there, so P = 0.
 template <bool GATED>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
-    const float* __restrict__ thr, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BH, int L, int nqb,
-    int words, float scale, float scale_log2, uint32_t* __restrict__ aux_bits) {
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BH, int L, int nqb, int words, float scale,
+    float scale_log2, const uint32_t* __restrict__ dbits, uint32_t* __restrict__ aux_bits) {
     using namespace bwdk;
-    // buf[0..3]: Q and dO tiles of two query blocks (A: buf[0], buf[1]; B:
+    // buf[0..3]: Q and dO tiles of two query blocks (buf[0], buf[1] and
     // buf[2], buf[3]); reused at the end for the cross-wave reduction.
     __shared__ __attribute__((aligned(1024))) uint8_t buf[4][BQ * 256];
     __shared__ __attribute__((aligned(1024))) uint8_t vtile[BK * 256];
-    __shared__ __attribute__((aligned(16))) float stA[3][BQ];  // thr, lse2, D of the block's rows
-    __shared__ __attribute__((aligned(16))) float stB[3][BQ];
-    __shared__ __attribute__((aligned(16))) int vote_sm[2][8];
+    __shared__ __attribute__((aligned(16))) float stA[2][BQ];  // lse2, D of the block's rows
+    __shared__ __attribute__((aligned(16))) float stB[2][BQ];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     const int kb = wave & 1, rq = wave >> 1;
-    const int t = int(blockIdx.x) / BH;  // 64-key tile; longest (t = 0) first
-    const int bh = int(blockIdx.x) % BH;
+    int t, bh;  // 64-key tile; longest (t = 0) first
+    balanced_item(int(blockIdx.x), BH, max(1, (2 * nqb) / 32), t, bh);
     const long hoff = long(bh) * L * D;
     const int key = t * BK + 32 * kb + j;
     const bool kvalid = key < L;
     const int qb0 = (t * BK) / BQ;  // first query block that sees the tile (its diagonal block)
     const u32x4 z4 = {0u, 0u, 0u, 0u};
-    uint8_t* qsA = buf[0];
-    uint8_t* osA = buf[1];
-    uint8_t* qsB = buf[2];
-    uint8_t* osB = buf[3];
 
     // K of this wave's 32 keys as B operands (lane = key, 8 contiguous d)
     u32x4 kf[8];
@@ -367,43 +371,64 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     // clamped) into registers before the tile prefetch is issued, written to
     // LDS (with the padding-row defaults) only at the end of the block, so
     // waiting for these loads never waits for the prefetch.
-    float stv[3];
+    float stv[2];
     int st_row = 0;
     auto stats_load = [&](int r0) {
         if (tid < BQ) {
             st_row = r0 + tid;
             const long ri = long(bh) * L + min(st_row, L - 1);
-            stv[0] = thr[ri];
-            stv[1] = lse2[ri];
-            stv[2] = Dv[ri];
+            stv[0] = lse2[ri];
+            stv[1] = Dv[ri];
         }
     };
     auto stats_store = [&](float (*st)[BQ]) {
         if (tid < BQ) {
             const bool ok = st_row < L;
             st[0][tid] = ok ? stv[0] : INFINITY;
-            st[1][tid] = ok ? stv[1] : INFINITY;
-            st[2][tid] = ok ? stv[2] : 0.f;
+            st[1][tid] = ok ? stv[1] : 0.f;
         }
     };
     // this wave's 32 keys of V, addressed with the Q-tile offsets
     const uint32_t va = lds_addr_of(vtile) + 8192 * kb - 8192 * rq;
 
-    // One query block: compute from (qs, os, st) while the next block streams
-    // into (qn, on, sn).  Only the diagonal block (qb == qb0) needs visibility
-    // masks: it is the only block with keys past some row, and the only block
-    // of the last tiles, whose keys may run past L.  Elsewhere every key is
-    // visible to every row.
-    auto block = [&](auto diag_tag, int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ],
-                     uint8_t* qn, uint8_t* on, float (*sn)[BQ]) {
+    // Kept query blocks of this tile, 64 at a time: bit i of kmask is block
+    // wbase + i (every lane fetches one block's decision word, a ballot packs
+    // the bits); the next window's words are fetched one window ahead.
+    const uint32_t tbit = 1u << (t & 31);
+    const uint32_t* dcol = GATED ? dbits + long(bh) * nqb * words + (t >> 5) : nullptr;
+    auto fetch = [&](int base) -> uint32_t {
+        const int qb = base + lane;
+        return (GATED && qb < nqb) ? dcol[long(qb) * words] : 0u;
+    };
+    int wbase = qb0;
+    uint64_t kmask = 0;
+    uint32_t wnext = 0;
+    if (GATED) {
+        kmask = __ballot((fetch(qb0) & tbit) != 0u);
+        wnext = fetch(qb0 + 64);
+    }
+    // first kept block >= qb (qb >= wbase), or nqb
+    auto kept_from = [&](int qb) -> int {
+        if (!GATED) return qb;
+        for (;;) {
+            const int sh = qb - wbase;
+            const uint64_t m = sh >= 64 ? 0ull : (kmask >> sh) << sh;
+            if (m) return wbase + __builtin_ctzll(m);
+            if (wbase + 64 >= nqb) return nqb;
+            wbase += 64;
+            qb = max(qb, wbase);
+            kmask = __ballot((wnext & tbit) != 0u);
+            wnext = fetch(wbase + 64);
+        }
+    };
+
+    // One kept query block, computed from (qs, os, st).  Only the diagonal
+    // block (qb == qb0) needs a visibility mask: it is the only block with
+    // keys past some row, and the only block of the last tiles, whose keys may
+    // run past L.  Elsewhere every key is visible to every row.
+    auto block = [&](auto diag_tag, int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ]) {
         constexpr bool diag = decltype(diag_tag)::value;
         const int r0 = qb * BQ;
-        const bool more = qb + 1 < nqb;
-        if (more) {
-            stats_load(r0 + BQ);
-            tile_async(q, qn, r0 + BQ);
-            tile_async(dout, on, r0 + BQ);
-        }
         const uint32_t qa = lds_addr_of(qs), oa = lds_addr_of(os);
         // S (32 rows x 32 keys) = Q K^T; register r holds row 32rq + 8(r/4) + 4hl + r%4, key j
         f32x16 sacc;
@@ -411,26 +436,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(qa) + qoff[s]), kf[s], sacc);
-        if (diag) {  // keys past the row -> -inf: they neither vote nor carry probability
+        if (diag) {  // keys past the row -> -inf: no probability
             const int lim = key - r0 - 32 * rq - 4 * hl;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (8 * (r >> 2) + (r & 3) < lim) sacc[r] = -INFINITY;
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (GATED) {
-            bool vote = false;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 th = *reinterpret_cast<const f32x4*>(&st[0][32 * rq + 8 * g + 4 * hl]);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) vote |= sacc[4 * g + x] >= th[x];
-            }
-            const bool wv = wave_any(vote);
-            if (lane == 0) vote_sm[qb & 1][wave] = wv ? 1 : 0;
-        }
-        // dP (32 rows x 32 keys) = dO V^T: issued before the vote barrier so
-        // that the MFMAs cover the exchange (wasted work on a skipped block)
+        // dP (32 rows x 32 keys) = dO V^T
         f32x16 pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
@@ -438,82 +451,86 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
         for (int s = 0; s < 8; ++s)
             pacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(oa) + qoff[s]),
                           *reinterpret_cast<const u32x4*>(lds_ptr(va) + qoff[s]), pacc);
-        bool keep = true;
-        if (GATED) {
-            lds_barrier();  // the next block's prefetch stays in flight
-            const u32x4 va0 = *reinterpret_cast<const u32x4*>(&vote_sm[qb & 1][0]);
-            const u32x4 va1 = *reinterpret_cast<const u32x4*>(&vote_sm[qb & 1][4]);
-            keep = ((va0[0] | va0[1] | va0[2] | va0[3]) | (va1[0] | va1[1] | va1[2] | va1[3])) != 0u;
+        __builtin_amdgcn_sched_barrier(0);
+        // P = exp(s - lse) (zero where masked; lse2 = +inf on rows past L),
+        // kept only as bf16 B operands: step hf holds registers 8hf .. 8hf+7.
+        u32x4 pf[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[0][32 * rq + 8 * g + 4 * hl]);
+            float p[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) p[x] = fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[x]));
+            pf[g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
+            pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (aux_bits && keep && tid == 0)
-            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (t >> 5)], 1u << (t & 31));
-        if (keep) {
-            // P = exp(s - lse) (zero where masked; lse2 = +inf on rows past L),
-            // kept only as bf16 B operands: step hf holds registers 8hf .. 8hf+7.
-            u32x4 pf[2];
+        // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[1][32 * rq + 8 * g + 4 * hl]);
-                float p[4];
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int x = 0; x < 4; ++x) p[x] = fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[x]));
-                pf[g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
-                pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
+            for (int hf = 0; hf < 2; ++hf)
+                dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+        // dS = P (dP - D), P taken from its bf16 operand copy
+        u32x4 dsf[2];
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-                    dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
-            // dS = P (dP - D), P taken from its bf16 operand copy
-            u32x4 dsf[2];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[2][32 * rq + 8 * g + 4 * hl]);
-                const uint32_t w0 = pf[g >> 1][2 * (g & 1)], w1 = pf[g >> 1][2 * (g & 1) + 1];
-                const float p0 = __uint_as_float(w0 << 16), p1 = __uint_as_float(w0 & 0xffff0000u);
-                const float p2 = __uint_as_float(w1 << 16), p3 = __uint_as_float(w1 & 0xffff0000u);
-                dsf[g >> 1][2 * (g & 1)] = pack_bf16x2(p0 * (pacc[4 * g + 0] - dd[0]), p1 * (pacc[4 * g + 1] - dd[1]));
-                dsf[g >> 1][2 * (g & 1) + 1] =
-                    pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // dK^T (d x keys) += Q^T dS
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-                    dkacc[db] = mfma32(tr_operand_at(qa + 256 * (16 * hf), troff[db]), dsf[hf], dkacc[db]);
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[1][32 * rq + 8 * g + 4 * hl]);
+            const uint32_t w0 = pf[g >> 1][2 * (g & 1)], w1 = pf[g >> 1][2 * (g & 1) + 1];
+            const float p0 = __uint_as_float(w0 << 16), p1 = __uint_as_float(w0 & 0xffff0000u);
+            const float p2 = __uint_as_float(w1 << 16), p3 = __uint_as_float(w1 & 0xffff0000u);
+            dsf[g >> 1][2 * (g & 1)] = pack_bf16x2(p0 * (pacc[4 * g + 0] - dd[0]), p1 * (pacc[4 * g + 1] - dd[1]));
+            dsf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
         }
-        if (more) stats_store(sn);
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffer landed
-        lds_barrier();                       // next buffer complete; every wave is done with this one
+        __builtin_amdgcn_sched_barrier(0);
+        // dK^T (d x keys) += Q^T dS
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                dkacc[db] = mfma32(tr_operand_at(qa + 256 * (16 * hf), troff[db]), dsf[hf], dkacc[db]);
+        if (aux_bits && tid == 0)  // the blocks this pass visited (parity statistics)
+            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (t >> 5)], tbit);
     };
 
-    // prologue: V tile, first block into buffer A
+    // prologue: V tile; the first kept block into buffers 0, 1
 #pragma unroll
     for (int it = 0; it < 2; ++it) {  // V tile: segments 2w, 2w+1 (rows 8w .. 8w+7)
         const int rt = 8 * wave + 4 * it + (lane >> 4);
         const uint32_t off = uint32_t(min(rt, L - 1 - t * BK) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
-        dma16s(v + hoff + long(t) * BK * D, off, __builtin_amdgcn_readfirstlane(lds_addr_of(vtile) + 2048 * wave + 1024 * it));
+        dma16s(v + hoff + long(t) * BK * D, off,
+               __builtin_amdgcn_readfirstlane(lds_addr_of(vtile) + 2048 * wave + 1024 * it));
     }
-    tile_async(q, qsA, qb0 * BQ);
-    tile_async(dout, osA, qb0 * BQ);
-    stats_load(qb0 * BQ);
+    int qb = kept_from(qb0);
+    if (qb < nqb) {
+        tile_async(q, buf[0], qb * BQ);
+        tile_async(dout, buf[1], qb * BQ);
+        stats_load(qb * BQ);
+    }
     __builtin_amdgcn_s_waitcnt(0x0f70);
     stats_store(stA);
     lds_barrier();
-    // diagonal block from buffer A, then alternate B, A, ...  (buffer chosen at
-    // run time so that the operand addresses stay two registers per buffer)
-    block(std::true_type{}, qb0, qsA, osA, stA, qsB, osB, stB);
-    for (int qb = qb0 + 1; qb < nqb; ++qb) {
-        const bool odd = (qb - qb0) & 1;
-        block(std::false_type{}, qb, odd ? qsB : qsA, odd ? osB : osA, odd ? stB : stA, odd ? qsA : qsB,
-              odd ? osA : osB, odd ? stA : stB);
-    }
+    // Each kept block is computed from one buffer pair while the next kept
+    // block streams into the other.  The diagonal block, if kept, is first.
+    bool odd = false;
+    auto advance = [&](auto diag_tag) {
+        const int qn = kept_from(qb + 1);
+        const bool more = qn < nqb;
+        if (more) {
+            stats_load(qn * BQ);
+            tile_async(q, odd ? buf[0] : buf[2], qn * BQ);
+            tile_async(dout, odd ? buf[1] : buf[3], qn * BQ);
+        }
+        block(diag_tag, qb, odd ? buf[2] : buf[0], odd ? buf[3] : buf[1], odd ? stB : stA);
+        if (more) stats_store(odd ? stA : stB);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffer landed
+        lds_barrier();                       // next buffer complete; every wave is done with this one
+        qb = qn;
+        odd = !odd;
+    };
+    if (qb == qb0) advance(std::true_type{});
+    while (qb < nqb) advance(std::false_type{});
 
     // Sum the four row quarters.  Accumulators hold dK^T, dV^T: lane = key,
     // register 4g + x of block db = d 32db + 8g + 4hl + x.  Wave w stores its
@@ -562,21 +579,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     const bool st = a.kept || a.legal || a.bits;
     hipError_t e = mark(a.ev[1], s);
     if (e != hipSuccess) return e;
-    if (a.gated)
-        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<true>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
-                           (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dk,
-                           (bf16_t*)a.dv, BH, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.aux_bits);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<false>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
-                           (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dk,
-                           (bf16_t*)a.dv, BH, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.aux_bits);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = mark(a.ev[2], s);
-    if (e != hipSuccess) return e;
 #define MALA_DQ_LAUNCH(G, S)                                                                                  \
     hipLaunchKernelGGL((bwd_dq_bf16_d128<G, S>), g2, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,       \
                        (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dq, BH, a.L, \
-                       a.nqb, a.words, a.scale, a.scale_log2, a.kept, a.legal, a.bits)
+                       a.nqb, a.words, a.scale, a.scale_log2, a.kept, a.legal, a.bits, a.dbits)
     if (a.gated) {
         if (st) MALA_DQ_LAUNCH(true, true);
         else MALA_DQ_LAUNCH(true, false);
@@ -585,6 +591,17 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
         else MALA_DQ_LAUNCH(false, false);
     }
 #undef MALA_DQ_LAUNCH
+    e = hipGetLastError();
+    if (e == hipSuccess) e = mark(a.ev[2], s);
+    if (e != hipSuccess) return e;
+    if (a.gated)
+        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<true>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
+                           (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, (bf16_t*)a.dk, (bf16_t*)a.dv,
+                           BH, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<false>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
+                           (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, (bf16_t*)a.dk, (bf16_t*)a.dv,
+                           BH, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits);
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(a.ev[3], s);
     return e;

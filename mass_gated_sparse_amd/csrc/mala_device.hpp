@@ -48,6 +48,19 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
                                                    0, 0, 0);
 }
 
+// Work item of workgroup i in a grid ordered by rank (i / BH) and head.  The
+// GPU deals workgroups to its 8 XCDs round-robin (i % 8), so with head =
+// i % BH every XCD would serve a fixed subset of the heads for the whole
+// launch, and an XCD whose heads skip most tiles would idle while the others
+// finish.  Rotating the head by one every `period` ranks (the shift is one
+// constant per rank, so each rank still covers every head once) moves every
+// XCD through all heads, while workgroups that run together on an XCD still
+// share a head and its L2 lines.
+__device__ __forceinline__ void balanced_item(int i, int BH, int period, int& rank, int& head) {
+    rank = i / BH;
+    head = (i - rank * BH + rank / period) % BH;
+}
+
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }

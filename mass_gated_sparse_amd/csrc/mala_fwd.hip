@@ -59,8 +59,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     __shared__ int vote_sm[2][4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
-    const int qb = nqb - 1 - int(blockIdx.x) / BH;  // longest query blocks first
-    const int bh = int(blockIdx.x) % BH;
+    int qrank, bh;
+    balanced_item(int(blockIdx.x), BH, max(1, nqb / 32), qrank, bh);
+    const int qb = nqb - 1 - qrank;  // longest query blocks first
     const long hoff = long(bh) * L * D;
     const bf16_t* kh = k + hoff;
     const bf16_t* vh = v + hoff;

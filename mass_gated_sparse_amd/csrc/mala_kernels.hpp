@@ -28,12 +28,13 @@ struct BwdArgs {
     const float* lse;
     void *dq, *dk, *dv;
     float *Dv, *lse2, *thr;  // per-row workspace arrays [B, H, L]
+    uint32_t* dbits;         // workspace: backward decisions [B, H, nqb, words], dQ pass -> dK/dV pass
     int B, H, L, d;
     int nqb, ntiles, words;
     float scale, scale_log2, log2_tau;
     bool gated, f32;
     int32_t *kept, *legal;
-    uint32_t *bits, *aux_bits;  // aux_bits: decisions as seen by the dK/dV kernel (debug)
+    uint32_t *bits, *aux_bits;  // aux_bits: the blocks the dK/dV kernel visited (debug)
     hipEvent_t ev[4];           // optional timing events (see mala_stats)
 };
 

@@ -62,7 +62,9 @@ def test_workspace_sizes(lib):
     from mass_gated_sparse_amd._lib import MALA_BF16, Tile
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for B, H, L in [(1, 4, 131072), (2, 3, 1000), (1, 1, 1)]:
-        assert lib.mala_bwd_workspace_size(B, H, L, 128, MALA_BF16, Tile(128, 64)) == 3 * a256(B * H * L * 4)
+        words = -(-(-(-L // 64)) // 32)
+        assert lib.mala_bwd_workspace_size(B, H, L, 128, MALA_BF16, Tile(128, 64)) == (
+            3 * a256(B * H * L * 4) + a256(B * H * (-(-L // 128)) * words * 4))
     assert lib.mala_bwd_workspace_size(0, 4, 10, 128, MALA_BF16, Tile(128, 64)) == 0
     for B, Hq, Hkv, Lk, d, split in [(16, 32, 8, 131073, 128, 4096), (1, 4, 1, 2500, 128, 1024), (3, 8, 2, 64, 128, 64)]:
         nsplit = math.ceil(Lk / split)
