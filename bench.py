@@ -176,8 +176,36 @@ def main():
                     "speedup_fwd": ms0["fwd"] / ms["fwd"], "speedup_bwd": ms0["bwd"] / ms["bwd"],
                     "speedup_decode": ms0["dec"] / ms["dec"], "speedup_step": wall0 / wall}
 
-    # ---- rooflines: algorithmic work per launch / live average launch duration
+    # ---- QK rate and vote overhead (forward and backward on the same inputs):
+    # at tau=+inf only the forced tiles keep, so the forward is QK + vote on
+    # every legal tile; tau=1e-30 votes on every tile but keeps all of them.
     tile_flop = 2.0 * tile[0] * tile[1] * d
+    extra = None
+    if not args.no_tau0:
+        ms_inf = kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws_b, tile, float("inf"), args.steps)
+        st = ops.prefill_stats_buffers(B, H, L, tile, q.device, dkdv=False)
+        ops.fwd_into(q, k, v, o, lse, float("inf"), tile, stats=st)
+        torch.cuda.synchronize()
+        fk_inf = int(st["kept"].sum())
+        qk_flop = tile_flop * (n_legal + fk_inf)
+        ms_vote = kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws_b, tile, 1e-30, args.steps)
+        extra = {
+            "qk_rate": {"tau": "inf", "fwd_ms": ms_inf["fwd"], "kept_tiles": fk_inf, "legal_tiles": n_legal,
+                        "executed_tflop": qk_flop / 1e12,
+                        "tflops": qk_flop / (ms_inf["fwd"] * 1e-3) / 1e12,
+                        "frac_of_peak": qk_flop / (ms_inf["fwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "note": "QK on every legal tile + vote; PV only on the forced tiles"},
+            "vote_overhead": {"tau": 1e-30, "fwd_ms": ms_vote["fwd"], "dq_ms": ms_vote["dq"],
+                              "dkdv_ms": ms_vote["dkdv"],
+                              "fwd_vs_tau0": ms_vote["fwd"] / out_tau0["fwd_ms"] if out_tau0 else None,
+                              "dq_vs_tau0": ms_vote["dq"] / out_tau0["dq_ms"] if out_tau0 else None,
+                              "dkdv_vs_tau0": ms_vote["dkdv"] / out_tau0["dkdv_ms"] if out_tau0 else None,
+                              "note": "every tile voted on and kept; ratio to the ungated (tau=0) kernels"},
+        }
+        log(f"tau=inf fwd {ms_inf['fwd']:.2f} ms (QK rate {extra['qk_rate']['tflops']:.0f} TFLOP/s); "
+            f"tau=1e-30 fwd {ms_vote['fwd']:.2f} dQ {ms_vote['dq']:.2f} dK/dV {ms_vote['dkdv']:.2f}")
+
+    # ---- rooflines: algorithmic work per launch / live average launch duration
     per_tile = f"2*{tile[0]}*{tile[1]}*{d} FLOP per tile product"
     traffic = load_traffic()
     kern = {
@@ -227,12 +255,31 @@ def main():
         "decode_dense_tflops": dense_dec / (ms["dec"] * 1e-3) / 1e12,
         "kept_frac": {"fwd": fk / n_legal, "bwd": bk_ / n_legal, "decode": dkp / dlg},
         "tau0": out_tau0,
+        "qk_rate": extra["qk_rate"] if extra else None,
+        "vote_overhead": extra["vote_overhead"] if extra else None,
         "roofline": roofline,
         "kernel_rooflines": rooflines,
         "sweep32k": sweep,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
+
+
+def kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, tau, steps):
+    """Mean per-kernel ms of forward and backward at tau (events recorded by the
+    library around each kernel), after one untimed warmup."""
+    ops.fwd_into(q, k, v, o, lse, tau, tile)
+    ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    for e in evs:
+        ops.fwd_into(q, k, v, o, lse, tau, tile, stats={"events": e[0:2]})
+        ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile, stats={"events": e[2:6]})
+    torch.cuda.synchronize()
+
+    def avg(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+    return {"fwd": avg(0, 1), "dq": avg(3, 4), "dkdv": avg(4, 5)}
 
 
 # kernel -> (instantiation timed by the bench at tau > 0, source files it is built from)
