@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     int qrank, bh;
-    balanced_item(int(blockIdx.x), BH, max(1, nqb / 32), qrank, bh);
+    balanced_item(int(blockIdx.x), BH, max(1, nqb / 8), qrank, bh);
     const int qb = nqb - 1 - qrank;  // longest query blocks first
     const long hoff = long(bh) * L * D;
     const bf16_t* kh = k + hoff;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     const int kb = wave & 1, rq = wave >> 1;
     int t, bh;  // 64-key tile; longest (t = 0) first
-    balanced_item(int(blockIdx.x), BH, max(1, (2 * nqb) / 32), t, bh);
+    balanced_item(int(blockIdx.x), BH, max(1, (2 * nqb) / 8), t, bh);
     const long hoff = long(bh) * L * D;
     const int key = t * BK + 32 * kb + j;
     const bool kvalid = key < L;

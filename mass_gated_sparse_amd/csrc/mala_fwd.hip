@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     int qrank, bh;
-    balanced_item(int(blockIdx.x), BH, max(1, nqb / 32), qrank, bh);
+    balanced_item(int(blockIdx.x), BH, max(1, nqb / 8), qrank, bh);
     const int qb = nqb - 1 - qrank;  // longest query blocks first
     const long hoff = long(bh) * L * D;
     const bf16_t* kh = k + hoff;
