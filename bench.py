@@ -336,10 +336,12 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
     rows = _csv_rows(trace_dir, "kernel_stats.csv")
     lines = ["# Kernel time: bench.py, 128K training step + 128K decode", "",
              "Command (from the repository root, on one MI355X):", "",
-             "    cd /tmp && export TMPDIR=/tmp && cd $GRAFT_REPO_ROOT && rocprofv3 --kernel-trace --stats "
-             "--output-format csv -d <dir> -o run -- python3 bench.py --steps 3 --warmup 1 --no-sweep "
-             "--no-cpu-baseline", "",
-             "Runs at tau=1 and tau=0 (stats passes, warmup and timed steps all included).", "",
+             "    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
+             "--output-format csv -d <dir> -o run -- python3 $GRAFT_REPO_ROOT/bench.py --steps 3 --warmup 1 "
+             "--no-tau0 --no-sweep --no-cpu-baseline", "",
+             "Runs at tau=1 only: every launch of an instantiation below is a tau=1 launch (the "
+             "statistics pass uses the separate `<..., true>` instantiations; warmup and timed steps "
+             "are included).", "",
              "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---:|---:|---:|---:|---:|---:|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
