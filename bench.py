@@ -50,6 +50,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison run")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 32K tau sweep")
+    ap.add_argument("--no-matched-work", action="store_true", help="skip the 8K matched-work measurement")
+    ap.add_argument("--fidelity", action="store_true",
+                    help="only run the tau=1 fidelity sweep from 1K to 32K (slots per query, omitted mass, "
+                         "rel-L2 of O against exact attention) and print it as one JSON line")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0,
                     help="query blocks in the CPU-oracle sample (0: three per OpenMP thread, at most 48)")
     ap.add_argument("--micro", action="store_true",
@@ -77,6 +81,11 @@ def main():
 
     if args.micro:
         print(json.dumps(micro(torch)))
+        return
+
+    if args.fidelity:
+        from mass_gated_sparse_amd import ops
+        print(json.dumps(fidelity_sweep(torch, ops)))
         return
 
     if args.copy_calibration:
@@ -230,6 +239,7 @@ def main():
     roofline = rooflines[max(rooflines, key=lambda n: rooflines[n]["ms"])]
 
     sweep = None if args.no_sweep else sweep32k(torch, ops, args.steps, args.warmup)
+    matched = None if args.no_matched_work else matched_work_8k(torch, ops, args.steps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -260,6 +270,7 @@ def main():
         "roofline": roofline,
         "kernel_rooflines": rooflines,
         "sweep32k": sweep,
+        "matched_work_8k": matched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
@@ -503,6 +514,117 @@ def sweep32k(torch, ops, steps, warmup):
                                               f"kept {r['kept_fwd']:.3f}/{r['kept_bwd']:.3f}" for t, r in res.items()))
         del q, k, v, do, o, dq, dk, dv
     return out
+
+
+def exact_row_stats(qh, kh, vh, keep, blocks, bq, bk, scale, o_gpu=None):
+    """Against exact causal softmax attention (fp64, numpy; a measurement, not
+    the oracle): for every row of the given query blocks of one head, the
+    probability mass of its visible keys in tiles the forward skipped, and the
+    number of its visible keys in kept tiles (post-score slots).  With o_gpu
+    (the GPU output rows of those blocks) also sum |O - O*|^2 and |O*|^2.
+    qh, kh, vh: [L, d] fp64; keep: [nqb, ntiles] forward decisions."""
+    L = kh.shape[0]
+    omitted, slots, err2, ref2 = [], [], 0.0, 0.0
+    cols = np.arange(L)
+    for qb in blocks:
+        rows = np.arange(qb * bq, min(qb * bq + bq, L))
+        s = (qh[rows] @ kh.T) * scale
+        vis = cols[None, :] <= rows[:, None]
+        s = np.where(vis, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        kt = keep[qb][cols // bk][None, :] & vis
+        omitted.append((p * (vis & ~kt)).sum(axis=1))
+        slots.append(kt.sum(axis=1))
+        if o_gpu is not None:
+            ref = p @ vh
+            err2 += float(((o_gpu[rows - qb * bq + blocks.index(qb) * bq] - ref) ** 2).sum())
+            ref2 += float((ref ** 2).sum())
+    return np.concatenate(omitted), np.concatenate(slots), err2, ref2
+
+
+def matched_work_8k(torch, ops, steps):
+    """The 8K matched-work shape (B1 H16 L8192 d128, bf16, 128x64 tiles, tau=1,
+    planted inputs with per-head sharpness c_h ~ U[0.5, 2]): GPU fwd/bwd ms and
+    kept-tile fractions, and -- on every 8th query block of every head -- the
+    mean omitted probability mass per query and the post-score slots per
+    query against exact attention."""
+    from synth import WORKLOADS, prefill_inputs, to_f64
+    w = WORKLOADS["mw8k"]
+    tile, tau = (w.bq, w.bk), 1.0
+    x = prefill_inputs(w)
+    q, k, v, do = (dev_bf16(torch, x[n]) for n in ("q", "k", "v", "do"))
+    B, H, L, d = q.shape
+    o, lse, st = ops.fwd(q, k, v, tau, tile=tile, stats=True)
+    dq, dk, dv, stb = ops.bwd(q, k, v, o, lse, do, tau, tile=tile, stats=True)
+    torch.cuda.synchronize()
+    n_legal = B * H * legal_tiles(L, *tile)
+    ws = ops.bwd_workspace(q, tile)
+    ms = kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, tau, steps)
+    nt = -(-L // w.bk)
+    keep = ops.bits_to_keep(st["keep_bits"], nt)[0]
+    og = o.float().cpu().numpy()[0]
+    blocks = list(range(0, -(-L // w.bq), 8))
+    scale = 1.0 / np.sqrt(d)
+    om, sl, e2, r2 = [], [], 0.0, 0.0
+    t0 = time.time()
+    for h in range(H):
+        qh, kh, vh = (to_f64(x[n][0, h], "bf16") for n in ("q", "k", "v"))
+        rows = np.concatenate([np.arange(b * w.bq, min(b * w.bq + w.bq, L)) for b in blocks])
+        a, b_, e, r = exact_row_stats(qh, kh, vh, keep[h], blocks, w.bq, w.bk, scale, og[h][rows])
+        om.append(a)
+        sl.append(b_)
+        e2 += e
+        r2 += r
+    om, sl = np.concatenate(om), np.concatenate(sl)
+    log(f"matched-work 8K: exact-attention sample took {time.time() - t0:.1f}s")
+    return {"workload": "mw8k (B1 H16 L8192 d128 bf16, 128x64 tiles, planted, c_h~U[0.5,2])", "tau": tau,
+            "fwd_ms": ms["fwd"], "dq_ms": ms["dq"], "dkdv_ms": ms["dkdv"],
+            "kept_frac_fwd": int(st["kept"].sum()) / n_legal, "kept_frac_bwd": int(stb["kept"].sum()) / n_legal,
+            "mean_omitted_mass_pct": 100.0 * float(om.mean()), "max_omitted_mass_pct": 100.0 * float(om.max()),
+            "omitted_mass_bound_pct": 100.0 * tau / (1.0 + tau),
+            "slots_per_query": float(sl.mean()), "rel_l2_O_vs_exact": float(np.sqrt(e2 / r2)),
+            "sample": f"every 8th query block ({len(blocks)} of {-(-L // w.bq)}) of all {H} heads",
+            "note": "omitted mass = exact softmax mass of a row's visible keys in forward-skipped tiles; "
+                    "slots = the row's visible keys in kept tiles; rel_l2 includes bf16 rounding of O"}
+
+
+def fidelity_sweep(torch, ops):
+    """tau=1 from 1K to 32K on the planted family of the 32K sweep shape
+    (H=8, d=128, bf16, 128x64 tiles): kept-tile fraction, post-score slots
+    per query, omitted mass and rel-L2 of O against exact attention on every
+    query block of L <= 4K and a sample of 16 blocks per head beyond."""
+    from synth import WORKLOADS, prefill_inputs, to_f64
+    w = WORKLOADS["sweep32k"]
+    tile, tau = (w.bq, w.bk), 1.0
+    out = {}
+    for L in (1024, 2048, 4096, 8192, 16384, 32768):
+        x = prefill_inputs(w, L=L)
+        q, k, v = (dev_bf16(torch, x[n]) for n in ("q", "k", "v"))
+        B, H, _, d = q.shape
+        o, lse, st = ops.fwd(q, k, v, tau, tile=tile, stats=True)
+        torch.cuda.synchronize()
+        nqb, nt = -(-L // w.bq), -(-L // w.bk)
+        keep = ops.bits_to_keep(st["keep_bits"], nt)[0]
+        og = o.float().cpu().numpy()[0]
+        blocks = list(range(nqb)) if nqb <= 32 else sorted(set(np.linspace(0, nqb - 1, 16).astype(int).tolist()))
+        om, sl, e2, r2 = [], [], 0.0, 0.0
+        for h in range(H):
+            qh, kh, vh = (to_f64(x[n][0, h], "bf16") for n in ("q", "k", "v"))
+            rows = np.concatenate([np.arange(b * w.bq, min(b * w.bq + w.bq, L)) for b in blocks])
+            a, b_, e, r = exact_row_stats(qh, kh, vh, keep[h], blocks, w.bq, w.bk, 1.0 / np.sqrt(d), og[h][rows])
+            om.append(a)
+            sl.append(b_)
+            e2 += e
+            r2 += r
+        om, sl = np.concatenate(om), np.concatenate(sl)
+        out[str(L)] = {"kept_frac_fwd": int(st["kept"].sum()) / (B * H * legal_tiles(L, *tile)),
+                       "slots_per_query": float(sl.mean()), "mean_omitted_mass_pct": 100.0 * float(om.mean()),
+                       "rel_l2_O_vs_exact": float(np.sqrt(e2 / r2)),
+                       "sample_blocks_per_head": len(blocks)}
+        log(f"fidelity L={L}: " + json.dumps(out[str(L)]))
+    return {"fidelity": out, "tau": tau, "workload": "sweep32k shape (H8 d128 bf16, 128x64 tiles), planted family",
+            "note": "slots = a row's visible keys in kept tiles; omitted mass against exact softmax"}
 
 
 def cpu_baseline(wx, wd, xp, xd0, nblocks, tau):
