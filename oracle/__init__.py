@@ -46,10 +46,13 @@ def _lib():
         lib.oracle_decode_groups.argtypes = [ctypes.c_long, _D, ctypes.c_int, _D, _D, ctypes.c_long, ctypes.c_long,
                                              ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_long,
                                              ctypes.c_int, ctypes.c_int, _U8, ctypes.c_double, _D, _D, _U8, _D]
+        lib.oracle_fwd_chunk_head.argtypes = [_D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_int,
+                                              ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int, _U8,
+                                              ctypes.c_double, _D, _D, _U8, _D]
         lib.oracle_omitted_head.argtypes = [_D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                             ctypes.c_int, _U8, _L, ctypes.c_long, _D, _D]
         for f in ("oracle_fwd_head", "oracle_bwd_head", "oracle_decode_group", "oracle_decode_groups",
-                  "oracle_omitted_head"):
+                  "oracle_omitted_head", "oracle_fwd_chunk_head"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -93,8 +96,18 @@ def _per_head(B, H, fn):
             f.result()
 
 
+def _group(H, k):
+    """Query heads per K/V head (grouped-query attention: q has H heads, k and
+    v have Hkv; query head h attends with K/V head h // (H / Hkv))."""
+    Hkv = k.shape[1]
+    if H % Hkv:
+        raise ValueError(f"H={H} is not a multiple of Hkv={Hkv}")
+    return H // Hkv
+
+
 def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     """MALA forward.  Returns (o, lse, keep, T); keep/T are [B, H, nqb, ntiles].
+    q is [B, H, L, d]; k, v are [B, Hkv, L, d] with H % Hkv == 0.
 
     qblocks: optional iterable of query-block indices (same for every head);
     rows of other blocks are left NaN.
@@ -103,6 +116,7 @@ def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, L, d = q.shape
+    G = _group(H, k)
     scale = default_scale(d) if scale is None else float(scale)
     nqb, nt = -(-L // bq), -(-L // bk)
     o = np.full((B, H, L, d), np.nan)
@@ -113,7 +127,8 @@ def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
 
     def one(b, h):
-        rc = _lib().oracle_fwd_head(_p(q[b, h], _D), _p(k[b, h], _D), _p(v[b, h], _D), L, d, scale, float(tau),
+        g = h // G  # the K/V head query head h reads
+        rc = _lib().oracle_fwd_head(_p(q[b, h], _D), _p(k[b, g], _D), _p(v[b, g], _D), L, d, scale, float(tau),
                                     bq, bk, _p(ids, _L), n, _p(None if rp is None else rp[b, h], _U8),
                                     float(band), _p(o[b, h], _D), _p(lse[b, h], _D), _p(keep[b, h], _U8),
                                     _p(T[b, h], _D))
@@ -123,18 +138,55 @@ def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     return o, lse, keep, T
 
 
+def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4):
+    """MALA forward of a query chunk against a key cache (chunked prefill).
+
+    q: [B, H, Lq, d], rows at key positions p0 .. p0 + Lq - 1; k, v:
+    [B, Hkv, >= p0 + Lq, d] (the first p0 + Lq rows are the keys the chunk
+    sees, its own included).  Row i has Lq_i = p0 + i + 1 visible keys.
+    Returns (o, lse, keep, T); keep/T are [B, H, ceil(Lq/bq), ceil((p0+Lq)/bk)].
+    """
+    q = _f64(q)
+    B, H, Lq, d = q.shape
+    G = _group(H, k)
+    Lk = int(p0) + Lq
+    k, v = _f64(k[:, :, :Lk]), _f64(v[:, :, :Lk])
+    scale = default_scale(d) if scale is None else float(scale)
+    nqb, nt = -(-Lq // bq), -(-Lk // bk)
+    o = np.full((B, H, Lq, d), np.nan)
+    lse = np.full((B, H, Lq), np.nan)
+    keep = np.zeros((B, H, nqb, nt), dtype=np.uint8)
+    T = np.full((B, H, nqb, nt), np.nan)
+    rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
+
+    def one(b, h):
+        g = h // G
+        rc = _lib().oracle_fwd_chunk_head(_p(q[b, h], _D), _p(k[b, g], _D), _p(v[b, g], _D), Lq, int(p0), d,
+                                          scale, float(tau), bq, bk, _p(None if rp is None else rp[b, h], _U8),
+                                          float(band), _p(o[b, h], _D), _p(lse[b, h], _D), _p(keep[b, h], _U8),
+                                          _p(T[b, h], _D))
+        _check(rc, "oracle_fwd_chunk_head")
+
+    _per_head(B, H, one)
+    return o, lse, keep, T
+
+
 def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None, ktiles=None):
     """MALA backward against the given forward state (o, lse).
 
     Returns (dq, dk, dv, keep, T).  qblocks / ktiles restrict which dq rows /
-    dk,dv rows are computed (others NaN).
+    dk,dv rows are computed (others NaN).  With grouped K/V heads
+    (k, v: [B, Hkv, L, d]) every query head's contribution is computed with
+    its shared K/V and dk, dv of a K/V head are the sum over its query heads
+    (the gradient of a tensor used by several heads).
     """
     q, k, v, o, lse, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(lse), _f64(do)
     B, H, L, d = q.shape
+    G = _group(H, k)
     scale = default_scale(d) if scale is None else float(scale)
     nqb, nt = -(-L // bq), -(-L // bk)
     dq = np.full((B, H, L, d), np.nan)
-    dk = np.full((B, H, L, d), np.nan)
+    dk = np.full((B, H, L, d), np.nan)  # per query head; summed per group below
     dv = np.full((B, H, L, d), np.nan)
     keep = np.zeros((B, H, nqb, nt), dtype=np.uint8)
     T = np.full((B, H, nqb, nt), np.nan)
@@ -143,7 +195,8 @@ def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qb
     rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
 
     def one(b, h):
-        rc = _lib().oracle_bwd_head(_p(q[b, h], _D), _p(k[b, h], _D), _p(v[b, h], _D), _p(o[b, h], _D),
+        g = h // G
+        rc = _lib().oracle_bwd_head(_p(q[b, h], _D), _p(k[b, g], _D), _p(v[b, g], _D), _p(o[b, h], _D),
                                     _p(lse[b, h], _D), _p(do[b, h], _D), L, d, scale, float(tau), bq, bk,
                                     _p(qi, _L), nq, _p(ki, _L), nk, _p(None if rp is None else rp[b, h], _U8),
                                     float(band), _p(dq[b, h], _D), _p(dk[b, h], _D), _p(dv[b, h], _D),
@@ -151,6 +204,9 @@ def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qb
         _check(rc, "oracle_bwd_head")
 
     _per_head(B, H, one)
+    if G > 1:
+        dk = dk.reshape(B, H // G, G, L, d).sum(axis=2)
+        dv = dv.reshape(B, H // G, G, L, d).sum(axis=2)
     return dq, dk, dv, keep, T
 
 

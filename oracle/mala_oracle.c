@@ -63,13 +63,19 @@ static long ceil_div(long a, long b) { return (a + b - 1) / b; }
 /* ------------------------------------------------------------------------ */
 /* Forward, one query block.  [forward], [threshold], [savings]              */
 /* ------------------------------------------------------------------------ */
-static int fwd_block(const double* q, const double* k, const double* v, long L, int d,
+/* Rows are the L query rows of a chunk whose first row sits at key position
+ * p0 (p0 = 0 for a whole sequence): row i is position p0 + i, sees keys
+ * 0 .. p0 + i, and has Lq_i = p0 + i + 1 visible keys.  Keys come from k, v
+ * ([p0 + L][d]); query blocks are counted from the chunk start, key tiles
+ * from key 0. */
+static int fwd_block(const double* q, const double* k, const double* v, long L, long p0, int d,
                      double scale, double tau, int bq, int bk, long qb, long ntiles,
                      const uint8_t* replay, double band,
                      double* o, double* lse, uint8_t* keep, double* T)
 {
     const long r0 = qb * (long)bq;
     const long r1 = (r0 + bq < L) ? r0 + bq : L;
+    const long Lk = p0 + L;
     const int nr = (int)(r1 - r0);
     double* m = malloc(sizeof(double) * nr);
     double* l = malloc(sizeof(double) * nr);
@@ -79,15 +85,15 @@ static int fwd_block(const double* q, const double* k, const double* v, long L, 
     for (int r = 0; r < nr; ++r) { m[r] = -INFINITY; l[r] = 0.0; }
 
     /* legal tiles of this block: 0 .. jmax, visited jmax down to 0 */
-    const long jmax = (r1 - 1) / bk;
+    const long jmax = (p0 + r1 - 1) / bk;
     for (long t = jmax; t >= 0; --t) {
         const long c0 = t * (long)bk;
-        const long c1 = (c0 + bk < L) ? c0 + bk : L;
+        const long c1 = (c0 + bk < Lk) ? c0 + bk : Lk;
         /* scores of every visible (i, j) in the tile */
         for (int r = 0; r < nr; ++r) {
             const long i = r0 + r;
             for (long j = c0; j < c1; ++j)
-                s[(size_t)r * bk + (j - c0)] = (j <= i) ? scale * dot(q + i * d, k + j * d, d) : -INFINITY;
+                s[(size_t)r * bk + (j - c0)] = (j <= p0 + i) ? scale * dot(q + i * d, k + j * d, d) : -INFINITY;
         }
         int kp;
         double Tt;
@@ -97,7 +103,7 @@ static int fwd_block(const double* q, const double* k, const double* v, long L, 
         } else {
             Tt = 0.0;
             for (int r = 0; r < nr; ++r) {
-                const long i = r0 + r;
+                const long i = p0 + r0 + r;            /* key position of the row */
                 if (c0 > i) continue;                  /* no visible key: abstain */
                 const long jl = (i < c1 - 1) ? i : c1 - 1;
                 double smax = -INFINITY;
@@ -115,7 +121,7 @@ static int fwd_block(const double* q, const double* k, const double* v, long L, 
         }
         if (kp) {
             for (int r = 0; r < nr; ++r) {
-                const long i = r0 + r;
+                const long i = p0 + r0 + r;            /* key position of the row */
                 if (c0 > i) continue;
                 const long jl = (i < c1 - 1) ? i : c1 - 1;
                 double smax = -INFINITY;
@@ -170,7 +176,32 @@ int oracle_fwd_head(const double* q, const double* k, const double* v, long L, i
     for (long u = 0; u < n; ++u) {
         const long qb = qblocks ? qblocks[u] : u;
         if (qb < 0 || qb >= nqb) { err = ORACLE_ERR_ARG; continue; }
-        int e = fwd_block(q, k, v, L, d, scale, tau, bq, bk, qb, ntiles, replay, band, o, lse, keep, T);
+        int e = fwd_block(q, k, v, L, 0, d, scale, tau, bq, bk, qb, ntiles, replay, band, o, lse, keep, T);
+        if (e) err = e;
+    }
+    return err;
+}
+
+/*
+ * Forward of a query chunk against a key cache, one (batch, head): q is
+ * [L][d] (the chunk's rows, at key positions p0 .. p0 + L - 1), k and v are
+ * [p0 + L][d] (every key the chunk can see, its own included).  Same test,
+ * visit order and update as the whole-sequence forward; Lq_i = p0 + i + 1
+ * ([threshold]: the row's count of visible keys).  keep and T are
+ * [nqb][ntiles] with nqb = ceil(L/bq), ntiles = ceil((p0 + L)/bk).
+ */
+int oracle_fwd_chunk_head(const double* q, const double* k, const double* v, long L, long p0, int d,
+                          double scale, double tau, int bq, int bk,
+                          const uint8_t* replay, double band,
+                          double* o, double* lse, uint8_t* keep, double* T)
+{
+    if (!q || !k || !v || !o || !lse || L <= 0 || p0 < 0 || d <= 0 || bq <= 0 || bk <= 0) return ORACLE_ERR_ARG;
+    if (!(tau >= 0.0)) return ORACLE_ERR_ARG;
+    const long nqb = ceil_div(L, bq), ntiles = ceil_div(p0 + L, bk);
+    int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long qb = 0; qb < nqb; ++qb) {
+        int e = fwd_block(q, k, v, L, p0, d, scale, tau, bq, bk, qb, ntiles, replay, band, o, lse, keep, T);
         if (e) err = e;
     }
     return err;

@@ -398,3 +398,113 @@ def test_invalid_tau_rejected():
     for bad in (-1.0, float("nan")):
         with pytest.raises(RuntimeError):
             oracle.fwd(q, q, q, bad, 2, 2)
+
+
+# ---------------------------------------------------------------- grouped K/V heads (GQA)
+def _gqa_small(L=700):
+    w = WORKLOADS["gqa8k"]
+    x = prefill_inputs(w, L=L, heads=range(4))  # query heads 0..3 = K/V head 0 (one group)
+    q = to_f64(x["q"][:, :4], w.dtype)
+    k, v = (to_f64(x[n][:, :1], w.dtype) for n in ("k", "v"))
+    do = to_f64(x["do"][:, :4], w.dtype)
+    return w, q, k, v, do
+
+
+def test_gqa_tau0_equals_dense_with_shared_kv():
+    """Grouped-query attention: every query head of a group attends with the
+    group's one K/V head, so at tau=0 the forward is dense attention with that
+    K/V repeated per head, and the gradient of the shared K (V) is the sum of
+    the per-head gradients (a tensor used by several heads)."""
+    w, q, k, v, do = _gqa_small()
+    G = q.shape[1]
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    scale = 1 / math.sqrt(w.d)
+    o, lse, _, _ = oracle.fwd(q, k, v, 0.0, w.bq, w.bk)
+    od, ld = dense.fwd(q, kr, vr, scale)
+    assert np.abs(o - od).max() <= 1e-12 * np.abs(od).max()
+    assert np.abs(lse - ld).max() <= 1e-12 * np.abs(ld).max()
+    dq, dk, dv, _, _ = oracle.bwd(q, k, v, o, lse, do, 0.0, w.bq, w.bk)
+    gq, gk, gv = dense.bwd(q, kr, vr, do, scale)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    assert np.abs(dq - gq).max() <= 1e-11 * np.abs(gq).max()
+    assert np.abs(dk - gk.sum(axis=1, keepdims=True)).max() <= 1e-11 * np.abs(gk).max()
+    assert np.abs(dv - gv.sum(axis=1, keepdims=True)).max() <= 1e-11 * np.abs(gv).max()
+
+
+@pytest.mark.parametrize("tau", [1.0, 4.0])
+def test_gqa_gated_equals_per_head_runs(tau):
+    """Decisions are per query head (each head's rows vote on its own tiles),
+    so with grouped K/V the gated result equals running every query head on
+    its own copy of the shared K/V, with the K/V gradients summed."""
+    w, q, k, v, do = _gqa_small()
+    G = q.shape[1]
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    o, lse, keep, _ = oracle.fwd(q, k, v, tau, w.bq, w.bk)
+    o2, lse2, keep2, _ = oracle.fwd(q, kr, vr, tau, w.bq, w.bk)
+    assert (keep == keep2).all() and (keep == 0).any()
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    dq, dk, dv, kb, _ = oracle.bwd(q, k, v, o, lse, do, tau, w.bq, w.bk)
+    dq2, dk2, dv2, kb2, _ = oracle.bwd(q, kr, vr, o, lse, do, tau, w.bq, w.bk)
+    assert (kb == kb2).all()
+    assert np.array_equal(dq, dq2)
+    assert np.abs(dk - dk2.sum(axis=1, keepdims=True)).max() <= 1e-12 * np.abs(dk).max()
+    assert np.abs(dv - dv2.sum(axis=1, keepdims=True)).max() <= 1e-12 * np.abs(dv).max()
+
+
+# ---------------------------------------------------------------- chunked prefill (query offset)
+def _chunk_case(P, Lq=300, heads=(2, 6)):
+    """A whole planted sequence of length P + Lq; the chunk is its last Lq rows."""
+    w, (q, k, v, do) = _prefill("mw8k", L=P + Lq, heads=list(heads))
+    return w, q, k, v
+
+
+@pytest.mark.parametrize("P", [0, 256, 333])
+def test_chunk_tau0_equals_dense_rows(P):
+    """Threshold paragraph: Lq is a row's count of visible keys, so a chunk at
+    offset P is causal attention of rows P.. over keys 0..P+i.  At tau=0 the
+    chunked forward equals those rows of dense causal attention."""
+    w, q, k, v = _chunk_case(P)
+    o, lse, keep, _ = oracle.fwd_chunk(q[:, :, P:], k, v, P, 0.0, 128, 64)
+    od, ld = dense.fwd(q, k, v, 1 / math.sqrt(w.d))
+    assert np.abs(o - od[:, :, P:]).max() <= 1e-12 * np.abs(od).max()
+    assert np.abs(lse - ld[:, :, P:]).max() <= 1e-12 * np.abs(ld).max()
+
+
+@pytest.mark.parametrize("tau", [1.0, 4.0])
+def test_chunk_aligned_equals_whole_sequence_blocks(tau):
+    """A query block's decisions and outputs depend only on its own rows and
+    the keys they see, so a chunk that starts on a query-block boundary
+    reproduces the whole-sequence forward's blocks exactly."""
+    P = 256
+    w, q, k, v = _chunk_case(P)
+    o, lse, keep, _ = oracle.fwd_chunk(q[:, :, P:], k, v, P, tau, 128, 64)
+    of, lf, kf, _ = oracle.fwd(q, k, v, tau, 128, 64)
+    assert (keep == kf[:, :, P // 128:]).all() and (keep == 0).any()
+    assert np.array_equal(o, of[:, :, P:]) and np.array_equal(lse, lf[:, :, P:])
+
+
+@pytest.mark.parametrize("tau", [1.0, 8.0])
+def test_chunk_unaligned_dense_over_kept_and_bounded(tau):
+    """Unaligned offset: the output is softmax attention over the keys of the
+    kept tiles (exact online update), the first tile visited is kept, and
+    every row's omitted mass stays below tau/(1+tau) (limits paragraph)."""
+    P = 333
+    w, q, k, v = _chunk_case(P)
+    Lq, Lk = q.shape[2] - P, q.shape[2]
+    o, lse, keep, _ = oracle.fwd_chunk(q[:, :, P:], k, v, P, tau, 128, 64)
+    scale = 1 / math.sqrt(w.d)
+    for h in range(q.shape[1]):
+        Pd = dense.probs_head(q[0, h], k[0, h], scale)[P:]
+        mask = np.zeros((Lq, Lk), bool)
+        for i in range(Lq):
+            jmax = (P + (i // 128) * 128 + min(128, Lq - (i // 128) * 128) - 1) // 64
+            assert keep[0, h, i // 128, jmax]
+            for t in range(keep.shape[3]):
+                if keep[0, h, i // 128, t]:
+                    mask[i, t * 64:(t + 1) * 64] = True
+        full = np.ones((Lk, Lk), bool)  # rows before the chunk: unused here
+        full[P:] = mask
+        od, ld = dense.fwd_head(q[0, h], k[0, h], v[0, h], scale, key_mask=full)
+        assert np.abs(o[0, h] - od[P:]).max() <= 1e-12 * np.abs(od[P:]).max()
+        om = (Pd * ~mask).sum(axis=1)
+        assert (om < tau / (1 + tau)).all()
