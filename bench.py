@@ -238,7 +238,9 @@ def main():
                            "work_per_launch": work, "per_unit": per_unit}
     roofline = rooflines[max(rooflines, key=lambda n: rooflines[n]["ms"])]
 
+    chunk = None if args.no_tau0 else chunked_prefill(torch, ops, q, k, v, args.tau, args.steps)
     sweep = None if args.no_sweep else sweep32k(torch, ops, args.steps, args.warmup)
+    gqa = None if args.no_sweep else gqa_8k(torch, ops, args.tau, args.steps)
     matched = None if args.no_matched_work else matched_work_8k(torch, ops, args.steps)
 
     cpu = None
@@ -271,6 +273,8 @@ def main():
         "kernel_rooflines": rooflines,
         "sweep32k": sweep,
         "matched_work_8k": matched,
+        "chunked_prefill": chunk,
+        "gqa8k": gqa,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res))
@@ -513,6 +517,56 @@ def sweep32k(torch, ops, steps, warmup):
         log(f"sweep32k {family}: " + ", ".join(f"tau={t}: fwd {r['fwd_ms']:.2f} bwd {r['bwd_ms']:.2f} "
                                               f"kept {r['kept_fwd']:.3f}/{r['kept_bwd']:.3f}" for t, r in res.items()))
         del q, k, v, do, o, dq, dk, dv
+    return out
+
+
+def chunked_prefill(torch, ops, q, k, v, tau, steps, Lq=16384):
+    """Chunked prefill on the 128K training shape: the last Lq query rows
+    (key offset P = L - Lq) against the K/V cache holding all L keys, at tau
+    and at tau=0.  Dense-equivalent FLOPs: 4*d per visible (row, key) pair."""
+    B, H, L, d = q.shape
+    P = L - Lq
+    qc = q[:, :, P:].contiguous()
+    tile = (128, 64)
+    out = {"workload": f"train128k shape, last {Lq} rows at key offset {P} against the {L}-key cache"}
+    pairs = B * H * (Lq * P + Lq * (Lq + 1) / 2)
+    for t in (tau, 0.0):
+        o, lse, st = ops.fwd_chunk(qc, k, v, P, t, stats=True)
+        torch.cuda.synchronize()
+        kept, legal = int(st["kept"].sum()), int(st["legal"].sum())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ops.fwd_chunk_into(qc, k, v, P, o, lse, t, tile)
+        e0.record()
+        for _ in range(steps):
+            ops.fwd_chunk_into(qc, k, v, P, o, lse, t, tile)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[f"tau={t}"] = {"ms": ms, "kept_frac": kept / legal, "dense_equiv_tflops": 4.0 * d * pairs / ms / 1e9}
+    log(f"chunked prefill: " + json.dumps(out))
+    return out
+
+
+def gqa_8k(torch, ops, tau, steps):
+    """Grouped K/V heads: B1, 8 query heads over 2 K/V heads, L=8192, d=128,
+    planted inputs; forward and backward ms at tau and at tau=0."""
+    from synth import WORKLOADS, prefill_inputs
+    w = WORKLOADS["gqa8k"]
+    x = prefill_inputs(w)
+    q, k, v, do = (dev_bf16(torch, x[n]) for n in ("q", "k", "v", "do"))
+    del x
+    tile = (w.bq, w.bk)
+    o, lse = ops.fwd(q, k, v, tau)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = ops.bwd_workspace(q, tile)
+    out = {"workload": "gqa8k (B1 H8 Hkv2 L8192 d128 bf16, 128x64 tiles, planted)"}
+    for t in (tau, 0.0):
+        ms = kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, t, steps)
+        st = ops.prefill_stats_buffers(*q.shape[:3], tile, q.device)
+        ops.fwd_into(q, k, v, o, lse, t, tile, stats=st)
+        torch.cuda.synchronize()
+        out[f"tau={t}"] = dict(ms, kept_frac_fwd=int(st["kept"].sum()) / int(st["legal"].sum()))
+    log("gqa8k: " + json.dumps(out))
     return out
 
 

@@ -42,9 +42,10 @@
  *  - Thread safety: calls may be made concurrently from several host threads.
  *
  * Supported shapes (anything else returns MALA_ERR_UNSUPPORTED)
- *  - prefill (fwd/bwd): H == Hkv; L >= 1 (ragged L allowed);
- *      MALA_BF16 with d = 128 and tile {128, 64};
- *      MALA_F32  with d = 64  and tile {64, 64}.
+ *  - prefill (fwd/bwd): H % Hkv == 0 (else MALA_ERR_INVALID_ARG); L >= 1
+ *      (ragged L allowed);
+ *      MALA_BF16 with d = 128 and tile {128, 64} (grouped K/V heads allowed);
+ *      MALA_F32  with d = 64  and tile {64, 64} (H == Hkv only).
  *  - decode: Hq % Hkv == 0 with G = Hq/Hkv <= 8; MALA_BF16, d = 128, bk = 64,
  *      split_keys a positive multiple of bk.
  */
@@ -107,7 +108,9 @@ typedef struct {
 /*
  * mala_fwd -- gated forward (forward paragraph, threshold paragraph).
  *
- * q, k, v: [B, H, L, d].  o: [B, H, L, d] (same dtype).  lse: float [B, H, L].
+ * q: [B, H, L, d]; k, v: [B, Hkv, L, d], query head h reading K/V head
+ * h / (H/Hkv) (grouped-query attention; Hkv == H is ordinary multi-head).
+ * o: [B, H, L, d] (same dtype).  lse: float [B, H, L].
  * For each query block of bq rows, key tiles t = jmax .. 0 (diagonal first)
  * are scored; row i of the block votes to keep tile t iff its running state
  * is empty or max_j exp(s_ij - m_i)/l_i >= tau/(i+1) over its visible keys
@@ -120,15 +123,40 @@ mala_status mala_fwd(const void* q, const void* k, const void* v,
                      float tau, mala_tile tile, float scale,
                      void* o, float* lse, mala_stats* stats, void* stream);
 
+/*
+ * mala_fwd_chunk -- gated forward of a query chunk against a key/value cache
+ * (chunked prefill; threshold paragraph: one test for training, prefill and
+ * decoding, with Lq the row's count of visible keys).
+ *
+ * q: [B, H, Lq, d], row i at key position P + i.  kcache, vcache:
+ * [B, Hkv, Lcap, d]; rows 0 .. P + Lq - 1 are valid (the cache holds the P
+ * earlier keys and the chunk's own keys at P .. P + Lq - 1); Lcap >= P + Lq.
+ * Query head h reads K/V head h / (H/Hkv).  Row i sees keys 0 .. P + i and
+ * Lq_i = P + i + 1.  Query blocks of bq rows are counted from the chunk
+ * start, key tiles of bk keys from key 0; each block visits its tiles from the
+ * one holding its last row's key back to key 0 with the forward's test and
+ * update.  With P = 0 and Lcap = Lq this is mala_fwd.  o: [B, H, Lq, d],
+ * lse: float [B, H, Lq].  Statistics as for mala_fwd with
+ * ntiles = ceil((P + Lq)/bk).  bf16, d = 128, tile {128, 64} only.
+ * Errors: P < 0 or P + Lq > Lcap -> MALA_ERR_INVALID_ARG; other dtypes ->
+ * MALA_ERR_UNSUPPORTED.
+ */
+mala_status mala_fwd_chunk(const void* q, const void* kcache, const void* vcache,
+                           int B, int H, int Hkv, int Lq, int P, int Lcap, int d, mala_dtype dtype,
+                           float tau, mala_tile tile, float scale,
+                           void* o, float* lse, mala_stats* stats, void* stream);
+
 /* Workspace bytes mala_bwd needs for these sizes (0 for invalid sizes). */
 size_t mala_bwd_workspace_size(int B, int H, int L, int d, mala_dtype dtype, mala_tile tile);
 
 /*
  * mala_bwd -- gated backward (backward paragraph).
  *
- * Inputs q, k, v, o, dout: [B, H, L, d]; lse: float [B, H, L] -- o and lse
- * exactly as mala_fwd wrote them (the ordinary attention state; no mask).
- * Outputs dq, dk, dv: [B, H, L, d], fully overwritten.
+ * Inputs q, o, dout: [B, H, L, d]; k, v: [B, Hkv, L, d] (as in mala_fwd);
+ * lse: float [B, H, L] -- o and lse exactly as mala_fwd wrote them (the
+ * ordinary attention state; no mask).  Outputs dq: [B, H, L, d], dk, dv:
+ * [B, Hkv, L, d], fully overwritten; with grouped heads dk and dv sum the
+ * contributions of the H/Hkv query heads that share a K/V head.
  * With P_ij = exp(s_ij - lse_i), a tile (query block, key tile) is kept iff
  * some row has a visible key with P_ij >= tau/(i+1) (no forced keep).  Kept
  * tiles contribute dV += P^T dO, dS = P o (dO V^T - D) with

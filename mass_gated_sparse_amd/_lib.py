@@ -28,7 +28,7 @@ class Stats(ctypes.Structure):
                 ("keep_bits_dkdv", ctypes.c_void_p), ("events", ctypes.c_void_p * 4)]
 
 
-EXPORTS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
+EXPORTS = ("mala_fwd", "mala_fwd_chunk", "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
            "mala_status_string", "mala_last_error", "mala_version")
 
 _LIB = None
@@ -48,6 +48,8 @@ def load(path=None):
     sp = ctypes.POINTER(Stats)
     lib.mala_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, i, f, Tile, f, vp, vp, sp, vp]
     lib.mala_fwd.restype = i
+    lib.mala_fwd_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, f, Tile, f, vp, vp, sp, vp]
+    lib.mala_fwd_chunk.restype = i
     lib.mala_bwd_workspace_size.argtypes = [i, i, i, i, i, Tile]
     lib.mala_bwd_workspace_size.restype = sz
     lib.mala_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, Tile, f, vp, vp, vp, sp, vp, sz, vp]

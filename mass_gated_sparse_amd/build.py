@@ -10,7 +10,10 @@ ARCH = "gfx950"
 # -amdgpu-mfma-vgpr-form: MFMA results go to arch VGPRs first; kernels that
 #   run one wave per SIMD then keep long-lived operands in AGPRs without the
 #   per-iteration AGPR<->VGPR copies and scratch spills the default form gives.
-HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+# -Werror=shadow-all: kernels are long lambdas over many locals; a name that
+#   shadows one of them (a compile-time tag named like a kernel argument) is
+#   an error, not a silent change of meaning.
+HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Werror=shadow-all",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 

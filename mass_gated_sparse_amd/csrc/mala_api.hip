@@ -52,7 +52,9 @@ mala_status check_prefill(const void* q, const void* k, const void* v, int B, in
     if (tile.bq <= 0 || tile.bk <= 0) return fail(MALA_ERR_INVALID_ARG, "tile sizes must be positive");
     if (!tau_ok(tau)) return fail(MALA_ERR_INVALID_ARG, "tau must be >= 0 (got %f)", double(tau));
     if (dt != MALA_BF16 && dt != MALA_F32) return fail(MALA_ERR_INVALID_ARG, "unknown dtype %d", int(dt));
-    if (H != Hkv) return fail(MALA_ERR_UNSUPPORTED, "prefill needs H == Hkv (got %d, %d)", H, Hkv);
+    if (H % Hkv) return fail(MALA_ERR_INVALID_ARG, "H (%d) not a multiple of Hkv (%d)", H, Hkv);
+    if (H != Hkv && dt != MALA_BF16)
+        return fail(MALA_ERR_UNSUPPORTED, "grouped K/V heads (H=%d, Hkv=%d) need bf16", H, Hkv);
     if (!prefill_supported(dt, d, tile))
         return fail(MALA_ERR_UNSUPPORTED, "unsupported prefill instantiation dtype=%d d=%d tile=%dx%d", int(dt), d,
                     tile.bq, tile.bk);
@@ -87,7 +89,8 @@ mala_status mala_fwd(const void* q, const void* k, const void* v, int B, int H, 
     if (!o || !lse) return fail(MALA_ERR_INVALID_ARG, "null output pointer");
     mala::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.B = B; a.H = H; a.L = L; a.d = d;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.L = L; a.d = d;
+    a.P = 0; a.Lk = L; a.Lkcap = L;
     a.nqb = int(cdiv(L, tile.bq));
     a.ntiles = int(cdiv(L, tile.bk));
     a.words = int(cdiv(a.ntiles, 32));
@@ -102,6 +105,37 @@ mala_status mala_fwd(const void* q, const void* k, const void* v, int B, int H, 
     if (e == hipSuccess) e = dtype == MALA_BF16 ? mala::launch_fwd_bf16(a, s) : mala::launch_simple_fwd_f32(a, s);
     if (e == hipSuccess) e = mala::mark(e1, s);
     return hip_status(e, "mala_fwd launch");
+}
+
+mala_status mala_fwd_chunk(const void* q, const void* kcache, const void* vcache, int B, int H, int Hkv, int Lq,
+                           int P, int Lcap, int d, mala_dtype dtype, float tau, mala_tile tile, float scale, void* o,
+                           float* lse, mala_stats* stats, void* stream) {
+    g_err[0] = 0;
+    mala_status st = check_prefill(q, kcache, vcache, B, H, Hkv, Lq, d, dtype, tau, tile);
+    if (st) return st;
+    if (!o || !lse) return fail(MALA_ERR_INVALID_ARG, "null output pointer");
+    if (P < 0) return fail(MALA_ERR_INVALID_ARG, "negative chunk offset P=%d", P);
+    if ((long)P + Lq > Lcap) return fail(MALA_ERR_INVALID_ARG, "P + Lq (%ld) exceeds Lcap (%d)", (long)P + Lq, Lcap);
+    if (dtype != MALA_BF16) return fail(MALA_ERR_UNSUPPORTED, "chunked prefill needs bf16");
+    if ((long)B * Hkv * Lcap * d >= (1L << 40)) return fail(MALA_ERR_UNSUPPORTED, "cache too large");
+    mala::FwdArgs a{};
+    a.q = q; a.k = kcache; a.v = vcache; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.L = Lq; a.d = d;
+    a.P = P; a.Lk = P + Lq; a.Lkcap = Lcap;
+    a.nqb = int(cdiv(Lq, tile.bq));
+    a.ntiles = int(cdiv(a.Lk, tile.bk));
+    a.words = int(cdiv(a.ntiles, 32));
+    const float sc = eff_scale(scale, d);
+    a.scale_log2 = sc * mala::kLog2e;
+    a.log2_tau = log2_tau_of(tau);
+    a.gated = tau != 0.f;
+    if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipEvent_t e0 = stats ? (hipEvent_t)stats->events[0] : nullptr, e1 = stats ? (hipEvent_t)stats->events[1] : nullptr;
+    hipError_t e = mala::mark(e0, s);
+    if (e == hipSuccess) e = mala::launch_fwd_bf16(a, s);
+    if (e == hipSuccess) e = mala::mark(e1, s);
+    return hip_status(e, "mala_fwd_chunk launch");
 }
 
 size_t mala_bwd_workspace_size(int B, int H, int L, int d, mala_dtype dtype, mala_tile tile) {
@@ -134,7 +168,7 @@ mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o,
     a.lse2 = reinterpret_cast<float*>(ws + align256(rows * 4));
     a.thr = reinterpret_cast<float*>(ws + 2 * align256(rows * 4));
     a.dbits = reinterpret_cast<uint32_t*>(ws + 3 * align256(rows * 4));
-    a.B = B; a.H = H; a.L = L; a.d = d;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.L = L; a.d = d;
     a.nqb = int(cdiv(L, tile.bq));
     a.ntiles = int(cdiv(L, tile.bk));
     a.words = int(cdiv(a.ntiles, 32));

@@ -53,7 +53,7 @@ template <bool GATED, bool STATS>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
-    const float* __restrict__ thr, bf16_t* __restrict__ dq, int BH, int L, int nqb, int words, float scale,
+    const float* __restrict__ thr, bf16_t* __restrict__ dq, int BH, int G, int L, int nqb, int words, float scale,
     float scale_log2, int32_t* __restrict__ kept, int32_t* __restrict__ legal, uint32_t* __restrict__ bits,
     uint32_t* __restrict__ dbits) {
     using namespace bwdk;
@@ -65,9 +65,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     int qrank, bh;
     balanced_item(int(blockIdx.x), BH, max(1, nqb / 8), qrank, bh);
     const int qb = nqb - 1 - qrank;  // longest query blocks first
-    const long hoff = long(bh) * L * D;
-    const bf16_t* kh = k + hoff;
-    const bf16_t* vh = v + hoff;
+    const long hoff = long(bh) * L * D;       // this query head
+    const long kvoff = long(bh / G) * L * D;  // its KV head (G query heads per KV head)
+    const bf16_t* kh = k + kvoff;
+    const bf16_t* vh = v + kvoff;
     const int row = qb * BQ + wave * 32 + j;
     const bool rvalid = row < L;
 
@@ -308,7 +309,7 @@ template <bool GATED>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BH, int L, int nqb, int words, float scale,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BHkv, int G, int L, int nqb, int words, float scale,
     float scale_log2, const uint32_t* __restrict__ dbits, uint32_t* __restrict__ aux_bits) {
     using namespace bwdk;
     // buf[0..3]: Q and dO tiles of two query blocks (buf[0], buf[1] and
@@ -320,9 +321,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     const int kb = wave & 1, rq = wave >> 1;
-    int t, bh;  // 64-key tile; longest (t = 0) first
-    balanced_item(int(blockIdx.x), BH, max(1, (2 * nqb) / 8), t, bh);
-    const long hoff = long(bh) * L * D;
+    int t, bkv;  // 64-key tile (longest, t = 0, first) and K/V head; its query heads are bkv*G .. +G-1
+    balanced_item(int(blockIdx.x), BHkv, max(1, (2 * nqb) / 8), t, bkv);
+    const long kvoff = long(bkv) * L * D;
     const int key = t * BK + 32 * kb + j;
     const bool kvalid = key < L;
     const int qb0 = (t * BK) / BQ;  // first query block that sees the tile (its diagonal block)
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     u32x4 kf[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-        kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(k + hoff + long(key) * D + 16 * s + 8 * hl) : z4;
+        kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(k + kvoff + long(key) * D + 16 * s + 8 * hl) : z4;
     f32x16 dvacc[4], dkacc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -343,9 +344,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     // issues segments 4w..4w+3 (rows 16w .. 16w+15); lane l of a segment fills
     // physical chunk l%16 of row l/16, i.e. it reads the logical chunk that the
     // swizzle puts there.  Rows past L read row L-1 instead (masked later).
-    auto tile_async = [&](const bf16_t* g, uint8_t* dst, int r0) {
+    auto tile_async = [&](const bf16_t* g, uint8_t* dst, int bh, int r0) {
         const uint32_t la = lds_addr_of(dst) + 4096 * wave;
-        const bf16_t* gb = g + hoff + long(r0) * D;  // wave-uniform
+        const bf16_t* gb = g + long(bh) * L * D + long(r0) * D;  // wave-uniform
         const int lim = L - 1 - r0;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     // waiting for these loads never waits for the prefetch.
     float stv[2];
     int st_row = 0;
-    auto stats_load = [&](int r0) {
+    auto stats_load = [&](int bh, int r0) {
         if (tid < BQ) {
             st_row = r0 + tid;
             const long ri = long(bh) * L + min(st_row, L - 1);
@@ -391,23 +392,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     // this wave's 32 keys of V, addressed with the Q-tile offsets
     const uint32_t va = lds_addr_of(vtile) + 8192 * kb - 8192 * rq;
 
-    // Kept query blocks of this tile, 64 at a time: bit i of kmask is block
-    // wbase + i (every lane fetches one block's decision word, a ballot packs
-    // the bits); the next window's words are fetched one window ahead.
+    // Work items are (query head of the group, kept query block), head by
+    // head.  Kept blocks of one head come 64 at a time: bit i of kmask is
+    // block wbase + i (every lane fetches one block's decision word, a ballot
+    // packs the bits); the next window's words are fetched one window ahead.
     const uint32_t tbit = 1u << (t & 31);
-    const uint32_t* dcol = GATED ? dbits + long(bh) * nqb * words + (t >> 5) : nullptr;
+    int ih = 0;  // query head within the group of the current window
     auto fetch = [&](int base) -> uint32_t {
         const int qb = base + lane;
-        return (GATED && qb < nqb) ? dcol[long(qb) * words] : 0u;
+        return (GATED && qb < nqb) ? dbits[(long(bkv * G + ih) * nqb + qb) * words + (t >> 5)] : 0u;
     };
     int wbase = qb0;
     uint64_t kmask = 0;
     uint32_t wnext = 0;
-    if (GATED) {
-        kmask = __ballot((fetch(qb0) & tbit) != 0u);
-        wnext = fetch(qb0 + 64);
-    }
-    // first kept block >= qb (qb >= wbase), or nqb
+    auto open_head = [&]() {
+        wbase = qb0;
+        if (GATED) {
+            kmask = __ballot((fetch(qb0) & tbit) != 0u);
+            wnext = fetch(qb0 + 64);
+        }
+    };
+    // first kept block >= qb (qb >= wbase) of head ih, or nqb
     auto kept_from = [&](int qb) -> int {
         if (!GATED) return qb;
         for (;;) {
@@ -421,12 +426,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
             wnext = fetch(wbase + 64);
         }
     };
+    // the work item after (ih, qb): the next kept block of this head, else
+    // the first kept block of the next head with one (ih == G: done)
+    auto next_item = [&](int qb) -> int {
+        int qn = kept_from(qb + 1);
+        while (qn >= nqb && ih + 1 < G) {
+            ++ih;
+            open_head();
+            qn = kept_from(qb0);
+        }
+        if (qn >= nqb) ih = G;
+        return qn;
+    };
 
     // One kept query block, computed from (qs, os, st).  Only the diagonal
     // block (qb == qb0) needs a visibility mask: it is the only block with
     // keys past some row, and the only block of the last tiles, whose keys may
     // run past L.  Elsewhere every key is visible to every row.
-    auto block = [&](auto diag_tag, int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ]) {
+    auto block = [&](auto diag_tag, int bh, int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ]) {
         constexpr bool diag = decltype(diag_tag)::value;
         const int r0 = qb * BQ;
         const uint32_t qa = lds_addr_of(qs), oa = lds_addr_of(os);
@@ -494,43 +511,50 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
             atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (t >> 5)], tbit);
     };
 
-    // prologue: V tile; the first kept block into buffers 0, 1
+    // prologue: V tile; the first work item into buffers 0, 1
 #pragma unroll
     for (int it = 0; it < 2; ++it) {  // V tile: segments 2w, 2w+1 (rows 8w .. 8w+7)
         const int rt = 8 * wave + 4 * it + (lane >> 4);
         const uint32_t off = uint32_t(min(rt, L - 1 - t * BK) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
-        dma16s(v + hoff + long(t) * BK * D, off,
+        dma16s(v + kvoff + long(t) * BK * D, off,
                __builtin_amdgcn_readfirstlane(lds_addr_of(vtile) + 2048 * wave + 1024 * it));
     }
+    open_head();
     int qb = kept_from(qb0);
-    if (qb < nqb) {
-        tile_async(q, buf[0], qb * BQ);
-        tile_async(dout, buf[1], qb * BQ);
-        stats_load(qb * BQ);
+    if (qb >= nqb) qb = next_item(nqb - 1);  // head 0 keeps nothing here: move on
+    if (ih < G) {
+        tile_async(q, buf[0], bkv * G + ih, qb * BQ);
+        tile_async(dout, buf[1], bkv * G + ih, qb * BQ);
+        stats_load(bkv * G + ih, qb * BQ);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
     stats_store(stA);
     lds_barrier();
-    // Each kept block is computed from one buffer pair while the next kept
-    // block streams into the other.  The diagonal block, if kept, is first.
+    // Each work item is computed from one buffer pair while the next streams
+    // into the other.  A head's diagonal block, if kept, is its first item.
     bool odd = false;
     auto advance = [&](auto diag_tag) {
-        const int qn = kept_from(qb + 1);
-        const bool more = qn < nqb;
+        const int bh = bkv * G + ih;
+        const int qcur = qb;
+        const int qn = next_item(qcur);
+        const bool more = ih < G;
         if (more) {
-            stats_load(qn * BQ);
-            tile_async(q, odd ? buf[0] : buf[2], qn * BQ);
-            tile_async(dout, odd ? buf[1] : buf[3], qn * BQ);
+            stats_load(bkv * G + ih, qn * BQ);
+            tile_async(q, odd ? buf[0] : buf[2], bkv * G + ih, qn * BQ);
+            tile_async(dout, odd ? buf[1] : buf[3], bkv * G + ih, qn * BQ);
         }
-        block(diag_tag, qb, odd ? buf[2] : buf[0], odd ? buf[3] : buf[1], odd ? stB : stA);
+        block(diag_tag, bh, qcur, odd ? buf[2] : buf[0], odd ? buf[3] : buf[1], odd ? stB : stA);
         if (more) stats_store(odd ? stA : stB);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffer landed
         lds_barrier();                       // next buffer complete; every wave is done with this one
         qb = qn;
         odd = !odd;
     };
-    if (qb == qb0) advance(std::true_type{});
-    while (qb < nqb) advance(std::false_type{});
+    while (ih < G) {
+        const int hcur = ih;
+        if (qb == qb0) advance(std::true_type{});
+        while (ih == hcur) advance(std::false_type{});
+    }
 
     // Sum the four row quarters.  Accumulators hold dK^T, dV^T: lane = key,
     // register 4g + x of block db = d 32db + 8g + 4hl + x.  Wave w stores its
@@ -564,7 +588,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
                 w[0] = pack_bf16x2(sum[0] * mul, sum[1] * mul);
                 w[1] = pack_bf16x2(sum[2] * mul, sum[3] * mul);
                 const int d0 = 32 * (dbg >> 2) + 8 * (dbg & 3) + 4 * (l >> 5);
-                *reinterpret_cast<u32x2*>(out + hoff + long(kk) * D + d0) = w;
+                *reinterpret_cast<u32x2*>(out + kvoff + long(kk) * D + d0) = w;
             }
         }
         lds_barrier();
@@ -575,13 +599,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     const int BH = a.B * a.H;
-    dim3 g1(unsigned(a.ntiles) * unsigned(BH)), b1(512), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
+    const int G = a.H / a.Hkv;  // query heads per K/V head (the API checked H % Hkv == 0)
+    if (G < 1 || a.H % a.Hkv) return hipErrorInvalidValue;
+    dim3 g1(unsigned(a.ntiles) * unsigned(a.B * a.Hkv)), b1(512), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
     const bool st = a.kept || a.legal || a.bits;
     hipError_t e = mark(a.ev[1], s);
     if (e != hipSuccess) return e;
-#define MALA_DQ_LAUNCH(G, S)                                                                                  \
-    hipLaunchKernelGGL((bwd_dq_bf16_d128<G, S>), g2, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,       \
-                       (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dq, BH, a.L, \
+#define MALA_DQ_LAUNCH(GT, ST)                                                                                \
+    hipLaunchKernelGGL((bwd_dq_bf16_d128<GT, ST>), g2, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,     \
+                       (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dq, BH, G, a.L, \
                        a.nqb, a.words, a.scale, a.scale_log2, a.kept, a.legal, a.bits, a.dbits)
     if (a.gated) {
         if (st) MALA_DQ_LAUNCH(true, true);
@@ -597,11 +623,11 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     if (a.gated)
         hipLaunchKernelGGL((bwd_dkdv_bf16_d128<true>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
                            (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, (bf16_t*)a.dk, (bf16_t*)a.dv,
-                           BH, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits);
+                           a.B * a.Hkv, G, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits);
     else
         hipLaunchKernelGGL((bwd_dkdv_bf16_d128<false>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
                            (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, (bf16_t*)a.dk, (bf16_t*)a.dv,
-                           BH, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits);
+                           a.B * a.Hkv, G, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits);
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(a.ev[3], s);
     return e;

@@ -154,8 +154,17 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
 
 // Same load with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
 // byte offset (the saddr form): one VGPR of address per lane instead of two.
+// The base must be the same in every lane; it is read from the first lane
+// so that it always sits in an SGPR pair.
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+    // (the builtin returns a signed int: both halves go through uint32_t so
+    // that the low half is zero-extended, never sign-extended)
+    const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))));
+    const uint32_t hi =
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32))));
+    const void* sb = reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo));
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(lds_addr)
                  : "memory", "m0");
 }
 

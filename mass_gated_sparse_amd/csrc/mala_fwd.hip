@@ -50,7 +50,8 @@ constexpr int BQ = 128, BK = 64, D = 128;
 template <bool GATED, bool STATS>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                                         const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
-                                                        float* __restrict__ lse, int BH, int L, int nqb, int words,
+                                                        float* __restrict__ lse, int BH, int G, int L, int P, int Lk,
+                                                        int Lkcap, int nqb, int words,
                                                         float scale_log2, float log2_tau, int32_t* __restrict__ kept,
                                                         int32_t* __restrict__ legal, uint32_t* __restrict__ bits) {
     using namespace fwdk;
@@ -62,9 +63,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     int qrank, bh;
     balanced_item(int(blockIdx.x), BH, max(1, nqb / 8), qrank, bh);
     const int qb = nqb - 1 - qrank;  // longest query blocks first
-    const long hoff = long(bh) * L * D;
-    const bf16_t* kh = k + hoff;
-    const bf16_t* vh = v + hoff;
+    const long hoff = long(bh) * L * D;              // this query head
+    const long kvoff = long(bh / G) * Lkcap * D;     // its KV head (G query heads per KV head)
+    const bf16_t* kh = k + kvoff;
+    const bf16_t* vh = v + kvoff;
     const int row = qb * BQ + wave * 32 + j;
     const bool rvalid = row < L;
 
@@ -81,13 +83,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m2 = -INFINITY, lsum = 0.f;
-    const float log2_lq = fast_log2(float(row + 1));
+    const float log2_lq = fast_log2(float(P + row + 1));  // the row sits at key position P + row
     const float inv_scale_log2 = 1.f / scale_log2;
-    const int jmax = (min(qb * BQ + BQ, L) - 1) / BK;
+    const int jmax = (P + min(qb * BQ + BQ, L) - 1) / BK;
+    const int tdiag = (P + qb * BQ) / BK;  // tiles t >= tdiag reach the block's first row
 
     auto tile_dma = [&](const bf16_t* g, uint8_t* dst, int t) {
         const uint32_t la = lds_addr_of(dst) + 4096 * wave;
-        const int rmax = L - 1 - t * BK;
+        const int rmax = Lk - 1 - t * BK;  // keys past Lk read key Lk-1 (masked)
         const bf16_t* gt = g + long(t) * BK * D;  // wave-uniform
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -151,15 +154,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     // the vote exchange.  After it: the K(t-3) and V(t) requests (each has a
     // whole step to land), this tile's statistics, the PV of the previous kept
     // tile t+1 and this tile's rescale.
-    // One step per tile; the tile parity P = t & 1 is a compile-time constant,
+    // One step per tile; the tile parity PAR = t & 1 is a compile-time constant,
     // so every LDS slot address is a constant (it folds into the instructions'
     // offset fields) and the score registers are renamed, not copied.
     auto step = [&](auto par_tag, int t) {
-        constexpr int P = decltype(par_tag)::value;
+        constexpr int PAR = decltype(par_tag)::value;
         // causal mask on the tiles that reach the diagonal: register r of key
         // block kb holds key t*64 + 32kb + 8(r/4) + 4hl + r%4, invisible when > row
-        if (t >= 2 * qb) {
-            const int lim = row - t * BK - 4 * hl;
+        if (t >= tdiag) {
+            const int lim = P + row - t * BK - 4 * hl;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -179,18 +182,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
             else if (lsum == 0.f) thr_raw = -FLT_MAX;  // empty row: any visible key keeps
             else thr_raw = (m2 + fast_log2(lsum) + log2_tau - log2_lq) * inv_scale_log2;
             const bool wv = wave_any(mx >= thr_raw);
-            if (lane == 0) vote_sm[P][wave] = wv ? 1 : 0;
+            if (lane == 0) vote_sm[PAR][wave] = wv ? 1 : 0;
         }
-        if (t >= 1) scores(kslot[1 - P], sn);
+        if (t >= 1) scores(kslot[1 - PAR], sn);
         // K(t-2) and V(t+1), requested in the previous step, have landed (with
         // statistics on, thread 0 also waits for its keep-bit stores)
         __builtin_amdgcn_s_waitcnt(0x0f70);
-        lds_barrier();  // votes, K(t-2), V(t+1) visible; every wave is done with kslot[1 - P]
+        lds_barrier();  // votes, K(t-2), V(t+1) visible; every wave is done with kslot[1 - PAR]
         int vflags = 1;
-        if (GATED) vflags = vote_sm[P][0] | vote_sm[P][1] | vote_sm[P][2] | vote_sm[P][3];
+        if (GATED) vflags = vote_sm[PAR][0] | vote_sm[PAR][1] | vote_sm[PAR][2] | vote_sm[PAR][3];
         const bool keep = vflags != 0;
-        if (t >= 3) tile_dma(kh, kslot[1 - P], t - 3);  // K(t-3) into the slot K(t-1) used
-        if (keep) tile_dma(vh, vslot[P], t);              // V only for kept tiles
+        if (t >= 3) tile_dma(kh, kslot[1 - PAR], t - 3);  // K(t-3) into the slot K(t-1) used
+        if (keep) tile_dma(vh, vslot[PAR], t);              // V only for kept tiles
 
         float alpha = 1.f;
         if (keep) {
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
             m2 = mn;
         }
         // PV of the previous kept tile (in its own frame), then this tile's rescale
-        if (pend) pv(vslot[1 - P], ppend);
+        if (pend) pv(vslot[1 - PAR], ppend);
         if (keep) {
             if (__ballot(alpha != 1.f) != 0ull) {  // skipped when no row's max moved (exact)
 #pragma unroll
@@ -280,12 +283,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
     const int BH = a.B * a.H;
+    if (a.Hkv < 1 || a.H % a.Hkv) return hipErrorInvalidValue;  // the API checked this already
     dim3 grid(unsigned(a.nqb) * unsigned(BH)), block(256);
     const bool st = a.kept || a.legal || a.bits;
-#define MALA_FWD_LAUNCH(G, S)                                                                                  \
-    hipLaunchKernelGGL((fwd_bf16_d128<G, S>), grid, block, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,       \
-                       (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, BH, a.L, a.nqb, a.words, a.scale_log2, a.log2_tau, \
-                       a.kept, a.legal, a.bits)
+#define MALA_FWD_LAUNCH(GT, ST)                                                                           \
+    hipLaunchKernelGGL((fwd_bf16_d128<GT, ST>), grid, block, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,   \
+                       (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, BH, a.H / a.Hkv, a.L, a.P, a.Lk, a.Lkcap,  \
+                       a.nqb, a.words,                                                                       \
+                       a.scale_log2, a.log2_tau, a.kept, a.legal, a.bits)
     if (a.gated) {
         if (st) MALA_FWD_LAUNCH(true, true);
         else MALA_FWD_LAUNCH(true, false);

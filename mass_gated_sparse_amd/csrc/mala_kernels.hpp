@@ -14,7 +14,8 @@ struct FwdArgs {
     const void *q, *k, *v;
     void* o;
     float* lse;
-    int B, H, L, d;
+    int B, H, Hkv, L, d;  // H query heads, Hkv key/value heads (H % Hkv == 0); L query rows
+    int P, Lk, Lkcap;     // first row's key position, valid keys (P + L), K/V rows per head
     int nqb, ntiles, words;
     float scale_log2;  // scale * log2(e)
     float log2_tau;    // log2(tau); +inf for tau = +inf
@@ -29,7 +30,7 @@ struct BwdArgs {
     void *dq, *dk, *dv;
     float *Dv, *lse2, *thr;  // per-row workspace arrays [B, H, L]
     uint32_t* dbits;         // workspace: backward decisions [B, H, nqb, words], dQ pass -> dK/dV pass
-    int B, H, L, d;
+    int B, H, Hkv, L, d;     // H query heads, Hkv key/value heads (H % Hkv == 0)
     int nqb, ntiles, words;
     float scale, scale_log2, log2_tau;
     bool gated, f32;

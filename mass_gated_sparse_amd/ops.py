@@ -89,6 +89,35 @@ def fwd(q, k, v, tau, tile=None, scale=0.0, stats=False):
     return (o, lse, st) if stats else (o, lse)
 
 
+def fwd_chunk_into(q, kc, vc, P, o, lse, tau, tile=None, scale=0.0, stats=None, stream=None):
+    """Queue mala_fwd_chunk: q [B,H,Lq,d] at key positions P.., caches [B,Hkv,Lcap,d]
+    holding keys 0 .. P+Lq-1; writes o [B,H,Lq,d] and lse [B,H,Lq]."""
+    B, H, Lq, d = q.shape
+    _, Hkv, Lcap, _ = kc.shape
+    tile = tile or DEFAULT_TILE[q.dtype]
+    rc = _lib.load().mala_fwd_chunk(_ptr(q), _ptr(kc), _ptr(vc), B, H, Hkv, Lq, int(P), Lcap, d, _dt(q), float(tau),
+                                    Tile(*tile), float(scale), _ptr(o), _ptr(lse), _stats_struct(stats),
+                                    _stream(stream))
+    _lib.check("mala_fwd_chunk", rc)
+
+
+def fwd_chunk(q, kc, vc, P, tau, tile=None, scale=0.0, stats=False):
+    """Chunked-prefill MALA forward against a K/V cache.  Returns (o, lse[, stats])."""
+    _check_dev(q, kc, vc)
+    B, H, Lq, d = q.shape
+    tile = tile or DEFAULT_TILE[q.dtype]
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, Lq, dtype=torch.float32, device=q.device)
+    st = None
+    if stats:
+        nqb, nt = -(-Lq // tile[0]), -(-(int(P) + Lq) // tile[1])
+        st = {"kept": torch.zeros(B, H, nqb, dtype=torch.int32, device=q.device),
+              "legal": torch.zeros(B, H, nqb, dtype=torch.int32, device=q.device),
+              "keep_bits": torch.zeros(B, H, nqb, -(-nt // 32), dtype=torch.int32, device=q.device)}
+    fwd_chunk_into(q, kc, vc, P, o, lse, tau, tile, scale, st)
+    return (o, lse, st) if stats else (o, lse)
+
+
 def bwd_workspace(q, tile=None):
     B, H, L, d = q.shape
     tile = tile or DEFAULT_TILE[q.dtype]
@@ -115,6 +144,32 @@ def bwd(q, k, v, o, lse, do, tau, tile=None, scale=0.0, stats=False):
     st = prefill_stats_buffers(B, H, L, tile, q.device, dkdv=True) if stats else None
     bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile, scale, st)
     return (dq, dk, dv, st) if stats else (dq, dk, dv)
+
+
+class _MalaAttention(torch.autograd.Function):
+    """Autograd binding: forward runs mala_fwd and keeps (o, lse) as the
+    attention state; backward runs mala_bwd against it."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, tau, tile, scale):
+        o, lse = fwd(q, k, v, tau, tile, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.tau, ctx.tile, ctx.scale = tau, tile, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), ctx.tau, ctx.tile, ctx.scale)
+        return dq, dk, dv, None, None, None
+
+
+def mala_attention(q, k, v, tau=1.0, tile=None, scale=0.0):
+    """Causal MALA attention with autograd, as a drop-in for a fused causal
+    attention call.  q: [B, H, L, d]; k, v: [B, Hkv, L, d] with H % Hkv == 0
+    (grouped-query attention when Hkv < H); bf16 with d = 128, or fp32 with
+    d = 64 and H == Hkv.  Returns o: [B, H, L, d]."""
+    return _MalaAttention.apply(q.contiguous(), k.contiguous(), v.contiguous(), float(tau), tile, float(scale))
 
 
 def decode_stats_buffers(B, Hkv, Lk, split_keys, bk, device):

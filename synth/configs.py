@@ -57,4 +57,8 @@ DECODE128K = Workload("decode128k", 4, "decode", B=16, H=32, Hkv=8, L=131073, d=
                       bq=4, bk=64, taus=(1.0, 0.0), split_keys=4096,
                       note="128K decode: 16 sequences, GQA 32/8, one new token, split-KV 4096")
 
-WORKLOADS = {w.name: w for w in (TINY, MW8K, SWEEP32K, TRAIN128K, DECODE128K)}
+GQA8K = Workload("gqa8k", 5, "prefill", B=1, H=8, Hkv=2, L=8192, d=128, dtype="bf16",
+                 bq=128, bk=64, taus=(1.0, 0.0),
+                 note="grouped-query prefill: 8 query heads over 2 K/V heads (4 per group), bf16, 128x64 tiles")
+
+WORKLOADS = {w.name: w for w in (TINY, MW8K, SWEEP32K, TRAIN128K, DECODE128K, GQA8K)}

@@ -139,7 +139,7 @@ def prefill_inputs(w: Workload, family: str = "planted", L: int = None, heads=No
     L = w.L if L is None else int(L)
     heads = range(w.H) if heads is None else list(heads)
     sdt = np.uint16 if w.dtype == "bf16" else np.float32
-    out = {n: np.zeros((w.B, w.H, L, w.d), dtype=sdt) for n in ("q", "k", "v", "do")}
+    out = {n: np.zeros((w.B, w.Hkv if n in ("k", "v") else w.H, L, w.d), dtype=sdt) for n in ("q", "k", "v", "do")}
     G = w.group
     for b in range(w.B):
         done_kv = set()

@@ -26,6 +26,14 @@ def legal_mask(L, bq, bk):
     return np.arange(nt)[None, :] <= jmax[:, None]
 
 
+def chunk_legal_mask(Lq, P, bq, bk):
+    """Legal tiles of a query chunk at key offset P: block b sees keys up to
+    P + min(b*bq + bq, Lq) - 1."""
+    nqb, nt = -(-Lq // bq), -(-(P + Lq) // bk)
+    jmax = (P + np.minimum(np.arange(nqb) * bq + bq, Lq) - 1) // bk
+    return np.arange(nt)[None, :] <= jmax[:, None]
+
+
 def decision_report(gpu_keep, ora_keep, ora_T, legal, band=BAND):
     """Returns (n_bad, n_near, near_list): mismatches outside the band, tiles in the band."""
     legal = np.broadcast_to(legal, gpu_keep.shape)

@@ -91,7 +91,8 @@ def fwd(lib, q=P, B=1, H=2, Hkv=2, L=256, d=128, dt=0, tau=1.0, tile=(128, 64), 
     ({"tau": float("nan")}, INVALID, "tau"),
     ({"dt": 5}, INVALID, "dtype"),
     ({"tile": (0, 64)}, INVALID, "tile"),
-    ({"Hkv": 1}, UNSUPPORTED, "H == Hkv"),
+    ({"H": 4, "Hkv": 3}, INVALID, "multiple"),
+    ({"H": 4, "Hkv": 2, "dt": 1, "d": 64, "tile": (64, 64)}, UNSUPPORTED, "grouped"),  # f32 path: H == Hkv only
     ({"d": 64}, UNSUPPORTED, "instantiation"),
     ({"tile": (64, 64)}, UNSUPPORTED, "instantiation"),
     ({"dt": 1}, UNSUPPORTED, "instantiation"),  # f32 path is d=64 only
@@ -99,6 +100,28 @@ def fwd(lib, q=P, B=1, H=2, Hkv=2, L=256, d=128, dt=0, tau=1.0, tile=(128, 64), 
 ])
 def test_fwd_rejects(lib, kw, status, msg):
     assert fwd(lib, **kw) == status
+    assert msg in lib.mala_last_error().decode()
+
+
+def fwd_chunk(lib, q=P, B=1, H=4, Hkv=2, Lq=256, Poff=1000, Lcap=2048, d=128, dt=0, tau=1.0, tile=(128, 64),
+              o=P, lse=P):
+    from mass_gated_sparse_amd._lib import Tile
+    return lib.mala_fwd_chunk(q, P, P, B, H, Hkv, Lq, Poff, Lcap, d, dt, tau, Tile(*tile), 0.0, o, lse, None, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    ({"q": None}, INVALID, "null input"),
+    ({"lse": None}, INVALID, "null output"),
+    ({"Poff": -1}, INVALID, "offset"),
+    ({"Lcap": 1255}, INVALID, "exceeds Lcap"),
+    ({"Lq": 0}, INVALID, "positive"),
+    ({"tau": float("nan")}, INVALID, "tau"),
+    ({"H": 4, "Hkv": 3}, INVALID, "multiple"),
+    ({"dt": 1, "d": 64, "tile": (64, 64), "H": 2, "Hkv": 2}, UNSUPPORTED, "bf16"),
+    ({"d": 64}, UNSUPPORTED, "instantiation"),
+])
+def test_fwd_chunk_rejects(lib, kw, status, msg):
+    assert fwd_chunk(lib, **kw) == status
     assert msg in lib.mala_last_error().decode()
 
 

@@ -100,6 +100,11 @@ def test_mw8k_full(ops):
     assert 0.0 < kept < 1.0
 
 
+def test_gqa8k_full(ops):
+    """Grouped K/V heads at 8K (8 query heads over 2 K/V heads), tau=1."""
+    _prefill_full(ops, "gqa8k", 1.0, qblocks=(0, 21, 63), ktiles=(0, 70, 127))
+
+
 @pytest.mark.parametrize("tau", [1.0, 0.0])
 def test_decode128k_full(ops, tau):
     w = WORKLOADS["decode128k"]

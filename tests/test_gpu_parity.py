@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 from synth import WORKLOADS, prefill_inputs, decode_inputs, to_f64
-from tests.parity import (BAND, TOL_GRAD, TOL_O, bf16_to_f64, decision_report, legal_mask, rel_l2)
+from tests.parity import (BAND, TOL_GRAD, TOL_O, bf16_to_f64, chunk_legal_mask, decision_report, legal_mask,
+                          rel_l2)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -123,6 +124,103 @@ def test_bwd_f32_tiny(ops, tau):
 def test_bwd_bf16(ops, L, heads, tau):
     w, x = _prefill_case("mw8k", L, heads)
     _check_bwd(ops, w, x, tau, 128, 64)
+
+
+@pytest.mark.parametrize("L", [1000, 2048])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 4.0, math.inf])
+def test_gqa_bf16(ops, L, tau):
+    """Grouped K/V heads (8 query heads over 2 K/V heads): forward decisions
+    and O per query head, backward decisions per query head, dK/dV summed
+    over each group."""
+    w = WORKLOADS["gqa8k"]
+    x = prefill_inputs(w, L=L)
+    assert x["k"].shape[1] == 2 and x["q"].shape[1] == 8
+    _check_fwd(ops, w, x, tau, 128, 64)
+    _check_bwd(ops, w, x, tau, 128, 64)
+
+
+@pytest.mark.parametrize("L", [64, 130, 200])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 4.0])
+def test_short_ragged_bf16(ops, L, tau):
+    """Sequences shorter than one or two query blocks, ragged in the last tile."""
+    w, x = _prefill_case("mw8k", L, (0, 3))
+    _check_fwd(ops, w, x, tau, 128, 64)
+    _check_bwd(ops, w, x, tau, 128, 64)
+
+
+@pytest.mark.parametrize("tau,family", [(0.0, "planted"), (1.0, "planted"), (0.0, "diffuse")])
+def test_autograd_wrapper(ops, tau, family):
+    """mala_attention's autograd gradients are the mala_bwd gradients against
+    its own forward state, bit for bit.  On diffuse inputs at tau=0 they also
+    match a float32 dense attention reference (CPU autograd) within the
+    backward tolerance.  (Not on planted inputs: their nearly one-hot rows make
+    dS = P (dP - D) a cancellation, and the bf16 rounding of O inside D alone
+    moves the exact dQ by about 1.2% there.)"""
+    w = WORKLOADS["gqa8k"]
+    x = prefill_inputs(w, L=640, family=family)
+    q, k, v, do = _dev_tensors(x, "bf16", ("q", "k", "v", "do"))
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = ops.mala_attention(qa, ka, va, tau)
+    o.backward(do)
+    o2, lse2 = ops.fwd(q, k, v, tau)
+    dq, dk, dv = ops.bwd(q, k, v, o2, lse2, do, tau)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    for g, r in ((qa.grad, dq), (ka.grad, dk), (va.grad, dv)):
+        assert torch.equal(g, r)
+    if family == "diffuse":
+        qf, kf, vf, dof = (t.float().cpu() for t in (q, k, v, do))
+        G = qf.shape[1] // kf.shape[1]
+        qf.requires_grad_(True)
+        kf.requires_grad_(True)
+        vf.requires_grad_(True)
+        kr, vr = kf.repeat_interleave(G, dim=1), vf.repeat_interleave(G, dim=1)
+        s_ = (qf @ kr.transpose(-1, -2).contiguous()) / math.sqrt(qf.shape[-1])
+        L = qf.shape[2]
+        s_ = s_.masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), float("-inf"))
+        ref = torch.softmax(s_, dim=-1) @ vr
+        ref.backward(dof)
+        e_o = rel_l2(o.detach().float().cpu().numpy(), ref.detach().numpy())
+        assert e_o <= TOL_O, e_o
+        errs = [rel_l2(g.float().cpu().numpy(), r.numpy())
+                for g, r in ((qa.grad, qf.grad), (ka.grad, kf.grad), (va.grad, vf.grad))]
+        assert max(errs) <= TOL_GRAD, errs
+
+
+@pytest.mark.parametrize("P,Lq,spare", [(0, 640, 0), (256, 300, 77), (333, 300, 0), (1000, 130, 64)])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 4.0])
+def test_fwd_chunk_bf16(ops, P, Lq, spare, tau):
+    """Chunked prefill: a query chunk at key offset P against a K/V cache
+    (grouped K/V heads, cache capacity beyond the valid keys), against the
+    oracle's chunk forward; a block-aligned chunk also reproduces the
+    whole-sequence forward's rows bit for bit."""
+    w = WORKLOADS["gqa8k"]
+    x = prefill_inputs(w, L=P + Lq)
+    qx = np.ascontiguousarray(x["q"][:, :, P:])
+    cache = {n: np.zeros(x[n].shape[:2] + (P + Lq + spare, w.d), x[n].dtype) for n in ("k", "v")}
+    for n in ("k", "v"):
+        cache[n][:, :, :P + Lq] = x[n]
+    q = torch.from_numpy(qx.view(np.int16)).view(torch.bfloat16).cuda()
+    kc, vc = (torch.from_numpy(cache[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("k", "v"))
+    o, lse, st = ops.fwd_chunk(q, kc, vc, P, tau, stats=True)
+    torch.cuda.synchronize()
+    nt = -(-(P + Lq) // 64)
+    gk = ops.bits_to_keep(st["keep_bits"], nt)
+    qf = to_f64(qx, "bf16")
+    kf, vf = (to_f64(x[n], "bf16") for n in ("k", "v"))
+    oo, ol, ok, oT = oracle.fwd_chunk(qf, kf, vf, P, tau, 128, 64, replay=gk, band=BAND)
+    legal = chunk_legal_mask(Lq, P, 128, 64)
+    bad, near, _ = decision_report(gk, ok, oT, legal)
+    assert bad == 0, f"chunk decisions differ outside the band on {bad} tiles"
+    assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)[None, None, :]).all()
+    assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
+    assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+    if P % 128 == 0:
+        qa, ka, va = _dev_tensors(x, "bf16", ("q", "k", "v"))
+        of, lf = ops.fwd(qa, ka, va, tau)
+        torch.cuda.synchronize()
+        assert torch.equal(o, of[:, :, P:]) and torch.equal(lse, lf[:, :, P:])
 
 
 def _decode_case(Lk, batches, Lcap=None):
