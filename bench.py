@@ -353,7 +353,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
              "Command (from the repository root, on one MI355X):", "",
              "    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
              "--output-format csv -d <dir> -o run -- python3 $GRAFT_REPO_ROOT/bench.py --steps 3 --warmup 1 "
-             "--no-tau0 --no-sweep --no-cpu-baseline", "",
+             "--no-tau0 --no-sweep --no-matched-work --no-cpu-baseline", "",
              "Runs at tau=1 only: every launch of an instantiation below is a tau=1 launch (the "
              "statistics pass uses the separate `<..., true>` instantiations; warmup and timed steps "
              "are included).", "",
@@ -377,7 +377,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
         "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
                    "python3 bench.py --copy-calibration"},
         "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- python3 "
-                   "bench.py --steps 1 --warmup 0 --no-tau0 --no-sweep --no-cpu-baseline",
+                   "bench.py --steps 1 --warmup 0 --no-tau0 --no-sweep --no-matched-work --no-cpu-baseline",
         "kernels": {}}
     md = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)", "",
           f"Commands: `{rec['command']}`; calibration: `{rec['calibration']['command']}` "
