@@ -53,7 +53,11 @@ def main():
     ap.add_argument("--no-matched-work", action="store_true", help="skip the 8K matched-work measurement")
     ap.add_argument("--fidelity", action="store_true",
                     help="only run the tau=1 fidelity sweep from 1K to 32K (slots per query, omitted mass, "
-                         "rel-L2 of O against exact attention) and print it as one JSON line")
+                         "rel-L2 of O against exact attention, per-row errors of O/dQ/dK/dV against tau=0) and "
+                         "print it as one JSON line")
+    ap.add_argument("--matched-work", action="store_true",
+                    help="only run the 8K matched-work study (MALA vs the reference-mass and position-only "
+                         "policies at the same tile count) and print it as one JSON line")
     ap.add_argument("--cpu-sample-blocks", type=int, default=0,
                     help="query blocks in the CPU-oracle sample (0: three per OpenMP thread, at most 48)")
     ap.add_argument("--micro", action="store_true",
@@ -85,7 +89,11 @@ def main():
 
     if args.fidelity:
         from mass_gated_sparse_amd import ops
-        print(json.dumps(fidelity_sweep(torch, ops)))
+        print(json.dumps({fam: fidelity_sweep(torch, ops, fam) for fam in ("planted", "diffuse")}))
+        return
+    if args.matched_work:
+        from mass_gated_sparse_amd import ops
+        print(json.dumps(matched_work_8k(torch, ops, args.steps)))
         return
 
     if args.copy_calibration:
@@ -597,12 +605,97 @@ def exact_row_stats(qh, kh, vh, keep, blocks, bq, bk, scale, o_gpu=None):
     return np.concatenate(omitted), np.concatenate(slots), err2, ref2
 
 
+def _jmax(qb, bq, bk, L):
+    return (min(qb * bq + bq, L) - 1) // bk
+
+
+def position_window(blocks, bq, bk, L, heads, target_tiles):
+    """Window w (in key tiles) of the position-only policy -- the sink tile 0
+    plus the w tiles ending at the block's diagonal -- whose tile count over
+    the sampled blocks of all heads is closest to target_tiles."""
+    def count(w):
+        return heads * sum(min(_jmax(b, bq, bk, L) + 1, w + 1) for b in blocks)
+    return min(range(1, _jmax(blocks[-1], bq, bk, L) + 2), key=lambda w: (abs(count(w) - target_tiles), w)), count
+
+
+def policy_fidelity(qh, kh, vh, keep_h, blocks, bq, bk, scale, window, o_gpu=None):
+    """One head of the matched-work study, against exact causal softmax
+    attention (fp64, numpy; a measurement, not the oracle).
+
+    Policies, each a set of (query block, key tile) pairs over the sampled
+    blocks: "mala" (the forward's decisions), "reference_mass" (the tiles of
+    largest exact probability mass, as many as MALA kept on this head: the
+    per-instance optimum of mean omitted mass at that tile budget) and
+    "position_only" (tile 0 plus the `window` tiles ending at the diagonal).
+    Per row: omitted mass (exact mass of visible keys outside the policy),
+    slots (visible keys inside it) and the relative L2 error of the policy's
+    output, softmax renormalized over its keys, against exact attention;
+    with o_gpu (GPU rows of the sampled blocks, in order) also the GPU
+    output's per-row relative error."""
+    L = kh.shape[0]
+    cols = np.arange(L)
+    probs, vis_l, mass = [], [], []
+    for qb in blocks:
+        rows = np.arange(qb * bq, min(qb * bq + bq, L))
+        s = (qh[rows] @ kh.T) * scale
+        vis = cols[None, :] <= rows[:, None]
+        s = np.where(vis, s, -np.inf)
+        pr = np.exp(s - s.max(axis=1, keepdims=True))
+        pr /= pr.sum(axis=1, keepdims=True)
+        probs.append(pr)
+        vis_l.append(vis)
+        nt = _jmax(qb, bq, bk, L) + 1
+        mass.append(np.array([pr[:, t * bk:(t + 1) * bk].sum() for t in range(nt)]))
+    # tile sets
+    sets = {"mala": [keep_h[qb][: _jmax(qb, bq, bk, L) + 1].astype(bool) for qb in blocks]}
+    budget = int(sum(m.sum() for m in sets["mala"]))
+    cand = sorted(((-m[t], i, t) for i, m in enumerate(mass) for t in range(len(m))))
+    ref = [np.zeros(len(m), bool) for m in mass]
+    for _, i, t in cand[:budget]:
+        ref[i][t] = True
+    sets["reference_mass"] = ref
+    pos = []
+    for qb in blocks:
+        jm = _jmax(qb, bq, bk, L)
+        m = np.zeros(jm + 1, bool)
+        m[0] = True
+        m[max(0, jm - window + 1):] = True
+        pos.append(m)
+    sets["position_only"] = pos
+    out = {}
+    for name, tiles in sets.items():
+        om, sl, rel = [], [], []
+        for i, qb in enumerate(blocks):
+            kt = np.zeros(L, bool)
+            kt[: len(tiles[i]) * bk] = np.repeat(tiles[i], bk)[:L]
+            sel = vis_l[i] & kt[None, :]
+            pm = probs[i] * sel
+            om.append(1.0 - pm.sum(axis=1))
+            sl.append(sel.sum(axis=1))
+            exact = probs[i] @ vh
+            z = pm.sum(axis=1, keepdims=True)
+            o_pol = np.where(z > 0, (pm @ vh) / np.where(z > 0, z, 1.0), 0.0)
+            rel.append(np.linalg.norm(o_pol - exact, axis=1) / np.linalg.norm(exact, axis=1))
+        out[name] = {"tiles": int(sum(t.sum() for t in tiles)), "omitted": np.concatenate(om),
+                     "slots": np.concatenate(sl), "rel": np.concatenate(rel)}
+    if o_gpu is not None:
+        rel = []
+        for i, qb in enumerate(blocks):
+            exact = probs[i] @ vh
+            n = exact.shape[0]
+            rel.append(np.linalg.norm(o_gpu[i * bq: i * bq + n] - exact, axis=1) / np.linalg.norm(exact, axis=1))
+        out["mala"]["rel_gpu"] = np.concatenate(rel)
+    return out
+
+
 def matched_work_8k(torch, ops, steps):
     """The 8K matched-work shape (B1 H16 L8192 d128, bf16, 128x64 tiles, tau=1,
     planted inputs with per-head sharpness c_h ~ U[0.5, 2]): GPU fwd/bwd ms and
     kept-tile fractions, and -- on every 8th query block of every head -- the
-    mean omitted probability mass per query and the post-score slots per
-    query against exact attention."""
+    matched-work comparison of MALA's forward decisions with the per-instance
+    reference-mass policy and the position-only policy at the same number of
+    tiles (mean omitted probability mass, post-score slots per query and mean
+    per-row relative output error against exact attention)."""
     from synth import WORKLOADS, prefill_inputs, to_f64
     w = WORKLOADS["mw8k"]
     tile, tau = (w.bq, w.bk), 1.0
@@ -620,43 +713,85 @@ def matched_work_8k(torch, ops, steps):
     og = o.float().cpu().numpy()[0]
     blocks = list(range(0, -(-L // w.bq), 8))
     scale = 1.0 / np.sqrt(d)
-    om, sl, e2, r2 = [], [], 0.0, 0.0
+    mala_tiles = int(sum(keep[h][b][: _jmax(b, w.bq, w.bk, L) + 1].sum() for h in range(H) for b in blocks))
+    window, count = position_window(blocks, w.bq, w.bk, L, H, mala_tiles)
+    acc = {}
     t0 = time.time()
+    rows = np.concatenate([np.arange(b * w.bq, min(b * w.bq + w.bq, L)) for b in blocks])
     for h in range(H):
         qh, kh, vh = (to_f64(x[n][0, h], "bf16") for n in ("q", "k", "v"))
-        rows = np.concatenate([np.arange(b * w.bq, min(b * w.bq + w.bq, L)) for b in blocks])
-        a, b_, e, r = exact_row_stats(qh, kh, vh, keep[h], blocks, w.bq, w.bk, scale, og[h][rows])
-        om.append(a)
-        sl.append(b_)
-        e2 += e
-        r2 += r
-    om, sl = np.concatenate(om), np.concatenate(sl)
+        r = policy_fidelity(qh, kh, vh, keep[h], blocks, w.bq, w.bk, scale, window, og[h][rows])
+        for name, dct in r.items():
+            a = acc.setdefault(name, {})
+            for key, val in dct.items():
+                a[key] = a.get(key, 0) + val if key == "tiles" else np.concatenate([a.get(key, np.zeros(0)), val])
     log(f"matched-work 8K: exact-attention sample took {time.time() - t0:.1f}s")
+    policies = {}
+    for name, a in acc.items():
+        policies[name] = {"tiles": int(a["tiles"]), "mean_omitted_mass_pct": 100.0 * float(a["omitted"].mean()),
+                          "max_omitted_mass_pct": 100.0 * float(a["omitted"].max()),
+                          "slots_per_query": float(a["slots"].mean()),
+                          "mean_rel_l2_O_pct": 100.0 * float(a["rel"].mean())}
+    policies["mala"]["mean_rel_l2_O_gpu_pct"] = 100.0 * float(acc["mala"]["rel_gpu"].mean())
+    policies["position_only"]["window_tiles"] = window
+    log("matched-work 8K policies: " + json.dumps(policies))
     return {"workload": "mw8k (B1 H16 L8192 d128 bf16, 128x64 tiles, planted, c_h~U[0.5,2])", "tau": tau,
             "fwd_ms": ms["fwd"], "dq_ms": ms["dq"], "dkdv_ms": ms["dkdv"],
             "kept_frac_fwd": int(st["kept"].sum()) / n_legal, "kept_frac_bwd": int(stb["kept"].sum()) / n_legal,
-            "mean_omitted_mass_pct": 100.0 * float(om.mean()), "max_omitted_mass_pct": 100.0 * float(om.max()),
+            "mean_omitted_mass_pct": policies["mala"]["mean_omitted_mass_pct"],
+            "max_omitted_mass_pct": policies["mala"]["max_omitted_mass_pct"],
             "omitted_mass_bound_pct": 100.0 * tau / (1.0 + tau),
-            "slots_per_query": float(sl.mean()), "rel_l2_O_vs_exact": float(np.sqrt(e2 / r2)),
+            "slots_per_query": policies["mala"]["slots_per_query"],
+            "policies": policies,
             "sample": f"every 8th query block ({len(blocks)} of {-(-L // w.bq)}) of all {H} heads",
-            "note": "omitted mass = exact softmax mass of a row's visible keys in forward-skipped tiles; "
-                    "slots = the row's visible keys in kept tiles; rel_l2 includes bf16 rounding of O"}
+            "note": "omitted mass = exact softmax mass of a row's visible keys outside the policy's tiles; "
+                    "slots = the row's visible keys inside them; a policy's output renormalizes the softmax over "
+                    "its keys (fp64), mala's GPU output also includes bf16 rounding; reference_mass = top exact-mass "
+                    "tiles of each head at MALA's tile count there; position_only = tile 0 plus a window of "
+                    "window_tiles tiles ending at the diagonal, window chosen so the total tile count is closest "
+                    "to MALA's"}
 
 
-def fidelity_sweep(torch, ops):
+def mean_row_rel(torch, a, ref):
+    """Mean over rows (last axis = features) of |a - ref| / |ref|, rows with
+    ref = 0 left out; computed in fp32 on the device."""
+    a, ref = a.float(), ref.float()
+    n, r = (a - ref).norm(dim=-1), ref.norm(dim=-1)
+    m = r > 0
+    return float((n[m] / r[m]).mean())
+
+
+def mean_head_rel(torch, a, ref):
+    """Mean over (batch, head) of the whole-head relative L2 error
+    |a - ref|_F / |ref|_F, in fp32 on the device."""
+    a, ref = a.float().flatten(2), ref.float().flatten(2)
+    return float(((a - ref).norm(dim=-1) / ref.norm(dim=-1)).mean())
+
+
+def fidelity_sweep(torch, ops, family="planted"):
     """tau=1 from 1K to 32K on the planted family of the 32K sweep shape
     (H=8, d=128, bf16, 128x64 tiles): kept-tile fraction, post-score slots
     per query, omitted mass and rel-L2 of O against exact attention on every
-    query block of L <= 4K and a sample of 16 blocks per head beyond."""
+    query block of L <= 4K and a sample of 16 blocks per head beyond; and,
+    over every row, the mean per-row relative L2 error of O, dQ, dK and dV
+    against the same kernels ungated (tau=0: full attention, the reference
+    operator), both in bf16."""
     from synth import WORKLOADS, prefill_inputs, to_f64
     w = WORKLOADS["sweep32k"]
     tile, tau = (w.bq, w.bk), 1.0
     out = {}
     for L in (1024, 2048, 4096, 8192, 16384, 32768):
-        x = prefill_inputs(w, L=L)
-        q, k, v = (dev_bf16(torch, x[n]) for n in ("q", "k", "v"))
+        x = prefill_inputs(w, L=L, family=family)
+        q, k, v, do = (dev_bf16(torch, x[n]) for n in ("q", "k", "v", "do"))
         B, H, _, d = q.shape
         o, lse, st = ops.fwd(q, k, v, tau, tile=tile, stats=True)
+        grads = ops.bwd(q, k, v, o, lse, do, tau, tile=tile)
+        o0, lse0 = ops.fwd(q, k, v, 0.0, tile=tile)
+        grads0 = ops.bwd(q, k, v, o0, lse0, do, 0.0, tile=tile)
+        pairs = list(zip(("O", "dQ", "dK", "dV"), (o,) + tuple(grads), (o0,) + tuple(grads0)))
+        rel_vs_full = {n: 100.0 * mean_row_rel(torch, a, b) for n, a, b in pairs}
+        head_vs_full = {n: 100.0 * mean_head_rel(torch, a, b) for n, a, b in pairs}
+        del grads, grads0, o0, lse0, do
         torch.cuda.synchronize()
         nqb, nt = -(-L // w.bq), -(-L // w.bk)
         keep = ops.bits_to_keep(st["keep_bits"], nt)[0]
@@ -675,10 +810,15 @@ def fidelity_sweep(torch, ops):
         out[str(L)] = {"kept_frac_fwd": int(st["kept"].sum()) / (B * H * legal_tiles(L, *tile)),
                        "slots_per_query": float(sl.mean()), "mean_omitted_mass_pct": 100.0 * float(om.mean()),
                        "rel_l2_O_vs_exact": float(np.sqrt(e2 / r2)),
+                       "mean_row_rel_l2_vs_full_pct": rel_vs_full,
+                       "mean_head_rel_l2_vs_full_pct": head_vs_full,
                        "sample_blocks_per_head": len(blocks)}
-        log(f"fidelity L={L}: " + json.dumps(out[str(L)]))
-    return {"fidelity": out, "tau": tau, "workload": "sweep32k shape (H8 d128 bf16, 128x64 tiles), planted family",
-            "note": "slots = a row's visible keys in kept tiles; omitted mass against exact softmax"}
+        log(f"fidelity {family} L={L}: " + json.dumps(out[str(L)]))
+    return {"fidelity": out, "tau": tau, "workload": f"sweep32k shape (H8 d128 bf16, 128x64 tiles), {family} family",
+            "note": "slots = a row's visible keys in kept tiles; omitted mass against exact softmax; "
+                    "mean_row_rel_l2_vs_full_pct: per-row relative L2 of the tau=1 outputs against the tau=0 "
+                    "(ungated) outputs of the same kernels, mean over all rows (key rows for dK, dV); "
+                    "mean_head_rel_l2_vs_full_pct: the same comparison over each whole head, mean over heads"}
 
 
 def cpu_baseline(wx, wd, xp, xd0, nblocks, tau):
