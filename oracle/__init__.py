@@ -46,13 +46,16 @@ def _lib():
         lib.oracle_decode_groups.argtypes = [ctypes.c_long, _D, ctypes.c_int, _D, _D, ctypes.c_long, ctypes.c_long,
                                              ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_long,
                                              ctypes.c_int, ctypes.c_int, _U8, ctypes.c_double, _D, _D, _U8, _D]
+        lib.oracle_decode_seeded_group.argtypes = lib.oracle_decode_group.argtypes
+        lib.oracle_decode_seeded_groups.argtypes = lib.oracle_decode_groups.argtypes
         lib.oracle_fwd_chunk_head.argtypes = [_D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_int,
                                               ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int, _U8,
                                               ctypes.c_double, _D, _D, _U8, _D]
         lib.oracle_omitted_head.argtypes = [_D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                             ctypes.c_int, _U8, _L, ctypes.c_long, _D, _D]
         for f in ("oracle_fwd_head", "oracle_bwd_head", "oracle_decode_group", "oracle_decode_groups",
-                  "oracle_omitted_head", "oracle_fwd_chunk_head"):
+                  "oracle_decode_seeded_group", "oracle_decode_seeded_groups", "oracle_omitted_head",
+                  "oracle_fwd_chunk_head"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -272,6 +275,76 @@ def decode_group_partials(q, k, v, Lk, tau, split_keys, bk, scale=None, rows_per
                                     R, None, 0.0, _p(o, _D), _p(lse, _D), _p(keep, _U8), _p(T, _D),
                                     _p(pm, _D), _p(pl, _D), _p(pa, _D))
     _check(rc, "oracle_decode_group")
+    return o, lse, keep, T, pm, pl, pa
+
+
+def seeded_decode_shapes(Lk, split_keys, bk):
+    """(nsplit, tps) of the seeded decode: partitions of split_keys/bk tiles
+    counted back from the tile holding the newest key."""
+    tps = split_keys // bk
+    return -(-((Lk - 1) // bk + 1) // tps), tps
+
+
+def decode_seeded(q, kc, vc, Lk, tau, split_keys, bk, scale=None, rows_per_vote=None, replay=None, band=1e-4,
+                  units=None):
+    """Split-KV MALA decode with seeded partitions (see
+    oracle_decode_seeded_group): partition 0 holds the newest split_keys/bk
+    tiles and starts empty; every older partition is tested against
+    partition 0's final normalizer plus its own kept keys, with no forced
+    keep.  Arguments and returns as decode(); keep/T are
+    [B, Hkv, G/rows_per_vote, nsplit, tps] with partition 0 the newest."""
+    q = _f64(q)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[1]
+    G = Hq // Hkv
+    R = G if rows_per_vote is None else int(rows_per_vote)
+    scale = default_scale(d) if scale is None else float(scale)
+    if split_keys % bk:
+        raise ValueError("split_keys must be a multiple of bk")
+    nsplit, tps = seeded_decode_shapes(Lk, split_keys, bk)
+    o = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    keep = np.zeros((B, Hkv, G // R, nsplit, tps), dtype=np.uint8)
+    T = np.full((B, Hkv, G // R, nsplit, tps), np.nan)
+    units = [(b, g) for b in range(B) for g in range(Hkv)] if units is None else list(units)
+    n = len(units)
+    qs = np.stack([q[b, g * G:(g + 1) * G] for b, g in units])
+    ks = np.stack([_f64(kc[b, g, :Lk]) for b, g in units])
+    vs = np.stack([_f64(vc[b, g, :Lk]) for b, g in units])
+    ou = np.zeros((n, G, d))
+    lu = np.zeros((n, G))
+    kb = np.zeros((n, G // R, nsplit, tps), dtype=np.uint8)
+    Tb = np.full((n, G // R, nsplit, tps), np.nan)
+    rp = None
+    if replay is not None:
+        rp = np.ascontiguousarray(np.stack([replay[b, g] for b, g in units]), dtype=np.uint8)
+    rc = _lib().oracle_decode_seeded_groups(n, _p(qs, _D), G, _p(ks, _D), _p(vs, _D), Lk * d, Lk, d, scale,
+                                            float(tau), split_keys, bk, R, _p(rp, _U8), float(band), _p(ou, _D),
+                                            _p(lu, _D), _p(kb, _U8), _p(Tb, _D))
+    _check(rc, "oracle_decode_seeded_groups")
+    for u, (b, g) in enumerate(units):
+        o[b, g * G:(g + 1) * G] = ou[u]
+        lse[b, g * G:(g + 1) * G] = lu[u]
+        keep[b, g] = kb[u]
+        T[b, g] = Tb[u]
+    return o, lse, keep, T
+
+
+def decode_seeded_group_partials(q, k, v, Lk, tau, split_keys, bk, scale=None, rows_per_vote=None):
+    """One KV group of the seeded decode (q [G, d], k/v [Lk, d]); also returns
+    the partitions' own states (m [G, nsplit], l [G, nsplit], acc [G, nsplit, d])."""
+    q, k, v = _f64(q), _f64(k[:Lk]), _f64(v[:Lk])
+    G, d = q.shape
+    R = G if rows_per_vote is None else int(rows_per_vote)
+    scale = default_scale(d) if scale is None else float(scale)
+    nsplit, tps = seeded_decode_shapes(Lk, split_keys, bk)
+    o = np.zeros((G, d)); lse = np.zeros(G)
+    keep = np.zeros((G // R, nsplit, tps), dtype=np.uint8); T = np.full((G // R, nsplit, tps), np.nan)
+    pm = np.zeros((G, nsplit)); pl = np.zeros((G, nsplit)); pa = np.zeros((G, nsplit, d))
+    rc = _lib().oracle_decode_seeded_group(_p(q, _D), G, _p(k, _D), _p(v, _D), Lk, d, scale, float(tau),
+                                           split_keys, bk, R, None, 0.0, _p(o, _D), _p(lse, _D), _p(keep, _U8),
+                                           _p(T, _D), _p(pm, _D), _p(pl, _D), _p(pa, _D))
+    _check(rc, "oracle_decode_seeded_group")
     return o, lse, keep, T, pm, pl, pa
 
 

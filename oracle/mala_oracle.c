@@ -458,6 +458,157 @@ int oracle_decode_groups(long n, const double* q, int G, const double* k, const 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Decode with seeded partitions, one (batch, KV group).                      */
+/* [threshold], [forward]: the test of a tile uses a normalizer established  */
+/* on the more recent keys; here every older partition starts from the       */
+/* state of the partition that holds the newest keys.                        */
+/* ------------------------------------------------------------------------ */
+/*
+ * Tiles are the bk-key tiles counted from key 0 (tile j = keys
+ * [j*bk, min((j+1)*bk, Lk))); jd = (Lk-1)/bk is the tile holding the newest
+ * key.  With tps = split_keys/bk (split_keys must be a multiple of bk),
+ * partition p holds tiles lo_p .. hi_p, hi_p = jd - p*tps,
+ * lo_p = max(0, hi_p - tps + 1): partition 0 is the newest.  Every partition
+ * visits its tiles from hi_p down to lo_p.
+ *   - Partition 0 starts from an empty state (its first visited tile is kept)
+ *     and is tested against its own running normalizer, as in plain decode.
+ *   - Partition p >= 1 is tested against the normalizer of partition 0's
+ *     final state plus the keys it has itself kept so far; nothing is kept
+ *     by force.  Its output state holds only its own kept keys.
+ * The output is the exact merge of the partitions' own states.
+ * keep/T: [G/rows_per_vote][nsplit][tps], bit t of partition p = tile lo_p + t.
+ * part_m, part_l: [G][nsplit]; part_acc: [G][nsplit][d] (own states), may be NULL.
+ */
+int oracle_decode_seeded_group(const double* q, int G, const double* k, const double* v, long Lk, int d,
+                               double scale, double tau, long split_keys, int bk, int rows_per_vote,
+                               const uint8_t* replay, double band,
+                               double* o, double* lse, uint8_t* keep, double* T,
+                               double* part_m, double* part_l, double* part_acc)
+{
+    if (!q || !k || !v || !o || G <= 0 || Lk <= 0 || d <= 0 || split_keys <= 0 || bk <= 0) return ORACLE_ERR_ARG;
+    if (split_keys % bk || rows_per_vote <= 0 || G % rows_per_vote) return ORACLE_ERR_ARG;
+    if (!(tau >= 0.0)) return ORACLE_ERR_ARG;
+    const long tps = split_keys / bk, jd = (Lk - 1) / bk, nsplit = ceil_div(jd + 1, tps);
+    const int R = rows_per_vote, nvg = G / R;
+    double* om = malloc(sizeof(double) * G * nsplit);  /* own state per (row, partition) */
+    double* ol = malloc(sizeof(double) * G * nsplit);
+    double* oa = calloc((size_t)G * nsplit * d, sizeof(double));
+    double* tm = malloc(sizeof(double) * R);             /* test state of the current partition */
+    double* tl = malloc(sizeof(double) * R);
+    double* s = malloc(sizeof(double) * (size_t)R * bk);
+    if (!om || !ol || !oa || !tm || !tl || !s) {
+        free(om); free(ol); free(oa); free(tm); free(tl); free(s);
+        return ORACLE_ERR_MEM;
+    }
+
+    for (int vg = 0; vg < nvg; ++vg) {
+        for (long p = 0; p < nsplit; ++p) {
+            const long hi = jd - p * tps;
+            const long lo = (hi - tps + 1 > 0) ? hi - tps + 1 : 0;
+            for (int r = 0; r < R; ++r) {
+                const int row = vg * R + r;
+                om[row * nsplit + p] = -INFINITY;
+                ol[row * nsplit + p] = 0.0;
+                /* partition 0: empty test state; later ones: partition 0's final state */
+                tm[r] = (p == 0) ? -INFINITY : om[row * nsplit + 0];
+                tl[r] = (p == 0) ? 0.0 : ol[row * nsplit + 0];
+            }
+            for (long j = hi; j >= lo; --j) {
+                const long c0 = j * bk;
+                const long c1 = (c0 + bk < Lk) ? c0 + bk : Lk;
+                for (int r = 0; r < R; ++r)
+                    for (long c = c0; c < c1; ++c)
+                        s[(size_t)r * bk + (c - c0)] = scale * dot(q + (size_t)(vg * R + r) * d, k + c * d, d);
+                const long idx = ((long)vg * nsplit + p) * tps + (j - lo);
+                int kp;
+                double Tt;
+                if (tau == 0.0) { kp = 1; Tt = NAN; }
+                else {
+                    Tt = 0.0;
+                    for (int r = 0; r < R; ++r) {
+                        double smax = -INFINITY;
+                        for (long c = c0; c < c1; ++c) if (s[(size_t)r * bk + (c - c0)] > smax) smax = s[(size_t)r * bk + (c - c0)];
+                        const double Tr = (tl[r] == 0.0) ? INFINITY : (exp(smax - tm[r]) / tl[r]) / (tau / (double)Lk);
+                        if (Tr > Tt) Tt = Tr;
+                    }
+                    kp = (Tt >= 1.0);
+                    if (replay && fabs(Tt - 1.0) <= band) kp = replay[idx] ? 1 : 0;
+                }
+                if (keep) keep[idx] = (uint8_t)kp;
+                if (T) T[idx] = Tt;
+                if (!kp) continue;
+                for (int r = 0; r < R; ++r) {
+                    const int row = vg * R + r;
+                    double smax = -INFINITY;
+                    for (long c = c0; c < c1; ++c) if (s[(size_t)r * bk + (c - c0)] > smax) smax = s[(size_t)r * bk + (c - c0)];
+                    /* the test normalizer absorbs the tile */
+                    const double mt = (smax > tm[r]) ? smax : tm[r];
+                    double lt = tl[r] * exp(tm[r] - mt);
+                    for (long c = c0; c < c1; ++c) lt += exp(s[(size_t)r * bk + (c - c0)] - mt);
+                    tm[r] = mt;
+                    tl[r] = lt;
+                    /* and so does the partition's own state */
+                    double* mr = om + row * nsplit + p;
+                    double* lr = ol + row * nsplit + p;
+                    double* ar = oa + ((size_t)row * nsplit + p) * d;
+                    const double mn = (smax > *mr) ? smax : *mr;
+                    const double a = exp(*mr - mn);
+                    *lr *= a;
+                    for (int c = 0; c < d; ++c) ar[c] *= a;
+                    for (long c = c0; c < c1; ++c) {
+                        const double pr = exp(s[(size_t)r * bk + (c - c0)] - mn);
+                        *lr += pr;
+                        for (int e = 0; e < d; ++e) ar[e] += pr * v[c * d + e];
+                    }
+                    *mr = mn;
+                }
+            }
+        }
+    }
+    /* exact merge of the partitions' own states (an empty state weighs 0) */
+    for (int row = 0; row < G; ++row) {
+        double M = -INFINITY;
+        for (long p = 0; p < nsplit; ++p) if (om[row * nsplit + p] > M) M = om[row * nsplit + p];
+        double Lam = 0.0;
+        for (int c = 0; c < d; ++c) o[(size_t)row * d + c] = 0.0;
+        for (long p = 0; p < nsplit; ++p) {
+            if (ol[row * nsplit + p] == 0.0) continue;
+            const double w = exp(om[row * nsplit + p] - M);
+            Lam += ol[row * nsplit + p] * w;
+            for (int c = 0; c < d; ++c) o[(size_t)row * d + c] += oa[((size_t)row * nsplit + p) * d + c] * w;
+        }
+        for (int c = 0; c < d; ++c) o[(size_t)row * d + c] /= Lam;
+        if (lse) lse[row] = M + log(Lam);
+    }
+    if (part_m) memcpy(part_m, om, sizeof(double) * G * nsplit);
+    if (part_l) memcpy(part_l, ol, sizeof(double) * G * nsplit);
+    if (part_acc) memcpy(part_acc, oa, sizeof(double) * (size_t)G * nsplit * d);
+    free(om); free(ol); free(oa); free(tm); free(tl); free(s);
+    return ORACLE_OK;
+}
+
+/* Many (batch, KV group) units of the seeded decode in parallel (layout as oracle_decode_groups). */
+int oracle_decode_seeded_groups(long n, const double* q, int G, const double* k, const double* v, long kstride,
+                                long Lk, int d, double scale, double tau, long split_keys, int bk,
+                                int rows_per_vote, const uint8_t* replay, double band,
+                                double* o, double* lse, uint8_t* keep, double* T)
+{
+    if (n <= 0 || rows_per_vote <= 0 || bk <= 0 || split_keys <= 0) return ORACLE_ERR_ARG;
+    const long tps = split_keys / bk, nsplit = ceil_div((Lk - 1) / bk + 1, tps > 0 ? tps : 1);
+    const long kb = (long)(G / rows_per_vote) * nsplit * tps;
+    int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long u = 0; u < n; ++u) {
+        int e = oracle_decode_seeded_group(q + u * G * d, G, k + u * kstride, v + u * kstride, Lk, d, scale, tau,
+                                           split_keys, bk, rows_per_vote, replay ? replay + u * kb : NULL, band,
+                                           o + u * G * d, lse ? lse + u * G : NULL,
+                                           keep ? keep + u * kb : NULL, T ? T + u * kb : NULL, NULL, NULL, NULL);
+        if (e) err = e;
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Derived quantities against the exact dense softmax                        */
 /* ------------------------------------------------------------------------ */
 /*

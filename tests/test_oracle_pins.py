@@ -508,3 +508,112 @@ def test_chunk_unaligned_dense_over_kept_and_bounded(tau):
         assert np.abs(o[0, h] - od[P:]).max() <= 1e-12 * np.abs(od[P:]).max()
         om = (Pd * ~mask).sum(axis=1)
         assert (om < tau / (1 + tau)).all()
+
+
+# ---------------------------------------------------------------- seeded decode partitions
+def _seeded_tiles_mask(keep_g, Lk, S, bk):
+    """Key mask of the kept tiles of one vote group of the seeded decode."""
+    nsplit, tps = oracle.seeded_decode_shapes(Lk, S, bk)
+    jd = (Lk - 1) // bk
+    mask = np.zeros(Lk, bool)
+    for p in range(nsplit):
+        hi = jd - p * tps
+        lo = max(0, hi - tps + 1)
+        for t in range(hi - lo + 1):
+            if keep_g[p, t]:
+                mask[(lo + t) * bk: min((lo + t + 1) * bk, Lk)] = True
+    return mask
+
+
+@pytest.mark.parametrize("tau", [1.0, 8.0])
+def test_seeded_decode_one_partition_is_plain_decode(tau):
+    """With one partition there is nothing to seed: the seeded decode is the
+    plain decode (same tiles from key 0, same visit order, empty start)."""
+    w, q, kc, vc = _decode_small(777)
+    o1, l1, k1, _ = oracle.decode(q, kc, vc, 777, tau, 1024, 64)
+    o2, l2, k2, _ = oracle.decode_seeded(q, kc, vc, 777, tau, 1024, 64)
+    assert (k1 == k2).all()
+    assert np.abs(o1 - o2).max() <= 1e-12 * np.abs(o1).max()
+    assert np.abs(l1 - l2).max() <= 1e-12
+
+
+def test_seeded_decode_tau0_is_dense():
+    w, q, kc, vc = _decode_small(1000)
+    o, lse, keep, _ = oracle.decode_seeded(q, kc, vc, 1000, 0.0, 256, 64)
+    for h in range(w.H):
+        g = h // w.group
+        s = kc[0, g, :1000] @ q[0, h] / math.sqrt(w.d)
+        p = np.exp(s - s.max())
+        assert np.abs(o[0, h] - p @ vc[0, g, :1000] / p.sum()).max() <= 1e-12 * np.abs(o[0, h]).max()
+        assert abs(lse[0, h] - (s.max() + math.log(p.sum()))) <= 1e-12
+
+
+def test_seeded_partition0_is_plain_last_partition():
+    """When Lk is a multiple of the partition size the newest partition of the
+    seeded decode is the last partition of the plain decode (same tiles, both
+    start empty), so its decisions and state are the same."""
+    w, q, kc, vc = _decode_small(1536)
+    Lk, S, bk = 1536, 512, 64
+    G = w.group
+    for g in (0, 3):
+        r1 = oracle.decode_group_partials(q[0, g * G:(g + 1) * G], kc[0, g], vc[0, g], Lk, 4.0, S, bk)
+        r2 = oracle.decode_seeded_group_partials(q[0, g * G:(g + 1) * G], kc[0, g], vc[0, g], Lk, 4.0, S, bk)
+        assert (r1[2][:, 2] == r2[2][:, 0]).all()
+        for a, b in zip(r1[4:], r2[4:]):
+            assert np.array_equal(a[:, 2], b[:, 0])
+
+
+def test_seeded_decode_keeps_nothing_by_force():
+    """Constructed case: one dominant key at the newest position, every other
+    key orthogonal to the queries (score 0).  Partition 0 keeps its diagonal
+    tile (forced, empty state) and skips the rest (ratio e^-30 < tau/Lk); every
+    older partition is tested against that normalizer and skips everything,
+    so the output is softmax attention over the diagonal tile.  The plain
+    decode starts each noise-only partition empty: its first visited tile is
+    forced, and the rest then pass (ratio 1/(64 n) >= tau/Lk), so it keeps
+    every tile of the three older partitions."""
+    Lk, S, bk, d, G = 1000, 256, 64, 128, 4
+    rng = np.random.default_rng(7)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = np.tile(u * math.sqrt(30.0 * math.sqrt(d)), (1, G, 1))  # score with k = u * sqrt(30 sqrt(d)) is 30
+    k = np.zeros((1, 1, Lk, d))
+    k[0, 0, Lk - 1] = u * math.sqrt(30.0 * math.sqrt(d))
+    v = rng.standard_normal((1, 1, Lk, d))
+    o, lse, keep, T = oracle.decode_seeded(q, k, v, Lk, 1.0, S, bk)
+    nsplit, tps = oracle.seeded_decode_shapes(Lk, S, bk)
+    assert nsplit == 4
+    assert keep.sum() == 1 and keep[0, 0, 0, 0, tps - 1] == 1  # only the diagonal tile (tile 15)
+    jd = (Lk - 1) // bk
+    s = np.zeros(Lk - jd * bk)
+    s[-1] = 30.0
+    p = np.exp(s - s.max())
+    ref = p @ v[0, 0, jd * bk:Lk] / p.sum()
+    for r in range(G):
+        assert np.abs(o[0, r] - ref).max() <= 1e-12 * np.abs(ref).max()
+        assert abs(lse[0, r] - (30.0 + math.log(p.sum()))) <= 1e-12
+    _, _, keep_plain, _ = oracle.decode(q, k, v, Lk, 1.0, S, bk)
+    assert keep_plain[0, 0, 0, :3].all() and keep_plain[0, 0, 0, 3].sum() == 1
+
+
+@pytest.mark.parametrize("tau", [1.0, 16.0])
+def test_seeded_decode_is_dense_over_kept_keys_and_bounded(tau):
+    """The output is softmax attention over the union of kept tiles, and the
+    omitted mass obeys the tau/(1+tau) bound: every skipped key's weight is
+    below tau/Lk of a normalizer made of kept keys only."""
+    w, q, kc, vc = _decode_small(1500)
+    Lk, S, bk = 1500, 512, 64
+    o, lse, keep, T = oracle.decode_seeded(q, kc, vc, Lk, tau, S, bk)
+    skipped = 0
+    for h in range(w.H):
+        g = h // w.group
+        mask = _seeded_tiles_mask(keep[0, g, 0], Lk, S, bk)
+        skipped += int((~mask).sum())
+        s = kc[0, g, :Lk] @ q[0, h] / math.sqrt(w.d)
+        e = np.exp(s[mask] - s[mask].max())
+        assert np.abs(o[0, h] - e @ vc[0, g, :Lk][mask] / e.sum()).max() <= 1e-12 * np.abs(o[0, h]).max()
+        P = np.exp(s - s.max())
+        P /= P.sum()
+        assert P[~mask].sum() < tau / (1 + tau)
+        assert keep[0, g, 0, 0, oracle.seeded_decode_shapes(Lk, S, bk)[1] - 1] == 1  # diagonal tile
+    assert skipped > 0
