@@ -246,6 +246,8 @@ def main():
                            "work_per_launch": work, "per_unit": per_unit}
     roofline = rooflines[max(rooflines, key=lambda n: rooflines[n]["ms"])]
 
+    seeded = None if args.no_tau0 else decode_seeded_128k(torch, ops, qd, kc, vc, od, lsed, ws_d, wd, args.tau,
+                                                             args.steps, ms["dec"])
     chunk = None if args.no_tau0 else chunked_prefill(torch, ops, q, k, v, args.tau, args.steps)
     sweep = None if args.no_sweep else sweep32k(torch, ops, args.steps, args.warmup)
     gqa = None if args.no_sweep else gqa_8k(torch, ops, args.tau, args.steps)
@@ -281,6 +283,7 @@ def main():
         "kernel_rooflines": rooflines,
         "sweep32k": sweep,
         "matched_work_8k": matched,
+        "decode_seeded": seeded,
         "chunked_prefill": chunk,
         "gqa8k": gqa,
         "cpu_baseline": cpu,
@@ -525,6 +528,33 @@ def sweep32k(torch, ops, steps, warmup):
         log(f"sweep32k {family}: " + ", ".join(f"tau={t}: fwd {r['fwd_ms']:.2f} bwd {r['bwd_ms']:.2f} "
                                               f"kept {r['kept_fwd']:.3f}/{r['kept_bwd']:.3f}" for t, r in res.items()))
         del q, k, v, do, o, dq, dk, dv
+    return out
+
+
+def decode_seeded_128k(torch, ops, qd, kc, vc, od, lsed, ws, wd, tau, steps, plain_ms):
+    """The decode128k shape with seeded partitions (mala_decode_seeded) at tau
+    and at tau=0: ms per call (events the library records around its
+    launches), kept-tile fraction, and HBM bytes of K (always) plus V of the
+    kept tiles per ms."""
+    Lk, split, bk = wd.L, wd.split_keys, wd.bk
+    out = {"workload": "decode128k (B16 Hq32 Hkv8 Lk131073 d128), partitions of 4096 keys counted back from "
+                       "the newest tile", "plain_decode_ms": plain_ms}
+    for t in (tau, 0.0):
+        st = ops.decode_stats_buffers(wd.B, wd.Hkv, Lk, split, bk, qd.device)
+        ops.decode_into(qd, kc, vc, Lk, od, lsed, t, ws, split, bk, stats=st, seeded=True)
+        torch.cuda.synchronize()
+        kept, legal = int(st["kept"].sum()), int(st["legal"].sum())
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in evs:
+            ops.decode_into(qd, kc, vc, Lk, od, lsed, t, ws, split, bk, stats={"events": e}, seeded=True)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        nbytes = wd.B * wd.Hkv * Lk * wd.d * 2 * (1.0 + kept / legal)
+        out[f"tau={t}"] = {"ms": ms, "kept_frac": kept / legal, "kept_tiles": kept, "legal_tiles": legal,
+                           "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9}
+    out["speedup_vs_plain_decode"] = plain_ms / out[f"tau={tau}"]["ms"]
+    out["speedup_vs_tau0"] = out["tau=0.0"]["ms"] / out[f"tau={tau}"]["ms"]
+    log("decode seeded: " + json.dumps(out))
     return out
 
 

@@ -197,6 +197,32 @@ mala_status mala_decode(const void* q, const void* kcache, const void* vcache,
                         void* o, float* lse, mala_stats* stats,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mala_decode_seeded -- mala_decode with seeded partitions (threshold and
+ * forward paragraphs: a tile is tested against a normalizer established on
+ * the more recent keys; seeding carries that normalizer across split-KV
+ * partitions).  Arguments, shapes, workspace and errors are mala_decode's.
+ *
+ * Tiles are the bk-key tiles counted from key 0; jd = (Lk-1)/bk is the tile
+ * of the newest key.  Partition p (p = 0 newest) holds tiles
+ * max(0, jd - (p+1)*tps + 1) .. jd - p*tps, tps = split_keys/bk, and is
+ * visited newest tile first.  Partition 0 starts from an empty state (its
+ * first visited tile is kept), exactly as a mala_decode partition.  Every
+ * older partition is tested against partition 0's final normalizer plus its
+ * own kept keys, and keeps nothing by force; its output state holds only its
+ * own kept keys, and the partitions' states are merged exactly.  Two kernel
+ * launches: partition 0, then the older partitions (tau = 0: one launch,
+ * every tile kept).  Statistics as for mala_decode with nsplit = ceil(Lk /
+ * split_keys) partitions in this order; bit t of partition p = its t-th tile
+ * from the oldest.  events[0] is recorded before the first launch and
+ * events[1] after the merge.
+ */
+mala_status mala_decode_seeded(const void* q, const void* kcache, const void* vcache,
+                               int B, int Hq, int Hkv, int Lk, int Lcap, int d, mala_dtype dtype,
+                               float tau, int split_keys, int bk, float scale,
+                               void* o, float* lse, mala_stats* stats,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* mala_status_string(mala_status status);
 /* Message of the last failing call on this host thread ("" if none). */

@@ -28,8 +28,8 @@ class Stats(ctypes.Structure):
                 ("keep_bits_dkdv", ctypes.c_void_p), ("events", ctypes.c_void_p * 4)]
 
 
-EXPORTS = ("mala_fwd", "mala_fwd_chunk", "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_workspace_size",
-           "mala_status_string", "mala_last_error", "mala_version")
+EXPORTS = ("mala_fwd", "mala_fwd_chunk", "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_seeded",
+           "mala_decode_workspace_size", "mala_status_string", "mala_last_error", "mala_version")
 
 _LIB = None
 
@@ -58,6 +58,8 @@ def load(path=None):
     lib.mala_decode_workspace_size.restype = sz
     lib.mala_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, i, f, vp, vp, sp, vp, sz, vp]
     lib.mala_decode.restype = i
+    lib.mala_decode_seeded.argtypes = lib.mala_decode.argtypes
+    lib.mala_decode_seeded.restype = i
     lib.mala_status_string.argtypes = [i]
     lib.mala_status_string.restype = ctypes.c_char_p
     lib.mala_last_error.argtypes = []

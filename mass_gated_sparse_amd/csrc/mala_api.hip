@@ -200,9 +200,10 @@ size_t mala_decode_workspace_size(int B, int Hq, int Hkv, int Lk, int d, int spl
     return align256(size_t(B) * Hq * nsplit * (d + 2) * sizeof(float));
 }
 
-mala_status mala_decode(const void* q, const void* kcache, const void* vcache, int B, int Hq, int Hkv, int Lk,
-                        int Lcap, int d, mala_dtype dtype, float tau, int split_keys, int bk, float scale, void* o,
-                        float* lse, mala_stats* stats, void* workspace, size_t workspace_bytes, void* stream) {
+static mala_status decode_call(const char* name, bool seeded, const void* q, const void* kcache, const void* vcache,
+                               int B, int Hq, int Hkv, int Lk, int Lcap, int d, mala_dtype dtype, float tau,
+                               int split_keys, int bk, float scale, void* o, float* lse, mala_stats* stats,
+                               void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (!q || !kcache || !vcache || !o) return fail(MALA_ERR_INVALID_ARG, "null pointer");
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || d <= 0 || split_keys <= 0 || bk <= 0)
@@ -224,9 +225,12 @@ mala_status mala_decode(const void* q, const void* kcache, const void* vcache, i
     a.part = static_cast<float*>(workspace);
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.Lk = Lk; a.Lcap = Lcap; a.d = d;
     a.split_keys = split_keys; a.bk = bk;
+    // plain: ceil(Lk/split) partitions from key 0; seeded: ceil(ntiles/tps) partitions counted back from
+    // the newest tile -- the same number, since split_keys is a multiple of bk
     a.nsplit = int(cdiv(Lk, split_keys));
     a.tps = split_keys / bk;
     a.words = int(cdiv(a.tps, 32));
+    a.seeded = seeded;
     const float sc = eff_scale(scale, d);
     a.scale_log2 = sc * mala::kLog2e;
     a.log2_tau = log2_tau_of(tau);
@@ -238,7 +242,22 @@ mala_status mala_decode(const void* q, const void* kcache, const void* vcache, i
     hipError_t e = mala::mark(e0, s);
     if (e == hipSuccess) e = mala::launch_decode_bf16(a, s);
     if (e == hipSuccess) e = mala::mark(e1, s);
-    return hip_status(e, "mala_decode launch");
+    return hip_status(e, name);
+}
+
+mala_status mala_decode(const void* q, const void* kcache, const void* vcache, int B, int Hq, int Hkv, int Lk,
+                        int Lcap, int d, mala_dtype dtype, float tau, int split_keys, int bk, float scale, void* o,
+                        float* lse, mala_stats* stats, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_call("mala_decode launch", false, q, kcache, vcache, B, Hq, Hkv, Lk, Lcap, d, dtype, tau,
+                       split_keys, bk, scale, o, lse, stats, workspace, workspace_bytes, stream);
+}
+
+mala_status mala_decode_seeded(const void* q, const void* kcache, const void* vcache, int B, int Hq, int Hkv,
+                               int Lk, int Lcap, int d, mala_dtype dtype, float tau, int split_keys, int bk,
+                               float scale, void* o, float* lse, mala_stats* stats, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return decode_call("mala_decode_seeded launch", true, q, kcache, vcache, B, Hq, Hkv, Lk, Lcap, d, dtype, tau,
+                       split_keys, bk, scale, o, lse, stats, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -21,6 +21,16 @@
 // fp32 accumulators are summed over the 16 key subsets once per partition.
 // Partial states (m2 = running max of s*log2(e), l, acc[d]) are written per
 // (sequence, query head, partition) and merged exactly by the combine kernel.
+//
+// Partitions.  Plain: partition p holds keys [p*S, min((p+1)*S, Lk)).
+// Seeded: tiles stay the 64-key tiles counted from key 0, but partition p
+// holds the S/64 tiles ending S/64*p tiles before the newest tile (partition
+// 0 is the newest; the oldest may be short).  A seeded decode runs in two
+// launches: partition 0 from an empty state, then every older partition with
+// partition 0's final (m2, l) added to its test normalizer (the normalizer
+// established on the most recent keys, extended across partitions).  Its own
+// output state still starts empty, so the exact merge counts no key twice,
+// and no tile is kept by force.
 #include <float.h>
 
 #include "mala_kernels.hpp"
@@ -33,12 +43,18 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-template <int G, bool GATED, bool STATS>
+// SEED: this launch covers the older partitions of a seeded decode and reads
+// partition 0's final state from `part` (written by the previous launch).
+// PREV: V tiles are fetched one tile ahead together with K, whatever the
+// vote decides.  Used for the newest partition alone (one workgroup per
+// sequence and KV head, keeping nearly every tile): there the V load would
+// otherwise add a memory latency per tile to a short, serial launch.
+template <int G, bool GATED, bool STATS, bool SEED, bool PREV>
 __global__ __launch_bounds__(256) void decode_split_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     float* __restrict__ part, int Hq, int Hkv, int Lk, int Lcap, int split_keys, int nsplit, int tps, int words,
     float scale_log2, float log2_tau, float log2_lq, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
-    uint32_t* __restrict__ bits) {
+    uint32_t* __restrict__ bits, int pbase, int seeded_grid) {
     constexpr int D = 128, BK = 64;
     __shared__ int vote_sm[2][4];
     __shared__ float wmax_sm[4][G];
@@ -47,12 +63,21 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
     __shared__ float red_sm[G][16][D + 4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int p = blockIdx.x;
+    const int p = int(blockIdx.x) + pbase;
     const int bg = blockIdx.y;  // b * Hkv + g
     const int b = bg / Hkv, g = bg % Hkv;
     const long kvbase = long(bg) * Lcap * D;
-    const int k0 = p * split_keys;
-    const int k1 = min(k0 + split_keys, Lk);
+    int k0, k1;
+    if (seeded_grid) {
+        const int jd = (Lk - 1) / BK;  // tile of the newest key
+        const int hi = jd - p * tps;
+        const int lo = max(0, hi - tps + 1);
+        k0 = lo * BK;
+        k1 = min(hi * BK + BK, Lk);
+    } else {
+        k0 = p * split_keys;
+        k1 = min(k0 + split_keys, Lk);
+    }
     const int nt = (k1 - k0 + BK - 1) / BK;
 
     // score mapping
@@ -74,9 +99,19 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
     for (int r = 0; r < G; ++r)
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
-    float m2[G], lsum[G];
+    // (m2, lsum): this partition's own state; ltest: the normalizer the test
+    // uses, which also holds the seed (the same as lsum without one)
+    float m2[G], lsum[G], ltest[G];
 #pragma unroll
-    for (int r = 0; r < G; ++r) { m2[r] = -INFINITY; lsum[r] = 0.f; }
+    for (int r = 0; r < G; ++r) { m2[r] = -INFINITY; lsum[r] = 0.f; ltest[r] = 0.f; }
+    if (SEED) {
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            const float* sp = part + (long(b) * Hq + g * G + r) * nsplit * (D + 2);  // partition 0
+            m2[r] = sp[0];
+            ltest[r] = sp[1];
+        }
+    }
 
     const u32x4 z4 = {0u, 0u, 0u, 0u};
     u32x4 kr[4];
@@ -92,11 +127,24 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
     if (STATS && bits && tid == 0)
         for (int w = ((nt - 1) >> 5) + 1; w < words; ++w) bits[(long(bg) * nsplit + p) * words + w] = 0u;
 
+    u32x4 vn[4] = {z4, z4, z4, z4};  // PREV: V of the next tile to visit
+    auto load_v = [&](int t, u32x4* dst) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int vk = k0 + t * BK + 16 * wave + 4 * i + ksub;
+            dst[i] = vk < k1 ? *reinterpret_cast<const u32x4*>(vc + kvbase + long(vk) * D + 8 * dch) : z4;
+        }
+    };
     load_k(nt - 1);
+    if (PREV) load_v(nt - 1, vn);
     for (int t = nt - 1; t >= 0; --t) {
         const int par = t & 1;
         u32x4 kcur[4] = {kr[0], kr[1], kr[2], kr[3]};
-        if (t > 0) load_k(t - 1);
+        u32x4 vcur[4] = {vn[0], vn[1], vn[2], vn[3]};
+        if (t > 0) {
+            load_k(t - 1);
+            if (PREV) load_v(t - 1, vn);
+        }
         const int key = k0 + t * BK + skey;
         const bool kvalid = key < k1;
         float s[G];
@@ -120,8 +168,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
             bool vote = false;
 #pragma unroll
             for (int r = 0; r < G; ++r) {
-                const float thr = (lsum[r] == 0.f) ? -FLT_MAX
-                                                   : (m2[r] + fast_log2(lsum[r]) + log2_tau - log2_lq) / scale_log2;
+                const float lz = SEED ? ltest[r] : lsum[r];
+                const float thr = (lz == 0.f) ? -FLT_MAX : (m2[r] + fast_log2(lz) + log2_tau - log2_lq) / scale_log2;
                 vote |= s[r] >= thr;
             }
             const bool wv = wave_any(vote);
@@ -141,10 +189,11 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
 
         // V loads for this tile (consumed after the normalizer update)
         u32x4 vr[4];
+        if (PREV) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int vk = k0 + t * BK + 16 * wave + 4 * i + ksub;
-            vr[i] = vk < k1 ? *reinterpret_cast<const u32x4*>(vc + kvbase + long(vk) * D + 8 * dch) : z4;
+            for (int i = 0; i < 4; ++i) vr[i] = vcur[i];
+        } else {
+            load_v(t, vr);
         }
         // running max over the tile's 64 keys, per row
         float mx[G];
@@ -177,7 +226,9 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < G; ++r) {
-            lsum[r] = lsum[r] * alpha[r] + ((wsum_sm[0][r] + wsum_sm[1][r]) + (wsum_sm[2][r] + wsum_sm[3][r]));
+            const float tsum = (wsum_sm[0][r] + wsum_sm[1][r]) + (wsum_sm[2][r] + wsum_sm[3][r]);
+            lsum[r] = lsum[r] * alpha[r] + tsum;
+            if (SEED) ltest[r] = ltest[r] * alpha[r] + tsum;
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[r][c] *= alpha[r];
         }
@@ -241,22 +292,31 @@ __global__ __launch_bounds__(128) void decode_combine_d128(const float* __restri
     if (lse && dd == 0) lse[bh] = (M + fast_log2(lam)) * kLn2;
 }
 
+template <int G, bool GT, bool ST, bool SD, bool PV = false>
+static void launch_decode_one(const DecArgs& a, hipStream_t s, int nparts, int pbase) {
+    hipLaunchKernelGGL((decode_split_bf16_d128<G, GT, ST, SD, PV>), dim3(nparts, a.B * a.Hkv), dim3(256), 0, s,
+                       (const bf16_t*)a.q, (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.part, a.Hq, a.Hkv, a.Lk,
+                       a.Lcap, a.split_keys, a.nsplit, a.tps, a.words, a.scale_log2, a.log2_tau, a.log2_lq, a.kept,
+                       a.legal, a.bits, pbase, a.seeded ? 1 : 0);
+}
+
+template <int G, bool ST>
+static void launch_decode_gs(const DecArgs& a, hipStream_t s) {
+    if (!a.gated) {
+        launch_decode_one<G, false, ST, false>(a, s, a.nsplit, 0);
+    } else if (!a.seeded) {
+        launch_decode_one<G, true, ST, false>(a, s, a.nsplit, 0);
+    } else {
+        // partition 0 first; the older partitions read its final state
+        launch_decode_one<G, true, ST, false, true>(a, s, 1, 0);
+        if (a.nsplit > 1) launch_decode_one<G, true, ST, true>(a, s, a.nsplit - 1, 1);
+    }
+}
+
 template <int G>
 static void launch_decode_g(const DecArgs& a, hipStream_t s) {
-    dim3 grid(a.nsplit, a.B * a.Hkv), block(256);
-    const bool st = a.kept || a.legal || a.bits;
-#define MALA_DEC_LAUNCH(GT, ST)                                                                                    \
-    hipLaunchKernelGGL((decode_split_bf16_d128<G, GT, ST>), grid, block, 0, s, (const bf16_t*)a.q,                \
-                       (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.part, a.Hq, a.Hkv, a.Lk, a.Lcap, a.split_keys, \
-                       a.nsplit, a.tps, a.words, a.scale_log2, a.log2_tau, a.log2_lq, a.kept, a.legal, a.bits)
-    if (a.gated) {
-        if (st) MALA_DEC_LAUNCH(true, true);
-        else MALA_DEC_LAUNCH(true, false);
-    } else {
-        if (st) MALA_DEC_LAUNCH(false, true);
-        else MALA_DEC_LAUNCH(false, false);
-    }
-#undef MALA_DEC_LAUNCH
+    if (a.kept || a.legal || a.bits) launch_decode_gs<G, true>(a, s);
+    else launch_decode_gs<G, false>(a, s);
 }
 
 hipError_t launch_decode_bf16(const DecArgs& a, hipStream_t s) {

@@ -48,6 +48,7 @@ struct DecArgs {
     int split_keys, bk, nsplit, tps, words;
     float scale_log2, log2_tau, log2_lq;
     bool gated;
+    bool seeded;  // partitions counted back from the newest tile; older ones seeded with the newest's state
     int32_t *kept, *legal;
     uint32_t* bits;
 };

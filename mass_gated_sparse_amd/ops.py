@@ -185,17 +185,21 @@ def decode_workspace(B, Hq, Hkv, Lk, d, split_keys, device):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys=4096, bk=64, scale=0.0, stats=None, stream=None):
+def decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys=4096, bk=64, scale=0.0, stats=None, stream=None,
+                seeded=False):
     B, Hq, d = q.shape
     _, Hkv, Lcap, _ = kc.shape
-    rc = _lib.load().mala_decode(_ptr(q), _ptr(kc), _ptr(vc), B, Hq, Hkv, int(Lk), Lcap, d, _dt(q), float(tau),
-                                 int(split_keys), int(bk), float(scale), _ptr(o), _ptr(lse), _stats_struct(stats),
-                                 _ptr(ws), ws.numel(), _stream(stream))
-    _lib.check("mala_decode", rc)
+    name = "mala_decode_seeded" if seeded else "mala_decode"
+    rc = getattr(_lib.load(), name)(_ptr(q), _ptr(kc), _ptr(vc), B, Hq, Hkv, int(Lk), Lcap, d, _dt(q), float(tau),
+                                    int(split_keys), int(bk), float(scale), _ptr(o), _ptr(lse),
+                                    _stats_struct(stats), _ptr(ws), ws.numel(), _stream(stream))
+    _lib.check(name, rc)
 
 
-def decode(q, kc, vc, Lk, tau, split_keys=4096, bk=64, scale=0.0, stats=False):
-    """Split-KV MALA decode.  q [B,Hq,d], caches [B,Hkv,Lcap,d].  Returns (o, lse[, stats])."""
+def decode(q, kc, vc, Lk, tau, split_keys=4096, bk=64, scale=0.0, stats=False, seeded=False):
+    """Split-KV MALA decode.  q [B,Hq,d], caches [B,Hkv,Lcap,d].  Returns (o, lse[, stats]).
+    seeded=True runs mala_decode_seeded (partitions counted back from the
+    newest tile, the older ones tested against the newest one's state)."""
     _check_dev(q, kc, vc)
     B, Hq, d = q.shape
     Hkv = kc.shape[1]
@@ -203,7 +207,7 @@ def decode(q, kc, vc, Lk, tau, split_keys=4096, bk=64, scale=0.0, stats=False):
     lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
     ws = decode_workspace(B, Hq, Hkv, Lk, d, split_keys, q.device)
     st = decode_stats_buffers(B, Hkv, Lk, split_keys, bk, q.device) if stats else None
-    decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys, bk, scale, st)
+    decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys, bk, scale, st, seeded=seeded)
     return (o, lse, st) if stats else (o, lse)
 
 

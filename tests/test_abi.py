@@ -36,8 +36,9 @@ def lib():
 
 def test_header_declares_the_documented_entry_points():
     fns = declared_functions()
-    for name in ("mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size", "mala_decode_workspace_size",
-                 "mala_status_string", "mala_last_error", "mala_version"):
+    for name in ("mala_fwd", "mala_fwd_chunk", "mala_bwd", "mala_decode", "mala_decode_seeded",
+                 "mala_bwd_workspace_size", "mala_decode_workspace_size", "mala_status_string", "mala_last_error",
+                 "mala_version"):
         assert name in fns
 
 
@@ -146,8 +147,9 @@ def test_bwd_rejects(lib, kw, status, msg):
 
 
 def dec(lib, q=P, B=2, Hq=8, Hkv=2, Lk=5000, Lcap=8192, d=128, dt=0, tau=1.0, split=4096, bk=64,
-        ws=ALIGNED_WS, ws_bytes=1 << 30):
-    return lib.mala_decode(q, P, P, B, Hq, Hkv, Lk, Lcap, d, dt, tau, split, bk, 0.0, P, P, None, ws, ws_bytes, None)
+        ws=ALIGNED_WS, ws_bytes=1 << 30, fn="mala_decode"):
+    return getattr(lib, fn)(q, P, P, B, Hq, Hkv, Lk, Lcap, d, dt, tau, split, bk, 0.0, P, P, None, ws, ws_bytes,
+                            None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -165,8 +167,9 @@ def dec(lib, q=P, B=2, Hq=8, Hkv=2, Lk=5000, Lcap=8192, d=128, dt=0, tau=1.0, sp
     ({"ws_bytes": 64}, INVALID, "workspace too small"),
     ({"ws": MISALIGNED_WS}, INVALID, "aligned"),
 ])
-def test_decode_rejects(lib, kw, status, msg):
-    assert dec(lib, **kw) == status
+@pytest.mark.parametrize("fn", ["mala_decode", "mala_decode_seeded"])
+def test_decode_rejects(lib, kw, status, msg, fn):
+    assert dec(lib, fn=fn, **kw) == status
     assert msg in lib.mala_last_error().decode()
 
 

@@ -131,3 +131,34 @@ def test_decode128k_full(ops, tau):
         assert rel_l2(og[b, hs], oo[0]) <= TOL_O
         assert np.abs(lg[b, hs] - ol[0]).max() <= 1e-3
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+
+
+@pytest.mark.parametrize("tau", [1.0])
+def test_decode128k_seeded_full(ops, tau):
+    """Seeded decode at the full decode shape, sampled (sequence, KV head)
+    groups against the oracle's seeded decode."""
+    w = WORKLOADS["decode128k"]
+    x = decode_inputs(w, threads=16)
+    q, kc, vc = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse, st = ops.decode(q, kc, vc, w.L, tau, split_keys=w.split_keys, bk=w.bk, stats=True, seeded=True)
+    torch.cuda.synchronize()
+    nsplit, tps = oracle.seeded_decode_shapes(w.L, w.split_keys, w.bk)
+    gk = ops.bits_to_keep(st["keep_bits"], tps)
+    jd = (w.L - 1) // w.bk
+    legal = np.zeros((nsplit, tps), bool)
+    for p in range(nsplit):
+        hi = jd - p * tps
+        legal[p, : hi - max(0, hi - tps + 1) + 1] = True
+    og, lg = bf16_to_f64(o), lse.cpu().numpy()
+    for b, g in [(0, 0), (7, 3), (15, 7)]:
+        hs = slice(g * w.group, (g + 1) * w.group)
+        qs = to_f64(x["q"][b:b + 1, hs], "bf16")
+        ks = to_f64(x["k"][b:b + 1, g:g + 1], "bf16")
+        vs = to_f64(x["v"][b:b + 1, g:g + 1], "bf16")
+        oo, ol, ok, oT = oracle.decode_seeded(qs, ks, vs, w.L, tau, w.split_keys, w.bk,
+                                              replay=gk[b:b + 1, g:g + 1, None], band=BAND)
+        bad, near, _ = decision_report(gk[b, g], ok[0, 0, 0], oT[0, 0, 0], legal)
+        assert bad == 0
+        assert rel_l2(og[b, hs], oo[0]) <= TOL_O
+        assert np.abs(lg[b, hs] - ol[0]).max() <= 1e-3
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()

@@ -253,6 +253,45 @@ def test_decode_bf16(ops, Lk, split, Lcap, tau):
     assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
 
 
+def seeded_legal(Lk, split, bk=64):
+    """[nsplit, tps] legal tiles of the seeded decode (partition 0 = newest)."""
+    nsplit, tps = oracle.seeded_decode_shapes(Lk, split, bk)
+    jd = (Lk - 1) // bk
+    legal = np.zeros((nsplit, tps), bool)
+    for p in range(nsplit):
+        hi = jd - p * tps
+        legal[p, : hi - max(0, hi - tps + 1) + 1] = True
+    return legal
+
+
+@pytest.mark.parametrize("Lk,split,Lcap", [(3000, 1024, None), (4097, 4096, 4200), (1536, 512, None),
+                                           (5000, 512, 5003), (64, 4096, None), (1, 64, 100), (20000, 4096, None)])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 16.0, math.inf])
+def test_decode_seeded_bf16(ops, Lk, split, Lcap, tau):
+    """mala_decode_seeded against the oracle's seeded decode: decisions per
+    partition (partition 0 the newest), O and lse; with one partition it is
+    mala_decode bit for bit."""
+    w, x = _decode_case(Lk, (0, 1), Lcap)
+    q, kc, vc = _dev_tensors(x, "bf16", ("q", "k", "v"))
+    o, lse, st = ops.decode(q, kc, vc, Lk, tau, split_keys=split, bk=64, stats=True, seeded=True)
+    torch.cuda.synchronize()
+    nsplit, tps = oracle.seeded_decode_shapes(Lk, split, 64)
+    gk = ops.bits_to_keep(st["keep_bits"], tps)  # [B, Hkv, nsplit, tps]
+    qf, kf, vf = (to_f64(x[n], "bf16") for n in ("q", "k", "v"))
+    oo, ol, ok, oT = oracle.decode_seeded(qf, kf, vf, Lk, tau, split, 64, replay=gk[:, :, None], band=BAND)
+    legal = seeded_legal(Lk, split)
+    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal)
+    assert bad == 0
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+    assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+    assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
+    assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+    if nsplit == 1:
+        o2, lse2 = ops.decode(q, kc, vc, Lk, tau, split_keys=split, bk=64)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
 def test_invalid_arguments_rejected(ops):
     from mass_gated_sparse_amd._lib import MalaError
     q = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16, device="cuda")
