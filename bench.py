@@ -62,8 +62,16 @@ def main():
                     help="query blocks in the CPU-oracle sample (0: three per OpenMP thread, at most 48)")
     ap.add_argument("--micro", action="store_true",
                     help="only run the ceiling microbenchmarks (MFMA, LDS, transposed LDS, HBM)")
+    ap.add_argument("--profile-op", choices=("fwd", "bwd", "decode"),
+                    help="only run one operation on --workload, --iters times after one warmup call, and print "
+                         "its mean time per kernel (a short program for rocprofv3 counter passes)")
+    ap.add_argument("--workload", default="sweep32k", help="workload of --profile-op (see synth.configs)")
+    ap.add_argument("--iters", type=int, default=2, help="timed calls of --profile-op")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter calibration)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="no GPU: NAME WORKLOAD TAU DIR... -- per-kernel means of the rocprofv3 --pmc csv dirs "
+                         "(one pass each, made with --profile-op on WORKLOAD at TAU) into profiles/NAME.md")
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("TRACE", "FETCH", "WRITE", "CFETCH", "CWRITE"),
                     help="no GPU: turn rocprofv3 csv output dirs (kernel trace of this bench; FETCH_SIZE and "
                          "WRITE_SIZE passes of a short bench run; the same two passes of --copy-calibration) "
@@ -71,6 +79,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -87,6 +98,10 @@ def main():
         print(json.dumps(micro(torch)))
         return
 
+    if args.profile_op:
+        from mass_gated_sparse_amd import ops
+        print(json.dumps(profile_op(torch, ops, args.profile_op, args.workload, args.tau, args.iters)))
+        return
     if args.fidelity:
         from mass_gated_sparse_amd import ops
         print(json.dumps({fam: fidelity_sweep(torch, ops, fam) for fam in ("planted", "diffuse")}))
@@ -355,6 +370,61 @@ def _counter_per_dispatch(d, counter):
     return out
 
 
+def summarize_counters(name, workload, tau, *dirs):
+    """profiles/<name>.md: per kernel, the mean per dispatch of every SQ
+    counter found in the --pmc csv dirs, plus derived fractions:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x SQ_BUSY_CU_CYCLES),
+    LDS active = SQ_LDS_IDX_ACTIVE / SQ_BUSY_CU_CYCLES, wave time waiting =
+    SQ_WAIT_ANY / SQ_WAVE_CYCLES, LDS-instruction waits = SQ_WAIT_INST_LDS /
+    SQ_WAVE_CYCLES."""
+    import collections
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    passes = []
+    for d in dirs:
+        names, per = {}, collections.defaultdict(float)
+        counters = set()
+        for r in _csv_rows(d, "counter_collection.csv"):
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            per[key] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            counters.add(r["Counter_Name"])
+        passes.append(sorted(counters))
+        for (disp, cn), v in per.items():
+            vals[names[disp]][cn].append(v)
+    lines = [f"# Hardware counters per dispatch: {workload}, tau={tau}", "",
+             "Commands (from the repository root, on one MI355X; one rocprofv3 pass per counter set):", ""]
+    for cs in dict.fromkeys(tuple(c) for c in passes):
+        lines.append(f"    cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {' '.join(cs)} --output-format csv "
+                     f"-d <dir> -o run -- python3 $GRAFT_REPO_ROOT/bench.py --profile-op <fwd|bwd> "
+                     f"--workload {workload} --tau {tau} --iters 1")
+    lines += ["", "Derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES); LDS active = "
+              "SQ_LDS_IDX_ACTIVE / SQ_BUSY_CU_CYCLES; waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES; LDS waits = "
+              "SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES.", ""]
+    for kern, cs in vals.items():
+        if not kern.startswith("mala::"):
+            continue
+        m = {cn: float(np.mean(v)) for cn, v in cs.items()}
+        lines += [f"## `{kern}`", "", "| counter | mean per dispatch |", "|---|---:|"]
+        lines += [f"| {cn} | {v:.4g} |" for cn, v in sorted(m.items())]
+        der = []
+        if m.get("SQ_BUSY_CU_CYCLES"):
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                der.append(f"MFMA busy {100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * m['SQ_BUSY_CU_CYCLES']):.0f}%")
+            if "SQ_LDS_IDX_ACTIVE" in m:
+                der.append(f"LDS active {100 * m['SQ_LDS_IDX_ACTIVE'] / m['SQ_BUSY_CU_CYCLES']:.0f}%")
+        if m.get("SQ_WAVE_CYCLES"):
+            if "SQ_WAIT_ANY" in m:
+                der.append(f"waiting {100 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.0f}%")
+            if "SQ_WAIT_INST_LDS" in m:
+                der.append(f"LDS waits {100 * m['SQ_WAIT_INST_LDS'] / m['SQ_WAVE_CYCLES']:.0f}%")
+        if "SQ_LDS_BANK_CONFLICT" in m:
+            der.append(f"LDS bank conflicts {m['SQ_LDS_BANK_CONFLICT']:.0f}")
+        lines += ["", "Derived: " + "; ".join(der) + ".", ""]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_profiles(trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
@@ -529,6 +599,54 @@ def sweep32k(torch, ops, steps, warmup):
                                               f"kept {r['kept_fwd']:.3f}/{r['kept_bwd']:.3f}" for t, r in res.items()))
         del q, k, v, do, o, dq, dk, dv
     return out
+
+
+def profile_op(torch, ops, op, workload, tau, iters):
+    """One operation of the path on a named workload: one warmup call, then
+    `iters` calls with the library's events around each kernel; mean ms per
+    kernel."""
+    from synth import WORKLOADS, decode_inputs, prefill_inputs
+    w = WORKLOADS[workload]
+    if (op == "decode") != (w.kind == "decode"):
+        raise SystemExit(f"--profile-op {op} needs a {'decode' if op == 'decode' else 'prefill'} workload")
+    if w.kind == "prefill":
+        x = prefill_inputs(w)
+        q, k, v, do = (dev_bf16(torch, x[n]) for n in ("q", "k", "v", "do"))
+        tile = (w.bq, w.bk)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        ops.fwd_into(q, k, v, o, lse, tau, tile)
+        if op == "fwd":
+            names = ("fwd",)
+
+            def call(e):
+                ops.fwd_into(q, k, v, o, lse, tau, tile, stats={"events": e})
+        else:
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = ops.bwd_workspace(q, tile)
+            names = ("bwd_prep", "dq", "dkdv")
+
+            def call(e):
+                ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile, stats={"events": e})
+    else:
+        x = decode_inputs(w, threads=16)
+        q, kc, vc = (dev_bf16(torch, x[n]) for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+        ws = ops.decode_workspace(w.B, w.H, w.Hkv, w.L, w.d, w.split_keys, q.device)
+        names = ("decode",)
+
+        def call(e):
+            ops.decode_into(q, kc, vc, w.L, o, lse, tau, ws, w.split_keys, w.bk, stats={"events": e})
+    n = len(names) + 1
+    call([torch.cuda.Event(enable_timing=True) for _ in range(n)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n)] for _ in range(iters)]
+    for e in evs:
+        call(e)
+    torch.cuda.synchronize()
+    return {"op": op, "workload": workload, "tau": tau, "iters": iters,
+            "ms": {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, nm in enumerate(names)}}
 
 
 def decode_seeded_128k(torch, ops, qd, kc, vc, od, lsed, ws, wd, tau, steps, plain_ms):
