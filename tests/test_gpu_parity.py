@@ -292,6 +292,39 @@ def test_decode_seeded_bf16(ops, Lk, split, Lcap, tau):
         assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (16, 2)])
+@pytest.mark.parametrize("Lk,split", [(3000, 1024), (4097, 4096)])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 16.0])
+@pytest.mark.parametrize("seeded", [False, True])
+def test_decode_groups_bf16(ops, Hq, Hkv, Lk, split, tau, seeded):
+    """Decode with 1, 2 and 8 query heads per K/V head (the vote rows of a
+    tile), plain and seeded, against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["decode128k"], B=2, H=Hq, Hkv=Hkv)
+    x = decode_inputs(w, Lk=Lk)
+    q, kc, vc = _dev_tensors(x, "bf16", ("q", "k", "v"))
+    o, lse, st = ops.decode(q, kc, vc, Lk, tau, split_keys=split, bk=64, stats=True, seeded=seeded)
+    torch.cuda.synchronize()
+    qf, kf, vf = (to_f64(x[n], "bf16") for n in ("q", "k", "v"))
+    if seeded:
+        nsplit, tps = oracle.seeded_decode_shapes(Lk, split, 64)
+        legal = seeded_legal(Lk, split)
+        ref = oracle.decode_seeded
+    else:
+        nsplit, tps = -(-Lk // split), split // 64
+        legal = np.zeros((nsplit, tps), bool)
+        for p in range(nsplit):
+            legal[p, : -(-(min((p + 1) * split, Lk) - p * split) // 64)] = True
+        ref = oracle.decode
+    gk = ops.bits_to_keep(st["keep_bits"], tps)
+    oo, ol, ok, oT = ref(qf, kf, vf, Lk, tau, split, 64, replay=gk[:, :, None], band=BAND)
+    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal)
+    assert bad == 0
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+    assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
+    assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+
+
 def test_invalid_arguments_rejected(ops):
     from mass_gated_sparse_amd._lib import MalaError
     q = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16, device="cuda")
