@@ -328,7 +328,7 @@ PROFILED = {
     "fwd_bf16_d128": ("fwd_bf16_d128<true, false>", ["mala_fwd.hip"]),
     "bwd_dkdv_bf16_d128": ("bwd_dkdv_bf16_d128<true>", ["mala_bwd.hip"]),
     "bwd_dq_bf16_d128": ("bwd_dq_bf16_d128<true, false>", ["mala_bwd.hip"]),
-    "decode_split_bf16_d128": ("decode_split_bf16_d128<4, true, false>", ["mala_decode.hip"]),
+    "decode_split_bf16_d128": ("decode_split_bf16_d128<4, true, false, false, false>", ["mala_decode.hip"]),
 }
 COMMON_SOURCES = ["mala_device.hpp", "mala_kernels.hpp"]
 CSRC = "mass_gated_sparse_amd/csrc"
