@@ -35,6 +35,48 @@ def _check_dev(*ts):
             raise ValueError("MALA tensors must be contiguous")
 
 
+def _expect(t, name, shape, dtype):
+    """The library sees raw pointers: every extent it derives from the sizes
+    passed must match the tensor actually behind the pointer."""
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _expect_qkv(q, k, v, nq_dims=4):
+    """q [B,H,L,d] (or [B,H,d] for decode) and k, v [B,Hkv,Lk,d] of q's dtype;
+    returns (B, H, Hkv, Lk, d)."""
+    if q.dim() != nq_dims or k.dim() != 4:
+        raise ValueError(f"q must be {nq_dims}-D and k 4-D (got {q.dim()}-D and {k.dim()}-D)")
+    _dt(q)
+    B, H, d = q.shape[0], q.shape[1], q.shape[-1]
+    Hkv, Lk = k.shape[1], k.shape[2]
+    _expect(k, "k", (B, Hkv, Lk, d), q.dtype)
+    _expect(v, "v", (B, Hkv, Lk, d), q.dtype)
+    return B, H, Hkv, Lk, d
+
+
+def _expect_stats(st, shapes):
+    """Caller-supplied statistics buffers must be int32 of the sizes the
+    library writes (shapes: name -> shape)."""
+    if st is None:
+        return
+    for n, shape in shapes.items():
+        if n in st and st[n] is not None:
+            _expect(st[n], f"stats[{n!r}]", shape, torch.int32)
+            _check_dev(st[n])
+    if len(st.get("events", ())) > 4:
+        raise ValueError("at most 4 events")
+
+
+def _prefill_stat_shapes(B, H, nqb, ntiles):
+    w = -(-ntiles // 32)
+    return {"kept": (B, H, nqb), "legal": (B, H, nqb), "keep_bits": (B, H, nqb, w), "keep_bits_dkdv": (B, H, nqb, w)}
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -70,8 +112,14 @@ def _stats_struct(st):
 
 def fwd_into(q, k, v, o, lse, tau, tile=None, scale=0.0, stats=None, stream=None):
     """Queue mala_fwd writing into preallocated o [B,H,L,d] and lse [B,H,L] (fp32)."""
-    B, H, L, d = q.shape
+    B, H, Hkv, L, d = _expect_qkv(q, k, v)
+    if q.shape[2] != L:
+        raise ValueError(f"q has {q.shape[2]} rows but k, v have {L} (use fwd_chunk for a query chunk)")
+    _expect(o, "o", q.shape, q.dtype)
+    _expect(lse, "lse", (B, H, L), torch.float32)
     tile = tile or DEFAULT_TILE[q.dtype]
+    _expect_stats(stats, _prefill_stat_shapes(B, H, -(-L // tile[0]), -(-L // tile[1])))
+    _check_dev(q, k, v, o, lse)
     rc = _lib.load().mala_fwd(_ptr(q), _ptr(k), _ptr(v), B, H, k.shape[1], L, d, _dt(q), float(tau), Tile(*tile),
                               float(scale), _ptr(o), _ptr(lse), _stats_struct(stats), _stream(stream))
     _lib.check("mala_fwd", rc)
@@ -92,9 +140,13 @@ def fwd(q, k, v, tau, tile=None, scale=0.0, stats=False):
 def fwd_chunk_into(q, kc, vc, P, o, lse, tau, tile=None, scale=0.0, stats=None, stream=None):
     """Queue mala_fwd_chunk: q [B,H,Lq,d] at key positions P.., caches [B,Hkv,Lcap,d]
     holding keys 0 .. P+Lq-1; writes o [B,H,Lq,d] and lse [B,H,Lq]."""
-    B, H, Lq, d = q.shape
-    _, Hkv, Lcap, _ = kc.shape
+    B, H, Hkv, Lcap, d = _expect_qkv(q, kc, vc)
+    Lq = q.shape[2]
+    _expect(o, "o", q.shape, q.dtype)
+    _expect(lse, "lse", (B, H, Lq), torch.float32)
     tile = tile or DEFAULT_TILE[q.dtype]
+    _expect_stats(stats, _prefill_stat_shapes(B, H, -(-Lq // tile[0]), -(-(int(P) + Lq) // tile[1])))
+    _check_dev(q, kc, vc, o, lse)
     rc = _lib.load().mala_fwd_chunk(_ptr(q), _ptr(kc), _ptr(vc), B, H, Hkv, Lq, int(P), Lcap, d, _dt(q), float(tau),
                                     Tile(*tile), float(scale), _ptr(o), _ptr(lse), _stats_struct(stats),
                                     _stream(stream))
@@ -126,8 +178,21 @@ def bwd_workspace(q, tile=None):
 
 
 def bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile=None, scale=0.0, stats=None, stream=None):
-    B, H, L, d = q.shape
+    """Queue mala_bwd writing into preallocated dq (like q) and dk, dv (like k);
+    ws from bwd_workspace."""
+    B, H, Hkv, L, d = _expect_qkv(q, k, v)
+    if q.shape[2] != L:
+        raise ValueError(f"q has {q.shape[2]} rows but k, v have {L}")
+    for t, n in ((o, "o"), (do, "do"), (dq, "dq")):
+        _expect(t, n, q.shape, q.dtype)
+    for t, n in ((dk, "dk"), (dv, "dv")):
+        _expect(t, n, k.shape, q.dtype)
+    _expect(lse, "lse", (B, H, L), torch.float32)
+    if ws is None or ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise ValueError("ws must be a 1-D uint8 workspace (see bwd_workspace)")
     tile = tile or DEFAULT_TILE[q.dtype]
+    _expect_stats(stats, _prefill_stat_shapes(B, H, -(-L // tile[0]), -(-L // tile[1])))
+    _check_dev(q, k, v, o, lse, do, dq, dk, dv, ws)
     rc = _lib.load().mala_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), B, H, k.shape[1], L, d,
                               _dt(q), float(tau), Tile(*tile), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
                               _stats_struct(stats), _ptr(ws), ws.numel(), _stream(stream))
@@ -187,8 +252,19 @@ def decode_workspace(B, Hq, Hkv, Lk, d, split_keys, device):
 
 def decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys=4096, bk=64, scale=0.0, stats=None, stream=None,
                 seeded=False):
-    B, Hq, d = q.shape
-    _, Hkv, Lcap, _ = kc.shape
+    """Queue mala_decode (or mala_decode_seeded): q [B,Hq,d], caches
+    [B,Hkv,Lcap,d] with Lk valid rows; writes o (like q) and lse [B,Hq] (or
+    None); ws from decode_workspace."""
+    B, Hq, Hkv, Lcap, d = _expect_qkv(q, kc, vc, nq_dims=3)
+    _expect(o, "o", q.shape, q.dtype)
+    if lse is not None:
+        _expect(lse, "lse", (B, Hq), torch.float32)
+    if ws is None or ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise ValueError("ws must be a 1-D uint8 workspace (see decode_workspace)")
+    if stats is not None and int(split_keys) > 0 and int(bk) > 0:  # (bad sizes: the library rejects them)
+        nsplit, w = -(-int(Lk) // int(split_keys)), -(-(int(split_keys) // int(bk)) // 32)
+        _expect_stats(stats, {"kept": (B, Hkv, nsplit), "legal": (B, Hkv, nsplit), "keep_bits": (B, Hkv, nsplit, w)})
+    _check_dev(q, kc, vc, o, ws, *([lse] if lse is not None else []))
     name = "mala_decode_seeded" if seeded else "mala_decode"
     rc = getattr(_lib.load(), name)(_ptr(q), _ptr(kc), _ptr(vc), B, Hq, Hkv, int(Lk), Lcap, d, _dt(q), float(tau),
                                     int(split_keys), int(bk), float(scale), _ptr(o), _ptr(lse),

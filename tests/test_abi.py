@@ -195,3 +195,36 @@ def test_python_error_carries_library_message(lib):
     assert fwd(lib, tau=-1.0) == INVALID
     with pytest.raises(_lib.MalaError, match="tau must be >= 0"):
         _lib.check("mala_fwd", INVALID)
+
+
+def test_python_wrappers_check_shapes_before_the_device():
+    """The C ABI sees raw pointers, so the binding checks every tensor's
+    shape and dtype against the sizes it passes (on host tensors these checks
+    fail before anything touches a device)."""
+    import torch
+    from mass_gated_sparse_amd import ops
+    bf = torch.bfloat16
+
+    def z(*s, dt=bf):
+        return torch.zeros(*s, dtype=dt)
+    q, k = z(1, 4, 256, 128), z(1, 2, 256, 128)
+    o, lse = z(1, 4, 256, 128), z(1, 4, 256, dt=torch.float32)
+    cases = [
+        (lambda: ops.fwd_into(q, z(1, 2, 200, 128), k, o, lse, 1.0), "shape"),        # k rows differ
+        (lambda: ops.fwd_into(q, k, z(1, 2, 256, 128, dt=torch.float32), o, lse, 1.0), "dtype"),
+        (lambda: ops.fwd_into(q, k, k, o, z(1, 4, 255, dt=torch.float32), 1.0), "lse"),
+        (lambda: ops.fwd_into(z(1, 4, 300, 128), k, k, z(1, 4, 300, 128), z(1, 4, 300, dt=torch.float32), 1.0),
+         "rows"),
+        (lambda: ops.fwd_into(q, k, k, o, lse, 1.0, stats={"kept": z(1, 4, 1, dt=torch.int32)}), "kept"),
+        (lambda: ops.fwd_chunk_into(q, k, z(1, 2, 300, 128), 0, o, lse, 1.0), "shape"),
+        (lambda: ops.bwd_into(q, k, k, o, lse, o, o, z(1, 4, 256, 128), k, 1.0, z(1024, dt=torch.uint8)), "dk"),
+        (lambda: ops.bwd_into(q, k, k, o, lse, o, o, k, k, 1.0, z(16, dt=torch.float32)), "workspace"),
+        (lambda: ops.decode_into(z(2, 8, 128), z(2, 2, 512, 128), z(2, 2, 500, 128), 500, z(2, 8, 128),
+                                 z(2, 8, dt=torch.float32), 1.0, z(4096, dt=torch.uint8)), "shape"),
+        (lambda: ops.decode_into(z(2, 8, 128), z(2, 2, 512, 128), z(2, 2, 512, 128), 500, z(2, 8, 128),
+                                 z(2, 8, dt=torch.float32), 1.0, z(4096, dt=torch.uint8), split_keys=128,
+                                 stats={"keep_bits": z(2, 2, 1, 1, dt=torch.int32)}), "keep_bits"),
+    ]
+    for fn, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            fn()
