@@ -45,7 +45,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--tau", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tau0", action="store_true", help="skip the tau=0 comparison run")
@@ -182,8 +182,8 @@ def main():
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t_start) * 1e3 / steps
 
-        def avg(a, b):
-            return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+        def avg(a, b):  # per-kernel time: median over the timed steps
+            return float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
         ms = {"fwd": avg(0, 1), "bwd": avg(2, 5), "bwd_prep": avg(2, 3), "dq": avg(3, 4), "dkdv": avg(4, 5),
               "dec": avg(6, 7)}
         return wall, ms
@@ -318,8 +318,8 @@ def kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, tau, ste
         ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile, stats={"events": e[2:6]})
     torch.cuda.synchronize()
 
-    def avg(a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+    def avg(a, b):  # median over the calls
+        return float(np.median([e[a].elapsed_time(e[b]) for e in evs]))
     return {"fwd": avg(0, 1), "dq": avg(3, 4), "dkdv": avg(4, 5)}
 
 
@@ -504,7 +504,8 @@ def load_traffic():
 def micro(torch):
     """Measured ceilings on this GPU: dense bf16 MFMA (32x32x16, 8 independent
     chains per wave), LDS read bandwidth (16-byte reads, conflict-free) and the
-    transposing 8-byte LDS reads, HBM streaming reads (8 GiB)."""
+    transposing 8-byte LDS reads, the hardware exp2 rate (8 independent chains
+    per thread), HBM streaming reads (8 GiB)."""
     import ctypes
     from mass_gated_sparse_amd.build import ubench_path
     lib = ctypes.CDLL(ubench_path())
@@ -537,6 +538,10 @@ def micro(torch):
     res["lds_read_tbs"] = cus * 2 * 4 * it * 8 * 1024 / t / 1e12
     t = timed(lambda: lib.ubench_lds_tr(vp(out.data_ptr()), cus * 2, it, st))
     res["lds_tr_read_bytes_per_clk_per_cu_at_2p4ghz"] = cus * 2 * 4 * it * 4 * 1024 / t / cus / 2.4e9
+    it = 4000
+    t = timed(lambda: lib.ubench_exp(vp(seed.data_ptr()), vp(out.data_ptr()), cus * 8, it, st))
+    res["exp2_per_clk_per_cu_at_2p4ghz"] = cus * 8 * 256 * it * 8 / t / cus / 2.4e9
+    res["exp2_gops"] = cus * 8 * 256 * it * 8 / t / 1e9
     n16 = (8 << 30) // 16
     buf = torch.empty(n16 * 4, dtype=torch.int32, device="cuda").fill_(1)
     t = timed(lambda: lib.ubench_hbm(vp(buf.data_ptr()), ctypes.c_long(n16), vp(out.data_ptr()), cus * 16, st))
@@ -575,7 +580,7 @@ def sweep32k(torch, ops, steps, warmup):
             for _ in range(warmup):
                 ops.fwd_into(q, k, v, o, lse, tau, tile)
                 ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
-            tf = tb = 0.0
+            tfs, tbs = [], []
             for _ in range(steps):
                 ev[0].record()
                 ops.fwd_into(q, k, v, o, lse, tau, tile)
@@ -583,9 +588,9 @@ def sweep32k(torch, ops, steps, warmup):
                 ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
                 ev[2].record()
                 torch.cuda.synchronize()
-                tf += ev[0].elapsed_time(ev[1])
-                tb += ev[1].elapsed_time(ev[2])
-            tf, tb = tf / steps, tb / steps
+                tfs.append(ev[0].elapsed_time(ev[1]))
+                tbs.append(ev[1].elapsed_time(ev[2]))
+            tf, tb = float(np.median(tfs)), float(np.median(tbs))  # medians over the timed steps
             res[str(tau)] = {"fwd_ms": tf, "bwd_ms": tb, "fwd_dense_tflops": dense_fwd / tf / 1e9,
                              "bwd_dense_tflops": 2.5 * dense_fwd / tb / 1e9,
                              "kept_fwd": fk / n_legal, "kept_bwd": bk_ / n_legal}
@@ -646,7 +651,7 @@ def profile_op(torch, ops, op, workload, tau, iters):
         call(e)
     torch.cuda.synchronize()
     return {"op": op, "workload": workload, "tau": tau, "iters": iters,
-            "ms": {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, nm in enumerate(names)}}
+            "ms": {nm: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, nm in enumerate(names)}}
 
 
 def decode_seeded_128k(torch, ops, qd, kc, vc, od, lsed, ws, wd, tau, steps, plain_ms):
@@ -666,7 +671,7 @@ def decode_seeded_128k(torch, ops, qd, kc, vc, od, lsed, ws, wd, tau, steps, pla
         for e in evs:
             ops.decode_into(qd, kc, vc, Lk, od, lsed, t, ws, split, bk, stats={"events": e}, seeded=True)
         torch.cuda.synchronize()
-        ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
         nbytes = wd.B * wd.Hkv * Lk * wd.d * 2 * (1.0 + kept / legal)
         out[f"tau={t}"] = {"ms": ms, "kept_frac": kept / legal, "kept_tiles": kept, "legal_tiles": legal,
                            "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9}
@@ -1002,8 +1007,14 @@ def cpu_baseline(wx, wd, xp, xd0, nblocks, tau):
     pairs_keys = sum(L - j for j in range(kts[0] * bk, L))
     flops = 4.0 * d * pairs_rows + 6.0 * d * pairs_rows + 8.0 * d * pairs_keys + 2 * wd.group * 4.0 * wd.L * d
     total = t_pre + t_dec
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {"value": flops / total / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": threads,
-            "kind": "oracle", "seconds": round(total, 2),
+            "cpu_model": cpu_model, "kind": "oracle", "seconds": round(total, 2),
             "sample": f"head 0 of train128k, last {nblocks} query blocks (rows {r0}..{L - 1}): fwd, dQ of those "
                       f"rows, dK/dV of key tiles {kts[0]}..{kts[-1]}; decode128k units (b0,g0),(b0,g1); "
                       f"tau={tau}; dense-equivalent FLOPs executed by the oracle"}

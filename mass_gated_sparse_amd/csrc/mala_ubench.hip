@@ -1,6 +1,7 @@
 // Microbenchmarks of the ceilings the MALA kernels run against on gfx950:
 // dense bf16 MFMA rate, LDS read bandwidth (plain 16-byte reads and the
-// transposing 8-byte reads), and HBM streaming read bandwidth.  Built into a
+// transposing 8-byte reads), HBM streaming read bandwidth, and the rate of
+// the hardware exp2 (the transcendental behind every kept score).  Built into a
 // separate library (libmala_ubench.so); not part of the operator.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -79,6 +80,23 @@ __global__ __launch_bounds__(256) void ub_hbm(const u32x4* __restrict__ src, lon
     out[blockIdx.x * blockDim.x + threadIdx.x] = x;
 }
 
+// 8 independent chains of x = exp2(-x) per thread: one v_exp_f32 per step
+// (the negation is a source modifier); x stays in (0.5, 1).
+__global__ __launch_bounds__(256) void ub_exp(const uint32_t* __restrict__ seed, float* __restrict__ out, int iters) {
+    const int tid = threadIdx.x;
+    float x[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = 0.5f + float(seed[(tid + c) & 255] & 0xffffu) * (0.5f / 65536.f);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) x[c] = fast_exp2(-x[c]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s += x[c];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 extern "C" {
 // Each runs the kernel once on `stream`; sizes are validated by the caller.
 int ubench_mfma(const void* seed, void* out, int blocks, int iters, void* stream) {
@@ -92,6 +110,11 @@ int ubench_lds(void* out, int blocks, int iters, void* stream) {
 }
 int ubench_lds_tr(void* out, int blocks, int iters, void* stream) {
     hipLaunchKernelGGL(ub_lds_tr, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (uint32_t*)out, iters);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+int ubench_exp(const void* seed, void* out, int blocks, int iters, void* stream) {
+    hipLaunchKernelGGL(ub_exp, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const uint32_t*)seed, (float*)out,
+                       iters);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 int ubench_hbm(const void* src, long n16, void* out, int blocks, void* stream) {
