@@ -41,13 +41,6 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                    0, 0, 0);
 }
 
-// 16x16x32 bf16 MFMA: lane l holds A[l%16][8*(l/16) .. +8], B[8*(l/16) .. +8][l%16];
-// D register r of lane l is D[4*(l/16) + r][l%16].
-__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-}
-
 // Work item of workgroup i in a grid ordered by rank (i / BH) and head.  The
 // GPU deals workgroups to its 8 XCDs round-robin (i % 8), so with head =
 // i % BH every XCD would serve a fixed subset of the heads for the whole
@@ -139,21 +132,17 @@ __device__ __forceinline__ u32x4 tr_operand(const uint8_t* tile, int rowbase, in
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// One direct global->LDS load: every lane reads 16 bytes at `gaddr`; lane l's
-// bytes land at LDS byte address lds_addr + 16*l (lds_addr must be the same in
-// all lanes).  The data goes to LDS, not to registers, and completion is
-// tracked by the callers with explicit s_waitcnt vmcnt(N) before the barrier
-// that publishes the tile.  Written as asm rather than with
-// __builtin_amdgcn_global_load_lds because the compiler cannot tell which LDS
-// bytes such a load writes and then waits for every outstanding load before
-// each later LDS access, which would serialize the prefetch.  The asm has no
-// register outputs (nothing can be overwritten late); it clobbers M0.
-__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(lds_addr) : "memory", "m0");
-}
-
-// Same load with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
-// byte offset (the saddr form): one VGPR of address per lane instead of two.
+// One direct global->LDS load: every lane reads 16 bytes at sbase + voff;
+// lane l's bytes land at LDS byte address lds_addr + 16*l (lds_addr must be
+// the same in all lanes).  The data goes to LDS, not to registers, and
+// completion is tracked by the callers with explicit s_waitcnt vmcnt(N)
+// before the barrier that publishes the tile.  Written as asm rather than
+// with __builtin_amdgcn_global_load_lds because the compiler cannot tell
+// which LDS bytes such a load writes and then waits for every outstanding
+// load before each later LDS access, which would serialize the prefetch.  The
+// asm has no register outputs (nothing can be overwritten late); it clobbers
+// M0.  The saddr form takes a wave-uniform 64-bit base in SGPRs and a
+// per-lane 32-bit byte offset: one VGPR of address per lane instead of two.
 // The base must be the same in every lane; it is read from the first lane
 // so that it always sits in an SGPR pair.
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
@@ -170,19 +159,6 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
     return uint32_t(reinterpret_cast<uintptr_t>((lds_void*)const_cast<void*>(p)));
-}
-
-// Direct global->LDS copy of rows [row0, row0 + nrows) of a 128-wide bf16
-// matrix into a swizzled tile, nrows/4 segments of 1 KiB: segment s holds
-// rows 4s..4s+3; lane l of the issuing wave fills physical chunk l%16 of row
-// 4s + l/16.  Rows at or past `rows_valid` read row rows_valid-1 instead
-// (callers mask them).  Each call issues one 16-byte load per lane.
-__device__ __forceinline__ void dma_segment(const bf16_t* g, long row0, int rows_valid, uint8_t* tile, int seg,
-                                            int lane) {
-    const int row = 4 * seg + (lane >> 4);
-    const int chunk = (lane & 15) ^ rowkey(row);
-    const int rr = min(row, rows_valid - 1);
-    dma16(g + (row0 + rr) * 128 + chunk * 8, __builtin_amdgcn_readfirstlane(lds_addr_of(tile + seg * 1024)));
 }
 
 }  // namespace mala
