@@ -243,8 +243,9 @@ def main():
     kern = {
         "fwd_bf16_d128": (ms["fwd"], tile_flop * (n_legal + fk), "mfma",
                           f"QK on every legal tile + PV on each kept tile; {per_tile}"),
-        "bwd_dkdv_bf16_d128": (ms["dkdv"], tile_flop * (n_legal + 3 * bk_), "mfma",
-                               f"S on every legal tile + dV, dP, dK on each kept tile; {per_tile}"),
+        "bwd_dkdv_bf16_d128": (ms["dkdv"], tile_flop * 4 * bk_, "mfma",
+                               f"S, dP, dV, dK on each kept tile (the dQ pass decides; this pass visits kept "
+                               f"tiles only); {per_tile}"),
         "bwd_dq_bf16_d128": (ms["dq"], tile_flop * (n_legal + 2 * bk_), "mfma",
                              f"S on every legal tile + dP, dQ on each kept tile; {per_tile}"),
         "decode_split_bf16_d128": (ms["dec"], Bd * wd.Hkv * Lk * d * 2 * (1.0 + dkp / dlg), "hbm",
