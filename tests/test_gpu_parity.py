@@ -139,11 +139,22 @@ def test_gqa_bf16(ops, L, tau):
     _check_bwd(ops, w, x, tau, 128, 64)
 
 
-@pytest.mark.parametrize("L", [64, 130, 200])
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 130, 200])
 @pytest.mark.parametrize("tau", [0.0, 1.0, 4.0])
 def test_short_ragged_bf16(ops, L, tau):
     """Sequences shorter than one or two query blocks, ragged in the last tile."""
     w, x = _prefill_case("mw8k", L, (0, 3))
+    _check_fwd(ops, w, x, tau, 128, 64)
+    _check_bwd(ops, w, x, tau, 128, 64)
+
+
+@pytest.mark.parametrize("tau", [0.0, 1.0, 4.0])
+def test_mqa_bf16(ops, tau):
+    """Eight query heads over a single K/V head (multi-query attention)."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["gqa8k"], Hkv=1)
+    x = prefill_inputs(w, L=700)
+    assert x["k"].shape[1] == 1 and x["q"].shape[1] == 8
     _check_fwd(ops, w, x, tau, 128, 64)
     _check_bwd(ops, w, x, tau, 128, 64)
 
@@ -187,7 +198,8 @@ def test_autograd_wrapper(ops, tau, family):
         assert max(errs) <= TOL_GRAD, errs
 
 
-@pytest.mark.parametrize("P,Lq,spare", [(0, 640, 0), (256, 300, 77), (333, 300, 0), (1000, 130, 64)])
+@pytest.mark.parametrize("P,Lq,spare", [(0, 640, 0), (256, 300, 77), (333, 300, 0), (1000, 130, 64),
+                                         (0, 1, 0), (511, 1, 0), (4095, 1, 1), (127, 129, 0), (64, 64, 0)])
 @pytest.mark.parametrize("tau", [0.0, 1.0, 4.0])
 def test_fwd_chunk_bf16(ops, P, Lq, spare, tau):
     """Chunked prefill: a query chunk at key offset P against a K/V cache
