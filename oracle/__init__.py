@@ -49,8 +49,8 @@ def _lib():
         lib.oracle_decode_seeded_group.argtypes = lib.oracle_decode_group.argtypes
         lib.oracle_decode_seeded_groups.argtypes = lib.oracle_decode_groups.argtypes
         lib.oracle_fwd_chunk_head.argtypes = [_D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_int,
-                                              ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int, _U8,
-                                              ctypes.c_double, _D, _D, _U8, _D]
+                                              ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int, _L,
+                                              ctypes.c_long, _U8, ctypes.c_double, _D, _D, _U8, _D]
         lib.oracle_omitted_head.argtypes = [_D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_int,
                                             ctypes.c_int, _U8, _L, ctypes.c_long, _D, _D]
         for f in ("oracle_fwd_head", "oracle_bwd_head", "oracle_decode_group", "oracle_decode_groups",
@@ -141,13 +141,15 @@ def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     return o, lse, keep, T
 
 
-def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4):
+def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     """MALA forward of a query chunk against a key cache (chunked prefill).
 
     q: [B, H, Lq, d], rows at key positions p0 .. p0 + Lq - 1; k, v:
     [B, Hkv, >= p0 + Lq, d] (the first p0 + Lq rows are the keys the chunk
     sees, its own included).  Row i has Lq_i = p0 + i + 1 visible keys.
     Returns (o, lse, keep, T); keep/T are [B, H, ceil(Lq/bq), ceil((p0+Lq)/bk)].
+    qblocks: optional query-block indices of the chunk to compute (others
+    left NaN / 0).
     """
     q = _f64(q)
     B, H, Lq, d = q.shape
@@ -161,11 +163,13 @@ def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4):
     keep = np.zeros((B, H, nqb, nt), dtype=np.uint8)
     T = np.full((B, H, nqb, nt), np.nan)
     rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
+    ids, n = _ids(qblocks)
 
     def one(b, h):
         g = h // G
         rc = _lib().oracle_fwd_chunk_head(_p(q[b, h], _D), _p(k[b, g], _D), _p(v[b, g], _D), Lq, int(p0), d,
-                                          scale, float(tau), bq, bk, _p(None if rp is None else rp[b, h], _U8),
+                                          scale, float(tau), bq, bk, _p(ids, _L), n,
+                                          _p(None if rp is None else rp[b, h], _U8),
                                           float(band), _p(o[b, h], _D), _p(lse[b, h], _D), _p(keep[b, h], _U8),
                                           _p(T[b, h], _D))
         _check(rc, "oracle_fwd_chunk_head")

@@ -192,15 +192,19 @@ int oracle_fwd_head(const double* q, const double* k, const double* v, long L, i
  */
 int oracle_fwd_chunk_head(const double* q, const double* k, const double* v, long L, long p0, int d,
                           double scale, double tau, int bq, int bk,
+                          const long* qblocks, long nqblocks,
                           const uint8_t* replay, double band,
                           double* o, double* lse, uint8_t* keep, double* T)
 {
     if (!q || !k || !v || !o || !lse || L <= 0 || p0 < 0 || d <= 0 || bq <= 0 || bk <= 0) return ORACLE_ERR_ARG;
     if (!(tau >= 0.0)) return ORACLE_ERR_ARG;
     const long nqb = ceil_div(L, bq), ntiles = ceil_div(p0 + L, bk);
+    const long n = qblocks ? nqblocks : nqb;
     int err = ORACLE_OK;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (long qb = 0; qb < nqb; ++qb) {
+    for (long u = 0; u < n; ++u) {
+        const long qb = qblocks ? qblocks[u] : u;
+        if (qb < 0 || qb >= nqb) { err = ORACLE_ERR_ARG; continue; }
         int e = fwd_block(q, k, v, L, p0, d, scale, tau, bq, bk, qb, ntiles, replay, band, o, lse, keep, T);
         if (e) err = e;
     }

@@ -162,3 +162,30 @@ def test_decode128k_seeded_full(ops, tau):
         assert rel_l2(og[b, hs], oo[0]) <= TOL_O
         assert np.abs(lg[b, hs] - ol[0]).max() <= 1e-3
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+
+
+def test_chunk16k_full(ops):
+    """Chunked prefill in the bench's configuration: the last 16,384 rows of
+    the 128K training shape as one chunk at key offset 114,688 against the
+    131,072-key cache, tau=1, on sampled query blocks of the chunk."""
+    w = WORKLOADS["train128k"]
+    P, Lq = w.L - 16384, 16384
+    x = prefill_inputs(w)
+    qc = np.ascontiguousarray(x["q"][:, :, P:])
+    q, k, v = _dev(qc), _dev(x["k"]), _dev(x["v"])
+    o, lse, st = ops.fwd_chunk(q, k, v, P, 1.0, stats=True)
+    torch.cuda.synchronize()
+    nt = -(-(P + Lq) // w.bk)
+    gk = ops.bits_to_keep(st["keep_bits"], nt)
+    qblocks = (0, 63, 127)
+    qf, kf, vf = to_f64(qc, "bf16"), to_f64(x["k"], "bf16"), to_f64(x["v"], "bf16")
+    oo, ol, ok, oT = oracle.fwd_chunk(qf, kf, vf, P, 1.0, w.bq, w.bk, replay=gk, band=BAND, qblocks=qblocks)
+    from tests.parity import chunk_legal_mask
+    legal = chunk_legal_mask(Lq, P, w.bq, w.bk)
+    sel = np.zeros_like(legal)
+    sel[list(qblocks)] = legal[list(qblocks)]
+    bad, near, _ = decision_report(gk, ok, oT, sel)
+    assert bad == 0, f"{bad} chunk decisions differ"
+    rows = _rows(qblocks, w.bq, Lq)
+    assert rel_l2(bf16_to_f64(o)[:, :, rows], oo[:, :, rows]) <= TOL_O
+    assert np.abs(lse.cpu().numpy()[:, :, rows] - ol[:, :, rows]).max() <= 1e-3

@@ -617,3 +617,20 @@ def test_seeded_decode_is_dense_over_kept_keys_and_bounded(tau):
         assert P[~mask].sum() < tau / (1 + tau)
         assert keep[0, g, 0, 0, oracle.seeded_decode_shapes(Lk, S, bk)[1] - 1] == 1  # diagonal tile
     assert skipped > 0
+
+
+def test_chunk_sampled_blocks_equal_full():
+    """Computing only some query blocks of a chunk gives exactly those blocks
+    of the full computation (every block's decisions depend on its own rows
+    only); the others are left unset."""
+    w = WORKLOADS["gqa8k"]
+    P, Lq = 300, 400
+    x = prefill_inputs(w, L=P + Lq, heads=range(4))
+    q = to_f64(np.ascontiguousarray(x["q"][:, :4, P:]), w.dtype)
+    k, v = (to_f64(x[n][:, :1], w.dtype) for n in ("k", "v"))
+    o, lse, keep, T = oracle.fwd_chunk(q, k, v, P, 1.0, 128, 64)
+    o2, lse2, keep2, T2 = oracle.fwd_chunk(q, k, v, P, 1.0, 128, 64, qblocks=[1, 3])
+    rows = np.r_[128:256, 384:400]
+    assert np.array_equal(o2[:, :, rows], o[:, :, rows]) and np.array_equal(lse2[:, :, rows], lse[:, :, rows])
+    assert np.array_equal(keep2[:, :, [1, 3]], keep[:, :, [1, 3]])
+    assert np.isnan(o2[:, :, :128]).all() and (keep2[:, :, [0, 2]] == 0).all()
