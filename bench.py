@@ -396,7 +396,7 @@ def summarize_counters(name, workload, tau, *dirs):
              "Commands (from the repository root, on one MI355X; one rocprofv3 pass per counter set):", ""]
     for cs in dict.fromkeys(tuple(c) for c in passes):
         lines.append(f"    cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {' '.join(cs)} --output-format csv "
-                     f"-d <dir> -o run -- python3 $GRAFT_REPO_ROOT/bench.py --profile-op <fwd|bwd> "
+                     f"-d <dir> -o run -- python3 <repo>/bench.py --profile-op <fwd|bwd> "
                      f"--workload {workload} --tau {tau} --iters 1")
     lines += ["", "Derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES); LDS active = "
               "SQ_LDS_IDX_ACTIVE / SQ_BUSY_CU_CYCLES; waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES; LDS waits = "
@@ -434,7 +434,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
     lines = ["# Kernel time: bench.py, 128K training step + 128K decode", "",
              "Command (from the repository root, on one MI355X):", "",
              "    cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
-             "--output-format csv -d <dir> -o run -- python3 $GRAFT_REPO_ROOT/bench.py --steps 3 --warmup 1 "
+             "--output-format csv -d <dir> -o run -- python3 <repo>/bench.py --steps 3 --warmup 1 "
              "--no-tau0 --no-sweep --no-matched-work --no-cpu-baseline", "",
              "Runs at tau=1 only: every launch of an instantiation below is a tau=1 launch (the "
              "statistics pass uses the separate `<..., true>` instantiations; warmup and timed steps "
