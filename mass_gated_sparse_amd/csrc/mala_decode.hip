@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
     uint32_t* __restrict__ bits, int pbase, int seeded_grid) {
     constexpr int D = 128, BK = 64;
     __shared__ int vote_sm[2][4];
-    __shared__ float wmax_sm[4][G];
+    __shared__ float wmax_sm[2][4][G];
     __shared__ float wsum_sm[4][G];
     __shared__ float p_sm[G][BK];
     __shared__ float red_sm[G][16][D + 4];
@@ -163,17 +163,30 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
             s[r] = kvalid ? a : -INFINITY;
         }
 
+        // per-row maximum over the wave's keys (wave-uniform): the vote tests it,
+        // and a kept tile's statistics need it; both go out in one exchange
+        float mx[G];
+#pragma unroll
+        for (int r = 0; r < G; ++r) {
+            float x = s[r];
+#pragma unroll
+            for (int m = 4; m <= 32; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+            mx[r] = x;
+        }
         bool keep = true;
         if (GATED) {
-            bool vote = false;
+            bool wv = false;
 #pragma unroll
             for (int r = 0; r < G; ++r) {
                 const float lz = SEED ? ltest[r] : lsum[r];
                 const float thr = (lz == 0.f) ? -FLT_MAX : (m2[r] + fast_log2(lz) + log2_tau - log2_lq) / scale_log2;
-                vote |= s[r] >= thr;
+                wv |= mx[r] >= thr;
             }
-            const bool wv = wave_any(vote);
-            if (lane == 0) vote_sm[par][wave] = wv ? 1 : 0;
+            if (lane == 0) {
+                vote_sm[par][wave] = wv ? 1 : 0;
+#pragma unroll
+                for (int r = 0; r < G; ++r) wmax_sm[par][wave][r] = mx[r];
+            }
             __syncthreads();
             keep = (vote_sm[par][0] | vote_sm[par][1] | vote_sm[par][2] | vote_sm[par][3]) != 0;
         }
@@ -195,23 +208,17 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
         } else {
             load_v(t, vr);
         }
-        // running max over the tile's 64 keys, per row
-        float mx[G];
+        if (!GATED) {  // (gated: the maxima went out with the vote)
+            if (lane == 0)
 #pragma unroll
-        for (int r = 0; r < G; ++r) {
-            float x = s[r];
-#pragma unroll
-            for (int m = 4; m <= 32; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-            mx[r] = x;
+                for (int r = 0; r < G; ++r) wmax_sm[par][wave][r] = mx[r];
+            __syncthreads();
         }
-        if (lane == 0)
-#pragma unroll
-            for (int r = 0; r < G; ++r) wmax_sm[wave][r] = mx[r];
-        __syncthreads();
         float mref[G], alpha[G];
 #pragma unroll
         for (int r = 0; r < G; ++r) {
-            const float tm = fmaxf(fmaxf(wmax_sm[0][r], wmax_sm[1][r]), fmaxf(wmax_sm[2][r], wmax_sm[3][r]));
+            const float tm = fmaxf(fmaxf(wmax_sm[par][0][r], wmax_sm[par][1][r]),
+                                   fmaxf(wmax_sm[par][2][r], wmax_sm[par][3][r]));
             const float mn = fmaxf(m2[r], tm * scale_log2);
             mref[r] = mn;  // finite: every tile holds at least one valid key
             alpha[r] = fast_exp2(m2[r] - mn);
