@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
     constexpr int D = 128, BK = 64;
     __shared__ int vote_sm[2][4];
     __shared__ float wmax_sm[2][4][G];
-    __shared__ float wsum_sm[4][G];
-    __shared__ float p_sm[G][BK];
+    __shared__ float wsum_sm[2][4][G];
+    __shared__ float p_sm[2][G][BK];
     __shared__ float red_sm[G][16][D + 4];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -227,13 +227,13 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
             float ps = (quarter == 0) ? pv : 0.f;
 #pragma unroll
             for (int m = 4; m <= 32; m <<= 1) ps += __shfl_xor(ps, m, 64);
-            if (quarter == 0) p_sm[r][skey] = pv;
-            if (lane == 0) wsum_sm[wave][r] = ps;
+            if (quarter == 0) p_sm[par][r][skey] = pv;
+            if (lane == 0) wsum_sm[par][wave][r] = ps;
         }
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < G; ++r) {
-            const float tsum = (wsum_sm[0][r] + wsum_sm[1][r]) + (wsum_sm[2][r] + wsum_sm[3][r]);
+            const float tsum = (wsum_sm[par][0][r] + wsum_sm[par][1][r]) + (wsum_sm[par][2][r] + wsum_sm[par][3][r]);
             lsum[r] = lsum[r] * alpha[r] + tsum;
             if (SEED) ltest[r] = ltest[r] * alpha[r] + tsum;
 #pragma unroll
@@ -250,13 +250,15 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
             }
 #pragma unroll
             for (int r = 0; r < G; ++r) {
-                const float pw = p_sm[r][kk];
+                const float pw = p_sm[par][r][kk];
 #pragma unroll
                 for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(pw, vf[c], acc[r][c]);
             }
         }
         (void)mref;
-        __syncthreads();  // p_sm / wmax_sm / wsum_sm are rewritten by the next kept tile
+        // (no barrier here: the next tile writes the other parity's buffers, and
+        // this parity's again only after the next tile's own barrier, which
+        // every thread reaches after its reads here)
     }
 
     // sum the 16 key subsets of every d chunk, write the partial state
