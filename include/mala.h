@@ -87,7 +87,11 @@ typedef struct {
  *   keep_bits_dkdv uint32 [B, H, nqb, words], mala_bwd only: the tiles the
  *             dK/dV pass actually processed (the dQ pass writes keep_bits and
  *             hands the same decisions to the dK/dV pass); the two must agree
- *             bit for bit.
+ *             bit for bit.  The call clears it (with a kernel) and the dK/dV
+ *             pass sets its bits.
+ * Every call only launches kernels on `stream` (no allocation, no memset, no
+ * synchronization), so it can be captured in a HIP graph; events in
+ * mala_stats are recorded with hipEventRecord and are for eager calls.
  *   events    up to 4 hipEvent_t handles (NULL entries skipped), recorded on
  *             `stream` around the call's kernels: mala_fwd and mala_decode
  *             record events[0] before and events[1] after their kernels;

@@ -183,7 +183,7 @@ mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o,
         a.aux_bits = stats->keep_bits_dkdv;
         for (int i = 0; i < 4; ++i) a.ev[i] = (hipEvent_t)stats->events[i];
         if (a.aux_bits) {  // the dK/dV pass ORs in the blocks it visits
-            hipError_t e0 = hipMemsetAsync(a.aux_bits, 0, size_t(B) * H * a.nqb * a.words * sizeof(uint32_t), s);
+            hipError_t e0 = mala::launch_zero_u32(a.aux_bits, long(B) * H * a.nqb * a.words, s);
             if (e0 != hipSuccess) return hip_status(e0, "mala_bwd stats clear");
         }
     }

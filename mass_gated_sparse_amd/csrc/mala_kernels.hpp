@@ -58,6 +58,7 @@ inline hipError_t mark(hipEvent_t e, hipStream_t s) { return e ? hipEventRecord(
 
 hipError_t launch_simple_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, long n, hipStream_t s);
 hipError_t launch_simple_bwd_f32(const BwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);

@@ -363,4 +363,17 @@ hipError_t launch_simple_bwd_f32(const BwdArgs& a, hipStream_t s) {
     return e;
 }
 
+// Zero n 32-bit words (a fill kernel rather than hipMemsetAsync, so that the
+// clear is an ordinary kernel node if the caller captures the call in a graph).
+__global__ __launch_bounds__(256) void zero_u32(uint32_t* __restrict__ p, long n) {
+    for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < n; i += long(gridDim.x) * 256) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(uint32_t* p, long n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const long blocks = min((n + 255) / 256, 4096L);
+    hipLaunchKernelGGL(zero_u32, dim3(unsigned(blocks)), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 }  // namespace mala

@@ -348,3 +348,52 @@ def test_invalid_arguments_rejected(ops):
     with pytest.raises(MalaError) as e:
         ops.fwd(q64, q64, q64, 1.0)
     assert e.value.status == -2
+
+
+def test_graph_capture_replays(ops):
+    """The library only launches kernels on the caller's stream, so forward,
+    backward (with the dK/dV statistics, which the call clears with a kernel)
+    and both decodes can be captured in one HIP graph.  The graph is replayed
+    several times, with other eager work and synchronizations between the
+    replays, and every replay must equal the eager results bit for bit."""
+    w, x = _prefill_case("mw8k", 1000, (0, 3))
+    q, k, v, do = _dev_tensors(x, "bf16", ("q", "k", "v", "do"))
+    o, lse = torch.empty_like(q), torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = ops.bwd_workspace(q)
+    st = ops.prefill_stats_buffers(q.shape[0], q.shape[1], 1000, (128, 64), q.device, dkdv=True)
+    wd, xd = _decode_case(5000, (0, 1))
+    qd, kc, vc = _dev_tensors(xd, "bf16", ("q", "k", "v"))
+    od, ld = torch.empty_like(qd), torch.empty(qd.shape[:2], dtype=torch.float32, device="cuda")
+    os_, ls_ = torch.empty_like(qd), torch.empty(qd.shape[:2], dtype=torch.float32, device="cuda")
+    wsd = ops.decode_workspace(2, wd.H, wd.Hkv, 5000, wd.d, 1024, qd.device)
+    wss = ops.decode_workspace(2, wd.H, wd.Hkv, 5000, wd.d, 1024, qd.device)
+
+    def run():
+        ops.fwd_into(q, k, v, o, lse, 1.0)
+        ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, 1.0, ws, stats=st)
+        ops.decode_into(qd, kc, vc, 5000, od, ld, 1.0, wsd, 1024)
+        ops.decode_into(qd, kc, vc, 5000, os_, ls_, 1.0, wss, 1024, seeded=True)
+
+    outs = (o, lse, dq, dk, dv, st["keep_bits"], st["keep_bits_dkdv"], od, ld, os_, ls_)
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on a side stream before capture
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
