@@ -553,12 +553,13 @@ def micro(torch):
 def sweep32k(torch, ops, steps, warmup):
     """32K tau sweep (B1 H8 L32768 d128 bf16): fwd/bwd ms, dense-equivalent
     TFLOP/s and kept-tile fractions at tau in {0, 0.5, 1, 2}, for the planted
-    and the diffuse input families."""
+    family (c_h ~ U[0.5, 2]), the planted family with c = 1 on every head,
+    and the diffuse family."""
     from synth import WORKLOADS, prefill_inputs
     w = WORKLOADS["sweep32k"]
     tile = (w.bq, w.bk)
     out = {}
-    for family in ("planted", "diffuse"):
+    for family in ("planted", "planted_c1", "diffuse"):
         x = prefill_inputs(w, family=family)
         q, k, v, do = (dev_bf16(torch, x[n]) for n in ("q", "k", "v", "do"))
         del x

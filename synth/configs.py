@@ -49,7 +49,7 @@ MW8K = Workload("mw8k", 1, "prefill", B=1, H=16, Hkv=16, L=8192, d=128, dtype="b
                 note="8K matched-work study shape, bf16, 128x64 tiles")
 SWEEP32K = Workload("sweep32k", 2, "prefill", B=1, H=8, Hkv=8, L=32768, d=128, dtype="bf16",
                     bq=128, bk=64, taus=(0.0, 0.5, 1.0, 2.0),
-                    note="32K tau sweep, planted and diffuse families")
+                    note="32K tau sweep; planted, planted with c=1 on every head, and diffuse families")
 TRAIN128K = Workload("train128k", 3, "prefill", B=1, H=4, Hkv=4, L=131072, d=128, dtype="bf16",
                      bq=128, bk=64, taus=(1.0, 0.0),
                      note="128K training shape: one GPU's 4-head share of a 32-head layer")

@@ -14,6 +14,8 @@ building each query from keys of those three kinds plus noise:
 
 with z_i ~ N(0, I), delta_i ~ U{0..31}, the r_ij drawn uniformly with
 replacement from {0..i}, and a per-head sharpness multiplier c_h ~ U[lo, hi].
+The planted_c1 family is the same recipe with c_h = 1 on every head (the
+multiplier draw is skipped, every other draw is the planted family's).
 K, V and dO rows are N(0, I).  The diffuse family draws Q and K i.i.d. N(0, I)
 (near-uniform rows).  Everything is built in fp64 and rounded once to the
 storage type: bf16 with round-to-nearest-even (kept as uint16 bit patterns),
@@ -93,20 +95,21 @@ def _sink(kf: np.ndarray) -> np.ndarray:
     return acc / n
 
 
-def planted_query(w: Workload, b: int, h: int, kf: np.ndarray, positions: np.ndarray) -> np.ndarray:
+def planted_query(w: Workload, b: int, h: int, kf: np.ndarray, positions: np.ndarray, c: float = None) -> np.ndarray:
     """fp64 planted queries for query head h at the given positions.
 
     kf: fp64 values of the (rounded) keys of head h's KV head, rows 0..max(positions).
     The noise, offsets, retrieval indices and multiplier come from head h's own
     streams; they are drawn for every position 0..max(positions) so that a
     position's query does not depend on which other positions are requested.
+    `c` replaces the head's drawn multiplier when given.
     """
     n = int(positions.max()) + 1
     z = _rng(w.seed, _Z, b, h).standard_normal((n, w.d))
     delta = _rng(w.seed, _DELTA, b, h).integers(0, 32, size=n)
     hi = np.arange(1, n + 1, dtype=np.int64)[:, None]
     ridx = _rng(w.seed, _RIDX, b, h).integers(0, hi, size=(n, 4))
-    c = sharpness(w, b, h)
+    c = sharpness(w, b, h) if c is None else float(c)
     i = positions.astype(np.int64)
     sink = _sink(kf)
     local = kf[np.maximum(i - delta[i], 0)]
@@ -152,6 +155,8 @@ def prefill_inputs(w: Workload, family: str = "planted", L: int = None, heads=No
             kf = to_f64(out["k"][b, g], w.dtype)
             if family == "planted":
                 qf = planted_query(w, b, h, kf, np.arange(L))
+            elif family == "planted_c1":
+                qf = planted_query(w, b, h, kf, np.arange(L), c=1.0)
             elif family == "diffuse":
                 qf = _normal_rows(w, _QDIFF, b, h, L)
             else:

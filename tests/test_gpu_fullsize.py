@@ -89,7 +89,7 @@ def test_train128k_full(ops, tau):
     assert viol <= 4, viol
 
 
-@pytest.mark.parametrize("tau,family", [(0.5, "planted"), (2.0, "planted"), (1.0, "diffuse")])
+@pytest.mark.parametrize("tau,family", [(0.5, "planted"), (2.0, "planted"), (1.0, "planted_c1"), (1.0, "diffuse")])
 def test_sweep32k_full(ops, tau, family):
     _prefill_full(ops, "sweep32k", tau, qblocks=(0, 77, 255), ktiles=(0, 300, 510, 511), family=family)
 
