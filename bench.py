@@ -550,6 +550,10 @@ def micro(torch):
     return res
 
 
+# timed repetitions of the shapes below 128K (at least; --steps raises it)
+SMALL_REPS = 10
+
+
 def sweep32k(torch, ops, steps, warmup):
     """32K tau sweep (B1 H8 L32768 d128 bf16): fwd/bwd ms, dense-equivalent
     TFLOP/s and kept-tile fractions at tau in {0, 0.5, 1, 2}, for the planted
@@ -583,7 +587,7 @@ def sweep32k(torch, ops, steps, warmup):
                 ops.fwd_into(q, k, v, o, lse, tau, tile)
                 ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
             tfs, tbs = [], []
-            for _ in range(steps):
+            for _ in range(max(SMALL_REPS, steps)):
                 ev[0].record()
                 ops.fwd_into(q, k, v, o, lse, tau, tile)
                 ev[1].record()
@@ -724,7 +728,7 @@ def gqa_8k(torch, ops, tau, steps):
     ws = ops.bwd_workspace(q, tile)
     out = {"workload": "gqa8k (B1 H8 Hkv2 L8192 d128 bf16, 128x64 tiles, planted)"}
     for t in (tau, 0.0):
-        ms = kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, t, steps)
+        ms = kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, t, max(SMALL_REPS, steps))
         st = ops.prefill_stats_buffers(*q.shape[:3], tile, q.device)
         ops.fwd_into(q, k, v, o, lse, t, tile, stats=st)
         torch.cuda.synchronize()
@@ -862,7 +866,7 @@ def matched_work_8k(torch, ops, steps):
     torch.cuda.synchronize()
     n_legal = B * H * legal_tiles(L, *tile)
     ws = ops.bwd_workspace(q, tile)
-    ms = kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, tau, steps)
+    ms = kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, tau, max(SMALL_REPS, steps))
     nt = -(-L // w.bk)
     keep = ops.bits_to_keep(st["keep_bits"], nt)[0]
     og = o.float().cpu().numpy()[0]
