@@ -262,8 +262,8 @@ def main():
                            "work_per_launch": work, "per_unit": per_unit}
     roofline = rooflines[max(rooflines, key=lambda n: rooflines[n]["ms"])]
 
-    seeded = None if args.no_tau0 else decode_seeded_128k(torch, ops, qd, kc, vc, od, lsed, ws_d, wd, args.tau,
-                                                             args.steps, ms["dec"])
+    dec_var = None if args.no_tau0 else decode_variants_128k(torch, ops, qd, kc, vc, od, lsed, ws_d, wd, args.tau,
+                                                                args.steps)
     chunk = None if args.no_tau0 else chunked_prefill(torch, ops, q, k, v, args.tau, args.steps)
     sweep = None if args.no_sweep else sweep32k(torch, ops, args.steps, args.warmup)
     gqa = None if args.no_sweep else gqa_8k(torch, ops, args.tau, args.steps)
@@ -299,7 +299,7 @@ def main():
         "kernel_rooflines": rooflines,
         "sweep32k": sweep,
         "matched_work_8k": matched,
-        "decode_seeded": seeded,
+        "decode_variants": dec_var,
         "chunked_prefill": chunk,
         "gqa8k": gqa,
         "cpu_baseline": cpu,
@@ -660,30 +660,53 @@ def profile_op(torch, ops, op, workload, tau, iters):
             "ms": {nm: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, nm in enumerate(names)}}
 
 
-def decode_seeded_128k(torch, ops, qd, kc, vc, od, lsed, ws, wd, tau, steps, plain_ms):
-    """The decode128k shape with seeded partitions (mala_decode_seeded) at tau
-    and at tau=0: ms per call (events the library records around its
-    launches), kept-tile fraction, and HBM bytes of K (always) plus V of the
-    kept tiles per ms."""
-    Lk, split, bk = wd.L, wd.split_keys, wd.bk
-    out = {"workload": "decode128k (B16 Hq32 Hkv8 Lk131073 d128), partitions of 4096 keys counted back from "
-                       "the newest tile", "plain_decode_ms": plain_ms}
-    for t in (tau, 0.0):
-        st = ops.decode_stats_buffers(wd.B, wd.Hkv, Lk, split, bk, qd.device)
-        ops.decode_into(qd, kc, vc, Lk, od, lsed, t, ws, split, bk, stats=st, seeded=True)
+def decode_variants_128k(torch, ops, qd, kc, vc, od, lsed, ws, wd, tau, steps, warmup=3):
+    """Every decode variant on the decode128k shape, timed back to back in
+    this function after warm-up calls of each: plain and seeded partitions
+    (mala_decode, mala_decode_seeded), each with the whole KV group voting
+    (rows_per_vote = G) and with one vote per query head (rows_per_vote = 1)
+    at tau, and both at tau = 0.  Per variant: ms per call (the library's
+    events around its launches), the fraction of (vote group, tile) pairs
+    kept, the fraction of tiles whose V is read (a tile is read when a vote
+    group of its KV head keeps it) and the algorithmic HBM rate (K always, V
+    of the read tiles)."""
+    Lk, split, bk, G = wd.L, wd.split_keys, wd.bk, wd.group
+    out = {"workload": "decode128k (B16 Hq32 Hkv8 Lk131073 d128, split 4096); seeded partitions are counted "
+                       "back from the newest tile",
+           "note": "timed back to back, 3 warm-up calls per variant; the step's own decode runs between the "
+                   "backward and the next forward"}
+
+    def one(seeded, rpv, t):
+        vg = G // rpv
+        kw = dict(seeded=seeded, rows_per_vote=rpv)
+        st = ops.decode_stats_buffers(wd.B, wd.Hkv, Lk, split, bk, qd.device, vote_groups=vg)
+        ops.decode_into(qd, kc, vc, Lk, od, lsed, t, ws, split, bk, stats=st, **kw)
         torch.cuda.synchronize()
         kept, legal = int(st["kept"].sum()), int(st["legal"].sum())
+        bits = st["keep_bits"].cpu().numpy().astype(np.uint32)  # [B, Hkv * vg, nsplit, words]
+        union = np.bitwise_or.reduce(bits.reshape(wd.B, wd.Hkv, vg, *bits.shape[2:]), axis=2)
+        v_frac = int(sum(bin(int(x)).count("1") for x in union.ravel())) / (legal // vg)
+        for _ in range(warmup):
+            ops.decode_into(qd, kc, vc, Lk, od, lsed, t, ws, split, bk, **kw)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         for e in evs:
-            ops.decode_into(qd, kc, vc, Lk, od, lsed, t, ws, split, bk, stats={"events": e}, seeded=True)
+            ops.decode_into(qd, kc, vc, Lk, od, lsed, t, ws, split, bk, stats={"events": e}, **kw)
         torch.cuda.synchronize()
         ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
-        nbytes = wd.B * wd.Hkv * Lk * wd.d * 2 * (1.0 + kept / legal)
-        out[f"tau={t}"] = {"ms": ms, "kept_frac": kept / legal, "kept_tiles": kept, "legal_tiles": legal,
-                           "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9}
-    out["speedup_vs_plain_decode"] = plain_ms / out[f"tau={tau}"]["ms"]
-    out["speedup_vs_tau0"] = out["tau=0.0"]["ms"] / out[f"tau={tau}"]["ms"]
-    log("decode seeded: " + json.dumps(out))
+        nbytes = wd.B * wd.Hkv * Lk * wd.d * 2 * (1.0 + v_frac)
+        return {"ms": ms, "kept_frac_vote_tiles": kept / legal, "v_read_frac": v_frac,
+                "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9}
+
+    for seeded in (False, True):
+        name = "seeded" if seeded else "plain"
+        for rpv in (G, 1):
+            out[f"{name}, tau={tau}, rows_per_vote={rpv}"] = one(seeded, rpv, tau)
+        out[f"{name}, tau=0.0"] = one(seeded, G, 0.0)
+    grp = f"rows_per_vote={G}"
+    out["seeded_vs_plain"] = out[f"plain, tau={tau}, {grp}"]["ms"] / out[f"seeded, tau={tau}, {grp}"]["ms"]
+    out["seeded_vs_tau0"] = out["plain, tau=0.0"]["ms"] / out[f"seeded, tau={tau}, {grp}"]["ms"]
+    out["plain_vs_tau0"] = out["plain, tau=0.0"]["ms"] / out[f"plain, tau={tau}, {grp}"]["ms"]
+    log("decode variants: " + json.dumps(out))
     return out
 
 

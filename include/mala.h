@@ -81,8 +81,10 @@ typedef struct {
  *   kept      int32 [B, H, nqb]         tiles kept per query block
  *   legal     int32 [B, H, nqb]         legal (tested) tiles per query block
  *   keep_bits uint32 [B, H, nqb, words] bit (t % 32) of word t/32 = tile t kept
- * Decode, nsplit = ceil(Lk/split_keys), tps = split_keys/bk, words = ceil(tps/32):
- *   kept, legal int32 [B, Hkv, nsplit];  keep_bits uint32 [B, Hkv, nsplit, words],
+ * Decode, nsplit = ceil(Lk/split_keys), tps = split_keys/bk, words = ceil(tps/32),
+ * V = Hkv * G/rows_per_vote vote groups per sequence ([B, Hkv, nsplit] when a
+ * whole KV group votes together):
+ *   kept, legal int32 [B, V, nsplit];  keep_bits uint32 [B, V, nsplit, words],
  *   bit t = tile t of the partition (tile 0 starts at the partition start).
  *   keep_bits_dkdv uint32 [B, H, nqb, words], mala_bwd only: the tiles the
  *             dK/dV pass actually processed (the dQ pass writes keep_bits and
@@ -190,14 +192,23 @@ size_t mala_decode_workspace_size(int B, int Hq, int Hkv, int Lk, int d, int spl
  * lse: float [B, Hq] or NULL.  Query head h uses KV head h / (Hq/Hkv).
  * Split-KV: keys are cut into partitions [p*split_keys, min((p+1)*split_keys, Lk));
  * each partition is cut into bk-key tiles from its start and visited last tile
- * first with its own running state (so its first visited tile is kept); the
- * G = Hq/Hkv query heads of a KV group vote together (the rows that share one
- * K/V tile); Lq = Lk.  Partition states are merged exactly.
+ * first with its own running state (so its first visited tile is kept); Lq =
+ * Lk.  Partition states are merged exactly.
+ * Votes: the G = Hq/Hkv query heads of a KV group share every K/V tile load
+ * and vote in groups of rows_per_vote consecutive heads (0 means G: the whole
+ * group votes together, so a skipped tile saves its V read; 1: every query
+ * head votes alone).  A tile is kept for a vote group iff one of its heads
+ * votes keep; only the heads of a group that keeps it update their state, and
+ * V is read iff some group keeps it.  rows_per_vote must divide G
+ * (MALA_ERR_INVALID_ARG otherwise).
+ * Statistics are per vote group: kept, legal [B, Hkv * G/rows_per_vote,
+ * nsplit] and keep_bits [B, Hkv * G/rows_per_vote, nsplit, ceil(split_keys /
+ * bk / 32)], group j of KV head g at index g * (G/rows_per_vote) + j.
  * workspace: at least mala_decode_workspace_size(...) bytes, 256-byte aligned.
  */
 mala_status mala_decode(const void* q, const void* kcache, const void* vcache,
                         int B, int Hq, int Hkv, int Lk, int Lcap, int d, mala_dtype dtype,
-                        float tau, int split_keys, int bk, float scale,
+                        float tau, int split_keys, int bk, int rows_per_vote, float scale,
                         void* o, float* lse, mala_stats* stats,
                         void* workspace, size_t workspace_bytes, void* stream);
 
@@ -223,7 +234,7 @@ mala_status mala_decode(const void* q, const void* kcache, const void* vcache,
  */
 mala_status mala_decode_seeded(const void* q, const void* kcache, const void* vcache,
                                int B, int Hq, int Hkv, int Lk, int Lcap, int d, mala_dtype dtype,
-                               float tau, int split_keys, int bk, float scale,
+                               float tau, int split_keys, int bk, int rows_per_vote, float scale,
                                void* o, float* lse, mala_stats* stats,
                                void* workspace, size_t workspace_bytes, void* stream);
 

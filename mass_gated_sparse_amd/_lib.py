@@ -56,7 +56,7 @@ def load(path=None):
     lib.mala_bwd.restype = i
     lib.mala_decode_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.mala_decode_workspace_size.restype = sz
-    lib.mala_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, i, f, vp, vp, sp, vp, sz, vp]
+    lib.mala_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, f, vp, vp, sp, vp, sz, vp]
     lib.mala_decode.restype = i
     lib.mala_decode_seeded.argtypes = lib.mala_decode.argtypes
     lib.mala_decode_seeded.restype = i

@@ -66,7 +66,7 @@ mala_status check_prefill(const void* q, const void* k, const void* v, int B, in
 
 extern "C" {
 
-int mala_version(void) { return 100; }
+int mala_version(void) { return 101; }
 
 const char* mala_status_string(mala_status s) {
     switch (s) {
@@ -202,8 +202,8 @@ size_t mala_decode_workspace_size(int B, int Hq, int Hkv, int Lk, int d, int spl
 
 static mala_status decode_call(const char* name, bool seeded, const void* q, const void* kcache, const void* vcache,
                                int B, int Hq, int Hkv, int Lk, int Lcap, int d, mala_dtype dtype, float tau,
-                               int split_keys, int bk, float scale, void* o, float* lse, mala_stats* stats,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               int split_keys, int bk, int rows_per_vote, float scale, void* o, float* lse,
+                               mala_stats* stats, void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     if (!q || !kcache || !vcache || !o) return fail(MALA_ERR_INVALID_ARG, "null pointer");
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || d <= 0 || split_keys <= 0 || bk <= 0)
@@ -216,6 +216,9 @@ static mala_status decode_call(const char* name, bool seeded, const void* q, con
     if (dtype != MALA_BF16 || d != 128 || bk != 64 || G > 8 || split_keys % bk)
         return fail(MALA_ERR_UNSUPPORTED, "unsupported decode instantiation dtype=%d d=%d bk=%d G=%d split=%d",
                     int(dtype), d, bk, G, split_keys);
+    if (rows_per_vote == 0) rows_per_vote = G;
+    if (rows_per_vote < 0 || G % rows_per_vote)
+        return fail(MALA_ERR_INVALID_ARG, "rows_per_vote (%d) must divide Hq/Hkv (%d)", rows_per_vote, G);
     const size_t need = mala_decode_workspace_size(B, Hq, Hkv, Lk, d, split_keys);
     if (!workspace || workspace_bytes < need)
         return fail(MALA_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
@@ -231,6 +234,7 @@ static mala_status decode_call(const char* name, bool seeded, const void* q, con
     a.tps = split_keys / bk;
     a.words = int(cdiv(a.tps, 32));
     a.seeded = seeded;
+    a.rpv = rows_per_vote;
     const float sc = eff_scale(scale, d);
     a.scale_log2 = sc * mala::kLog2e;
     a.log2_tau = log2_tau_of(tau);
@@ -246,18 +250,19 @@ static mala_status decode_call(const char* name, bool seeded, const void* q, con
 }
 
 mala_status mala_decode(const void* q, const void* kcache, const void* vcache, int B, int Hq, int Hkv, int Lk,
-                        int Lcap, int d, mala_dtype dtype, float tau, int split_keys, int bk, float scale, void* o,
-                        float* lse, mala_stats* stats, void* workspace, size_t workspace_bytes, void* stream) {
+                        int Lcap, int d, mala_dtype dtype, float tau, int split_keys, int bk, int rows_per_vote,
+                        float scale, void* o, float* lse, mala_stats* stats, void* workspace,
+                        size_t workspace_bytes, void* stream) {
     return decode_call("mala_decode launch", false, q, kcache, vcache, B, Hq, Hkv, Lk, Lcap, d, dtype, tau,
-                       split_keys, bk, scale, o, lse, stats, workspace, workspace_bytes, stream);
+                       split_keys, bk, rows_per_vote, scale, o, lse, stats, workspace, workspace_bytes, stream);
 }
 
 mala_status mala_decode_seeded(const void* q, const void* kcache, const void* vcache, int B, int Hq, int Hkv,
                                int Lk, int Lcap, int d, mala_dtype dtype, float tau, int split_keys, int bk,
-                               float scale, void* o, float* lse, mala_stats* stats, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               int rows_per_vote, float scale, void* o, float* lse, mala_stats* stats,
+                               void* workspace, size_t workspace_bytes, void* stream) {
     return decode_call("mala_decode_seeded launch", true, q, kcache, vcache, B, Hq, Hkv, Lk, Lcap, d, dtype, tau,
-                       split_keys, bk, scale, o, lse, stats, workspace, workspace_bytes, stream);
+                       split_keys, bk, rows_per_vote, scale, o, lse, stats, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -9,8 +9,12 @@
 // QK; a skipped tile saves its V read, so decode is bound by cache traffic.
 //
 // One workgroup (4 waves) per (sequence, KV head, partition).  The G query
-// heads sharing the KV head are the rows of the vote: they share every K/V
-// tile load, so a skipped tile really saves the V bytes.  The kernel is
+// heads sharing the KV head are the rows of the workgroup; they share every
+// K/V tile load.  Votes run over groups of rpv consecutive rows (rpv = G: the
+// whole group, so a skipped tile really saves the V bytes; rpv = 1: one vote
+// per query head).  A tile is kept for a vote group iff one of its rows votes
+// keep; only that group's rows update their state, and V is read iff some
+// group keeps the tile.  The kernel is
 // HBM-bound: K tiles are prefetched one tile ahead into registers; V is read
 // only for kept tiles.
 //
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     float* __restrict__ part, int Hq, int Hkv, int Lk, int Lcap, int split_keys, int nsplit, int tps, int words,
     float scale_log2, float log2_tau, float log2_lq, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
-    uint32_t* __restrict__ bits, int pbase, int seeded_grid) {
+    uint32_t* __restrict__ bits, int pbase, int seeded_grid, int rpv) {
     constexpr int D = 128, BK = 64;
     __shared__ int vote_sm[2][4];
     __shared__ float wmax_sm[2][4][G];
@@ -79,6 +83,11 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
         k1 = min(k0 + split_keys, Lk);
     }
     const int nt = (k1 - k0 + BK - 1) / BK;
+    // vote groups: row r belongs to group r / rpv; gm[r] = bits of its group's rows
+    const int nvg = G / rpv;
+    uint32_t gm[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) gm[r] = ((1u << rpv) - 1u) << (r / rpv * rpv);
 
     // score mapping
     const int skey = tid >> 2, quarter = tid & 3;
@@ -122,10 +131,12 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
         for (int c = 0; c < 4; ++c) kr[c] = key < k1 ? *reinterpret_cast<const u32x4*>(src + 8 * c) : z4;
     };
 
+    // statistics of vote group tid (threads 0 .. nvg-1), at unit (bg*nvg + tid, p)
+    const long sidx = (long(bg) * nvg + tid) * nsplit + p;
     int nkept = 0;
     uint32_t word = 0;
-    if (STATS && bits && tid == 0)
-        for (int w = ((nt - 1) >> 5) + 1; w < words; ++w) bits[(long(bg) * nsplit + p) * words + w] = 0u;
+    if (STATS && bits && tid < nvg)
+        for (int w = ((nt - 1) >> 5) + 1; w < words; ++w) bits[sidx * words + w] = 0u;
 
     u32x4 vn[4] = {z4, z4, z4, z4};  // PREV: V of the next tile to visit
     auto load_v = [&](int t, u32x4* dst) {
@@ -173,32 +184,37 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
             for (int m = 4; m <= 32; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
             mx[r] = x;
         }
-        bool keep = true;
+        uint32_t rk = (1u << G) - 1u;  // rows whose vote group keeps the tile
         if (GATED) {
-            bool wv = false;
+            uint32_t vm = 0;  // rows of this wave's keys that vote keep
 #pragma unroll
             for (int r = 0; r < G; ++r) {
                 const float lz = SEED ? ltest[r] : lsum[r];
                 const float thr = (lz == 0.f) ? -FLT_MAX : (m2[r] + fast_log2(lz) + log2_tau - log2_lq) / scale_log2;
-                wv |= mx[r] >= thr;
+                if (mx[r] >= thr) vm |= 1u << r;
             }
             if (lane == 0) {
-                vote_sm[par][wave] = wv ? 1 : 0;
+                vote_sm[par][wave] = int(vm);
 #pragma unroll
                 for (int r = 0; r < G; ++r) wmax_sm[par][wave][r] = mx[r];
             }
             __syncthreads();
-            keep = (vote_sm[par][0] | vote_sm[par][1] | vote_sm[par][2] | vote_sm[par][3]) != 0;
+            const uint32_t rv = uint32_t(vote_sm[par][0] | vote_sm[par][1] | vote_sm[par][2] | vote_sm[par][3]);
+            rk = 0;
+#pragma unroll
+            for (int r = 0; r < G; ++r)
+                if (rv & gm[r]) rk |= 1u << r;
         }
-        if (STATS && tid == 0) {
-            nkept += keep;
-            if (keep) word |= 1u << (t & 31);
+        if (STATS && tid < nvg) {
+            const bool gk = (rk >> (tid * rpv)) & 1u;
+            nkept += gk;
+            if (gk) word |= 1u << (t & 31);
             if (bits && (t & 31) == 0) {
-                bits[(long(bg) * nsplit + p) * words + (t >> 5)] = word;
+                bits[sidx * words + (t >> 5)] = word;
                 word = 0;
             }
         }
-        if (!keep) continue;
+        if (rk == 0) continue;
 
         // V loads for this tile (consumed after the normalizer update)
         u32x4 vr[4];
@@ -214,16 +230,17 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
                 for (int r = 0; r < G; ++r) wmax_sm[par][wave][r] = mx[r];
             __syncthreads();
         }
-        float mref[G], alpha[G];
+        float alpha[G];
 #pragma unroll
         for (int r = 0; r < G; ++r) {
+            // a row whose group skips the tile keeps its state: alpha = 1, no probability
+            const bool rkeep = (rk >> r) & 1u;
             const float tm = fmaxf(fmaxf(wmax_sm[par][0][r], wmax_sm[par][1][r]),
                                    fmaxf(wmax_sm[par][2][r], wmax_sm[par][3][r]));
-            const float mn = fmaxf(m2[r], tm * scale_log2);
-            mref[r] = mn;  // finite: every tile holds at least one valid key
-            alpha[r] = fast_exp2(m2[r] - mn);
+            const float mn = rkeep ? fmaxf(m2[r], tm * scale_log2) : m2[r];  // kept: finite (a valid key)
+            alpha[r] = rkeep ? fast_exp2(m2[r] - mn) : 1.f;
             m2[r] = mn;
-            const float pv = fast_exp2(fmaf(s[r], scale_log2, -mn));  // -inf (invalid key) gives 0
+            const float pv = rkeep ? fast_exp2(fmaf(s[r], scale_log2, -mn)) : 0.f;  // invalid key (-inf): 0
             float ps = (quarter == 0) ? pv : 0.f;
 #pragma unroll
             for (int m = 4; m <= 32; m <<= 1) ps += __shfl_xor(ps, m, 64);
@@ -255,7 +272,6 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
                 for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(pw, vf[c], acc[r][c]);
             }
         }
-        (void)mref;
         // (no barrier here: the next tile writes the other parity's buffers, and
         // this parity's again only after the next tile's own barrier, which
         // every thread reaches after its reads here)
@@ -276,9 +292,9 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
         dst[2 + dd] = x;
         if (dd == 0) { dst[0] = m2[r]; dst[1] = lsum[r]; }
     }
-    if (STATS && tid == 0) {
-        if (kept) kept[long(bg) * nsplit + p] = nkept;
-        if (legal) legal[long(bg) * nsplit + p] = nt;
+    if (STATS && tid < nvg) {
+        if (kept) kept[sidx] = nkept;
+        if (legal) legal[sidx] = nt;
     }
 }
 
@@ -306,7 +322,7 @@ static void launch_decode_one(const DecArgs& a, hipStream_t s, int nparts, int p
     hipLaunchKernelGGL((decode_split_bf16_d128<G, GT, ST, SD, PV>), dim3(nparts, a.B * a.Hkv), dim3(256), 0, s,
                        (const bf16_t*)a.q, (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.part, a.Hq, a.Hkv, a.Lk,
                        a.Lcap, a.split_keys, a.nsplit, a.tps, a.words, a.scale_log2, a.log2_tau, a.log2_lq, a.kept,
-                       a.legal, a.bits, pbase, a.seeded ? 1 : 0);
+                       a.legal, a.bits, pbase, a.seeded ? 1 : 0, a.rpv);
 }
 
 template <int G, bool ST>

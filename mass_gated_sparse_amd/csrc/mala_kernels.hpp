@@ -49,6 +49,7 @@ struct DecArgs {
     float scale_log2, log2_tau, log2_lq;
     bool gated;
     bool seeded;  // partitions counted back from the newest tile; older ones seeded with the newest's state
+    int rpv;      // query heads per vote (divides G)
     int32_t *kept, *legal;
     uint32_t* bits;
 };

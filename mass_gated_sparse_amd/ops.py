@@ -237,12 +237,23 @@ def mala_attention(q, k, v, tau=1.0, tile=None, scale=0.0):
     return _MalaAttention.apply(q.contiguous(), k.contiguous(), v.contiguous(), float(tau), tile, float(scale))
 
 
-def decode_stats_buffers(B, Hkv, Lk, split_keys, bk, device):
+def decode_stats_buffers(B, Hkv, Lk, split_keys, bk, device, vote_groups=1):
+    """Decode statistics for B sequences, Hkv KV heads and vote_groups vote
+    groups per KV head (G / rows_per_vote; 1 when the whole group votes)."""
     nsplit = -(-Lk // split_keys)
     words = -(-(split_keys // bk) // 32)
-    return {"kept": torch.zeros(B, Hkv, nsplit, dtype=torch.int32, device=device),
-            "legal": torch.zeros(B, Hkv, nsplit, dtype=torch.int32, device=device),
-            "keep_bits": torch.zeros(B, Hkv, nsplit, words, dtype=torch.int32, device=device)}
+    V = Hkv * vote_groups
+    return {"kept": torch.zeros(B, V, nsplit, dtype=torch.int32, device=device),
+            "legal": torch.zeros(B, V, nsplit, dtype=torch.int32, device=device),
+            "keep_bits": torch.zeros(B, V, nsplit, words, dtype=torch.int32, device=device)}
+
+
+def _vote_groups(Hq, Hkv, rows_per_vote):
+    """Vote groups per KV head, or None when rows_per_vote does not divide
+    G (the library rejects the call)."""
+    G = Hq // Hkv
+    R = int(rows_per_vote) or G
+    return G // R if R > 0 and G % R == 0 else None
 
 
 def decode_workspace(B, Hq, Hkv, Lk, d, split_keys, device):
@@ -251,39 +262,46 @@ def decode_workspace(B, Hq, Hkv, Lk, d, split_keys, device):
 
 
 def decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys=4096, bk=64, scale=0.0, stats=None, stream=None,
-                seeded=False):
+                seeded=False, rows_per_vote=0):
     """Queue mala_decode (or mala_decode_seeded): q [B,Hq,d], caches
     [B,Hkv,Lcap,d] with Lk valid rows; writes o (like q) and lse [B,Hq] (or
-    None); ws from decode_workspace."""
+    None); ws from decode_workspace.  rows_per_vote: query heads per vote
+    (0: the whole KV group)."""
     B, Hq, Hkv, Lcap, d = _expect_qkv(q, kc, vc, nq_dims=3)
     _expect(o, "o", q.shape, q.dtype)
     if lse is not None:
         _expect(lse, "lse", (B, Hq), torch.float32)
     if ws is None or ws.dtype != torch.uint8 or ws.dim() != 1:
         raise ValueError("ws must be a 1-D uint8 workspace (see decode_workspace)")
-    if stats is not None and int(split_keys) > 0 and int(bk) > 0:  # (bad sizes: the library rejects them)
+    vg = _vote_groups(Hq, Hkv, rows_per_vote)
+    if stats is not None and int(split_keys) > 0 and int(bk) > 0 and vg:  # (bad sizes: the library rejects them)
         nsplit, w = -(-int(Lk) // int(split_keys)), -(-(int(split_keys) // int(bk)) // 32)
-        _expect_stats(stats, {"kept": (B, Hkv, nsplit), "legal": (B, Hkv, nsplit), "keep_bits": (B, Hkv, nsplit, w)})
+        V = Hkv * vg
+        _expect_stats(stats, {"kept": (B, V, nsplit), "legal": (B, V, nsplit), "keep_bits": (B, V, nsplit, w)})
     _check_dev(q, kc, vc, o, ws, *([lse] if lse is not None else []))
     name = "mala_decode_seeded" if seeded else "mala_decode"
     rc = getattr(_lib.load(), name)(_ptr(q), _ptr(kc), _ptr(vc), B, Hq, Hkv, int(Lk), Lcap, d, _dt(q), float(tau),
-                                    int(split_keys), int(bk), float(scale), _ptr(o), _ptr(lse),
+                                    int(split_keys), int(bk), int(rows_per_vote), float(scale), _ptr(o), _ptr(lse),
                                     _stats_struct(stats), _ptr(ws), ws.numel(), _stream(stream))
     _lib.check(name, rc)
 
 
-def decode(q, kc, vc, Lk, tau, split_keys=4096, bk=64, scale=0.0, stats=False, seeded=False):
+def decode(q, kc, vc, Lk, tau, split_keys=4096, bk=64, scale=0.0, stats=False, seeded=False, rows_per_vote=0):
     """Split-KV MALA decode.  q [B,Hq,d], caches [B,Hkv,Lcap,d].  Returns (o, lse[, stats]).
     seeded=True runs mala_decode_seeded (partitions counted back from the
-    newest tile, the older ones tested against the newest one's state)."""
+    newest tile, the older ones tested against the newest one's state).
+    rows_per_vote: query heads per vote (0: the whole KV group votes)."""
     _check_dev(q, kc, vc)
     B, Hq, d = q.shape
     Hkv = kc.shape[1]
     o = torch.empty_like(q)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
     ws = decode_workspace(B, Hq, Hkv, Lk, d, split_keys, q.device)
-    st = decode_stats_buffers(B, Hkv, Lk, split_keys, bk, q.device) if stats else None
-    decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys, bk, scale, st, seeded=seeded)
+    st = None
+    if stats:
+        st = decode_stats_buffers(B, Hkv, Lk, split_keys, bk, q.device, _vote_groups(Hq, Hkv, rows_per_vote) or 1)
+    decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys, bk, scale, st, seeded=seeded,
+                rows_per_vote=rows_per_vote)
     return (o, lse, st) if stats else (o, lse)
 
 

@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mala_version() == 100
+    assert lib.mala_version() == 101
     assert lib.mala_status_string(OK) == b"ok"
     assert lib.mala_status_string(INVALID) == b"invalid argument"
     assert lib.mala_status_string(UNSUPPORTED) == b"unsupported configuration"
@@ -146,10 +146,10 @@ def test_bwd_rejects(lib, kw, status, msg):
     assert msg in lib.mala_last_error().decode()
 
 
-def dec(lib, q=P, B=2, Hq=8, Hkv=2, Lk=5000, Lcap=8192, d=128, dt=0, tau=1.0, split=4096, bk=64,
+def dec(lib, q=P, B=2, Hq=8, Hkv=2, Lk=5000, Lcap=8192, d=128, dt=0, tau=1.0, split=4096, bk=64, rpv=0,
         ws=ALIGNED_WS, ws_bytes=1 << 30, fn="mala_decode"):
-    return getattr(lib, fn)(q, P, P, B, Hq, Hkv, Lk, Lcap, d, dt, tau, split, bk, 0.0, P, P, None, ws, ws_bytes,
-                            None)
+    return getattr(lib, fn)(q, P, P, B, Hq, Hkv, Lk, Lcap, d, dt, tau, split, bk, rpv, 0.0, P, P, None, ws,
+                            ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -166,6 +166,9 @@ def dec(lib, q=P, B=2, Hq=8, Hkv=2, Lk=5000, Lcap=8192, d=128, dt=0, tau=1.0, sp
     ({"split": 4000}, UNSUPPORTED, "instantiation"),      # not a multiple of 64
     ({"ws_bytes": 64}, INVALID, "workspace too small"),
     ({"ws": MISALIGNED_WS}, INVALID, "aligned"),
+    ({"rpv": 3}, INVALID, "rows_per_vote"),                # does not divide G = 4
+    ({"rpv": -1}, INVALID, "rows_per_vote"),
+    ({"rpv": 8}, INVALID, "rows_per_vote"),
 ])
 @pytest.mark.parametrize("fn", ["mala_decode", "mala_decode_seeded"])
 def test_decode_rejects(lib, kw, status, msg, fn):
@@ -224,6 +227,10 @@ def test_python_wrappers_check_shapes_before_the_device():
         (lambda: ops.decode_into(z(2, 8, 128), z(2, 2, 512, 128), z(2, 2, 512, 128), 500, z(2, 8, 128),
                                  z(2, 8, dt=torch.float32), 1.0, z(4096, dt=torch.uint8), split_keys=128,
                                  stats={"keep_bits": z(2, 2, 1, 1, dt=torch.int32)}), "keep_bits"),
+        # one vote per query head: statistics are per head (8), not per KV head (2)
+        (lambda: ops.decode_into(z(2, 8, 128), z(2, 2, 512, 128), z(2, 2, 512, 128), 500, z(2, 8, 128),
+                                 z(2, 8, dt=torch.float32), 1.0, z(4096, dt=torch.uint8), split_keys=128,
+                                 rows_per_vote=1, stats={"kept": z(2, 2, 4, dt=torch.int32)}), "kept"),
     ]
     for fn, msg in cases:
         with pytest.raises(ValueError, match=msg):

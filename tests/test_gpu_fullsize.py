@@ -164,6 +164,50 @@ def test_decode128k_seeded_full(ops, tau):
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
 
 
+@pytest.mark.parametrize("seeded", [False, True])
+def test_decode128k_per_head_votes_full(ops, seeded):
+    """The full decode shape with one vote per query head (rows_per_vote = 1),
+    tau = 1, plain and seeded: sampled (sequence, KV head) groups against the
+    oracle with the same vote groups."""
+    w = WORKLOADS["decode128k"]
+    x = decode_inputs(w, threads=16)
+    q, kc, vc = (_dev(x[n]) for n in ("q", "k", "v"))
+    o, lse, st = ops.decode(q, kc, vc, w.L, 1.0, split_keys=w.split_keys, bk=w.bk, stats=True, seeded=seeded,
+                            rows_per_vote=1)
+    torch.cuda.synchronize()
+    G = w.group
+    if seeded:
+        nsplit, tps = oracle.seeded_decode_shapes(w.L, w.split_keys, w.bk)
+        jd = (w.L - 1) // w.bk
+        legal = np.zeros((nsplit, tps), bool)
+        for p in range(nsplit):
+            hi = jd - p * tps
+            legal[p, : hi - max(0, hi - tps + 1) + 1] = True
+        ref = oracle.decode_seeded
+    else:
+        nsplit, tps = -(-w.L // w.split_keys), w.split_keys // w.bk
+        legal = np.zeros((nsplit, tps), bool)
+        for p in range(nsplit):
+            legal[p, : -(-(min((p + 1) * w.split_keys, w.L) - p * w.split_keys) // w.bk)] = True
+        ref = oracle.decode
+    gk = ops.bits_to_keep(st["keep_bits"], tps)  # [B, Hq, nsplit, tps]: one vote group per query head
+    assert gk.shape == (w.B, w.H, nsplit, tps)
+    og, lg = bf16_to_f64(o), lse.cpu().numpy()
+    for b, g in [(0, 0), (9, 5), (15, 7)]:
+        hs = slice(g * G, (g + 1) * G)
+        qs = to_f64(x["q"][b:b + 1, hs], "bf16")
+        ks = to_f64(x["k"][b:b + 1, g:g + 1], "bf16")
+        vs = to_f64(x["v"][b:b + 1, g:g + 1], "bf16")
+        oo, ol, ok, oT = ref(qs, ks, vs, w.L, 1.0, w.split_keys, w.bk, rows_per_vote=1,
+                             replay=gk[b:b + 1, hs][:, None], band=BAND)
+        bad, near, _ = decision_report(gk[b, hs], ok[0, 0], oT[0, 0], legal)
+        assert bad == 0
+        assert rel_l2(og[b, hs], oo[0]) <= TOL_O
+        assert np.abs(lg[b, hs] - ol[0]).max() <= 1e-3
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+    assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+
+
 def test_chunk16k_full(ops):
     """Chunked prefill in the bench's configuration: the last 16,384 rows of
     the 128K training shape as one chunk at key offset 114,688 against the

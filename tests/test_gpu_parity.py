@@ -337,6 +337,59 @@ def test_decode_groups_bf16(ops, Hq, Hkv, Lk, split, tau, seeded):
     assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
 
 
+@pytest.mark.parametrize("Hq,Hkv,rpv", [(32, 8, 1), (32, 8, 2), (16, 2, 1), (16, 2, 4)])
+@pytest.mark.parametrize("Lk,split", [(3000, 1024), (4097, 4096)])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 16.0, math.inf])
+@pytest.mark.parametrize("seeded", [False, True])
+def test_decode_rows_per_vote_bf16(ops, Hq, Hkv, rpv, Lk, split, tau, seeded):
+    """Votes over rows_per_vote query heads of a KV group (one vote per head
+    when 1), plain and seeded, against the oracle with the same vote groups:
+    decisions and kept counts per vote group, O and lse."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["decode128k"], B=2, H=Hq, Hkv=Hkv)
+    x = decode_inputs(w, Lk=Lk)
+    q, kc, vc = _dev_tensors(x, "bf16", ("q", "k", "v"))
+    o, lse, st = ops.decode(q, kc, vc, Lk, tau, split_keys=split, bk=64, stats=True, seeded=seeded,
+                            rows_per_vote=rpv)
+    torch.cuda.synchronize()
+    qf, kf, vf = (to_f64(x[n], "bf16") for n in ("q", "k", "v"))
+    if seeded:
+        nsplit, tps = oracle.seeded_decode_shapes(Lk, split, 64)
+        legal = seeded_legal(Lk, split)
+        ref = oracle.decode_seeded
+    else:
+        nsplit, tps = -(-Lk // split), split // 64
+        legal = np.zeros((nsplit, tps), bool)
+        for p in range(nsplit):
+            legal[p, : -(-(min((p + 1) * split, Lk) - p * split) // 64)] = True
+        ref = oracle.decode
+    vg = (Hq // Hkv) // rpv
+    gk = ops.bits_to_keep(st["keep_bits"], tps)  # [B, Hkv * vg, nsplit, tps]
+    assert gk.shape == (2, Hkv * vg, nsplit, tps)
+    oo, ol, ok, oT = ref(qf, kf, vf, Lk, tau, split, 64, rows_per_vote=rpv,
+                         replay=gk.reshape(2, Hkv, vg, nsplit, tps), band=BAND)
+    ok, oT = ok.reshape(gk.shape), oT.reshape(gk.shape)
+    bad, near, _ = decision_report(gk, ok, oT, legal)
+    assert bad == 0
+    assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+    assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+    assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
+    assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+
+
+@pytest.mark.parametrize("seeded", [False, True])
+def test_decode_rows_per_vote_g_is_default(ops, seeded):
+    """rows_per_vote = G is the default whole-group vote, bit for bit."""
+    w, x = _decode_case(5000, (0, 1))
+    q, kc, vc = _dev_tensors(x, "bf16", ("q", "k", "v"))
+    a = ops.decode(q, kc, vc, 5000, 1.0, split_keys=1024, stats=True, seeded=seeded)
+    b = ops.decode(q, kc, vc, 5000, 1.0, split_keys=1024, stats=True, seeded=seeded, rows_per_vote=w.group)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for n in ("kept", "legal", "keep_bits"):
+        assert torch.equal(a[2][n], b[2][n]), n
+
+
 def test_invalid_arguments_rejected(ops):
     from mass_gated_sparse_amd._lib import MalaError
     q = torch.zeros(1, 1, 128, 128, dtype=torch.bfloat16, device="cuda")
