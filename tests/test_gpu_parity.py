@@ -338,7 +338,7 @@ def test_decode_groups_bf16(ops, Hq, Hkv, Lk, split, tau, seeded):
 
 
 @pytest.mark.parametrize("Hq,Hkv,rpv", [(32, 8, 1), (32, 8, 2), (16, 2, 1), (16, 2, 4)])
-@pytest.mark.parametrize("Lk,split", [(3000, 1024), (4097, 4096)])
+@pytest.mark.parametrize("Lk,split", [(3000, 1024), (4097, 4096), (65, 64), (1, 64)])
 @pytest.mark.parametrize("tau", [0.0, 1.0, 16.0, math.inf])
 @pytest.mark.parametrize("seeded", [False, True])
 def test_decode_rows_per_vote_bf16(ops, Hq, Hkv, rpv, Lk, split, tau, seeded):
