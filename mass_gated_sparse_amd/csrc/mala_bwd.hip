@@ -19,7 +19,7 @@
 //                S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K, B = Q);
 //                it tests every legal tile and writes the decision bits into
 //                the backward's workspace;
-//   dK/dV pass -- one workgroup per 64-key tile (8 waves), runs second and
+//   dK/dV pass -- one workgroup per pair of 64-key tiles (8 waves), runs second and
 //                visits only the query blocks those bits keep.
 // No mask passes from forward to backward: the bits are made and consumed
 // inside one mala_bwd call, from the final lse.
@@ -288,23 +288,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 }
 
 // ---------------------------------------------------------------------- dK/dV
-// One workgroup of 8 waves per 64-key tile: wave w owns keys 32(w&1) .. +31
-// of the tile and rows 32(w>>1) .. +31 of every query block, so two waves
-// share each SIMD.  K of the wave's keys is held in registers (B operand of
-// S = Q K^T); the V tile sits in LDS (B operand of dP = dO V^T).
+// One workgroup of 8 waves per pair of 64-key tiles (128 keys, tiles 2u and
+// 2u+1): wave w owns keys 32kq .. +31 of the pair, kq = 2(w>>2) + (w&1) (so
+// tile 2u + w/4), and rows 32((w>>1)&1) .. +31 of every 64-row half of a
+// query block; waves w and w+4 share a SIMD.  K of the wave's keys is held in registers (B operand of
+// S = Q K^T); the V tiles of the pair sit in LDS (B operand of dP = dO V^T).
 //
 // Decisions.  The dQ pass runs first and tests every tile against the final
 // lse; its decision bits reach this pass through the backward's workspace.
-// This pass visits only the kept query blocks of its key tile: a skipped
-// block costs no Q/dO load, no S and no post-score work, and both passes use
-// the same decisions by construction.
+// This pass visits the query blocks that keep at least one tile of its pair,
+// and within a block the waves of a skipped tile do nothing: a block skipped
+// by both tiles costs no Q/dO load, no S and no post-score work, and both
+// passes use the same decisions by construction.
 //
-// The Q and dO tiles of successive kept query blocks are double-buffered in
-// LDS: while one block is computed, the next streams into the other buffer
-// with direct global->LDS loads.  Each wave accumulates dK^T and dV^T over
-// its own 32 rows of every block; the four row quarters are summed through
-// LDS at the end.  Rows past L are read clamped to row L-1; their lse is
-// +inf there, so P = 0.
+// A query block is processed in two 64-row halves, so one 16 KiB half of Q
+// and of dO feeds 128 keys.  The halves of successive kept blocks are
+// double-buffered in LDS: while one is computed, the next streams into the
+// other buffer with direct global->LDS loads.  Each wave accumulates dK^T and
+// dV^T over its 32 rows of every half; the two row groups are summed through
+// LDS at the end.  Rows past L are read clamped to row L-1; their lse is +inf
+// there, so P = 0, and a half with no row below L is not visited.
 template <bool GATED>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -312,21 +315,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BHkv, int G, int L, int nqb, int words, float scale,
     float scale_log2, const uint32_t* __restrict__ dbits, uint32_t* __restrict__ aux_bits) {
     using namespace bwdk;
-    // buf[0..3]: Q and dO tiles of two query blocks (buf[0], buf[1] and
-    // buf[2], buf[3]); reused at the end for the cross-wave reduction.
-    __shared__ __attribute__((aligned(1024))) uint8_t buf[4][BQ * 256];
-    __shared__ __attribute__((aligned(1024))) uint8_t vtile[BK * 256];
-    __shared__ __attribute__((aligned(16))) float stA[2][BQ];  // lse2, D of the block's rows
-    __shared__ __attribute__((aligned(16))) float stB[2][BQ];
+    constexpr int HB = 64, KP = 2 * BK;  // rows per half block, keys per workgroup
+    // hbuf[0..3]: Q and dO halves of two work units (hbuf[0], hbuf[1] and
+    // hbuf[2], hbuf[3]); reused at the end for the cross-wave reduction.
+    __shared__ __attribute__((aligned(1024))) uint8_t hbuf[4][HB * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t vtile[KP * 256];
+    __shared__ __attribute__((aligned(16))) float stA[2][HB];  // lse2, D of the half's rows
+    __shared__ __attribute__((aligned(16))) float stB[2][HB];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
-    const int kb = wave & 1, rq = wave >> 1;
-    int t, bkv;  // 64-key tile (longest, t = 0, first) and K/V head; its query heads are bkv*G .. +G-1
-    balanced_item(int(blockIdx.x), BHkv, max(1, (2 * nqb) / 8), t, bkv);
+    const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, j = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it stay scalar
+    // waves w and w+4 share a SIMD and work on different tiles of the pair, so
+    // a block that keeps one tile still has a wave on every SIMD
+    const int tt = wave >> 2, kq = 2 * tt + (wave & 1), rh = (wave >> 1) & 1;
+    int u, bkv;  // tile pair (longest, u = 0, first) and K/V head; its query heads are bkv*G .. +G-1
+    balanced_item(int(blockIdx.x), BHkv, max(1, nqb / 8), u, bkv);
     const long kvoff = long(bkv) * L * D;
-    const int key = t * BK + 32 * kb + j;
+    const int key = u * KP + 32 * kq + j;
     const bool kvalid = key < L;
-    const int qb0 = (t * BK) / BQ;  // first query block that sees the tile (its diagonal block)
+    const int qb0 = u;  // the pair's diagonal block: the first query block that sees it
+    const bool t1 = 2 * u + 1 < (L + BK - 1) / BK;  // the pair's second tile exists
     const u32x4 z4 = {0u, 0u, 0u, 0u};
 
     // K of this wave's 32 keys as B operands (lane = key, 8 contiguous d)
@@ -340,94 +348,107 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dvacc[db][r] = 0.f; dkacc[db][r] = 0.f; }
 
-    // Direct loads of one 128x128 tile: 32 segments of 4 rows (1 KiB); wave w
-    // issues segments 4w..4w+3 (rows 16w .. 16w+15); lane l of a segment fills
+    // Direct loads of one 64x128 half: 16 segments of 4 rows (1 KiB); wave w
+    // issues segments 2w, 2w+1 (rows 8w .. 8w+7); lane l of a segment fills
     // physical chunk l%16 of row l/16, i.e. it reads the logical chunk that the
-    // swizzle puts there.  Rows past L read row L-1 instead (masked later).
-    auto tile_async = [&](const bf16_t* g, uint8_t* dst, int bh, int r0) {
-        const uint32_t la = lds_addr_of(dst) + 4096 * wave;
+    // swizzle puts there.  Rows past L read row L-1 instead (r0 < L always).
+    auto half_async = [&](const bf16_t* g, uint8_t* dst, int bh, int r0) {
+        const uint32_t la = lds_addr_of(dst) + 2048 * wave;
         const bf16_t* gb = g + long(bh) * L * D + long(r0) * D;  // wave-uniform
         const int lim = L - 1 - r0;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int rt = 16 * wave + 4 * it + (lane >> 4);
+        for (int it = 0; it < 2; ++it) {
+            const int rt = 8 * wave + 4 * it + (lane >> 4);
             const uint32_t off = uint32_t(min(rt, lim) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
             dma16s(gb, off, __builtin_amdgcn_readfirstlane(la + 1024 * it));
         }
     };
-    // Operand read offsets within a Q or dO tile, this wave's row quarter
-    // folded in: normal (row-major) reads of row 32rq + j, chunk 2s + hl, and
-    // the transposed reads of tr_operand_at (rowbase 32rq).
+    // Operand read offsets within a Q or dO half, this wave's row group folded
+    // in: normal (row-major) reads of row 32rh + j, chunk 2s + hl, and the
+    // transposed reads of tr_operand_at (rowbase 32rh).
     int qoff[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qoff[s] = swz(j, 2 * s + hl) + 8192 * rq;
+    for (int s = 0; s < 8; ++s) qoff[s] = swz(j, 2 * s + hl) + 8192 * rh;
     int troff[4][2];
     tr_offsets(lane, troff);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        troff[db][0] += 8192 * rq;
-        troff[db][1] += 8192 * rq;
+        troff[db][0] += 8192 * rh;
+        troff[db][1] += 8192 * rh;
     }
-    // Per-row state of a block, held by threads 0..127: loaded raw (row index
-    // clamped) into registers before the tile prefetch is issued, written to
-    // LDS (with the padding-row defaults) only at the end of the block, so
+    // Per-row state of a half, held by threads 0..63: loaded raw (row index
+    // clamped) into registers before the next half's loads are issued, written
+    // to LDS (with the padding-row defaults) only at the end of the unit, so
     // waiting for these loads never waits for the prefetch.
     float stv[2];
     int st_row = 0;
     auto stats_load = [&](int bh, int r0) {
-        if (tid < BQ) {
+        if (tid < HB) {
             st_row = r0 + tid;
             const long ri = long(bh) * L + min(st_row, L - 1);
             stv[0] = lse2[ri];
             stv[1] = Dv[ri];
         }
     };
-    auto stats_store = [&](float (*st)[BQ]) {
-        if (tid < BQ) {
+    auto stats_store = [&](float (*st)[HB]) {
+        if (tid < HB) {
             const bool ok = st_row < L;
             st[0][tid] = ok ? stv[0] : INFINITY;
             st[1][tid] = ok ? stv[1] : 0.f;
         }
     };
-    // this wave's 32 keys of V, addressed with the Q-tile offsets
-    const uint32_t va = lds_addr_of(vtile) + 8192 * kb - 8192 * rq;
+    // this wave's 32 keys of V, addressed with the Q-half offsets
+    const uint32_t va = lds_addr_of(vtile) + 8192 * kq - 8192 * rh;
 
-    // Work items are (query head of the group, kept query block), head by
-    // head.  Kept blocks of one head come 64 at a time: bit i of kmask is
-    // block wbase + i (every lane fetches one block's decision word, a ballot
-    // packs the bits); the next window's words are fetched one window ahead.
-    const uint32_t tbit = 1u << (t & 31);
+    // Work units are (query head of the group, kept query block, half),
+    // head by head.  Kept blocks of one head come 64 at a time: bit i of km0
+    // (km1) is block wbase + i keeping tile 2u (2u+1) -- every lane fetches
+    // one block's decision word, ballots pack the bits; the next window's words
+    // are fetched one window ahead.  Both tiles sit in one word.
+    const int w0 = (2 * u) >> 5;
+    const uint32_t bit0 = 1u << ((2 * u) & 31), bit1 = bit0 << 1;
     int ih = 0;  // query head within the group of the current window
     auto fetch = [&](int base) -> uint32_t {
         const int qb = base + lane;
-        return (GATED && qb < nqb) ? dbits[(long(bkv * G + ih) * nqb + qb) * words + (t >> 5)] : 0u;
+        return (GATED && qb < nqb) ? dbits[(long(bkv * G + ih) * nqb + qb) * words + w0] : 0u;
     };
     int wbase = qb0;
-    uint64_t kmask = 0;
+    uint64_t km0 = 0, km1 = 0;
     uint32_t wnext = 0;
+    auto load_window = [&](uint32_t w) {
+        km0 = __ballot((w & bit0) != 0u);
+        km1 = __ballot(t1 && (w & bit1) != 0u);
+    };
     auto open_head = [&]() {
         wbase = qb0;
         if (GATED) {
-            kmask = __ballot((fetch(qb0) & tbit) != 0u);
+            load_window(fetch(qb0));
             wnext = fetch(qb0 + 64);
         }
     };
-    // first kept block >= qb (qb >= wbase) of head ih, or nqb
+    // first block >= qb (qb >= wbase) of head ih keeping a tile of the pair, or nqb
     auto kept_from = [&](int qb) -> int {
         if (!GATED) return qb;
         for (;;) {
             const int sh = qb - wbase;
-            const uint64_t m = sh >= 64 ? 0ull : (kmask >> sh) << sh;
+            const uint64_t m = sh >= 64 ? 0ull : ((km0 | km1) >> sh) << sh;
             if (m) return wbase + __builtin_ctzll(m);
             if (wbase + 64 >= nqb) return nqb;
             wbase += 64;
             qb = max(qb, wbase);
-            kmask = __ballot((wnext & tbit) != 0u);
+            load_window(wnext);
             wnext = fetch(wbase + 64);
         }
     };
-    // the work item after (ih, qb): the next kept block of this head, else
-    // the first kept block of the next head with one (ih == G: done)
+    // which tiles of the pair block qb keeps (bit 0: tile 2u, bit 1: 2u+1);
+    // qb is in the current window
+    auto flags_of = [&](int qb) -> int {
+        if (!GATED) return t1 ? 3 : 1;
+        const int sh = qb - wbase;
+        return int((km0 >> sh) & 1ull) | (int((km1 >> sh) & 1ull) << 1);
+    };
+    // the block after (ih, qb) keeping a tile: the next one of this head, else
+    // the first one of the next head with one (ih == G: done)
     auto next_item = [&](int qb) -> int {
         int qn = kept_from(qb + 1);
         while (qn >= nqb && ih + 1 < G) {
@@ -439,22 +460,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
         return qn;
     };
 
-    // One kept query block, computed from (qs, os, st).  Only the diagonal
-    // block (qb == qb0) needs a visibility mask: it is the only block with
-    // keys past some row, and the only block of the last tiles, whose keys may
-    // run past L.  Elsewhere every key is visible to every row.
-    auto block = [&](auto diag_tag, int bh, int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ]) {
+    // One unit: half h of block qb, computed from (qs, os, st).  Only the
+    // diagonal block needs a visibility mask (keys past the row, including
+    // keys past L); in its first half the second tile's keys lie past every
+    // row, so those waves skip it.
+    auto unit = [&](auto diag_tag, int bh, int qb, int h, int fl, const uint8_t* qs, const uint8_t* os,
+                    const float (*st)[HB]) {
         constexpr bool diag = decltype(diag_tag)::value;
-        const int r0 = qb * BQ;
+        if (aux_bits && tid == 0 && h == 0)  // the tiles this pass visits (parity statistics)
+            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + w0], ((fl & 1) ? bit0 : 0u) | ((fl & 2) ? bit1 : 0u));
+        if (!((fl >> tt) & 1)) return;        // this wave's tile is skipped for the block
+        if (diag && h == 0 && kq >= 2) return;  // every key past every row of the half
+        const int r0 = qb * BQ + HB * h;
         const uint32_t qa = lds_addr_of(qs), oa = lds_addr_of(os);
-        // S (32 rows x 32 keys) = Q K^T; register r holds row 32rq + 8(r/4) + 4hl + r%4, key j
+        // S (32 rows x 32 keys) = Q K^T; register r holds row 32rh + 8(r/4) + 4hl + r%4, key j
         f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(qa) + qoff[s]), kf[s], sacc);
         if (diag) {  // keys past the row -> -inf: no probability
-            const int lim = key - r0 - 32 * rq - 4 * hl;
+            const int lim = key - r0 - 32 * rh - 4 * hl;
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (8 * (r >> 2) + (r & 3) < lim) sacc[r] = -INFINITY;
@@ -474,7 +500,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
         u32x4 pf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[0][32 * rq + 8 * g + 4 * hl]);
+            const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[0][32 * rh + 8 * g + 4 * hl]);
             float p[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) p[x] = fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[x]));
@@ -493,10 +519,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
         u32x4 dsf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[1][32 * rq + 8 * g + 4 * hl]);
-            const uint32_t w0 = pf[g >> 1][2 * (g & 1)], w1 = pf[g >> 1][2 * (g & 1) + 1];
-            const float p0 = __uint_as_float(w0 << 16), p1 = __uint_as_float(w0 & 0xffff0000u);
-            const float p2 = __uint_as_float(w1 << 16), p3 = __uint_as_float(w1 & 0xffff0000u);
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[1][32 * rh + 8 * g + 4 * hl]);
+            const uint32_t w0p = pf[g >> 1][2 * (g & 1)], w1p = pf[g >> 1][2 * (g & 1) + 1];
+            const float p0 = __uint_as_float(w0p << 16), p1 = __uint_as_float(w0p & 0xffff0000u);
+            const float p2 = __uint_as_float(w1p << 16), p3 = __uint_as_float(w1p & 0xffff0000u);
             dsf[g >> 1][2 * (g & 1)] = pack_bf16x2(p0 * (pacc[4 * g + 0] - dd[0]), p1 * (pacc[4 * g + 1] - dd[1]));
             dsf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
         }
@@ -507,89 +533,87 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
                 dkacc[db] = mfma32(tr_operand_at(qa + 256 * (16 * hf), troff[db]), dsf[hf], dkacc[db]);
-        if (aux_bits && tid == 0)  // the blocks this pass visited (parity statistics)
-            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (t >> 5)], tbit);
     };
 
-    // prologue: V tile; the first work item into buffers 0, 1
+    // prologue: V of the pair (segments 4w .. 4w+3, rows 16w .. 16w+15); the
+    // first unit into buffers 0, 1
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {  // V tile: segments 2w, 2w+1 (rows 8w .. 8w+7)
-        const int rt = 8 * wave + 4 * it + (lane >> 4);
-        const uint32_t off = uint32_t(min(rt, L - 1 - t * BK) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
-        dma16s(v + kvoff + long(t) * BK * D, off,
-               __builtin_amdgcn_readfirstlane(lds_addr_of(vtile) + 2048 * wave + 1024 * it));
+    for (int it = 0; it < 4; ++it) {
+        const int rt = 16 * wave + 4 * it + (lane >> 4);
+        const uint32_t off = uint32_t(min(rt, L - 1 - u * KP) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
+        dma16s(v + kvoff + long(u) * KP * D, off,
+               __builtin_amdgcn_readfirstlane(lds_addr_of(vtile) + 4096 * wave + 1024 * it));
     }
     open_head();
     int qb = kept_from(qb0);
     if (qb >= nqb) qb = next_item(nqb - 1);  // head 0 keeps nothing here: move on
+    int h = 0, fl = 0;
     if (ih < G) {
-        tile_async(q, buf[0], bkv * G + ih, qb * BQ);
-        tile_async(dout, buf[1], bkv * G + ih, qb * BQ);
+        fl = flags_of(qb);
+        half_async(q, hbuf[0], bkv * G + ih, qb * BQ);
+        half_async(dout, hbuf[1], bkv * G + ih, qb * BQ);
         stats_load(bkv * G + ih, qb * BQ);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
     stats_store(stA);
     lds_barrier();
-    // Each work item is computed from one buffer pair while the next streams
-    // into the other.  A head's diagonal block, if kept, is its first item.
+    // Each unit is computed from one buffer pair while the next streams into
+    // the other.  A head's diagonal block, if kept, is its first block.
     bool odd = false;
     auto advance = [&](auto diag_tag) {
-        const int bh = bkv * G + ih;
-        const int qcur = qb;
-        const int qn = next_item(qcur);
+        const int bh = bkv * G + ih, qcur = qb, hcur = h, fcur = fl;
+        if (h == 0 && qb * BQ + HB < L) {
+            h = 1;  // second half of the same block
+        } else {
+            qb = next_item(qb);
+            h = 0;
+            if (ih < G) fl = flags_of(qb);
+        }
         const bool more = ih < G;
         if (more) {
-            stats_load(bkv * G + ih, qn * BQ);
-            tile_async(q, odd ? buf[0] : buf[2], bkv * G + ih, qn * BQ);
-            tile_async(dout, odd ? buf[1] : buf[3], bkv * G + ih, qn * BQ);
+            const int r0n = qb * BQ + HB * h;
+            stats_load(bkv * G + ih, r0n);
+            half_async(q, odd ? hbuf[0] : hbuf[2], bkv * G + ih, r0n);
+            half_async(dout, odd ? hbuf[1] : hbuf[3], bkv * G + ih, r0n);
         }
-        block(diag_tag, bh, qcur, odd ? buf[2] : buf[0], odd ? buf[3] : buf[1], odd ? stB : stA);
+        unit(diag_tag, bh, qcur, hcur, fcur, odd ? hbuf[2] : hbuf[0], odd ? hbuf[3] : hbuf[1], odd ? stB : stA);
         if (more) stats_store(odd ? stA : stB);
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffer landed
-        lds_barrier();                       // next buffer complete; every wave is done with this one
-        qb = qn;
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffers landed
+        lds_barrier();                       // next buffers complete; every wave is done with these
         odd = !odd;
     };
     while (ih < G) {
         const int hcur = ih;
-        if (qb == qb0) advance(std::true_type{});
+        while (ih == hcur && qb == qb0) advance(std::true_type{});  // at most its two halves
         while (ih == hcur) advance(std::false_type{});
     }
 
-    // Sum the four row quarters.  Accumulators hold dK^T, dV^T: lane = key,
-    // register 4g + x of block db = d 32db + 8g + 4hl + x.  Wave w stores its
-    // 16 (db, g) groups as float4 at red[(16w + 4db + g) * 64 + lane]; output
-    // group gi = (kb, 4db + g, lane) sums waves kb, kb + 2, kb + 4, kb + 6.
-    f32x4* red = reinterpret_cast<f32x4*>(&buf[0][0]);
+    // Sum the two row groups.  Accumulators hold dK^T, dV^T: lane = key,
+    // register 4g + x of block db = d 32db + 8g + 4hl + x.  Waves of row group
+    // 1 park theirs as float4 at red[(16kq + 4db + g) * 64 + lane]; the waves of
+    // row group 0 with the same keys add them and write the result.
+    f32x4* red = reinterpret_cast<f32x4*>(&hbuf[0][0]);
     auto reduce_store = [&](const f32x16* acc, bf16_t* out, float mul) {
+        if (rh == 1) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                red[(16 * wave + 4 * db + g) * 64 + lane] =
-                    f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+                for (int g = 0; g < 4; ++g)
+                    red[(16 * kq + 4 * db + g) * 64 + lane] =
+                        f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+        }
         lds_barrier();
+        if (rh == 0 && kvalid) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int gi = tid + 512 * i;
-            const int l = gi & 63, dbg = (gi >> 6) & 15, kh = gi >> 10;
-            f32x4 sum = red[(16 * kh + dbg) * 64 + l];
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int rr = 1; rr < 4; ++rr) {
-                const f32x4 x = red[(16 * (kh + 2 * rr) + dbg) * 64 + l];
-                sum[0] += x[0];
-                sum[1] += x[1];
-                sum[2] += x[2];
-                sum[3] += x[3];
-            }
-            const int kk = t * BK + 32 * kh + (l & 31);
-            if (kk < L) {
-                u32x2 w;
-                w[0] = pack_bf16x2(sum[0] * mul, sum[1] * mul);
-                w[1] = pack_bf16x2(sum[2] * mul, sum[3] * mul);
-                const int d0 = 32 * (dbg >> 2) + 8 * (dbg & 3) + 4 * (l >> 5);
-                *reinterpret_cast<u32x2*>(out + kvoff + long(kk) * D + d0) = w;
-            }
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 x = red[(16 * kq + 4 * db + g) * 64 + lane];
+                    u32x2 w;
+                    w[0] = pack_bf16x2((acc[db][4 * g] + x[0]) * mul, (acc[db][4 * g + 1] + x[1]) * mul);
+                    w[1] = pack_bf16x2((acc[db][4 * g + 2] + x[2]) * mul, (acc[db][4 * g + 3] + x[3]) * mul);
+                    *reinterpret_cast<u32x2*>(out + kvoff + long(key) * D + 32 * db + 8 * g + 4 * hl) = w;
+                }
         }
         lds_barrier();
     };
@@ -601,7 +625,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     const int BH = a.B * a.H;
     const int G = a.H / a.Hkv;  // query heads per K/V head (the API checked H % Hkv == 0)
     if (G < 1 || a.H % a.Hkv) return hipErrorInvalidValue;
-    dim3 g1(unsigned(a.ntiles) * unsigned(a.B * a.Hkv)), b1(512), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
+    dim3 g1(unsigned(a.nqb) * unsigned(a.B * a.Hkv)), b1(512), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
     const bool st = a.kept || a.legal || a.bits;
     hipError_t e = mark(a.ev[1], s);
     if (e != hipSuccess) return e;
