@@ -243,9 +243,9 @@ def main():
     kern = {
         "fwd_bf16_d128": (ms["fwd"], tile_flop * (n_legal + fk), "mfma",
                           f"QK on every legal tile + PV on each kept tile; {per_tile}"),
-        "bwd_dkdv_bf16_d128": (ms["dkdv"], tile_flop * 4 * bk_, "mfma",
-                               f"S, dP, dV, dK on each kept tile (the dQ pass decides; this pass visits kept "
-                               f"tiles only); {per_tile}"),
+        "bwd_dkdv_pair_bf16_d128": (ms["dkdv"], tile_flop * 4 * bk_, "mfma",
+                                    f"S, dP, dV, dK on each kept tile (the dQ pass decides; this pass visits "
+                                    f"kept tiles only); {per_tile}"),
         "bwd_dq_bf16_d128": (ms["dq"], tile_flop * (n_legal + 2 * bk_), "mfma",
                              f"S on every legal tile + dP, dQ on each kept tile; {per_tile}"),
         "decode_split_bf16_d128": (ms["dec"], Bd * wd.Hkv * Lk * d * 2 * (1.0 + dkp / dlg), "hbm",
@@ -327,7 +327,7 @@ def kernel_times(torch, ops, q, k, v, o, lse, do, dq, dk, dv, ws, tile, tau, ste
 # kernel -> (instantiation timed by the bench at tau > 0, source files it is built from)
 PROFILED = {
     "fwd_bf16_d128": ("fwd_bf16_d128<true, false>", ["mala_fwd.hip"]),
-    "bwd_dkdv_bf16_d128": ("bwd_dkdv_bf16_d128<true>", ["mala_bwd.hip"]),
+    "bwd_dkdv_pair_bf16_d128": ("bwd_dkdv_pair_bf16_d128<true>", ["mala_bwd.hip"]),
     "bwd_dq_bf16_d128": ("bwd_dq_bf16_d128<true, false>", ["mala_bwd.hip"]),
     "decode_split_bf16_d128": ("decode_split_bf16_d128<4, true, false, false, false>", ["mala_decode.hip"]),
 }

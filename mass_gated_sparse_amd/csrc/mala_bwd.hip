@@ -288,7 +288,322 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 }
 
 // ---------------------------------------------------------------------- dK/dV
-// One workgroup of 8 waves per pair of 64-key tiles (128 keys, tiles 2u and
+// Two layouts of the same pass.  Per workgroup: one 64-key tile
+// (bwd_dkdv_tile_bf16_d128), or a pair of them (bwd_dkdv_pair_bf16_d128), which
+// halves the Q/dO loads per FLOP but needs twice the work per workgroup; the
+// launcher takes the pair layout when its grid still has at least two
+// workgroups per CU.
+//
+// Tile layout.  One workgroup of 8 waves per 64-key tile: wave w owns keys 32(w&1) .. +31
+// of the tile and rows 32(w>>1) .. +31 of every query block, so two waves
+// share each SIMD.  K of the wave's keys is held in registers (B operand of
+// S = Q K^T); the V tile sits in LDS (B operand of dP = dO V^T).
+//
+// Decisions.  The dQ pass runs first and tests every tile against the final
+// lse; its decision bits reach this pass through the backward's workspace.
+// This pass visits only the kept query blocks of its key tile: a skipped
+// block costs no Q/dO load, no S and no post-score work, and both passes use
+// the same decisions by construction.
+//
+// The Q and dO tiles of successive kept query blocks are double-buffered in
+// LDS: while one block is computed, the next streams into the other buffer
+// with direct global->LDS loads.  Each wave accumulates dK^T and dV^T over
+// its own 32 rows of every block; the four row quarters are summed through
+// LDS at the end.  Rows past L are read clamped to row L-1; their lse is
+// +inf there, so P = 0.
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_tile_bf16_d128(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BHkv, int G, int L, int nqb, int words, float scale,
+    float scale_log2, const uint32_t* __restrict__ dbits, uint32_t* __restrict__ aux_bits) {
+    using namespace bwdk;
+    // buf[0..3]: Q and dO tiles of two query blocks (buf[0], buf[1] and
+    // buf[2], buf[3]); reused at the end for the cross-wave reduction.
+    __shared__ __attribute__((aligned(1024))) uint8_t buf[4][BQ * 256];
+    __shared__ __attribute__((aligned(1024))) uint8_t vtile[BK * 256];
+    __shared__ __attribute__((aligned(16))) float stA[2][BQ];  // lse2, D of the block's rows
+    __shared__ __attribute__((aligned(16))) float stB[2][BQ];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
+    const int kb = wave & 1, rq = wave >> 1;
+    int t, bkv;  // 64-key tile (longest, t = 0, first) and K/V head; its query heads are bkv*G .. +G-1
+    balanced_item(int(blockIdx.x), BHkv, max(1, (2 * nqb) / 8), t, bkv);
+    const long kvoff = long(bkv) * L * D;
+    const int key = t * BK + 32 * kb + j;
+    const bool kvalid = key < L;
+    const int qb0 = (t * BK) / BQ;  // first query block that sees the tile (its diagonal block)
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+
+    // K of this wave's 32 keys as B operands (lane = key, 8 contiguous d)
+    u32x4 kf[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(k + kvoff + long(key) * D + 16 * s + 8 * hl) : z4;
+    f32x16 dvacc[4], dkacc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dvacc[db][r] = 0.f; dkacc[db][r] = 0.f; }
+
+    // Direct loads of one 128x128 tile: 32 segments of 4 rows (1 KiB); wave w
+    // issues segments 4w..4w+3 (rows 16w .. 16w+15); lane l of a segment fills
+    // physical chunk l%16 of row l/16, i.e. it reads the logical chunk that the
+    // swizzle puts there.  Rows past L read row L-1 instead (masked later).
+    auto tile_async = [&](const bf16_t* g, uint8_t* dst, int bh, int r0) {
+        const uint32_t la = lds_addr_of(dst) + 4096 * wave;
+        const bf16_t* gb = g + long(bh) * L * D + long(r0) * D;  // wave-uniform
+        const int lim = L - 1 - r0;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int rt = 16 * wave + 4 * it + (lane >> 4);
+            const uint32_t off = uint32_t(min(rt, lim) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
+            dma16s(gb, off, __builtin_amdgcn_readfirstlane(la + 1024 * it));
+        }
+    };
+    // Operand read offsets within a Q or dO tile, this wave's row quarter
+    // folded in: normal (row-major) reads of row 32rq + j, chunk 2s + hl, and
+    // the transposed reads of tr_operand_at (rowbase 32rq).
+    int qoff[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qoff[s] = swz(j, 2 * s + hl) + 8192 * rq;
+    int troff[4][2];
+    tr_offsets(lane, troff);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        troff[db][0] += 8192 * rq;
+        troff[db][1] += 8192 * rq;
+    }
+    // Per-row state of a block, held by threads 0..127: loaded raw (row index
+    // clamped) into registers before the tile prefetch is issued, written to
+    // LDS (with the padding-row defaults) only at the end of the block, so
+    // waiting for these loads never waits for the prefetch.
+    float stv[2];
+    int st_row = 0;
+    auto stats_load = [&](int bh, int r0) {
+        if (tid < BQ) {
+            st_row = r0 + tid;
+            const long ri = long(bh) * L + min(st_row, L - 1);
+            stv[0] = lse2[ri];
+            stv[1] = Dv[ri];
+        }
+    };
+    auto stats_store = [&](float (*st)[BQ]) {
+        if (tid < BQ) {
+            const bool ok = st_row < L;
+            st[0][tid] = ok ? stv[0] : INFINITY;
+            st[1][tid] = ok ? stv[1] : 0.f;
+        }
+    };
+    // this wave's 32 keys of V, addressed with the Q-tile offsets
+    const uint32_t va = lds_addr_of(vtile) + 8192 * kb - 8192 * rq;
+
+    // Work items are (query head of the group, kept query block), head by
+    // head.  Kept blocks of one head come 64 at a time: bit i of kmask is
+    // block wbase + i (every lane fetches one block's decision word, a ballot
+    // packs the bits); the next window's words are fetched one window ahead.
+    const uint32_t tbit = 1u << (t & 31);
+    int ih = 0;  // query head within the group of the current window
+    auto fetch = [&](int base) -> uint32_t {
+        const int qb = base + lane;
+        return (GATED && qb < nqb) ? dbits[(long(bkv * G + ih) * nqb + qb) * words + (t >> 5)] : 0u;
+    };
+    int wbase = qb0;
+    uint64_t kmask = 0;
+    uint32_t wnext = 0;
+    auto open_head = [&]() {
+        wbase = qb0;
+        if (GATED) {
+            kmask = __ballot((fetch(qb0) & tbit) != 0u);
+            wnext = fetch(qb0 + 64);
+        }
+    };
+    // first kept block >= qb (qb >= wbase) of head ih, or nqb
+    auto kept_from = [&](int qb) -> int {
+        if (!GATED) return qb;
+        for (;;) {
+            const int sh = qb - wbase;
+            const uint64_t m = sh >= 64 ? 0ull : (kmask >> sh) << sh;
+            if (m) return wbase + __builtin_ctzll(m);
+            if (wbase + 64 >= nqb) return nqb;
+            wbase += 64;
+            qb = max(qb, wbase);
+            kmask = __ballot((wnext & tbit) != 0u);
+            wnext = fetch(wbase + 64);
+        }
+    };
+    // the work item after (ih, qb): the next kept block of this head, else
+    // the first kept block of the next head with one (ih == G: done)
+    auto next_item = [&](int qb) -> int {
+        int qn = kept_from(qb + 1);
+        while (qn >= nqb && ih + 1 < G) {
+            ++ih;
+            open_head();
+            qn = kept_from(qb0);
+        }
+        if (qn >= nqb) ih = G;
+        return qn;
+    };
+
+    // One kept query block, computed from (qs, os, st).  Only the diagonal
+    // block (qb == qb0) needs a visibility mask: it is the only block with
+    // keys past some row, and the only block of the last tiles, whose keys may
+    // run past L.  Elsewhere every key is visible to every row.
+    auto block = [&](auto diag_tag, int bh, int qb, const uint8_t* qs, const uint8_t* os, const float (*st)[BQ]) {
+        constexpr bool diag = decltype(diag_tag)::value;
+        const int r0 = qb * BQ;
+        const uint32_t qa = lds_addr_of(qs), oa = lds_addr_of(os);
+        // S (32 rows x 32 keys) = Q K^T; register r holds row 32rq + 8(r/4) + 4hl + r%4, key j
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(qa) + qoff[s]), kf[s], sacc);
+        if (diag) {  // keys past the row -> -inf: no probability
+            const int lim = key - r0 - 32 * rq - 4 * hl;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (8 * (r >> 2) + (r & 3) < lim) sacc[r] = -INFINITY;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dP (32 rows x 32 keys) = dO V^T
+        f32x16 pacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            pacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(oa) + qoff[s]),
+                          *reinterpret_cast<const u32x4*>(lds_ptr(va) + qoff[s]), pacc);
+        __builtin_amdgcn_sched_barrier(0);
+        // P = exp(s - lse) (zero where masked; lse2 = +inf on rows past L),
+        // kept only as bf16 B operands: step hf holds registers 8hf .. 8hf+7.
+        u32x4 pf[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[0][32 * rq + 8 * g + 4 * hl]);
+            float p[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) p[x] = fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[x]));
+            pf[g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
+            pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+        // dS = P (dP - D), P taken from its bf16 operand copy
+        u32x4 dsf[2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[1][32 * rq + 8 * g + 4 * hl]);
+            const uint32_t w0 = pf[g >> 1][2 * (g & 1)], w1 = pf[g >> 1][2 * (g & 1) + 1];
+            const float p0 = __uint_as_float(w0 << 16), p1 = __uint_as_float(w0 & 0xffff0000u);
+            const float p2 = __uint_as_float(w1 << 16), p3 = __uint_as_float(w1 & 0xffff0000u);
+            dsf[g >> 1][2 * (g & 1)] = pack_bf16x2(p0 * (pacc[4 * g + 0] - dd[0]), p1 * (pacc[4 * g + 1] - dd[1]));
+            dsf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // dK^T (d x keys) += Q^T dS
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                dkacc[db] = mfma32(tr_operand_at(qa + 256 * (16 * hf), troff[db]), dsf[hf], dkacc[db]);
+        if (aux_bits && tid == 0)  // the blocks this pass visited (parity statistics)
+            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + (t >> 5)], tbit);
+    };
+
+    // prologue: V tile; the first work item into buffers 0, 1
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {  // V tile: segments 2w, 2w+1 (rows 8w .. 8w+7)
+        const int rt = 8 * wave + 4 * it + (lane >> 4);
+        const uint32_t off = uint32_t(min(rt, L - 1 - t * BK) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
+        dma16s(v + kvoff + long(t) * BK * D, off,
+               __builtin_amdgcn_readfirstlane(lds_addr_of(vtile) + 2048 * wave + 1024 * it));
+    }
+    open_head();
+    int qb = kept_from(qb0);
+    if (qb >= nqb) qb = next_item(nqb - 1);  // head 0 keeps nothing here: move on
+    if (ih < G) {
+        tile_async(q, buf[0], bkv * G + ih, qb * BQ);
+        tile_async(dout, buf[1], bkv * G + ih, qb * BQ);
+        stats_load(bkv * G + ih, qb * BQ);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    stats_store(stA);
+    lds_barrier();
+    // Each work item is computed from one buffer pair while the next streams
+    // into the other.  A head's diagonal block, if kept, is its first item.
+    bool odd = false;
+    auto advance = [&](auto diag_tag) {
+        const int bh = bkv * G + ih;
+        const int qcur = qb;
+        const int qn = next_item(qcur);
+        const bool more = ih < G;
+        if (more) {
+            stats_load(bkv * G + ih, qn * BQ);
+            tile_async(q, odd ? buf[0] : buf[2], bkv * G + ih, qn * BQ);
+            tile_async(dout, odd ? buf[1] : buf[3], bkv * G + ih, qn * BQ);
+        }
+        block(diag_tag, bh, qcur, odd ? buf[2] : buf[0], odd ? buf[3] : buf[1], odd ? stB : stA);
+        if (more) stats_store(odd ? stA : stB);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffer landed
+        lds_barrier();                       // next buffer complete; every wave is done with this one
+        qb = qn;
+        odd = !odd;
+    };
+    while (ih < G) {
+        const int hcur = ih;
+        if (qb == qb0) advance(std::true_type{});
+        while (ih == hcur) advance(std::false_type{});
+    }
+
+    // Sum the four row quarters.  Accumulators hold dK^T, dV^T: lane = key,
+    // register 4g + x of block db = d 32db + 8g + 4hl + x.  Wave w stores its
+    // 16 (db, g) groups as float4 at red[(16w + 4db + g) * 64 + lane]; output
+    // group gi = (kb, 4db + g, lane) sums waves kb, kb + 2, kb + 4, kb + 6.
+    f32x4* red = reinterpret_cast<f32x4*>(&buf[0][0]);
+    auto reduce_store = [&](const f32x16* acc, bf16_t* out, float mul) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                red[(16 * wave + 4 * db + g) * 64 + lane] =
+                    f32x4{acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gi = tid + 512 * i;
+            const int l = gi & 63, dbg = (gi >> 6) & 15, kh = gi >> 10;
+            f32x4 sum = red[(16 * kh + dbg) * 64 + l];
+#pragma unroll
+            for (int rr = 1; rr < 4; ++rr) {
+                const f32x4 x = red[(16 * (kh + 2 * rr) + dbg) * 64 + l];
+                sum[0] += x[0];
+                sum[1] += x[1];
+                sum[2] += x[2];
+                sum[3] += x[3];
+            }
+            const int kk = t * BK + 32 * kh + (l & 31);
+            if (kk < L) {
+                u32x2 w;
+                w[0] = pack_bf16x2(sum[0] * mul, sum[1] * mul);
+                w[1] = pack_bf16x2(sum[2] * mul, sum[3] * mul);
+                const int d0 = 32 * (dbg >> 2) + 8 * (dbg & 3) + 4 * (l >> 5);
+                *reinterpret_cast<u32x2*>(out + kvoff + long(kk) * D + d0) = w;
+            }
+        }
+        lds_barrier();
+    };
+    reduce_store(dkacc, dk, scale);
+    reduce_store(dvacc, dv, 1.f);
+}
+
+// Pair layout.  One workgroup of 8 waves per pair of 64-key tiles (128 keys, tiles 2u and
 // 2u+1): wave w owns keys 32kq .. +31 of the pair, kq = 2(w>>2) + (w&1) (so
 // tile 2u + w/4), and rows 32((w>>1)&1) .. +31 of every 64-row half of a
 // query block; waves w and w+4 share a SIMD.  K of the wave's keys is held in registers (B operand of
@@ -309,7 +624,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
 // LDS at the end.  Rows past L are read clamped to row L-1; their lse is +inf
 // there, so P = 0, and a half with no row below L is not visited.
 template <bool GATED>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_d128(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int BHkv, int G, int L, int nqb, int words, float scale,
@@ -625,7 +940,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     const int BH = a.B * a.H;
     const int G = a.H / a.Hkv;  // query heads per K/V head (the API checked H % Hkv == 0)
     if (G < 1 || a.H % a.Hkv) return hipErrorInvalidValue;
-    dim3 g1(unsigned(a.nqb) * unsigned(a.B * a.Hkv)), b1(512), g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
+    dim3 g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
     const bool st = a.kept || a.legal || a.bits;
     hipError_t e = mark(a.ev[1], s);
     if (e != hipSuccess) return e;
@@ -644,14 +959,21 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(a.ev[2], s);
     if (e != hipSuccess) return e;
-    if (a.gated)
-        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<true>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
-                           (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, (bf16_t*)a.dk, (bf16_t*)a.dv,
-                           a.B * a.Hkv, G, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_bf16_d128<false>), g1, b1, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
-                           (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, (bf16_t*)a.dk, (bf16_t*)a.dv,
-                           a.B * a.Hkv, G, a.L, a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits);
+    // pair layout when its grid keeps at least two workgroups per CU busy
+    const bool pairs = long(a.nqb) * a.B * a.Hkv >= 2L * kNumCUs;
+    const dim3 gk(unsigned(pairs ? a.nqb : a.ntiles) * unsigned(a.B * a.Hkv)), bk(512);
+#define MALA_DKDV_LAUNCH(KERNEL, GT)                                                                           \
+    hipLaunchKernelGGL((KERNEL<GT>), gk, bk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, \
+                       (const bf16_t*)a.dout, a.Dv, a.lse2, (bf16_t*)a.dk, (bf16_t*)a.dv, a.B * a.Hkv, G, a.L,    \
+                       a.nqb, a.words, a.scale, a.scale_log2, a.dbits, a.aux_bits)
+    if (pairs) {
+        if (a.gated) MALA_DKDV_LAUNCH(bwd_dkdv_pair_bf16_d128, true);
+        else MALA_DKDV_LAUNCH(bwd_dkdv_pair_bf16_d128, false);
+    } else {
+        if (a.gated) MALA_DKDV_LAUNCH(bwd_dkdv_tile_bf16_d128, true);
+        else MALA_DKDV_LAUNCH(bwd_dkdv_tile_bf16_d128, false);
+    }
+#undef MALA_DKDV_LAUNCH
     e = hipGetLastError();
     if (e == hipSuccess) e = mark(a.ev[3], s);
     return e;

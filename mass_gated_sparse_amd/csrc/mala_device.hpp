@@ -14,6 +14,8 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// compute units of a gfx950 GPU (MI350X / MI355X: 8 XCDs x 32 CUs); launchers size grids against it
+constexpr int kNumCUs = 256;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 
