@@ -550,8 +550,11 @@ def micro(torch):
     return res
 
 
-# timed repetitions of the shapes below 128K (at least; --steps raises it)
+# timed repetitions and warm-up calls of the 32K sweep configurations (at
+# least; --steps / --warmup raise them): the first few calls of a
+# configuration in a process can read several percent slow
 SMALL_REPS = 10
+SMALL_WARMUP = 10
 
 
 def sweep32k(torch, ops, steps, warmup):
@@ -583,7 +586,7 @@ def sweep32k(torch, ops, steps, warmup):
             torch.cuda.synchronize()
             fk, bk_ = int(st["kept"].sum()), int(stb["kept"].sum())
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            for _ in range(warmup):
+            for _ in range(max(SMALL_WARMUP, warmup)):
                 ops.fwd_into(q, k, v, o, lse, tau, tile)
                 ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
             tfs, tbs = [], []
