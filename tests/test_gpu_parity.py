@@ -126,6 +126,50 @@ def test_bwd_bf16(ops, L, heads, tau):
     _check_bwd(ops, w, x, tau, 128, 64)
 
 
+@pytest.mark.parametrize("L,H,Hkv", [(1000, 64, 64), (900, 64, 64), (2048, 64, 32)])
+@pytest.mark.parametrize("tau", [0.0, 1.0, math.inf])
+def test_bwd_pair_layout_bf16(ops, L, H, Hkv, tau):
+    """dK/dV in the tile-pair layout, which the launcher takes when
+    B * Hkv * ceil(L/128) >= 512 (every case here): ragged lengths whose last
+    pair has no second tile and whose last block has no second 64-row half
+    (L=900), a ragged last block with both (L=1000), and grouped K/V heads.
+    Decisions of both passes, and dQ/dK/dV against the oracle on sampled
+    query blocks and key tiles, the last ones included."""
+    import dataclasses
+    w = dataclasses.replace(WORKLOADS["mw8k"], H=H, Hkv=Hkv)
+    nqb, nt = -(-L // 128), -(-L // 64)
+    assert nqb * Hkv >= 512
+    x = prefill_inputs(w, L=L)
+    q, k, v, do = _dev_tensors(x, "bf16", ("q", "k", "v", "do"))
+    o, lse = ops.fwd(q, k, v, tau)
+    dq, dk, dv, st = ops.bwd(q, k, v, o, lse, do, tau, stats=True)
+    torch.cuda.synchronize()
+    gk = ops.bits_to_keep(st["keep_bits"], nt)
+    gk2 = ops.bits_to_keep(st["keep_bits_dkdv"], nt)
+    legal = legal_mask(L, 128, 64)
+    assert (gk[..., legal] == gk2[..., legal]).all(), "dQ and dK/dV passes disagree"
+    if tau == math.inf:
+        assert all(float(t.abs().max()) == 0.0 for t in (dq, dk, dv))
+        return
+    qblocks, ktiles = (0, nqb // 2, nqb - 1), (0, 1, nt // 2, nt - 2, nt - 1)
+    qf, kf, vf, dof = (to_f64(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    of, lf = bf16_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    gq, gkk, gv, okb, oTb = oracle.bwd(qf, kf, vf, of, lf, dof, tau, 128, 64, replay=gk, band=BAND,
+                                       qblocks=qblocks, ktiles=ktiles)
+    sel = np.zeros_like(legal)
+    sel[list(qblocks)] = legal[list(qblocks)]
+    for t in ktiles:
+        sel[:, t] |= legal[:, t]
+    bad, near, _ = decision_report(gk, okb, oTb, sel)
+    assert bad == 0, f"backward decisions differ on {bad} tiles"
+    rows = np.concatenate([np.arange(b * 128, min(b * 128 + 128, L)) for b in qblocks])
+    krows = np.concatenate([np.arange(t * 64, min(t * 64 + 64, L)) for t in ktiles])
+    e = [rel_l2(bf16_to_f64(dq)[:, :, rows], gq[:, :, rows]),
+         rel_l2(bf16_to_f64(dk)[:, :, krows], gkk[:, :, krows]),
+         rel_l2(bf16_to_f64(dv)[:, :, krows], gv[:, :, krows])]
+    assert max(e) <= TOL_GRAD, e
+
+
 @pytest.mark.parametrize("L", [1000, 2048])
 @pytest.mark.parametrize("tau", [0.0, 1.0, 4.0, math.inf])
 def test_gqa_bf16(ops, L, tau):
