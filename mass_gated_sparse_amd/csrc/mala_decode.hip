@@ -20,7 +20,8 @@
 //
 // Thread mapping.  Scores: thread t handles key t/4 of the tile and a
 // 32-element quarter of d (four 16-byte loads), bf16 dot2 products in fp32,
-// summed over the 4 quarters with lane shuffles.  PV: thread t handles an
+// summed over the 4 quarters with lane shuffles; the query quarters are read
+// from LDS (every thread of a quarter reads the same addresses).  PV: thread t handles an
 // 8-element d chunk (t%16) of keys 16*wave + 4*i + (t/16)%4, i = 0..3; its
 // fp32 accumulators are summed over the 16 key subsets once per partition.
 // Partial states (m2 = running max of s*log2(e), l, acc[d]) are written per
@@ -53,8 +54,12 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // vote decides.  Used for the newest partition alone (one workgroup per
 // sequence and KV head, keeping nearly every tile): there the V load would
 // otherwise add a memory latency per tile to a short, serial launch.
+// Occupancy: four workgroups per CU (at most 128 VGPRs, so the query rows
+// live in LDS) give the HBM stream enough independent tiles in flight; the
+// PREV launch runs one workgroup per (sequence, KV head) and keeps the
+// registers its extra V prefetch needs instead.
 template <int G, bool GATED, bool STATS, bool SEED, bool PREV>
-__global__ __launch_bounds__(256) void decode_split_bf16_d128(
+__global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     float* __restrict__ part, int Hq, int Hkv, int Lk, int Lcap, int split_keys, int nsplit, int tps, int words,
     float scale_log2, float log2_tau, float log2_lq, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
@@ -65,6 +70,7 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
     __shared__ float wsum_sm[2][4][G];
     __shared__ float p_sm[2][G][BK];
     __shared__ float red_sm[G][16][D + 4];
+    __shared__ __attribute__((aligned(16))) uint32_t q_sm[G][D / 2];  // the G query rows (bf16 pairs)
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int p = int(blockIdx.x) + pbase;
@@ -91,16 +97,12 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
 
     // score mapping
     const int skey = tid >> 2, quarter = tid & 3;
-    uint32_t qr[G][16];
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-        const bf16_t* qrow = q + (long(b) * Hq + g * G + r) * D + 32 * quarter;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 8 * c);
-            qr[r][4 * c + 0] = x[0]; qr[r][4 * c + 1] = x[1]; qr[r][4 * c + 2] = x[2]; qr[r][4 * c + 3] = x[3];
-        }
+    if (tid < G * 16) {  // 16-byte pieces of the G rows
+        const int r = tid >> 4, c = tid & 15;
+        *reinterpret_cast<u32x4*>(&q_sm[r][4 * c]) =
+            *reinterpret_cast<const u32x4*>(q + (long(b) * Hq + g * G + r) * D + 8 * c);
     }
+    __syncthreads();
     // PV mapping
     const int dch = tid & 15, ksub = (tid >> 4) & 3;
     float acc[G][8];
@@ -164,10 +166,11 @@ __global__ __launch_bounds__(256) void decode_split_bf16_d128(
             float a = 0.f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                a = dot2(qr[r][4 * c + 0], kcur[c][0], a);
-                a = dot2(qr[r][4 * c + 1], kcur[c][1], a);
-                a = dot2(qr[r][4 * c + 2], kcur[c][2], a);
-                a = dot2(qr[r][4 * c + 3], kcur[c][3], a);
+                const u32x4 qx = *reinterpret_cast<const u32x4*>(&q_sm[r][16 * quarter + 4 * c]);
+                a = dot2(qx[0], kcur[c][0], a);
+                a = dot2(qx[1], kcur[c][1], a);
+                a = dot2(qx[2], kcur[c][2], a);
+                a = dot2(qx[3], kcur[c][3], a);
             }
             a += __shfl_xor(a, 1, 64);
             a += __shfl_xor(a, 2, 64);
