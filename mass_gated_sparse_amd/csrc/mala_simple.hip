@@ -137,6 +137,37 @@ __global__ void bwd_prep(const T* __restrict__ o, const T* __restrict__ dout, co
     }
 }
 
+// The same per-row state for bf16 rows of 128: 16 lanes per row, each
+// reading 16 bytes of O and of dO (one wave covers four rows).
+__global__ __launch_bounds__(256) void bwd_prep_bf16_d128(const bf16_t* __restrict__ o,
+                                                          const bf16_t* __restrict__ dout,
+                                                          const float* __restrict__ lse, float* __restrict__ Dv,
+                                                          float* __restrict__ lse2, float* __restrict__ thr,
+                                                          long rows, int L, float scale_log2, float log2_tau) {
+    constexpr int D = 128;
+    const long r = (long(blockIdx.x) * 256 + threadIdx.x) >> 4;
+    const int sub = threadIdx.x & 15;
+    float s = 0.f;
+    if (r < rows) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(o + r * D + 8 * sub);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(dout + r * D + 8 * sub);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), s);
+            s = fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(b[e] & 0xffff0000u), s);
+        }
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);  // within the row's 16 lanes
+    if (r < rows && sub == 0) {
+        const int i = int(r % L);
+        const float l2 = lse[r] * kLog2e;
+        Dv[r] = s;
+        lse2[r] = l2;
+        thr[r] = (l2 + log2_tau - fast_log2(float(i + 1))) / scale_log2;
+    }
+}
+
 // dK, dV: one thread per key of a BK-key tile column; loops over query blocks.
 template <int BQ, int BK, int D, bool GATED>
 __global__ __launch_bounds__(BK, 1) void simple_bwd_dkdv_f32(
@@ -322,14 +353,16 @@ hipError_t launch_simple_fwd_f32(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t s) {
     const long rows = long(a.B) * a.H * a.L;
-    const int per_block = 4;  // one wave per row
-    dim3 grid(unsigned((rows + per_block - 1) / per_block)), block(64 * per_block);
-    if (a.f32)
+    if (a.f32) {
+        const int per_block = 4;  // one wave per row
+        dim3 grid(unsigned((rows + per_block - 1) / per_block)), block(64 * per_block);
         hipLaunchKernelGGL((bwd_prep<float, 64>), grid, block, 0, s, (const float*)a.o, (const float*)a.dout,
                            a.lse, a.Dv, a.lse2, a.thr, rows, a.L, a.scale_log2, a.log2_tau);
-    else
-        hipLaunchKernelGGL((bwd_prep<bf16_t, 128>), grid, block, 0, s, (const bf16_t*)a.o, (const bf16_t*)a.dout,
-                           a.lse, a.Dv, a.lse2, a.thr, rows, a.L, a.scale_log2, a.log2_tau);
+    } else {
+        dim3 grid(unsigned((rows + 15) / 16)), block(256);  // 16 rows per workgroup
+        hipLaunchKernelGGL(bwd_prep_bf16_d128, grid, block, 0, s, (const bf16_t*)a.o, (const bf16_t*)a.dout, a.lse,
+                           a.Dv, a.lse2, a.thr, rows, a.L, a.scale_log2, a.log2_tau);
+    }
     return hipGetLastError();
 }
 
