@@ -578,31 +578,35 @@ def sweep32k(torch, ops, steps, warmup):
         n_legal = B * H * legal_tiles(L, *tile)
         dense_fwd = 2.0 * B * H * L * L * d
         res = {}
-        for tau in w.taus:
+        for tau in w.taus:  # decisions and kept fractions
             st = ops.prefill_stats_buffers(B, H, L, tile, q.device)
             ops.fwd_into(q, k, v, o, lse, tau, tile, stats=st)
             stb = ops.prefill_stats_buffers(B, H, L, tile, q.device)
             ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile, stats=stb)
             torch.cuda.synchronize()
-            fk, bk_ = int(st["kept"].sum()), int(stb["kept"].sum())
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            for _ in range(max(SMALL_WARMUP, warmup)):
+            res[str(tau)] = {"kept_fwd": int(st["kept"].sum()) / n_legal, "kept_bwd": int(stb["kept"].sum()) / n_legal}
+        # timing interleaved over tau (every repetition visits every tau), so
+        # drift during the sweep lands on all of them alike
+        for _ in range(max(SMALL_WARMUP, warmup)):
+            for tau in w.taus:
                 ops.fwd_into(q, k, v, o, lse, tau, tile)
                 ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
-            tfs, tbs = [], []
-            for _ in range(max(SMALL_REPS, steps)):
+        times = {tau: ([], []) for tau in w.taus}
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for _ in range(max(SMALL_REPS, steps)):
+            for tau in w.taus:
                 ev[0].record()
                 ops.fwd_into(q, k, v, o, lse, tau, tile)
                 ev[1].record()
                 ops.bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile)
                 ev[2].record()
                 torch.cuda.synchronize()
-                tfs.append(ev[0].elapsed_time(ev[1]))
-                tbs.append(ev[1].elapsed_time(ev[2]))
-            tf, tb = float(np.median(tfs)), float(np.median(tbs))  # medians over the timed steps
-            res[str(tau)] = {"fwd_ms": tf, "bwd_ms": tb, "fwd_dense_tflops": dense_fwd / tf / 1e9,
-                             "bwd_dense_tflops": 2.5 * dense_fwd / tb / 1e9,
-                             "kept_fwd": fk / n_legal, "kept_bwd": bk_ / n_legal}
+                times[tau][0].append(ev[0].elapsed_time(ev[1]))
+                times[tau][1].append(ev[1].elapsed_time(ev[2]))
+        for tau in w.taus:
+            tf, tb = float(np.median(times[tau][0])), float(np.median(times[tau][1]))  # medians over the repetitions
+            res[str(tau)].update({"fwd_ms": tf, "bwd_ms": tb, "fwd_dense_tflops": dense_fwd / tf / 1e9,
+                                  "bwd_dense_tflops": 2.5 * dense_fwd / tb / 1e9})
         for tau in w.taus:
             if tau != 0.0:
                 r = res[str(tau)]
