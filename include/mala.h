@@ -91,6 +91,17 @@ typedef struct {
  *             hands the same decisions to the dK/dV pass); the two must agree
  *             bit for bit.  The call clears it (with a kernel) and the dK/dV
  *             pass sets its bits.
+ *   test_stat float, bf16 only (MALA_ERR_UNSUPPORTED on the fp32 path): log2
+ *             of each tested tile's statistic T, i.e. the largest margin
+ *             c*max_j s_ij - (running log2 max + log2 l + log2 tau - log2 Lq_i)
+ *             of a voting row, c = scale*log2(e), s_ij = <q_i, k_j>; the tile
+ *             is kept iff it is >= 0 (up to fp32 rounding of the two forms).
+ *             +inf for an empty running state, -inf when no row votes (tau =
+ *             +inf), NaN at tau = 0 (no test).  Forward (and mala_fwd_chunk):
+ *             the running state before the tile, [B, H, nqb, ceil(Lk/bk)];
+ *             mala_bwd (dQ pass): the final lse, [B, H, nqb, ntiles]; decode:
+ *             per vote group, [B, V, nsplit, split_keys/bk].  Entries of
+ *             tiles that are not tested are not written.
  * Every call only launches kernels on `stream` (no allocation, no memset, no
  * synchronization), so it can be captured in a HIP graph; events in
  * mala_stats are recorded with hipEventRecord and are for eager calls.
@@ -109,6 +120,7 @@ typedef struct {
     uint32_t* keep_bits;
     uint32_t* keep_bits_dkdv;
     void* events[4];
+    float* test_stat;
 } mala_stats;
 
 /*

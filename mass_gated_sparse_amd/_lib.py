@@ -25,7 +25,7 @@ class Tile(ctypes.Structure):
 
 class Stats(ctypes.Structure):
     _fields_ = [("kept", ctypes.c_void_p), ("legal", ctypes.c_void_p), ("keep_bits", ctypes.c_void_p),
-                ("keep_bits_dkdv", ctypes.c_void_p), ("events", ctypes.c_void_p * 4)]
+                ("keep_bits_dkdv", ctypes.c_void_p), ("events", ctypes.c_void_p * 4), ("test_stat", ctypes.c_void_p)]
 
 
 EXPORTS = ("mala_fwd", "mala_fwd_chunk", "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_seeded",

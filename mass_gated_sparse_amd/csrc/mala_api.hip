@@ -66,7 +66,7 @@ mala_status check_prefill(const void* q, const void* k, const void* v, int B, in
 
 extern "C" {
 
-int mala_version(void) { return 101; }
+int mala_version(void) { return 102; }
 
 const char* mala_status_string(mala_status s) {
     switch (s) {
@@ -98,7 +98,11 @@ mala_status mala_fwd(const void* q, const void* k, const void* v, int B, int H, 
     a.scale_log2 = sc * mala::kLog2e;
     a.log2_tau = log2_tau_of(tau);
     a.gated = tau != 0.f;
-    if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; }
+    if (stats) {
+        if (stats->test_stat && dtype != MALA_BF16)
+            return fail(MALA_ERR_UNSUPPORTED, "test_stat needs bf16 (not written by the fp32 path)");
+        a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; a.tstat = stats->test_stat;
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipEvent_t e0 = stats ? (hipEvent_t)stats->events[0] : nullptr, e1 = stats ? (hipEvent_t)stats->events[1] : nullptr;
     hipError_t e = mala::mark(e0, s);
@@ -129,7 +133,7 @@ mala_status mala_fwd_chunk(const void* q, const void* kcache, const void* vcache
     a.scale_log2 = sc * mala::kLog2e;
     a.log2_tau = log2_tau_of(tau);
     a.gated = tau != 0.f;
-    if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; }
+    if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; a.tstat = stats->test_stat; }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipEvent_t e0 = stats ? (hipEvent_t)stats->events[0] : nullptr, e1 = stats ? (hipEvent_t)stats->events[1] : nullptr;
     hipError_t e = mala::mark(e0, s);
@@ -179,7 +183,9 @@ mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o,
     a.f32 = dtype == MALA_F32;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (stats) {
-        a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits;
+        if (stats->test_stat && a.f32)
+            return fail(MALA_ERR_UNSUPPORTED, "test_stat needs bf16 (not written by the fp32 path)");
+        a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; a.tstat = stats->test_stat;
         a.aux_bits = stats->keep_bits_dkdv;
         for (int i = 0; i < 4; ++i) a.ev[i] = (hipEvent_t)stats->events[i];
         if (a.aux_bits) {  // the dK/dV pass ORs in the blocks it visits
@@ -240,7 +246,7 @@ static mala_status decode_call(const char* name, bool seeded, const void* q, con
     a.log2_tau = log2_tau_of(tau);
     a.log2_lq = log2f(float(Lk));
     a.gated = tau != 0.f;
-    if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; }
+    if (stats) { a.kept = stats->kept; a.legal = stats->legal; a.bits = stats->keep_bits; a.tstat = stats->test_stat; }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipEvent_t e0 = stats ? (hipEvent_t)stats->events[0] : nullptr, e1 = stats ? (hipEvent_t)stats->events[1] : nullptr;
     hipError_t e = mala::mark(e0, s);

@@ -55,9 +55,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
     const float* __restrict__ thr, bf16_t* __restrict__ dq, int BH, int G, int L, int nqb, int words, float scale,
     float scale_log2, int32_t* __restrict__ kept, int32_t* __restrict__ legal, uint32_t* __restrict__ bits,
-    uint32_t* __restrict__ dbits) {
+    uint32_t* __restrict__ dbits, float* __restrict__ tstat) {
     using namespace bwdk;
     __shared__ __attribute__((aligned(1024))) uint8_t kring[3][BK * 256];
+    __shared__ float tstat_sm[2][4];  // statistics only: each wave's largest test margin
     __shared__ __attribute__((aligned(1024))) uint8_t vtile[BK * 256];
     __shared__ int vote_sm[2][4];
 
@@ -146,6 +147,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
         return wave_any(vote);
     };
 
+    // statistics: log2 of a tile's test statistic, the largest margin
+    // c*(max_j s_ij - thr_i) = c*max_j s_ij - (lse2_i + log2 tau - log2 Lq_i) of
+    // a voting row (rows without a visible key, and rows past L, abstain)
+    auto margin_of = [&](const f32x16* sacc) -> float {
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        float dl = (mx == -INFINITY) ? -INFINITY : (mx - th) * scale_log2;
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) dl = fmaxf(dl, shfl_xor_f(dl, m));
+        return dl;
+    };
+    const int ntk = (L + BK - 1) / BK;
+
     int nkept = 0;
     uint32_t word = 0;
     if (STATS && bits && tid == 0)
@@ -165,6 +183,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     if (GATED) {
         const bool wv = vote_of(sc);
         if (lane == 0) vote_sm[jmax & 1][wave] = wv ? 1 : 0;
+        if (STATS && tstat) {
+            const float dl = margin_of(sc);
+            if (lane == 0) tstat_sm[jmax & 1][wave] = dl;
+        }
     }
 
     // One step per tile; R = t % 3 is a compile-time constant, so the ring slot
@@ -181,6 +203,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
         int vflags = 1;
         if (GATED) vflags = vote_sm[t & 1][0] | vote_sm[t & 1][1] | vote_sm[t & 1][2] | vote_sm[t & 1][3];
         const bool keep = vflags != 0;
+        if (STATS && tstat && tid == 0)  // tau = 0 runs no test: NaN
+            tstat[(long(bh) * nqb + qb) * ntk + t] =
+                GATED ? fmaxf(fmaxf(tstat_sm[t & 1][0], tstat_sm[t & 1][1]), fmaxf(tstat_sm[t & 1][2], tstat_sm[t & 1][3]))
+                      : NAN;
         if (keep) tile_dma(vh, vta, t);
         if (t >= 2) tile_dma(kh, ks2, t - 2);
         // P = exp(s - lse) (zero on invisible entries) as bf16 B operands; step
@@ -206,6 +232,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
             if (GATED) {
                 const bool wv = vote_of(sc);
                 if (lane == 0) vote_sm[(t - 1) & 1][wave] = wv ? 1 : 0;
+                if (STATS && tstat) {
+                    const float dl = margin_of(sc);
+                    if (lane == 0) tstat_sm[(t - 1) & 1][wave] = dl;
+                }
             }
         }
         if (keep) {
@@ -941,13 +971,13 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
     const int G = a.H / a.Hkv;  // query heads per K/V head (the API checked H % Hkv == 0)
     if (G < 1 || a.H % a.Hkv) return hipErrorInvalidValue;
     dim3 g2(unsigned(a.nqb) * unsigned(BH)), blk(256);
-    const bool st = a.kept || a.legal || a.bits;
+    const bool st = a.kept || a.legal || a.bits || a.tstat;
     hipError_t e = mark(a.ev[1], s);
     if (e != hipSuccess) return e;
 #define MALA_DQ_LAUNCH(GT, ST)                                                                                \
     hipLaunchKernelGGL((bwd_dq_bf16_d128<GT, ST>), g2, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,     \
                        (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dq, BH, G, a.L, \
-                       a.nqb, a.words, a.scale, a.scale_log2, a.kept, a.legal, a.bits, a.dbits)
+                       a.nqb, a.words, a.scale, a.scale_log2, a.kept, a.legal, a.bits, a.dbits, a.tstat)
     if (a.gated) {
         if (st) MALA_DQ_LAUNCH(true, true);
         else MALA_DQ_LAUNCH(true, false);

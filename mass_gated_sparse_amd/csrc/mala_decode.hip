@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     float* __restrict__ part, int Hq, int Hkv, int Lk, int Lcap, int split_keys, int nsplit, int tps, int words,
     float scale_log2, float log2_tau, float log2_lq, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
-    uint32_t* __restrict__ bits, int pbase, int seeded_grid, int rpv) {
+    uint32_t* __restrict__ bits, int pbase, int seeded_grid, int rpv, float* __restrict__ tstat) {
     constexpr int D = 128, BK = 64;
     __shared__ int vote_sm[2][4];
     __shared__ float wmax_sm[2][4][G];
@@ -207,6 +207,27 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
 #pragma unroll
             for (int r = 0; r < G; ++r)
                 if (rv & gm[r]) rk |= 1u << r;
+            if (STATS && tstat && tid < nvg) {
+                // log2 of the vote group's test statistic: the largest margin
+                // c*max_j s_rj - (m2 + log2 l + log2 tau - log2 Lq) of its rows,
+                // from the state the vote used (+inf for an empty state)
+                float dl = -INFINITY;
+#pragma unroll
+                for (int r = 0; r < G; ++r) {
+                    if (r / rpv != tid) continue;
+                    const float tm = fmaxf(fmaxf(wmax_sm[par][0][r], wmax_sm[par][1][r]),
+                                           fmaxf(wmax_sm[par][2][r], wmax_sm[par][3][r]));
+                    const float lz = SEED ? ltest[r] : lsum[r];
+                    float dr;
+                    if (tm == -INFINITY) dr = -INFINITY;
+                    else if (lz == 0.f) dr = INFINITY;
+                    else dr = tm * scale_log2 - (m2[r] + fast_log2(lz) + log2_tau - log2_lq);
+                    dl = fmaxf(dl, dr);
+                }
+                tstat[sidx * tps + t] = dl;
+            }
+        } else if (STATS && tstat && tid < nvg) {
+            tstat[sidx * tps + t] = NAN;  // tau = 0 runs no test
         }
         if (STATS && tid < nvg) {
             const bool gk = (rk >> (tid * rpv)) & 1u;
@@ -325,7 +346,7 @@ static void launch_decode_one(const DecArgs& a, hipStream_t s, int nparts, int p
     hipLaunchKernelGGL((decode_split_bf16_d128<G, GT, ST, SD, PV>), dim3(nparts, a.B * a.Hkv), dim3(256), 0, s,
                        (const bf16_t*)a.q, (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.part, a.Hq, a.Hkv, a.Lk,
                        a.Lcap, a.split_keys, a.nsplit, a.tps, a.words, a.scale_log2, a.log2_tau, a.log2_lq, a.kept,
-                       a.legal, a.bits, pbase, a.seeded ? 1 : 0, a.rpv);
+                       a.legal, a.bits, pbase, a.seeded ? 1 : 0, a.rpv, a.tstat);
 }
 
 template <int G, bool ST>
@@ -343,7 +364,7 @@ static void launch_decode_gs(const DecArgs& a, hipStream_t s) {
 
 template <int G>
 static void launch_decode_g(const DecArgs& a, hipStream_t s) {
-    if (a.kept || a.legal || a.bits) launch_decode_gs<G, true>(a, s);
+    if (a.kept || a.legal || a.bits || a.tstat) launch_decode_gs<G, true>(a, s);
     else launch_decode_gs<G, false>(a, s);
 }
 

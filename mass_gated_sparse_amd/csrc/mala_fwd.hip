@@ -53,11 +53,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
                                                         float* __restrict__ lse, int BH, int G, int L, int P, int Lk,
                                                         int Lkcap, int nqb, int words,
                                                         float scale_log2, float log2_tau, int32_t* __restrict__ kept,
-                                                        int32_t* __restrict__ legal, uint32_t* __restrict__ bits) {
+                                                        int32_t* __restrict__ legal, uint32_t* __restrict__ bits,
+                                                        float* __restrict__ tstat) {
     using namespace fwdk;
     __shared__ __attribute__((aligned(1024))) uint8_t kslot[2][BK * 256];  // K tile t in kslot[t & 1]
     __shared__ __attribute__((aligned(1024))) uint8_t vslot[2][BK * 256];  // V tile t in vslot[t & 1]
     __shared__ int vote_sm[2][4];
+    __shared__ float tstat_sm[2][4];  // statistics only: each wave's largest test margin
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     int qrank, bh;
@@ -87,6 +89,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     const float inv_scale_log2 = 1.f / scale_log2;
     const int jmax = (P + min(qb * BQ + BQ, L) - 1) / BK;
     const int tdiag = (P + qb * BQ) / BK;  // tiles t >= tdiag reach the block's first row
+    const int ntk = (Lk + BK - 1) / BK;    // key tiles of the cache (test-statistic row length)
 
     auto tile_dma = [&](const bf16_t* g, uint8_t* dst, int t) {
         const uint32_t la = lds_addr_of(dst) + 4096 * wave;
@@ -183,6 +186,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
             else thr_raw = (m2 + fast_log2(lsum) + log2_tau - log2_lq) * inv_scale_log2;
             const bool wv = wave_any(mx >= thr_raw);
             if (lane == 0) vote_sm[PAR][wave] = wv ? 1 : 0;
+            if (STATS && tstat) {
+                // log2 of the tile's test statistic: the largest margin
+                // c*max_j s_ij - (m2 + log2 l + log2 tau - log2 Lq) of a voting row
+                // (+inf for an empty state; rows without a visible key abstain)
+                const float rmx = fmaxf(mx, shfl_xor_f(mx, 32));
+                float dl;
+                if (!rvalid || rmx == -INFINITY) dl = -INFINITY;
+                else if (lsum == 0.f) dl = INFINITY;
+                else dl = rmx * scale_log2 - (m2 + fast_log2(lsum) + log2_tau - log2_lq);
+#pragma unroll
+                for (int m = 16; m >= 1; m >>= 1) dl = fmaxf(dl, shfl_xor_f(dl, m));
+                if (lane == 0) tstat_sm[PAR][wave] = dl;
+            }
         }
         if (t >= 1) scores(kslot[1 - PAR], sn);
         // K(t-2) and V(t+1), requested in the previous step, have landed (with
@@ -192,6 +208,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
         int vflags = 1;
         if (GATED) vflags = vote_sm[PAR][0] | vote_sm[PAR][1] | vote_sm[PAR][2] | vote_sm[PAR][3];
         const bool keep = vflags != 0;
+        if (STATS && tstat && tid == 0)  // tau = 0 runs no test: NaN
+            tstat[(long(bh) * nqb + qb) * ntk + t] =
+                GATED ? fmaxf(fmaxf(tstat_sm[PAR][0], tstat_sm[PAR][1]), fmaxf(tstat_sm[PAR][2], tstat_sm[PAR][3]))
+                      : NAN;
         if (t >= 3) tile_dma(kh, kslot[1 - PAR], t - 3);  // K(t-3) into the slot K(t-1) used
         if (keep) tile_dma(vh, vslot[PAR], t);              // V only for kept tiles
 
@@ -285,12 +305,12 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
     const int BH = a.B * a.H;
     if (a.Hkv < 1 || a.H % a.Hkv) return hipErrorInvalidValue;  // the API checked this already
     dim3 grid(unsigned(a.nqb) * unsigned(BH)), block(256);
-    const bool st = a.kept || a.legal || a.bits;
+    const bool st = a.kept || a.legal || a.bits || a.tstat;
 #define MALA_FWD_LAUNCH(GT, ST)                                                                           \
     hipLaunchKernelGGL((fwd_bf16_d128<GT, ST>), grid, block, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,   \
                        (const bf16_t*)a.v, (bf16_t*)a.o, a.lse, BH, a.H / a.Hkv, a.L, a.P, a.Lk, a.Lkcap,  \
                        a.nqb, a.words,                                                                       \
-                       a.scale_log2, a.log2_tau, a.kept, a.legal, a.bits)
+                       a.scale_log2, a.log2_tau, a.kept, a.legal, a.bits, a.tstat)
     if (a.gated) {
         if (st) MALA_FWD_LAUNCH(true, true);
         else MALA_FWD_LAUNCH(true, false);

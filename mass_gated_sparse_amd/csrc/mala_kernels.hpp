@@ -22,6 +22,7 @@ struct FwdArgs {
     bool gated;        // false for tau = 0
     int32_t *kept, *legal;
     uint32_t* bits;
+    float* tstat;      // statistics: log2 of each tile's test statistic [B, H, nqb, ceil(Lk/64)]
 };
 
 struct BwdArgs {
@@ -36,6 +37,7 @@ struct BwdArgs {
     bool gated, f32;
     int32_t *kept, *legal;
     uint32_t *bits, *aux_bits;  // aux_bits: the blocks the dK/dV kernel visited (debug)
+    float* tstat;               // statistics: log2 of each tile's test statistic [B, H, nqb, ntiles]
     hipEvent_t ev[4];           // optional timing events (see mala_stats)
 };
 
@@ -52,6 +54,7 @@ struct DecArgs {
     int rpv;      // query heads per vote (divides G)
     int32_t *kept, *legal;
     uint32_t* bits;
+    float* tstat;  // statistics: log2 of each (vote group, tile) test statistic [B, V, nsplit, tps]
 };
 
 // Records e on s when e is non-null.

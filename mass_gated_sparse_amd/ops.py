@@ -60,13 +60,13 @@ def _expect_qkv(q, k, v, nq_dims=4):
 
 
 def _expect_stats(st, shapes):
-    """Caller-supplied statistics buffers must be int32 of the sizes the
-    library writes (shapes: name -> shape)."""
+    """Caller-supplied statistics buffers must be of the sizes and types the
+    library writes (shapes: name -> shape; test_stat float32, the rest int32)."""
     if st is None:
         return
     for n, shape in shapes.items():
         if n in st and st[n] is not None:
-            _expect(st[n], f"stats[{n!r}]", shape, torch.int32)
+            _expect(st[n], f"stats[{n!r}]", shape, torch.float32 if n == "test_stat" else torch.int32)
             _check_dev(st[n])
     if len(st.get("events", ())) > 4:
         raise ValueError("at most 4 events")
@@ -74,7 +74,8 @@ def _expect_stats(st, shapes):
 
 def _prefill_stat_shapes(B, H, nqb, ntiles):
     w = -(-ntiles // 32)
-    return {"kept": (B, H, nqb), "legal": (B, H, nqb), "keep_bits": (B, H, nqb, w), "keep_bits_dkdv": (B, H, nqb, w)}
+    return {"kept": (B, H, nqb), "legal": (B, H, nqb), "keep_bits": (B, H, nqb, w), "keep_bits_dkdv": (B, H, nqb, w),
+            "test_stat": (B, H, nqb, ntiles)}
 
 
 def _stream(stream=None):
@@ -82,15 +83,20 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def prefill_stats_buffers(B, H, L, tile, device, dkdv=False):
+def prefill_stats_buffers(B, H, L, tile, device, dkdv=False, test_stat=False, Lk=None):
+    """Statistics buffers of a prefill call (Lk: key count when it differs
+    from L, as in a chunk).  test_stat (bf16 only) starts as NaN: entries of
+    tiles that are not tested stay NaN."""
     bq, bk = tile
-    nqb, nt = -(-L // bq), -(-L // bk)
+    nqb, nt = -(-L // bq), -(-(L if Lk is None else Lk) // bk)
     words = -(-nt // 32)
     st = {"kept": torch.zeros(B, H, nqb, dtype=torch.int32, device=device),
           "legal": torch.zeros(B, H, nqb, dtype=torch.int32, device=device),
           "keep_bits": torch.zeros(B, H, nqb, words, dtype=torch.int32, device=device)}
     if dkdv:
         st["keep_bits_dkdv"] = torch.zeros(B, H, nqb, words, dtype=torch.int32, device=device)
+    if test_stat:
+        st["test_stat"] = torch.full((B, H, nqb, nt), float("nan"), dtype=torch.float32, device=device)
     return st
 
 
@@ -102,6 +108,8 @@ def _stats_struct(st):
         return None
     s = Stats(*(ctypes.c_void_p(st[n].data_ptr()) if n in st else None
                 for n in ("kept", "legal", "keep_bits", "keep_bits_dkdv")))
+    if st.get("test_stat") is not None:
+        s.test_stat = ctypes.c_void_p(st["test_stat"].data_ptr())
     for i, ev in enumerate(st.get("events", ())):
         if ev is not None:
             if not ev.cuda_event:
@@ -132,7 +140,7 @@ def fwd(q, k, v, tau, tile=None, scale=0.0, stats=False):
     tile = tile or DEFAULT_TILE[q.dtype]
     o = torch.empty_like(q)
     lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device)
-    st = prefill_stats_buffers(B, H, L, tile, q.device) if stats else None
+    st = prefill_stats_buffers(B, H, L, tile, q.device, test_stat=q.dtype == torch.bfloat16) if stats else None
     fwd_into(q, k, v, o, lse, tau, tile, scale, st)
     return (o, lse, st) if stats else (o, lse)
 
@@ -160,12 +168,7 @@ def fwd_chunk(q, kc, vc, P, tau, tile=None, scale=0.0, stats=False):
     tile = tile or DEFAULT_TILE[q.dtype]
     o = torch.empty_like(q)
     lse = torch.empty(B, H, Lq, dtype=torch.float32, device=q.device)
-    st = None
-    if stats:
-        nqb, nt = -(-Lq // tile[0]), -(-(int(P) + Lq) // tile[1])
-        st = {"kept": torch.zeros(B, H, nqb, dtype=torch.int32, device=q.device),
-              "legal": torch.zeros(B, H, nqb, dtype=torch.int32, device=q.device),
-              "keep_bits": torch.zeros(B, H, nqb, -(-nt // 32), dtype=torch.int32, device=q.device)}
+    st = prefill_stats_buffers(B, H, Lq, tile, q.device, test_stat=True, Lk=int(P) + Lq) if stats else None
     fwd_chunk_into(q, kc, vc, P, o, lse, tau, tile, scale, st)
     return (o, lse, st) if stats else (o, lse)
 
@@ -206,7 +209,7 @@ def bwd(q, k, v, o, lse, do, tau, tile=None, scale=0.0, stats=False):
     tile = tile or DEFAULT_TILE[q.dtype]
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = bwd_workspace(q, tile)
-    st = prefill_stats_buffers(B, H, L, tile, q.device, dkdv=True) if stats else None
+    st = prefill_stats_buffers(B, H, L, tile, q.device, dkdv=True, test_stat=q.dtype == torch.bfloat16) if stats else None
     bwd_into(q, k, v, o, lse, do, dq, dk, dv, tau, ws, tile, scale, st)
     return (dq, dk, dv, st) if stats else (dq, dk, dv)
 
@@ -237,15 +240,20 @@ def mala_attention(q, k, v, tau=1.0, tile=None, scale=0.0):
     return _MalaAttention.apply(q.contiguous(), k.contiguous(), v.contiguous(), float(tau), tile, float(scale))
 
 
-def decode_stats_buffers(B, Hkv, Lk, split_keys, bk, device, vote_groups=1):
+def decode_stats_buffers(B, Hkv, Lk, split_keys, bk, device, vote_groups=1, test_stat=False):
     """Decode statistics for B sequences, Hkv KV heads and vote_groups vote
-    groups per KV head (G / rows_per_vote; 1 when the whole group votes)."""
+    groups per KV head (G / rows_per_vote; 1 when the whole group votes);
+    test_stat starts as NaN."""
     nsplit = -(-Lk // split_keys)
-    words = -(-(split_keys // bk) // 32)
+    tps = split_keys // bk
+    words = -(-tps // 32)
     V = Hkv * vote_groups
-    return {"kept": torch.zeros(B, V, nsplit, dtype=torch.int32, device=device),
-            "legal": torch.zeros(B, V, nsplit, dtype=torch.int32, device=device),
-            "keep_bits": torch.zeros(B, V, nsplit, words, dtype=torch.int32, device=device)}
+    st = {"kept": torch.zeros(B, V, nsplit, dtype=torch.int32, device=device),
+          "legal": torch.zeros(B, V, nsplit, dtype=torch.int32, device=device),
+          "keep_bits": torch.zeros(B, V, nsplit, words, dtype=torch.int32, device=device)}
+    if test_stat:
+        st["test_stat"] = torch.full((B, V, nsplit, tps), float("nan"), dtype=torch.float32, device=device)
+    return st
 
 
 def _vote_groups(Hq, Hkv, rows_per_vote):
@@ -277,7 +285,8 @@ def decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys=4096, bk=64, scale=0.
     if stats is not None and int(split_keys) > 0 and int(bk) > 0 and vg:  # (bad sizes: the library rejects them)
         nsplit, w = -(-int(Lk) // int(split_keys)), -(-(int(split_keys) // int(bk)) // 32)
         V = Hkv * vg
-        _expect_stats(stats, {"kept": (B, V, nsplit), "legal": (B, V, nsplit), "keep_bits": (B, V, nsplit, w)})
+        _expect_stats(stats, {"kept": (B, V, nsplit), "legal": (B, V, nsplit), "keep_bits": (B, V, nsplit, w),
+                              "test_stat": (B, V, nsplit, int(split_keys) // int(bk))})
     _check_dev(q, kc, vc, o, ws, *([lse] if lse is not None else []))
     name = "mala_decode_seeded" if seeded else "mala_decode"
     rc = getattr(_lib.load(), name)(_ptr(q), _ptr(kc), _ptr(vc), B, Hq, Hkv, int(Lk), Lcap, d, _dt(q), float(tau),
@@ -299,7 +308,8 @@ def decode(q, kc, vc, Lk, tau, split_keys=4096, bk=64, scale=0.0, stats=False, s
     ws = decode_workspace(B, Hq, Hkv, Lk, d, split_keys, q.device)
     st = None
     if stats:
-        st = decode_stats_buffers(B, Hkv, Lk, split_keys, bk, q.device, _vote_groups(Hq, Hkv, rows_per_vote) or 1)
+        st = decode_stats_buffers(B, Hkv, Lk, split_keys, bk, q.device, _vote_groups(Hq, Hkv, rows_per_vote) or 1,
+                                  test_stat=True)
     decode_into(q, kc, vc, Lk, o, lse, tau, ws, split_keys, bk, scale, st, seeded=seeded,
                 rows_per_vote=rows_per_vote)
     return (o, lse, st) if stats else (o, lse)

@@ -48,3 +48,29 @@ def bf16_to_f64(t):
     """fp64 numpy values of a torch bf16/fp32 tensor."""
     import torch
     return t.detach().to(torch.float64).cpu().numpy()
+
+
+# log2 units: fp32 scores and running sums against fp64.  Measured worst
+# differences are 1.4e-5 (prefill, L <= 4096) and 5e-6 (decode); 1e-4 stays
+# below the 1.44e-4 that the |T - 1| <= 1e-4 decision band spans in log2 T,
+# so a statistic within it cannot flip a decision outside the band.
+TOL_TSTAT = 1e-4
+
+
+def tstat_report(gpu_ts, ora_T, legal, tau):
+    """The GPU's per-tile statistic (log2 T) against the oracle's T on every
+    legal tile: returns (worst |difference| over tiles where both are finite,
+    number of tiles where they disagree otherwise).  At tau = 0 the GPU writes
+    NaN (no test is run)."""
+    g = np.asarray(gpu_ts, dtype=np.float64)
+    legal = np.broadcast_to(legal, g.shape)
+    if tau == 0.0:
+        return 0.0, int((legal & ~np.isnan(g)).sum())
+    with np.errstate(divide="ignore"):
+        o = np.log2(np.asarray(ora_T, dtype=np.float64))
+    fin = legal & np.isfinite(g) & np.isfinite(o)
+    worst = float(np.abs(g[fin] - o[fin]).max()) if fin.any() else 0.0
+    other = legal & ~fin
+    bad = int((other & ~(np.isinf(g) & np.isinf(o) & (np.sign(g) == np.sign(o)))).sum())
+    return worst, bad
+

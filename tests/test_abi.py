@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mala_version() == 101
+    assert lib.mala_version() == 102
     assert lib.mala_status_string(OK) == b"ok"
     assert lib.mala_status_string(INVALID) == b"invalid argument"
     assert lib.mala_status_string(UNSUPPORTED) == b"unsupported configuration"
@@ -124,6 +124,20 @@ def fwd_chunk(lib, q=P, B=1, H=4, Hkv=2, Lq=256, Poff=1000, Lcap=2048, d=128, dt
 def test_fwd_chunk_rejects(lib, kw, status, msg):
     assert fwd_chunk(lib, **kw) == status
     assert msg in lib.mala_last_error().decode()
+
+
+def test_test_stat_layout_and_fp32_rejection(lib):
+    """mala_stats ends with the test_stat pointer (after the four events);
+    the fp32 path does not write it and says so before queuing anything."""
+    from mass_gated_sparse_amd._lib import Stats, Tile
+    assert Stats.test_stat.offset == 8 * 8 and ctypes.sizeof(Stats) == 9 * 8
+    st = Stats()
+    st.test_stat = P
+    rc = lib.mala_fwd(P, P, P, 1, 2, 2, 256, 64, 1, 1.0, Tile(64, 64), 0.0, P, P, ctypes.byref(st), None)
+    assert rc == UNSUPPORTED and "test_stat" in lib.mala_last_error().decode()
+    rc = lib.mala_bwd(P, P, P, P, P, P, 1, 2, 2, 256, 64, 1, 1.0, Tile(64, 64), 0.0, P, P, P, ctypes.byref(st),
+                      ALIGNED_WS, 1 << 30, None)
+    assert rc == UNSUPPORTED and "test_stat" in lib.mala_last_error().decode()
 
 
 def bwd(lib, ws=ALIGNED_WS, ws_bytes=1 << 30, dq=P, dout=P, tau=1.0, d=128):

@@ -13,8 +13,8 @@ import pytest
 
 import oracle
 from synth import WORKLOADS, prefill_inputs, decode_inputs, to_f64
-from tests.parity import (BAND, TOL_GRAD, TOL_O, bf16_to_f64, chunk_legal_mask, decision_report, legal_mask,
-                          rel_l2)
+from tests.parity import (BAND, TOL_GRAD, TOL_O, TOL_TSTAT, bf16_to_f64, chunk_legal_mask, decision_report,
+                          legal_mask, rel_l2, tstat_report)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -67,6 +67,9 @@ def _check_fwd(ops, w, x, tau, bq, bk):
     e_l = float(np.abs(lse.cpu().numpy() - ol).max())
     assert e_o <= TOL_O, e_o
     assert e_l <= 1e-3, e_l
+    if "test_stat" in st:  # the GPU's own test statistic, tile by tile
+        worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT, legal, tau)
+        assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     return dict(o=o, lse=lse, keep=gk, T=oT, near=near, err_o=e_o, legal=legal)
 
 
@@ -103,6 +106,9 @@ def _check_bwd(ops, w, x, tau, bq, bk):
     bad, near, near_list = decision_report(gk, ok, oT, legal)
     assert bad == 0, f"backward decisions differ on {bad} tiles"
     assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+    if "test_stat" in st:
+        worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT, legal, tau)
+        assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     errs = [rel_l2(bf16_to_f64(a), b) for a, b in ((dq, gq), (dk, gkk), (dv, gv))]
     if tau == math.inf:
         assert all(float(t.abs().max()) == 0.0 for t in (dq, dk, dv))
@@ -307,6 +313,8 @@ def test_decode_bf16(ops, Lk, split, Lcap, tau):
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
     assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+    worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT[:, :, 0], legal, tau)
+    assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
 
 
 def seeded_legal(Lk, split, bk=64):
@@ -415,6 +423,8 @@ def test_decode_rows_per_vote_bf16(ops, Hq, Hkv, rpv, Lk, split, tau, seeded):
     ok, oT = ok.reshape(gk.shape), oT.reshape(gk.shape)
     bad, near, _ = decision_report(gk, ok, oT, legal)
     assert bad == 0
+    worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT, legal, tau)
+    assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
     assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
