@@ -241,6 +241,7 @@ def test_python_wrappers_check_shapes_before_the_device():
         (lambda: ops.decode_into(z(2, 8, 128), z(2, 2, 512, 128), z(2, 2, 512, 128), 500, z(2, 8, 128),
                                  z(2, 8, dt=torch.float32), 1.0, z(4096, dt=torch.uint8), split_keys=128,
                                  stats={"keep_bits": z(2, 2, 1, 1, dt=torch.int32)}), "keep_bits"),
+        (lambda: ops.fwd_into(q, k, k, o, lse, 1.0, stats={"test_stat": z(1, 4, 2, 4)}), "test_stat"),  # bf16, not f32
         # one vote per query head: statistics are per head (8), not per KV head (2)
         (lambda: ops.decode_into(z(2, 8, 128), z(2, 2, 512, 128), z(2, 2, 512, 128), 500, z(2, 8, 128),
                                  z(2, 8, dt=torch.float32), 1.0, z(4096, dt=torch.uint8), split_keys=128,

@@ -274,6 +274,8 @@ def test_fwd_chunk_bf16(ops, P, Lq, spare, tau):
     legal = chunk_legal_mask(Lq, P, 128, 64)
     bad, near, _ = decision_report(gk, ok, oT, legal)
     assert bad == 0, f"chunk decisions differ outside the band on {bad} tiles"
+    worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT, legal, tau)
+    assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
     assert (st["legal"].cpu().numpy() == legal.sum(-1)[None, None, :]).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
@@ -346,6 +348,8 @@ def test_decode_seeded_bf16(ops, Lk, split, Lcap, tau):
     legal = seeded_legal(Lk, split)
     bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal)
     assert bad == 0
+    worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT[:, :, 0], legal, tau)
+    assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
     assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
