@@ -264,6 +264,36 @@ def test_decisions_by_direct_sums(tau):
     assert flips > 0
 
 
+@pytest.mark.parametrize("tau", [0.5, 1.0, 4.0])
+def test_backward_statistic_by_direct_probabilities(tau):
+    """Backward paragraph: every legal tile is tested against the final
+    log-normalizer.  Recomputed here from P_ij = exp(s_ij - lse_i) with the
+    lse the forward wrote: T = max over rows with a visible key of
+    max_j P_ij * Lq_i / tau, kept iff T >= 1, with no forced keep; the
+    oracle's backward T and decisions must match."""
+    w, (q, k, v, do) = _prefill("mw8k", L=520, heads=[1, 4])
+    bq, bk = 128, 64
+    o, lse, _, _ = oracle.fwd(q, k, v, tau, bq, bk)
+    _, _, _, kb, Tb = oracle.bwd(q, k, v, o, lse, do, tau, bq, bk)
+    L = q.shape[2]
+    scale = 1 / math.sqrt(w.d)
+    skipped = 0
+    for h in range(q.shape[1]):
+        P = np.exp(scale * q[0, h] @ k[0, h].T - lse[0, h][:, None])
+        for b in range(kb.shape[2]):
+            rows = np.arange(b * bq, min(b * bq + bq, L))
+            for t in range(rows[-1] // bk + 1):
+                cols = np.arange(t * bk, min(t * bk + bk, L))
+                vis = cols[None, :] <= rows[:, None]
+                voting = vis.any(axis=1)
+                ratio = np.where(vis, P[np.ix_(rows, cols)], 0.0).max(axis=1) * (rows + 1) / tau
+                Tt = ratio[voting].max()
+                assert abs(Tt - Tb[0, h, b, t]) <= 1e-9 * Tt, (h, b, t)
+                assert bool(kb[0, h, b, t]) == (Tt >= 1.0), (h, b, t, Tt)
+                skipped += Tt < 1.0
+    assert skipped > 0
+
+
 # ---------------------------------------------------------------- P9: log-domain form of the test
 @pytest.mark.parametrize("tau", [0.5, 1.0, 4.0])
 def test_log_domain_test_gives_same_decisions(tau):
