@@ -392,6 +392,46 @@ def test_decode_one_split_one_row_equals_forward_row(tau):
         assert (keep[0, g, h % w.group, 0, :nt] == kf[0, 0, Lk - 1, :nt]).all()
 
 
+@pytest.mark.parametrize("tau,rpv", [(1.0, None), (4.0, None), (4.0, 2), (16.0, 1)])
+def test_decode_decisions_by_direct_sums(tau, rpv):
+    """Decode's statistic recomputed without online rescaling: in each
+    partition, tiles are visited newest first, each row's normalizer is the
+    plain sum of exp(s) over keys of previously kept tiles of that partition
+    (none at the first tile, which is therefore kept), and a vote group's
+    T = max over its rows of max_j exp(s_j)/Z * Lk/tau."""
+    w, q, kc, vc = _decode_small(1500)
+    Lk, S, bk = 1500, 512, 64
+    o, lse, keep, T = oracle.decode(q, kc, vc, Lk, tau, S, bk, rows_per_vote=rpv)
+    G = w.group
+    R = G if rpv is None else rpv
+    nsplit, tps = oracle.decode_shapes(Lk, S, bk)
+    skipped = 0
+    for g in range(kc.shape[1]):
+        s = q[0, g * G:(g + 1) * G] @ kc[0, g, :Lk].T / math.sqrt(w.d)
+        for vg in range(G // R):
+            rows = range(vg * R, vg * R + R)
+            for p in range(nsplit):
+                Z = {r: 0.0 for r in rows}
+                k1 = min(p * S + S, Lk)
+                for t in range(-(-(k1 - p * S) // bk) - 1, -1, -1):
+                    cols = range(p * S + t * bk, min(p * S + t * bk + bk, k1))
+                    Tt = 0.0
+                    for r in rows:
+                        if Z[r] == 0.0:
+                            Tt = math.inf
+                            continue
+                        Tt = max(Tt, max(math.exp(s[r, j]) for j in cols) / Z[r] * Lk / tau)
+                    kp = Tt >= 1.0
+                    assert kp == bool(keep[0, g, vg, p, t]), (g, vg, p, t, Tt)
+                    if math.isfinite(Tt):
+                        assert abs(Tt - T[0, g, vg, p, t]) <= 1e-9 * Tt, (g, vg, p, t)
+                    if kp:
+                        for r in rows:
+                            Z[r] += sum(math.exp(s[r, j]) for j in cols)
+                    skipped += not kp
+    assert skipped > 0
+
+
 @pytest.mark.parametrize("tau", [1.0, 16.0])
 def test_decode_is_dense_over_kept_keys_and_bounded(tau):
     """The exact merge of partition states makes decode output the softmax over
