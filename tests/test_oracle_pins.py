@@ -666,6 +666,52 @@ def test_seeded_decode_keeps_nothing_by_force():
     assert keep_plain[0, 0, 0, :3].all() and keep_plain[0, 0, 0, 3].sum() == 1
 
 
+@pytest.mark.parametrize("tau,rpv", [(1.0, None), (4.0, 2), (16.0, 1)])
+def test_seeded_decode_decisions_by_direct_sums(tau, rpv):
+    """Seeded decode recomputed with plain sums: partition 0 is the newest
+    split_keys/bk tiles and starts with an empty normalizer; each older
+    partition (tiles counted back from there, the oldest one ragged) starts
+    from partition 0's final sum and adds its own kept tiles, newest first;
+    a vote group's T = max over its rows of max_j exp(s_j)/Z * Lk/tau."""
+    w, q, kc, vc = _decode_small(1500)
+    Lk, S, bk = 1500, 256, 64
+    o, lse, keep, T = oracle.decode_seeded(q, kc, vc, Lk, tau, S, bk, rows_per_vote=rpv)
+    G = w.group
+    R = G if rpv is None else rpv
+    tps, jd = S // bk, (Lk - 1) // bk
+    nsplit = -(-(jd + 1) // tps)
+    assert keep.shape[3] == nsplit
+    skipped = 0
+    for g in range(kc.shape[1]):
+        s = q[0, g * G:(g + 1) * G] @ kc[0, g, :Lk].T / math.sqrt(w.d)
+        for vg in range(G // R):
+            rows = range(vg * R, vg * R + R)
+            Z0 = None
+            for p in range(nsplit):
+                Z = {r: 0.0 for r in rows} if p == 0 else dict(Z0)
+                hi = jd - p * tps
+                lo = max(hi - tps + 1, 0)
+                for j in range(hi, lo - 1, -1):
+                    cols = range(j * bk, min(j * bk + bk, Lk))
+                    Tt = 0.0
+                    for r in rows:
+                        if Z[r] == 0.0:
+                            Tt = math.inf
+                            continue
+                        Tt = max(Tt, max(math.exp(s[r, c]) for c in cols) / Z[r] * Lk / tau)
+                    kp = Tt >= 1.0
+                    assert kp == bool(keep[0, g, vg, p, j - lo]), (g, vg, p, j, Tt)
+                    if math.isfinite(Tt):
+                        assert abs(Tt - T[0, g, vg, p, j - lo]) <= 1e-9 * Tt, (g, vg, p, j)
+                    if kp:
+                        for r in rows:
+                            Z[r] += sum(math.exp(s[r, c]) for c in cols)
+                    skipped += not kp
+                if p == 0:
+                    Z0 = Z
+    assert skipped > 0
+
+
 @pytest.mark.parametrize("tau", [1.0, 16.0])
 def test_seeded_decode_is_dense_over_kept_keys_and_bounded(tau):
     """The output is softmax attention over the union of kept tiles, and the
