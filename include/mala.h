@@ -46,8 +46,9 @@
  *      (ragged L allowed);
  *      MALA_BF16 with d = 128 and tile {128, 64} (grouped K/V heads allowed);
  *      MALA_F32  with d = 64  and tile {64, 64} (H == Hkv only).
- *  - decode: Hq % Hkv == 0 with G = Hq/Hkv <= 8; MALA_BF16, d = 128, bk = 64,
- *      split_keys a positive multiple of bk.
+ *  - decode: Hq % Hkv == 0 (else MALA_ERR_INVALID_ARG) with G = Hq/Hkv one of
+ *      1, 2, 4, 8; MALA_BF16, d = 128, bk = 64, split_keys a positive multiple
+ *      of bk.
  */
 #ifndef MALA_H
 #define MALA_H

@@ -219,7 +219,9 @@ static mala_status decode_call(const char* name, bool seeded, const void* q, con
     if (dtype != MALA_BF16 && dtype != MALA_F32) return fail(MALA_ERR_INVALID_ARG, "unknown dtype %d", int(dtype));
     if (Hq % Hkv) return fail(MALA_ERR_INVALID_ARG, "Hq (%d) not a multiple of Hkv (%d)", Hq, Hkv);
     const int G = Hq / Hkv;
-    if (dtype != MALA_BF16 || d != 128 || bk != 64 || G > 8 || split_keys % bk)
+    // kernel instantiations exist for G = 1, 2, 4 and 8 query heads per KV head
+    const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
+    if (dtype != MALA_BF16 || d != 128 || bk != 64 || !g_ok || split_keys % bk)
         return fail(MALA_ERR_UNSUPPORTED, "unsupported decode instantiation dtype=%d d=%d bk=%d G=%d split=%d",
                     int(dtype), d, bk, G, split_keys);
     if (rows_per_vote == 0) rows_per_vote = G;

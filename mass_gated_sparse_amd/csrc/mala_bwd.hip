@@ -54,8 +54,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dout, const float* __restrict__ Dv, const float* __restrict__ lse2,
     const float* __restrict__ thr, bf16_t* __restrict__ dq, int BH, int G, int L, int nqb, int words, float scale,
-    float scale_log2, int32_t* __restrict__ kept, int32_t* __restrict__ legal, uint32_t* __restrict__ bits,
-    uint32_t* __restrict__ dbits, float* __restrict__ tstat) {
+    float scale_log2, float log2_tau, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
+    uint32_t* __restrict__ bits, uint32_t* __restrict__ dbits, float* __restrict__ tstat) {
     using namespace bwdk;
     __shared__ __attribute__((aligned(1024))) uint8_t kring[3][BK * 256];
     __shared__ float tstat_sm[2][4];  // statistics only: each wave's largest test margin
@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
             for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
         mx = fmaxf(mx, shfl_xor_f(mx, 32));
         float dl = (mx == -INFINITY) ? -INFINITY : (mx - th) * scale_log2;
+        if (row == 0 && mx != -INFINITY) dl = -log2_tau;  // row 0: P_00 = 1, T = 1/tau exactly
 #pragma unroll
         for (int m = 16; m >= 1; m >>= 1) dl = fmaxf(dl, shfl_xor_f(dl, m));
         return dl;
@@ -977,7 +978,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
 #define MALA_DQ_LAUNCH(GT, ST)                                                                                \
     hipLaunchKernelGGL((bwd_dq_bf16_d128<GT, ST>), g2, blk, 0, s, (const bf16_t*)a.q, (const bf16_t*)a.k,     \
                        (const bf16_t*)a.v, (const bf16_t*)a.dout, a.Dv, a.lse2, a.thr, (bf16_t*)a.dq, BH, G, a.L, \
-                       a.nqb, a.words, a.scale, a.scale_log2, a.kept, a.legal, a.bits, a.dbits, a.tstat)
+                       a.nqb, a.words, a.scale, a.scale_log2, a.log2_tau, a.kept, a.legal, a.bits, a.dbits,    \
+                       a.tstat)
     if (a.gated) {
         if (st) MALA_DQ_LAUNCH(true, true);
         else MALA_DQ_LAUNCH(true, false);

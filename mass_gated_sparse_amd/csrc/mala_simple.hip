@@ -7,6 +7,8 @@
 // paragraphs.  All tests are done in the log2 domain: with s2 = s * log2(e)
 // a row keeps a tile iff max_j s2_ij >= m2_i + log2(l_i) + log2(tau) - log2(Lq_i),
 // which is the ratio test exp(max s - m)/l >= tau/Lq written with logarithms.
+#include <float.h>
+
 #include "mala_kernels.hpp"
 
 namespace mala {
@@ -117,6 +119,15 @@ __global__ __launch_bounds__(BQ) void simple_fwd_f32(const float* __restrict__ q
 //   thr[i]  = (lse2_i + log2(tau) - log2(i+1)) / (scale*log2(e))  -- the raw
 //             dot-product level a score must reach for row i to keep a tile.
 // Both backward kernels read these same values, so their decisions agree.
+// Row 0 is exact: it sees only key 0, which the forward always keeps, so its
+// final normalizer is exp(s_00), P_00 = 1 and its vote is 1 >= tau (equality
+// keeps).  A threshold derived from the fp32 lse would leave that tie at
+// tau = 1 to rounding, so row 0 gets -FLT_MAX (its one finite score always
+// passes; masked scores, -inf, never do) when tau <= 1 and +inf otherwise.
+__device__ __forceinline__ float bwd_row_threshold(int i, float l2, float log2_tau, float scale_log2) {
+    if (i == 0) return log2_tau <= 0.f ? -FLT_MAX : INFINITY;
+    return (l2 + log2_tau - fast_log2(float(i + 1))) / scale_log2;
+}
 template <typename T, int D>
 __global__ void bwd_prep(const T* __restrict__ o, const T* __restrict__ dout, const float* __restrict__ lse,
                          float* __restrict__ Dv, float* __restrict__ lse2, float* __restrict__ thr, long rows, int L,
@@ -133,7 +144,7 @@ __global__ void bwd_prep(const T* __restrict__ o, const T* __restrict__ dout, co
         const float l2 = lse[r] * kLog2e;
         Dv[r] = s;
         lse2[r] = l2;
-        thr[r] = (l2 + log2_tau - fast_log2(float(i + 1))) / scale_log2;
+        thr[r] = bwd_row_threshold(i, l2, log2_tau, scale_log2);
     }
 }
 
@@ -164,7 +175,7 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16_d128(const bf16_t* __restri
         const float l2 = lse[r] * kLog2e;
         Dv[r] = s;
         lse2[r] = l2;
-        thr[r] = (l2 + log2_tau - fast_log2(float(i + 1))) / scale_log2;
+        thr[r] = bwd_row_threshold(i, l2, log2_tau, scale_log2);
     }
 }
 

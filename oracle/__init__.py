@@ -36,10 +36,10 @@ def _lib():
         lib = ctypes.CDLL(p)
         lib.oracle_fwd_head.argtypes = [_D, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                         ctypes.c_int, ctypes.c_int, _L, ctypes.c_long, _U8, ctypes.c_double,
-                                        _D, _D, _U8, _D]
+                                        _D, _D, _U8, _D, _D]
         lib.oracle_bwd_head.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double,
                                         ctypes.c_double, ctypes.c_int, ctypes.c_int, _L, ctypes.c_long, _L,
-                                        ctypes.c_long, _U8, ctypes.c_double, _D, _D, _D, _U8, _D]
+                                        ctypes.c_long, _U8, ctypes.c_double, _D, _D, _D, _U8, _D, _D]
         lib.oracle_decode_group.argtypes = [_D, ctypes.c_int, _D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double,
                                             ctypes.c_double, ctypes.c_long, ctypes.c_int, ctypes.c_int, _U8,
                                             ctypes.c_double, _D, _D, _U8, _D, _D, _D, _D]
@@ -50,12 +50,9 @@ def _lib():
         lib.oracle_decode_seeded_groups.argtypes = lib.oracle_decode_groups.argtypes
         lib.oracle_fwd_chunk_head.argtypes = [_D, _D, _D, ctypes.c_long, ctypes.c_long, ctypes.c_int,
                                               ctypes.c_double, ctypes.c_double, ctypes.c_int, ctypes.c_int, _L,
-                                              ctypes.c_long, _U8, ctypes.c_double, _D, _D, _U8, _D]
-        lib.oracle_omitted_head.argtypes = [_D, _D, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_int,
-                                            ctypes.c_int, _U8, _L, ctypes.c_long, _D, _D]
+                                              ctypes.c_long, _U8, ctypes.c_double, _D, _D, _U8, _D, _D]
         for f in ("oracle_fwd_head", "oracle_bwd_head", "oracle_decode_group", "oracle_decode_groups",
-                  "oracle_decode_seeded_group", "oracle_decode_seeded_groups", "oracle_omitted_head",
-                  "oracle_fwd_chunk_head"):
+                  "oracle_decode_seeded_group", "oracle_decode_seeded_groups", "oracle_fwd_chunk_head"):
             getattr(lib, f).restype = ctypes.c_int
         _LIB = lib
     return _LIB
@@ -108,7 +105,7 @@ def _group(H, k):
     return H // Hkv
 
 
-def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
+def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None, scales=False):
     """MALA forward.  Returns (o, lse, keep, T); keep/T are [B, H, nqb, ntiles].
     q is [B, H, L, d]; k, v are [B, Hkv, L, d] with H % Hkv == 0.
 
@@ -116,6 +113,8 @@ def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     rows of other blocks are left NaN.
     replay: optional uint8 [B, H, nqb, ntiles] decisions adopted on tiles with
     |T - 1| <= band.
+    scales: also return each row's error scale rs [B, H, L] (see
+    oracle_fwd_head), for the parity tests' per-row bound.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, L, d = q.shape
@@ -128,20 +127,21 @@ def fwd(q, k, v, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
     T = np.full((B, H, nqb, nt), np.nan)
     ids, n = _ids(qblocks)
     rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
+    rs = np.full((B, H, L), np.nan) if scales else None
 
     def one(b, h):
         g = h // G  # the K/V head query head h reads
         rc = _lib().oracle_fwd_head(_p(q[b, h], _D), _p(k[b, g], _D), _p(v[b, g], _D), L, d, scale, float(tau),
                                     bq, bk, _p(ids, _L), n, _p(None if rp is None else rp[b, h], _U8),
                                     float(band), _p(o[b, h], _D), _p(lse[b, h], _D), _p(keep[b, h], _U8),
-                                    _p(T[b, h], _D))
+                                    _p(T[b, h], _D), _p(None if rs is None else rs[b, h], _D))
         _check(rc, "oracle_fwd_head")
 
     _per_head(B, H, one)
-    return o, lse, keep, T
+    return (o, lse, keep, T, rs) if scales else (o, lse, keep, T)
 
 
-def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None):
+def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None, scales=False):
     """MALA forward of a query chunk against a key cache (chunked prefill).
 
     q: [B, H, Lq, d], rows at key positions p0 .. p0 + Lq - 1; k, v:
@@ -149,7 +149,7 @@ def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4, qblo
     sees, its own included).  Row i has Lq_i = p0 + i + 1 visible keys.
     Returns (o, lse, keep, T); keep/T are [B, H, ceil(Lq/bq), ceil((p0+Lq)/bk)].
     qblocks: optional query-block indices of the chunk to compute (others
-    left NaN / 0).
+    left NaN / 0).  scales: also return the rows' error scales [B, H, Lq].
     """
     q = _f64(q)
     B, H, Lq, d = q.shape
@@ -164,6 +164,7 @@ def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4, qblo
     T = np.full((B, H, nqb, nt), np.nan)
     rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
     ids, n = _ids(qblocks)
+    rs = np.full((B, H, Lq), np.nan) if scales else None
 
     def one(b, h):
         g = h // G
@@ -171,14 +172,15 @@ def fwd_chunk(q, k, v, p0, tau, bq, bk, scale=None, replay=None, band=1e-4, qblo
                                           scale, float(tau), bq, bk, _p(ids, _L), n,
                                           _p(None if rp is None else rp[b, h], _U8),
                                           float(band), _p(o[b, h], _D), _p(lse[b, h], _D), _p(keep[b, h], _U8),
-                                          _p(T[b, h], _D))
+                                          _p(T[b, h], _D), _p(None if rs is None else rs[b, h], _D))
         _check(rc, "oracle_fwd_chunk_head")
 
     _per_head(B, H, one)
-    return o, lse, keep, T
+    return (o, lse, keep, T, rs) if scales else (o, lse, keep, T)
 
 
-def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None, ktiles=None):
+def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qblocks=None, ktiles=None,
+        scales=False):
     """MALA backward against the given forward state (o, lse).
 
     Returns (dq, dk, dv, keep, T).  qblocks / ktiles restrict which dq rows /
@@ -186,6 +188,9 @@ def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qb
     (k, v: [B, Hkv, L, d]) every query head's contribution is computed with
     its shared K/V and dk, dv of a K/V head are the sum over its query heads
     (the gradient of a tensor used by several heads).
+    scales: also return a dict of the rows' error scales (see oracle_bwd_head):
+    "rq", "cq" [B, H, L] for dq rows; "rk", "ck", "rv" [B, Hkv, L] for dk and
+    dv rows (root sum of squares over the query heads of a group).
     """
     q, k, v, o, lse, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(lse), _f64(do)
     B, H, L, d = q.shape
@@ -200,6 +205,7 @@ def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qb
     qi, nq = _ids(qblocks)
     ki, nk = _ids(ktiles)
     rp = None if replay is None else np.ascontiguousarray(replay, dtype=np.uint8)
+    es = np.full((B, H, 5, L), np.nan) if scales else None
 
     def one(b, h):
         g = h // G
@@ -207,14 +213,18 @@ def bwd(q, k, v, o, lse, do, tau, bq, bk, scale=None, replay=None, band=1e-4, qb
                                     _p(lse[b, h], _D), _p(do[b, h], _D), L, d, scale, float(tau), bq, bk,
                                     _p(qi, _L), nq, _p(ki, _L), nk, _p(None if rp is None else rp[b, h], _U8),
                                     float(band), _p(dq[b, h], _D), _p(dk[b, h], _D), _p(dv[b, h], _D),
-                                    _p(keep[b, h], _U8), _p(T[b, h], _D))
+                                    _p(keep[b, h], _U8), _p(T[b, h], _D), _p(None if es is None else es[b, h], _D))
         _check(rc, "oracle_bwd_head")
 
     _per_head(B, H, one)
     if G > 1:
         dk = dk.reshape(B, H // G, G, L, d).sum(axis=2)
         dv = dv.reshape(B, H // G, G, L, d).sum(axis=2)
-    return dq, dk, dv, keep, T
+    if not scales:
+        return dq, dk, dv, keep, T
+    kv = np.sqrt((es[:, :, 2:] ** 2).reshape(B, H // G, G, 3, L).sum(axis=2))
+    sc = {"rq": es[:, :, 0], "cq": es[:, :, 1], "rk": kv[:, :, 0], "ck": kv[:, :, 1], "rv": kv[:, :, 2]}
+    return dq, dk, dv, keep, T, sc
 
 
 def decode_shapes(Lk, split_keys, bk):
@@ -350,23 +360,3 @@ def decode_seeded_group_partials(q, k, v, Lk, tau, split_keys, bk, scale=None, r
                                            _p(T, _D), _p(pm, _D), _p(pl, _D), _p(pa, _D))
     _check(rc, "oracle_decode_seeded_group")
     return o, lse, keep, T, pm, pl, pa
-
-
-def omitted(q, k, keep, bq, bk, scale=None, qblocks=None):
-    """Per-row omitted dense mass and kept slots for forward decisions `keep`.
-    Returns (omitted [B, H, L], slots [B, H, L]) (NaN outside computed blocks)."""
-    q, k = _f64(q), _f64(k)
-    B, H, L, d = q.shape
-    scale = default_scale(d) if scale is None else float(scale)
-    om = np.full((B, H, L), np.nan)
-    sl = np.full((B, H, L), np.nan)
-    ids, n = _ids(qblocks)
-    kp = np.ascontiguousarray(keep, dtype=np.uint8)
-
-    def one(b, h):
-        rc = _lib().oracle_omitted_head(_p(q[b, h], _D), _p(k[b, h], _D), L, d, scale, bq, bk,
-                                        _p(kp[b, h], _U8), _p(ids, _L), n, _p(om[b, h], _D), _p(sl[b, h], _D))
-        _check(rc, "oracle_omitted_head")
-
-    _per_head(B, H, one)
-    return om, sl

@@ -36,6 +36,8 @@
  *   - tau = 0 bypasses the test (every legal tile kept: full attention).
  *   - Backward: P = exp(s - lse) with the forward lse, D_i = sum_c dO_ic O_ic
  *     with the forward O; no forced keep; same tiles and vote as forward.
+ *     Row 0's only key is key 0, which the forward always keeps, so its P_00
+ *     is 1 by definition (taken as such, not from a rounded lse).
  *
  * The test statistic of a tile is T = max over voting rows of
  * (largest ratio of the row) / (tau / Lq_i); the tile is kept iff T >= 1.
@@ -68,10 +70,12 @@ static long ceil_div(long a, long b) { return (a + b - 1) / b; }
  * 0 .. p0 + i, and has Lq_i = p0 + i + 1 visible keys.  Keys come from k, v
  * ([p0 + L][d]); query blocks are counted from the chunk start, key tiles
  * from key 0. */
+static double sq_norm(const double* a, int d) { return dot(a, a, d); }
+
 static int fwd_block(const double* q, const double* k, const double* v, long L, long p0, int d,
                      double scale, double tau, int bq, int bk, long qb, long ntiles,
                      const uint8_t* replay, double band,
-                     double* o, double* lse, uint8_t* keep, double* T)
+                     double* o, double* lse, uint8_t* keep, double* T, double* rs)
 {
     const long r0 = qb * (long)bq;
     const long r1 = (r0 + bq < L) ? r0 + bq : L;
@@ -81,7 +85,8 @@ static int fwd_block(const double* q, const double* k, const double* v, long L, 
     double* l = malloc(sizeof(double) * nr);
     double* acc = calloc((size_t)nr * d, sizeof(double));
     double* s = malloc(sizeof(double) * (size_t)nr * bk);
-    if (!m || !l || !acc || !s) { free(m); free(l); free(acc); free(s); return ORACLE_ERR_MEM; }
+    double* r2 = calloc((size_t)nr, sizeof(double)); /* error scale: sum of (exp(s - m) |v_j|)^2 */
+    if (!m || !l || !acc || !s || !r2) { free(m); free(l); free(acc); free(s); free(r2); return ORACLE_ERR_MEM; }
     for (int r = 0; r < nr; ++r) { m[r] = -INFINITY; l[r] = 0.0; }
 
     /* legal tiles of this block: 0 .. jmax, visited jmax down to 0 */
@@ -134,11 +139,13 @@ static int fwd_block(const double* q, const double* k, const double* v, long L, 
                 double* ar = acc + (size_t)r * d;
                 l[r] *= a;
                 for (int c = 0; c < d; ++c) ar[c] *= a;
+                if (rs) r2[r] *= a * a;
                 for (long j = c0; j <= jl; ++j) {
                     const double p = exp(s[(size_t)r * bk + (j - c0)] - mn);
                     l[r] += p;
                     const double* vj = v + j * d;
                     for (int c = 0; c < d; ++c) ar[c] += p * vj[c];
+                    if (rs) r2[r] += p * p * sq_norm(vj, d);
                 }
                 m[r] = mn;
             }
@@ -150,8 +157,9 @@ static int fwd_block(const double* q, const double* k, const double* v, long L, 
         const long i = r0 + r;
         for (int c = 0; c < d; ++c) o[i * d + c] = acc[(size_t)r * d + c] / l[r];
         lse[i] = m[r] + log(l[r]);
+        if (rs) rs[i] = sqrt(r2[r]) / l[r];
     }
-    free(m); free(l); free(acc); free(s);
+    free(m); free(l); free(acc); free(s); free(r2);
     return ORACLE_OK;
 }
 
@@ -160,12 +168,19 @@ static int fwd_block(const double* q, const double* k, const double* v, long L, 
  * blocks to compute (NULL: all).  o [L][d] and lse [L] are written for the
  * rows of computed blocks; keep and T ([nqb][ntiles], ntiles = ceil(L/bk))
  * for their legal tiles.  replay (same layout) may be NULL.
+ *
+ * rs [L] (may be NULL) receives an error scale of every computed row for the
+ * parity tests' per-row bound; it is not part of the method:
+ *   rs[i] = sqrt(sum over the row's kept keys j of (p_ij |v_j|)^2),
+ * p_ij = exp(s_ij - lse_i), |.| the Euclidean norm.  A kernel that rounds each
+ * p_ij to bf16 (relative error at most u = 2^-8, independent across keys)
+ * before the PV product moves O_i by about u * rs[i] / sqrt(3).
  */
 int oracle_fwd_head(const double* q, const double* k, const double* v, long L, int d,
                     double scale, double tau, int bq, int bk,
                     const long* qblocks, long nqblocks,
                     const uint8_t* replay, double band,
-                    double* o, double* lse, uint8_t* keep, double* T)
+                    double* o, double* lse, uint8_t* keep, double* T, double* rs)
 {
     if (!q || !k || !v || !o || !lse || L <= 0 || d <= 0 || bq <= 0 || bk <= 0) return ORACLE_ERR_ARG;
     if (!(tau >= 0.0)) return ORACLE_ERR_ARG;           /* rejects NaN and tau < 0 */
@@ -176,7 +191,7 @@ int oracle_fwd_head(const double* q, const double* k, const double* v, long L, i
     for (long u = 0; u < n; ++u) {
         const long qb = qblocks ? qblocks[u] : u;
         if (qb < 0 || qb >= nqb) { err = ORACLE_ERR_ARG; continue; }
-        int e = fwd_block(q, k, v, L, 0, d, scale, tau, bq, bk, qb, ntiles, replay, band, o, lse, keep, T);
+        int e = fwd_block(q, k, v, L, 0, d, scale, tau, bq, bk, qb, ntiles, replay, band, o, lse, keep, T, rs);
         if (e) err = e;
     }
     return err;
@@ -194,7 +209,7 @@ int oracle_fwd_chunk_head(const double* q, const double* k, const double* v, lon
                           double scale, double tau, int bq, int bk,
                           const long* qblocks, long nqblocks,
                           const uint8_t* replay, double band,
-                          double* o, double* lse, uint8_t* keep, double* T)
+                          double* o, double* lse, uint8_t* keep, double* T, double* rs)
 {
     if (!q || !k || !v || !o || !lse || L <= 0 || p0 < 0 || d <= 0 || bq <= 0 || bk <= 0) return ORACLE_ERR_ARG;
     if (!(tau >= 0.0)) return ORACLE_ERR_ARG;
@@ -205,7 +220,7 @@ int oracle_fwd_chunk_head(const double* q, const double* k, const double* v, lon
     for (long u = 0; u < n; ++u) {
         const long qb = qblocks ? qblocks[u] : u;
         if (qb < 0 || qb >= nqb) { err = ORACLE_ERR_ARG; continue; }
-        int e = fwd_block(q, k, v, L, p0, d, scale, tau, bq, bk, qb, ntiles, replay, band, o, lse, keep, T);
+        int e = fwd_block(q, k, v, L, p0, d, scale, tau, bq, bk, qb, ntiles, replay, band, o, lse, keep, T, rs);
         if (e) err = e;
     }
     return err;
@@ -214,6 +229,17 @@ int oracle_fwd_chunk_head(const double* q, const double* k, const double* v, lon
 /* ------------------------------------------------------------------------ */
 /* Backward.  [backward], [motivation]                                        */
 /* ------------------------------------------------------------------------ */
+
+/* Backward probability of key j for row i against the final normalizer:
+ * P_ij = exp(s_ij - lse_i).  Row 0 sees only key 0, and the forward always
+ * keeps the first tile it visits, so row 0's final normalizer is exp(s_00)
+ * and P_00 = 1 exactly; it is taken from that definition, because an lse
+ * rounded to fp32 cannot represent it, and at tau = 1 its test 1 >= tau/1 is
+ * an exact tie that equality keeps ([forward], [backward], ties keep). */
+static double bwd_prob(double s, double lse_i, long i)
+{
+    return (i == 0) ? 1.0 : exp(s - lse_i);
+}
 
 /* Scores of tile (qb, t) into s [bq][bk] (-inf where j > i) and the tile's
  * backward decision against the final lse. */
@@ -234,7 +260,7 @@ static int bwd_decide(const double* q, const double* k, long L, int d, double sc
         if (c0 > i) continue;                          /* abstain */
         const long jl = (i < c1 - 1) ? i : c1 - 1;
         for (long j = c0; j <= jl; ++j) {
-            const double Tr = exp(s[(i - r0) * bk + (j - c0)] - lse[i]) / (tau / (double)(i + 1));
+            const double Tr = bwd_prob(s[(i - r0) * bk + (j - c0)], lse[i], i) / (tau / (double)(i + 1));
             if (Tr > Tt) Tt = Tr;
         }
     }
@@ -244,26 +270,53 @@ static int bwd_decide(const double* q, const double* k, long L, int d, double sc
     return kp;
 }
 
+/* sum_c |a_c b_c| */
+static double abs_dot(const double* a, const double* b, int d) {
+    double s = 0.0;
+    for (int c = 0; c < d; ++c) s += fabs(a[c] * b[c]);
+    return s;
+}
+
 /*
  * Backward of one (batch, head).  Inputs [L][d] (lse [L]) as produced by a
  * forward pass.  dq rows of the listed query blocks and dk/dv rows of the
  * listed key tiles are written (NULL list: all).  keep/T [nqb][ntiles] get
  * the decision of every tile visited.
+ *
+ * es (may be NULL) receives five [L] arrays of error scales for the parity
+ * tests' per-row bound (not part of the method), over the kept tiles, with
+ * a_ij = sum_c |dO_ic v_jc| and b_i = sum_c |dO_ic O_ic| (the magnitudes
+ * behind the dot products dP_ij and D_i):
+ *   es[0][i] = scale sqrt(sum_j (dS_ij |k_j|)^2)            (dQ row i)
+ *   es[1][i] = scale sqrt(sum_j (P_ij (a_ij + b_i) |k_j|)^2)  (dQ row i)
+ *   es[2][j] = scale sqrt(sum_i (dS_ij |q_i|)^2)            (dK row j)
+ *   es[3][j] = scale sqrt(sum_i (P_ij (a_ij + b_i) |q_i|)^2)  (dK row j)
+ *   es[4][j] = sqrt(sum_i (P_ij |dO_i|)^2)                  (dV row j)
+ * The first of each pair sizes the effect of rounding P and dS to bf16
+ * (relative u each, independent across terms); the second the effect of fp32
+ * rounding in the dot products that form dP - D, which cancel where a row's
+ * probability sits on one key.
  */
 int oracle_bwd_head(const double* q, const double* k, const double* v, const double* o,
                     const double* lse, const double* dout, long L, int d,
                     double scale, double tau, int bq, int bk,
                     const long* qblocks, long nq, const long* ktiles, long nk,
                     const uint8_t* replay, double band,
-                    double* dq, double* dk, double* dv, uint8_t* keep, double* T)
+                    double* dq, double* dk, double* dv, uint8_t* keep, double* T, double* es)
 {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || L <= 0 || d <= 0 || bq <= 0 || bk <= 0)
         return ORACLE_ERR_ARG;
     if (!(tau >= 0.0)) return ORACLE_ERR_ARG;
     const long nqb = ceil_div(L, bq), ntiles = ceil_div(L, bk);
     double* D = malloc(sizeof(double) * L);
-    if (!D) return ORACLE_ERR_MEM;
-    for (long i = 0; i < L; ++i) D[i] = dot(dout + i * d, o + i * d, d);
+    double* Dabs = malloc(sizeof(double) * L);
+    if (!D || !Dabs) { free(D); free(Dabs); return ORACLE_ERR_MEM; }
+    for (long i = 0; i < L; ++i) {
+        D[i] = dot(dout + i * d, o + i * d, d);
+        Dabs[i] = abs_dot(dout + i * d, o + i * d, d);
+    }
+    double *erq = es ? es : NULL, *ecq = es ? es + L : NULL, *erk = es ? es + 2 * L : NULL;
+    double *eck = es ? es + 3 * L : NULL, *erv = es ? es + 4 * L : NULL;
     int err = ORACLE_OK;
 
     /* dQ: one query block at a time, over its legal tiles */
@@ -276,7 +329,10 @@ int oracle_bwd_head(const double* q, const double* k, const double* v, const dou
         if (!s) { err = ORACLE_ERR_MEM; continue; }
         const long r0 = qb * (long)bq;
         const long r1 = (r0 + bq < L) ? r0 + bq : L;
-        for (long i = r0; i < r1; ++i) memset(dq + i * d, 0, sizeof(double) * d);
+        for (long i = r0; i < r1; ++i) {
+            memset(dq + i * d, 0, sizeof(double) * d);
+            if (es) { erq[i] = 0.0; ecq[i] = 0.0; }
+        }
         const long jmax = (r1 - 1) / bk;
         for (long t = 0; t <= jmax; ++t) {
             double Tt;
@@ -288,13 +344,21 @@ int oracle_bwd_head(const double* q, const double* k, const double* v, const dou
             const long c1 = (c0 + bk < L) ? c0 + bk : L;
             for (long i = r0; i < r1; ++i) {
                 for (long j = c0; j < c1 && j <= i; ++j) {
-                    const double P = exp(s[(i - r0) * bk + (j - c0)] - lse[i]);
+                    const double P = bwd_prob(s[(i - r0) * bk + (j - c0)], lse[i], i);
                     const double dP = dot(dout + i * d, v + j * d, d);
                     const double dS = P * (dP - D[i]);
                     for (int c = 0; c < d; ++c) dq[i * d + c] += scale * dS * k[j * d + c];
+                    if (es) {
+                        const double kn2 = sq_norm(k + j * d, d);
+                        const double g = P * (abs_dot(dout + i * d, v + j * d, d) + Dabs[i]);
+                        erq[i] += dS * dS * kn2;
+                        ecq[i] += g * g * kn2;
+                    }
                 }
             }
         }
+        if (es)
+            for (long i = r0; i < r1; ++i) { erq[i] = scale * sqrt(erq[i]); ecq[i] = scale * sqrt(ecq[i]); }
         free(s);
     }
 
@@ -308,7 +372,11 @@ int oracle_bwd_head(const double* q, const double* k, const double* v, const dou
         if (!s) { err = ORACLE_ERR_MEM; continue; }
         const long c0 = t * (long)bk;
         const long c1 = (c0 + bk < L) ? c0 + bk : L;
-        for (long j = c0; j < c1; ++j) { memset(dk + j * d, 0, sizeof(double) * d); memset(dv + j * d, 0, sizeof(double) * d); }
+        for (long j = c0; j < c1; ++j) {
+            memset(dk + j * d, 0, sizeof(double) * d);
+            memset(dv + j * d, 0, sizeof(double) * d);
+            if (es) { erk[j] = 0.0; eck[j] = 0.0; erv[j] = 0.0; }
+        }
         for (long qb = c0 / bq; qb < nqb; ++qb) {
             double Tt;
             const int kp = bwd_decide(q, k, L, d, scale, tau, bq, bk, qb, t, ntiles, lse, replay, band, s, &Tt);
@@ -319,19 +387,33 @@ int oracle_bwd_head(const double* q, const double* k, const double* v, const dou
             const long r1 = (r0 + bq < L) ? r0 + bq : L;
             for (long i = r0; i < r1; ++i) {
                 for (long j = c0; j < c1 && j <= i; ++j) {
-                    const double P = exp(s[(i - r0) * bk + (j - c0)] - lse[i]);
+                    const double P = bwd_prob(s[(i - r0) * bk + (j - c0)], lse[i], i);
                     const double dP = dot(dout + i * d, v + j * d, d);
                     const double dS = P * (dP - D[i]);
                     for (int c = 0; c < d; ++c) {
                         dk[j * d + c] += scale * dS * q[i * d + c];
                         dv[j * d + c] += P * dout[i * d + c];
                     }
+                    if (es) {
+                        const double qn2 = sq_norm(q + i * d, d);
+                        const double g = P * (abs_dot(dout + i * d, v + j * d, d) + Dabs[i]);
+                        erk[j] += dS * dS * qn2;
+                        eck[j] += g * g * qn2;
+                        erv[j] += P * P * sq_norm(dout + i * d, d);
+                    }
                 }
             }
         }
+        if (es)
+            for (long j = c0; j < c1; ++j) {
+                erk[j] = scale * sqrt(erk[j]);
+                eck[j] = scale * sqrt(eck[j]);
+                erv[j] = sqrt(erv[j]);
+            }
         free(s);
     }
     free(D);
+    free(Dabs);
     return err;
 }
 
@@ -608,50 +690,6 @@ int oracle_decode_seeded_groups(long n, const double* q, int G, const double* k,
                                            o + u * G * d, lse ? lse + u * G : NULL,
                                            keep ? keep + u * kb : NULL, T ? T + u * kb : NULL, NULL, NULL, NULL);
         if (e) err = e;
-    }
-    return err;
-}
-
-/* ------------------------------------------------------------------------ */
-/* Derived quantities against the exact dense softmax                        */
-/* ------------------------------------------------------------------------ */
-/*
- * For each row i of the listed query blocks (NULL: all): the exact dense
- * causal softmax P*_ij = exp(s_ij - lse*_i) over j <= i, and
- *   omitted[i] = sum of P*_ij over keys j in tiles (qb(i), t) with keep = 0,
- *   slots[i]   = number of visible keys j of row i in kept tiles.
- */
-int oracle_omitted_head(const double* q, const double* k, long L, int d, double scale,
-                        int bq, int bk, const uint8_t* keep, const long* qblocks, long nq,
-                        double* omitted, double* slots)
-{
-    if (!q || !k || !keep || !omitted || !slots || L <= 0 || d <= 0 || bq <= 0 || bk <= 0) return ORACLE_ERR_ARG;
-    const long nqb = ceil_div(L, bq), ntiles = ceil_div(L, bk);
-    const long n = qblocks ? nq : nqb;
-    int err = ORACLE_OK;
-#pragma omp parallel for schedule(dynamic, 1)
-    for (long u = 0; u < n; ++u) {
-        const long qb = qblocks ? qblocks[u] : u;
-        if (qb < 0 || qb >= nqb) { err = ORACLE_ERR_ARG; continue; }
-        double* s = malloc(sizeof(double) * L);
-        if (!s) { err = ORACLE_ERR_MEM; continue; }
-        const long r0 = qb * (long)bq;
-        const long r1 = (r0 + bq < L) ? r0 + bq : L;
-        for (long i = r0; i < r1; ++i) {
-            double mx = -INFINITY;
-            for (long j = 0; j <= i; ++j) { s[j] = scale * dot(q + i * d, k + j * d, d); if (s[j] > mx) mx = s[j]; }
-            double z = 0.0;
-            for (long j = 0; j <= i; ++j) z += exp(s[j] - mx);
-            const double lz = mx + log(z);
-            double om = 0.0, sl = 0.0;
-            for (long j = 0; j <= i; ++j) {
-                if (keep[qb * ntiles + j / bk]) sl += 1.0;
-                else om += exp(s[j] - lz);
-            }
-            omitted[i] = om;
-            slots[i] = sl;
-        }
-        free(s);
     }
     return err;
 }

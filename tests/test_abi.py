@@ -177,6 +177,9 @@ def dec(lib, q=P, B=2, Hq=8, Hkv=2, Lk=5000, Lcap=8192, d=128, dt=0, tau=1.0, sp
     ({"d": 64}, UNSUPPORTED, "instantiation"),
     ({"bk": 32}, UNSUPPORTED, "instantiation"),
     ({"Hq": 32, "Hkv": 2}, UNSUPPORTED, "instantiation"),  # group of 16 > 8
+    ({"Hq": 24, "Hkv": 8}, UNSUPPORTED, "instantiation"),  # group of 3: no kernel for it
+    ({"Hq": 12, "Hkv": 2}, UNSUPPORTED, "instantiation"),  # group of 6
+    ({"Hq": 7, "Hkv": 1}, UNSUPPORTED, "instantiation"),   # group of 7
     ({"split": 4000}, UNSUPPORTED, "instantiation"),      # not a multiple of 64
     ({"ws_bytes": 64}, INVALID, "workspace too small"),
     ({"ws": MISALIGNED_WS}, INVALID, "aligned"),

@@ -3,8 +3,11 @@
 Inputs are seeded instances of the named workloads (synth); the oracle runs
 on exactly the values the GPU received.  Forward/decode decisions must match
 tile for tile outside the |T-1| <= 1e-4 band (the oracle replays the GPU's
-decisions inside it); backward decisions must match tile for tile given the
-GPU's own O and lse; O within rel-L2 5e-3, gradients within 1e-2.
+decisions inside it, and the band tiles are printed); backward decisions must
+match the free-running oracle tile for tile given the GPU's own O and lse, and
+kept counts must equal the oracle's; O within rel-L2 5e-3, gradients within
+1e-2 over the tensor, and every row within the per-row bounds of
+tests/parity.py.
 """
 import math
 
@@ -13,8 +16,8 @@ import pytest
 
 import oracle
 from synth import WORKLOADS, prefill_inputs, decode_inputs, to_f64
-from tests.parity import (BAND, TOL_GRAD, TOL_O, TOL_TSTAT, bf16_to_f64, chunk_legal_mask, decision_report,
-                          legal_mask, rel_l2, tstat_report)
+from tests.parity import (BAND, TOL_GRAD, TOL_O, TOL_TSTAT, bf16_to_f64, bwd_decision_check, check_rows,
+                          chunk_legal_mask, decision_report, legal_mask, rel_l2, tstat_report)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -56,17 +59,21 @@ def _check_fwd(ops, w, x, tau, bq, bk):
     nt = -(-L // bk)
     gk = ops.bits_to_keep(st["keep_bits"], nt)
     qf, kf, vf = (to_f64(x[n], w.dtype) for n in ("q", "k", "v"))
-    oo, ol, ok, oT = oracle.fwd(qf, kf, vf, tau, bq, bk, replay=gk, band=BAND)
+    oo, ol, ok, oT, rs = oracle.fwd(qf, kf, vf, tau, bq, bk, replay=gk, band=BAND, scales=True)
     legal = legal_mask(L, bq, bk)
-    bad, near, near_list = decision_report(gk, ok, oT, legal)
+    what = f"fwd L={L} tau={tau}"
+    ts = st["test_stat"].cpu().numpy() if "test_stat" in st else None
+    bad, near, near_list = decision_report(gk, ok, oT, legal, what=what, gpu_ts=ts)
     assert bad == 0, f"forward decisions differ outside the band on {bad} tiles"
     kept = st["kept"].cpu().numpy()
     assert (kept == (gk * legal).sum(-1)).all()
+    assert (kept == (ok * legal).sum(-1)).all(), "kept counts differ from the oracle's"
     assert (st["legal"].cpu().numpy() == legal.sum(-1)[None, None, :]).all()
     e_o = rel_l2(bf16_to_f64(o), oo)
     e_l = float(np.abs(lse.cpu().numpy() - ol).max())
     assert e_o <= TOL_O, e_o
     assert e_l <= 1e-3, e_l
+    check_rows("o", bf16_to_f64(o), oo, what, r=rs)
     if "test_stat" in st:  # the GPU's own test statistic, tile by tile
         worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT, legal, tau)
         assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
@@ -102,18 +109,24 @@ def _check_bwd(ops, w, x, tau, bq, bk):
     assert (gk[..., legal] == gk2[..., legal]).all(), "dQ and dK/dV passes disagree"
     qf, kf, vf, dof = (to_f64(x[n], w.dtype) for n in ("q", "k", "v", "do"))
     of, lf = bf16_to_f64(o), lse.cpu().numpy().astype(np.float64)
-    gq, gkk, gv, ok, oT = oracle.bwd(qf, kf, vf, of, lf, dof, tau, bq, bk, replay=gk, band=BAND)
-    bad, near, near_list = decision_report(gk, ok, oT, legal)
-    assert bad == 0, f"backward decisions differ on {bad} tiles"
+    # the free-running oracle (no replay): backward decisions must be bit-identical
+    gq, gkk, gv, ok, oT, sc = oracle.bwd(qf, kf, vf, of, lf, dof, tau, bq, bk, scales=True)
+    what = f"bwd L={L} tau={tau}"
+    ts = st["test_stat"].cpu().numpy() if "test_stat" in st else None
+    near = bwd_decision_check(gk, ok, oT, legal, what=what, gpu_ts=ts)
+    assert (st["kept"].cpu().numpy() == (ok * legal).sum(-1)).all(), "kept counts differ from the oracle's"
     assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
-    if "test_stat" in st:
-        worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT, legal, tau)
+    if ts is not None:
+        worst, nbad = tstat_report(ts, oT, legal, tau)
         assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     errs = [rel_l2(bf16_to_f64(a), b) for a, b in ((dq, gq), (dk, gkk), (dv, gv))]
     if tau == math.inf:
         assert all(float(t.abs().max()) == 0.0 for t in (dq, dk, dv))
     else:
         assert max(errs) <= TOL_GRAD, errs
+        check_rows("dq", bf16_to_f64(dq), gq, what, r=sc["rq"], c=sc["cq"])
+        check_rows("dk", bf16_to_f64(dk), gkk, what, r=sc["rk"], c=sc["ck"])
+        check_rows("dv", bf16_to_f64(dv), gv, what, r=sc["rv"])
     return dict(keep=gk, errs=errs, near=near)
 
 
@@ -160,20 +173,25 @@ def test_bwd_pair_layout_bf16(ops, L, H, Hkv, tau):
     qblocks, ktiles = (0, nqb // 2, nqb - 1), (0, 1, nt // 2, nt - 2, nt - 1)
     qf, kf, vf, dof = (to_f64(x[n], "bf16") for n in ("q", "k", "v", "do"))
     of, lf = bf16_to_f64(o), lse.cpu().numpy().astype(np.float64)
-    gq, gkk, gv, okb, oTb = oracle.bwd(qf, kf, vf, of, lf, dof, tau, 128, 64, replay=gk, band=BAND,
-                                       qblocks=qblocks, ktiles=ktiles)
+    gq, gkk, gv, okb, oTb, sc = oracle.bwd(qf, kf, vf, of, lf, dof, tau, 128, 64, qblocks=qblocks, ktiles=ktiles,
+                                           scales=True)
     sel = np.zeros_like(legal)
     sel[list(qblocks)] = legal[list(qblocks)]
     for t in ktiles:
         sel[:, t] |= legal[:, t]
-    bad, near, _ = decision_report(gk, okb, oTb, sel)
-    assert bad == 0, f"backward decisions differ on {bad} tiles"
+    what = f"bwd pairs L={L} H={H} Hkv={Hkv} tau={tau}"
+    bwd_decision_check(gk, okb, oTb, sel, what=what)
+    sq = list(qblocks)
+    assert (st["kept"].cpu().numpy()[:, :, sq] == (okb * legal).sum(-1)[:, :, sq]).all()
     rows = np.concatenate([np.arange(b * 128, min(b * 128 + 128, L)) for b in qblocks])
     krows = np.concatenate([np.arange(t * 64, min(t * 64 + 64, L)) for t in ktiles])
-    e = [rel_l2(bf16_to_f64(dq)[:, :, rows], gq[:, :, rows]),
-         rel_l2(bf16_to_f64(dk)[:, :, krows], gkk[:, :, krows]),
-         rel_l2(bf16_to_f64(dv)[:, :, krows], gv[:, :, krows])]
+    pairs = (("dq", bf16_to_f64(dq)[:, :, rows], gq[:, :, rows], sc["rq"][:, :, rows], sc["cq"][:, :, rows]),
+             ("dk", bf16_to_f64(dk)[:, :, krows], gkk[:, :, krows], sc["rk"][:, :, krows], sc["ck"][:, :, krows]),
+             ("dv", bf16_to_f64(dv)[:, :, krows], gv[:, :, krows], sc["rv"][:, :, krows], None))
+    e = [rel_l2(a, b) for _, a, b, _, _ in pairs]
     assert max(e) <= TOL_GRAD, e
+    for n, a, b, r, c in pairs:
+        check_rows(n, a, b, what, r=r, c=c)
 
 
 @pytest.mark.parametrize("L", [1000, 2048])
@@ -270,16 +288,20 @@ def test_fwd_chunk_bf16(ops, P, Lq, spare, tau):
     gk = ops.bits_to_keep(st["keep_bits"], nt)
     qf = to_f64(qx, "bf16")
     kf, vf = (to_f64(x[n], "bf16") for n in ("k", "v"))
-    oo, ol, ok, oT = oracle.fwd_chunk(qf, kf, vf, P, tau, 128, 64, replay=gk, band=BAND)
+    oo, ol, ok, oT, rs = oracle.fwd_chunk(qf, kf, vf, P, tau, 128, 64, replay=gk, band=BAND, scales=True)
     legal = chunk_legal_mask(Lq, P, 128, 64)
-    bad, near, _ = decision_report(gk, ok, oT, legal)
+    what = f"chunk P={P} Lq={Lq} tau={tau}"
+    ts = st["test_stat"].cpu().numpy()
+    bad, near, _ = decision_report(gk, ok, oT, legal, what=what, gpu_ts=ts)
     assert bad == 0, f"chunk decisions differ outside the band on {bad} tiles"
-    worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT, legal, tau)
+    worst, nbad = tstat_report(ts, oT, legal, tau)
     assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+    assert (st["kept"].cpu().numpy() == (ok * legal).sum(-1)).all()
     assert (st["legal"].cpu().numpy() == legal.sum(-1)[None, None, :]).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
     assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+    check_rows("o", bf16_to_f64(o), oo, what, r=rs)
     if P % 128 == 0:
         qa, ka, va = _dev_tensors(x, "bf16", ("q", "k", "v"))
         of, lf = ops.fwd(qa, ka, va, tau)
@@ -310,13 +332,17 @@ def test_decode_bf16(ops, Lk, split, Lcap, tau):
     legal = np.zeros((nsplit, tps), bool)
     for p in range(nsplit):
         legal[p, : -(-(min((p + 1) * split, Lk) - p * split) // 64)] = True
-    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal)
+    what = f"decode Lk={Lk} split={split} tau={tau}"
+    ts = st["test_stat"].cpu().numpy()
+    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal, what=what, gpu_ts=ts)
     assert bad == 0
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+    assert (st["kept"].cpu().numpy() == (ok[:, :, 0] * legal).sum(-1)).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
     assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
-    worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT[:, :, 0], legal, tau)
+    worst, nbad = tstat_report(ts, oT[:, :, 0], legal, tau)
     assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
+    check_rows("o_decode", bf16_to_f64(o), oo, what)
 
 
 def seeded_legal(Lk, split, bk=64):
@@ -346,14 +372,18 @@ def test_decode_seeded_bf16(ops, Lk, split, Lcap, tau):
     qf, kf, vf = (to_f64(x[n], "bf16") for n in ("q", "k", "v"))
     oo, ol, ok, oT = oracle.decode_seeded(qf, kf, vf, Lk, tau, split, 64, replay=gk[:, :, None], band=BAND)
     legal = seeded_legal(Lk, split)
-    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal)
+    what = f"seeded decode Lk={Lk} split={split} tau={tau}"
+    ts = st["test_stat"].cpu().numpy()
+    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal, what=what, gpu_ts=ts)
     assert bad == 0
-    worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT[:, :, 0], legal, tau)
+    worst, nbad = tstat_report(ts, oT[:, :, 0], legal, tau)
     assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
     assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+    assert (st["kept"].cpu().numpy() == (ok[:, :, 0] * legal).sum(-1)).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
     assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+    check_rows("o_decode", bf16_to_f64(o), oo, what)
     if nsplit == 1:
         o2, lse2 = ops.decode(q, kc, vc, Lk, tau, split_keys=split, bk=64)
         torch.cuda.synchronize()
@@ -386,11 +416,15 @@ def test_decode_groups_bf16(ops, Hq, Hkv, Lk, split, tau, seeded):
         ref = oracle.decode
     gk = ops.bits_to_keep(st["keep_bits"], tps)
     oo, ol, ok, oT = ref(qf, kf, vf, Lk, tau, split, 64, replay=gk[:, :, None], band=BAND)
-    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal)
+    what = f"decode groups Hq={Hq} Hkv={Hkv} Lk={Lk} seeded={seeded} tau={tau}"
+    bad, near, _ = decision_report(gk, ok[:, :, 0], oT[:, :, 0], legal, what=what,
+                                   gpu_ts=st["test_stat"].cpu().numpy())
     assert bad == 0
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
+    assert (st["kept"].cpu().numpy() == (ok[:, :, 0] * legal).sum(-1)).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
     assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+    check_rows("o_decode", bf16_to_f64(o), oo, what)
 
 
 @pytest.mark.parametrize("Hq,Hkv,rpv", [(32, 8, 1), (32, 8, 2), (16, 2, 1), (16, 2, 4)])
@@ -425,14 +459,18 @@ def test_decode_rows_per_vote_bf16(ops, Hq, Hkv, rpv, Lk, split, tau, seeded):
     oo, ol, ok, oT = ref(qf, kf, vf, Lk, tau, split, 64, rows_per_vote=rpv,
                          replay=gk.reshape(2, Hkv, vg, nsplit, tps), band=BAND)
     ok, oT = ok.reshape(gk.shape), oT.reshape(gk.shape)
-    bad, near, _ = decision_report(gk, ok, oT, legal)
+    what = f"decode votes Hq={Hq} Hkv={Hkv} rpv={rpv} Lk={Lk} seeded={seeded} tau={tau}"
+    ts = st["test_stat"].cpu().numpy()
+    bad, near, _ = decision_report(gk, ok, oT, legal, what=what, gpu_ts=ts)
     assert bad == 0
-    worst, nbad = tstat_report(st["test_stat"].cpu().numpy(), oT, legal, tau)
+    worst, nbad = tstat_report(ts, oT, legal, tau)
     assert nbad == 0 and worst <= TOL_TSTAT, (worst, nbad)
     assert (st["legal"].cpu().numpy() == legal.sum(-1)).all()
     assert (st["kept"].cpu().numpy() == (gk * legal).sum(-1)).all()
+    assert (st["kept"].cpu().numpy() == (ok * legal).sum(-1)).all()
     assert rel_l2(bf16_to_f64(o), oo) <= TOL_O
     assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+    check_rows("o_decode", bf16_to_f64(o), oo, what)
 
 
 @pytest.mark.parametrize("seeded", [False, True])

@@ -141,8 +141,10 @@ def test_no_empty_row(small_bf16, tau):
 # ---------------------------------------------------------------- P4: nesting
 @pytest.mark.parametrize("tau", [0.5, 1.0, 2.0, 16.0])
 def test_backward_support_nested_in_forward(small_bf16, tau):
-    """Backward paragraph: testing against the final normalizer can only shrink the
-    ratios, so every forward-skipped tile is skipped in backward too."""
+    """MassAlloc Attention digest (agihunt.info), backward paragraph: the final
+    normalizer sums every kept tile, so it is never smaller than the running one
+    a forward test used; each backward ratio is at most its forward ratio and a
+    tile forward skipped stays skipped in backward."""
     w, (q, k, v, do) = small_bf16
     o, lse, kf, _ = oracle.fwd(q, k, v, tau, 128, 64)
     _, _, _, kb, _ = oracle.bwd(q, k, v, o, lse, do, tau, 128, 64)
@@ -750,3 +752,79 @@ def test_chunk_sampled_blocks_equal_full():
     assert np.array_equal(o2[:, :, rows], o[:, :, rows]) and np.array_equal(lse2[:, :, rows], lse[:, :, rows])
     assert np.array_equal(keep2[:, :, [1, 3]], keep[:, :, [1, 3]])
     assert np.isnan(o2[:, :, :128]).all() and (keep2[:, :, [0, 2]] == 0).all()
+
+
+# ---------------------------------------------------------------- row 0 of the backward
+@pytest.mark.parametrize("tau", [0.5, 1.0, 2.0])
+def test_backward_row0_probability_is_one(tau):
+    """Forward paragraph: the first tile a block visits is always kept, and row
+    0 sees only key 0, so its final normalizer is exp(s_00) and P_00 = 1.  With
+    a single row the backward statistic is then exactly 1/tau (kept iff
+    tau <= 1; equality keeps), and a kept tile gives dV_0 = dO_0 and
+    dK_0 = dQ_0 = 0 (dS_00 = dP_00 - D_0 = <dO_0, v_0 - O_0> with O_0 = v_0)."""
+    w, (q, k, v, do) = _prefill("mw8k", L=1, heads=[0, 3])
+    o, lse, _, _ = oracle.fwd(q, k, v, tau, 128, 64)
+    assert np.array_equal(o, v)
+    # an lse off by a rounding error does not move row 0's decision
+    lse_r = lse * (1 + 3e-8)
+    dq, dk, dv, kb, Tb = oracle.bwd(q, k, v, o, lse_r, do, tau, 128, 64)
+    assert (Tb[..., 0, 0] == 1.0 / tau).all()
+    assert (kb[..., 0, 0] == (1 if tau <= 1.0 else 0)).all()
+    if tau <= 1.0:
+        assert np.array_equal(dv, do) and not dk.any() and not dq.any()
+    else:
+        assert not dv.any() and not dk.any() and not dq.any()
+
+
+# ---------------------------------------------------------------- error scales of the rows
+def _kept_keys(keep, i, bq, bk):
+    """Keys of row i inside the tiles its block kept."""
+    b = i // bq
+    return [j for j in range(i + 1) if keep[b, j // bk]]
+
+
+@pytest.mark.parametrize("tau", [1.0, 4.0])
+def test_forward_row_error_scale(tau):
+    """rs_i = sqrt(sum_j (p_ij |v_j|)^2) over the row's kept keys: for a row with
+    one key it is |O_i| (row 0: O_0 = v_0); by Cauchy-Schwarz
+    |O_i| <= sqrt(n_i) rs_i for a row with n_i kept keys; and it never exceeds
+    max_j |v_j| (the p_ij sum to 1)."""
+    w, (q, k, v, do) = _prefill("mw8k", L=600, heads=[1, 6])
+    o, lse, keep, T, rs = oracle.fwd(q, k, v, tau, 128, 64, scales=True)
+    vmax = np.linalg.norm(v, axis=-1).max()
+    for h in range(2):
+        on = np.linalg.norm(o[0, h], axis=-1)
+        assert abs(rs[0, h, 0] - on[0]) <= 1e-12 * on[0]
+        assert abs(rs[0, h, 0] - np.linalg.norm(v[0, h, 0])) <= 1e-12 * on[0]
+        for i in range(q.shape[2]):
+            n = len(_kept_keys(keep[0, h], i, 128, 64))
+            assert on[i] <= math.sqrt(n) * rs[0, h, i] * (1 + 1e-12)
+            assert rs[0, h, i] <= vmax * (1 + 1e-12)
+
+
+@pytest.mark.parametrize("tau", [1.0, 4.0])
+def test_backward_row_error_scales(tau):
+    """The backward error scales (oracle_bwd_head): the last key is seen by the
+    last row only, so its dK and dV rows are single terms and equal their
+    scales rk, rv; every row obeys Cauchy-Schwarz, |X_i| <= sqrt(n_i) r_i with
+    n_i terms; and |dS_ij| = P_ij |dP_ij - D_i| <= P_ij (a_ij + b_i), so each
+    r is at most its c."""
+    w, (q, k, v, do) = _prefill("mw8k", L=600, heads=[1, 6])
+    o, lse, _, _ = oracle.fwd(q, k, v, tau, 128, 64)
+    dq, dk, dv, kb, Tb, sc = oracle.bwd(q, k, v, o, lse, do, tau, 128, 64, scales=True)
+    L = q.shape[2]
+    for h in range(2):
+        nk, nv = np.linalg.norm(dk[0, h], axis=-1), np.linalg.norm(dv[0, h], axis=-1)
+        nq = np.linalg.norm(dq[0, h], axis=-1)
+        if kb[0, h, (L - 1) // 128, (L - 1) // 64]:
+            assert abs(sc["rk"][0, h, L - 1] - nk[L - 1]) <= 1e-9 * max(nk[L - 1], 1e-300)
+            assert abs(sc["rv"][0, h, L - 1] - nv[L - 1]) <= 1e-12 * nv[L - 1]
+        for i in range(L):
+            nqi = len(_kept_keys(kb[0, h], i, 128, 64))
+            assert nq[i] <= math.sqrt(max(nqi, 1)) * sc["rq"][0, h, i] * (1 + 1e-9) + 1e-300
+            rows_j = [r for r in range(i, L) if kb[0, h, r // 128, i // 64]]
+            assert nk[i] <= math.sqrt(max(len(rows_j), 1)) * sc["rk"][0, h, i] * (1 + 1e-9) + 1e-300
+            assert nv[i] <= math.sqrt(max(len(rows_j), 1)) * sc["rv"][0, h, i] * (1 + 1e-9) + 1e-300
+        assert (sc["rq"][0, h] <= sc["cq"][0, h] * (1 + 1e-12)).all()
+        assert (sc["rk"][0, h] <= sc["ck"][0, h] * (1 + 1e-12)).all()
+        assert (sc["rv"][0, h] > 0).any() and (sc["rq"][0, h] > 0).any()
