@@ -251,6 +251,33 @@ mala_status mala_decode_seeded(const void* q, const void* kcache, const void* vc
                                void* o, float* lse, mala_stats* stats,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mala_decode_noalloc -- mala_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes mala_decode's arguments without the workspace
+ * and computes exactly what mala_decode computes (the same kernels, bit for
+ * bit), keeping the split partial states in a static device array of
+ * MALA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends.  It calls no hipMalloc or hipFree; its
+ * first call on a device (with that device current) looks the array's address
+ * up with hipGetSymbolAddress and keeps it.
+ *
+ * Limit: the partials need B * Hq * ceil(Lk/split_keys) * (d + 2) * 4 bytes
+ * (8.8 MB for 16 sequences x 32 heads x 131,073 keys with 4096-key splits);
+ * a call needing more than MALA_DECODE_NOALLOC_SCRATCH_BYTES returns
+ * MALA_ERR_UNSUPPORTED before anything is queued.  Nothing in the array needs
+ * clearing: every call writes each partial it reads.
+ * Concurrency: every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (on different streams, or from several host threads
+ * without ordering) race; serialize them, e.g. on one stream.  The call runs
+ * on the current device, to which `stream` must belong.
+ */
+#define MALA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+mala_status mala_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                                int B, int Hq, int Hkv, int Lk, int Lcap, int d, mala_dtype dtype,
+                                float tau, int split_keys, int bk, int rows_per_vote, float scale,
+                                void* o, float* lse, mala_stats* stats, void* stream);
+
 /* Static description of a status code. */
 const char* mala_status_string(mala_status status);
 /* Message of the last failing call on this host thread ("" if none). */

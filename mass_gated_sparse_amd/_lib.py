@@ -29,7 +29,10 @@ class Stats(ctypes.Structure):
 
 
 EXPORTS = ("mala_fwd", "mala_fwd_chunk", "mala_bwd", "mala_bwd_workspace_size", "mala_decode", "mala_decode_seeded",
-           "mala_decode_workspace_size", "mala_status_string", "mala_last_error", "mala_version")
+           "mala_decode_noalloc", "mala_decode_workspace_size", "mala_status_string", "mala_last_error",
+           "mala_version")
+# bytes of the static device scratch behind mala_decode_noalloc (MALA_DECODE_NOALLOC_SCRATCH_BYTES)
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _LIB = None
 
@@ -60,6 +63,8 @@ def load(path=None):
     lib.mala_decode.restype = i
     lib.mala_decode_seeded.argtypes = lib.mala_decode.argtypes
     lib.mala_decode_seeded.restype = i
+    lib.mala_decode_noalloc.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, f, i, i, i, f, vp, vp, sp, vp]
+    lib.mala_decode_noalloc.restype = i
     lib.mala_status_string.argtypes = [i]
     lib.mala_status_string.restype = ctypes.c_char_p
     lib.mala_last_error.argtypes = []

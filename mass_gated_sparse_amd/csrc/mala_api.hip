@@ -6,8 +6,17 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/mala.h"
 #include "mala_kernels.hpp"
+
+// Device scratch of mala_decode_noalloc: the split partial states live here
+// instead of in a caller's workspace.  Every GPU the library runs on holds its
+// own copy, from the loading of the code object until the process ends.  On
+// the host, `scratch` names a host-side stand-in, never device memory: host
+// code uses only the per-device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[MALA_DECODE_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -66,7 +75,7 @@ mala_status check_prefill(const void* q, const void* k, const void* v, int B, in
 
 extern "C" {
 
-int mala_version(void) { return 102; }
+int mala_version(void) { return 103; }
 
 const char* mala_status_string(mala_status s) {
     switch (s) {
@@ -206,10 +215,38 @@ size_t mala_decode_workspace_size(int B, int Hq, int Hkv, int Lk, int d, int spl
     return align256(size_t(B) * Hq * nsplit * (d + 2) * sizeof(float));
 }
 
+// Address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept for the life of the process.
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static float* g_scratch_dev[kMaxDevices] = {};
+
+static mala_status scratch_of_current_device(float** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "mala_decode_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MALA_ERR_UNSUPPORTED, "mala_decode_noalloc: device ordinal %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "mala_decode_noalloc: hipGetSymbolAddress(scratch)");
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 255))
+            return fail(MALA_ERR_HIP, "mala_decode_noalloc: scratch address %p unusable", p);
+        g_scratch_dev[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return MALA_OK;
+}
+
+// use_scratch: the partials go to this device's `scratch` (workspace and
+// workspace_bytes are ignored), after every argument has been checked.
 static mala_status decode_call(const char* name, bool seeded, const void* q, const void* kcache, const void* vcache,
                                int B, int Hq, int Hkv, int Lk, int Lcap, int d, mala_dtype dtype, float tau,
                                int split_keys, int bk, int rows_per_vote, float scale, void* o, float* lse,
-                               mala_stats* stats, void* workspace, size_t workspace_bytes, void* stream) {
+                               mala_stats* stats, void* workspace, size_t workspace_bytes, void* stream,
+                               bool use_scratch = false) {
     g_err[0] = 0;
     if (!q || !kcache || !vcache || !o) return fail(MALA_ERR_INVALID_ARG, "null pointer");
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || d <= 0 || split_keys <= 0 || bk <= 0)
@@ -228,6 +265,18 @@ static mala_status decode_call(const char* name, bool seeded, const void* q, con
     if (rows_per_vote < 0 || G % rows_per_vote)
         return fail(MALA_ERR_INVALID_ARG, "rows_per_vote (%d) must divide Hq/Hkv (%d)", rows_per_vote, G);
     const size_t need = mala_decode_workspace_size(B, Hq, Hkv, Lk, d, split_keys);
+    if (use_scratch) {
+        if (need > size_t(MALA_DECODE_NOALLOC_SCRATCH_BYTES))
+            return fail(MALA_ERR_UNSUPPORTED,
+                        "split partials need %zu bytes, more than the %zu-byte static scratch (B*Hq*ceil(Lk/"
+                        "split_keys)*(d+2)*4 bytes must fit)",
+                        need, size_t(MALA_DECODE_NOALLOC_SCRATCH_BYTES));
+        float* sp = nullptr;
+        const mala_status st = scratch_of_current_device(&sp);
+        if (st) return st;
+        workspace = sp;
+        workspace_bytes = MALA_DECODE_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need)
         return fail(MALA_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
     if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(MALA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
@@ -263,6 +312,14 @@ mala_status mala_decode(const void* q, const void* kcache, const void* vcache, i
                         size_t workspace_bytes, void* stream) {
     return decode_call("mala_decode launch", false, q, kcache, vcache, B, Hq, Hkv, Lk, Lcap, d, dtype, tau,
                        split_keys, bk, rows_per_vote, scale, o, lse, stats, workspace, workspace_bytes, stream);
+}
+
+mala_status mala_decode_noalloc(const void* q, const void* kcache, const void* vcache, int B, int Hq, int Hkv,
+                                int Lk, int Lcap, int d, mala_dtype dtype, float tau, int split_keys, int bk,
+                                int rows_per_vote, float scale, void* o, float* lse, mala_stats* stats,
+                                void* stream) {
+    return decode_call("mala_decode_noalloc launch", false, q, kcache, vcache, B, Hq, Hkv, Lk, Lcap, d, dtype, tau,
+                       split_keys, bk, rows_per_vote, scale, o, lse, stats, nullptr, 0, stream, true);
 }
 
 mala_status mala_decode_seeded(const void* q, const void* kcache, const void* vcache, int B, int Hq, int Hkv,

@@ -315,6 +315,29 @@ def decode(q, kc, vc, Lk, tau, split_keys=4096, bk=64, scale=0.0, stats=False, s
     return (o, lse, st) if stats else (o, lse)
 
 
+def decode_noalloc_into(q, kc, vc, Lk, o, lse, tau, split_keys=4096, bk=64, scale=0.0, stats=None, stream=None,
+                        rows_per_vote=0):
+    """Queue mala_decode_noalloc: mala_decode with the split partials in the
+    library's static device scratch (no workspace, no device allocation by
+    the library); writes o (like q) and lse [B,Hq] (or None).  Calls that
+    overlap on one GPU share that scratch: keep them on one stream."""
+    B, Hq, Hkv, Lcap, d = _expect_qkv(q, kc, vc, nq_dims=3)
+    _expect(o, "o", q.shape, q.dtype)
+    if lse is not None:
+        _expect(lse, "lse", (B, Hq), torch.float32)
+    vg = _vote_groups(Hq, Hkv, rows_per_vote)
+    if stats is not None and int(split_keys) > 0 and int(bk) > 0 and vg:
+        nsplit, w = -(-int(Lk) // int(split_keys)), -(-(int(split_keys) // int(bk)) // 32)
+        V = Hkv * vg
+        _expect_stats(stats, {"kept": (B, V, nsplit), "legal": (B, V, nsplit), "keep_bits": (B, V, nsplit, w),
+                              "test_stat": (B, V, nsplit, int(split_keys) // int(bk))})
+    _check_dev(q, kc, vc, o, *([lse] if lse is not None else []))
+    rc = _lib.load().mala_decode_noalloc(_ptr(q), _ptr(kc), _ptr(vc), B, Hq, Hkv, int(Lk), Lcap, d, _dt(q),
+                                         float(tau), int(split_keys), int(bk), int(rows_per_vote), float(scale),
+                                         _ptr(o), _ptr(lse), _stats_struct(stats), _stream(stream))
+    _lib.check("mala_decode_noalloc", rc)
+
+
 def bits_to_keep(bits, ntiles):
     """Unpack int32 keep-bit words [..., words] to a uint8 array [..., ntiles] (numpy)."""
     import numpy as np

@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_documented_entry_points():
     fns = declared_functions()
-    for name in ("mala_fwd", "mala_fwd_chunk", "mala_bwd", "mala_decode", "mala_decode_seeded",
+    for name in ("mala_fwd", "mala_fwd_chunk", "mala_bwd", "mala_decode", "mala_decode_seeded", "mala_decode_noalloc",
                  "mala_bwd_workspace_size", "mala_decode_workspace_size", "mala_status_string", "mala_last_error",
                  "mala_version"):
         assert name in fns
@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.mala_version() == 102
+    assert lib.mala_version() == 103
     assert lib.mala_status_string(OK) == b"ok"
     assert lib.mala_status_string(INVALID) == b"invalid argument"
     assert lib.mala_status_string(UNSUPPORTED) == b"unsupported configuration"
@@ -253,3 +253,31 @@ def test_python_wrappers_check_shapes_before_the_device():
     for fn, msg in cases:
         with pytest.raises(ValueError, match=msg):
             fn()
+
+
+def dec_noalloc(lib, q=P, B=2, Hq=8, Hkv=2, Lk=5000, Lcap=8192, d=128, dt=0, tau=1.0, split=4096, bk=64, rpv=0):
+    return lib.mala_decode_noalloc(q, P, P, B, Hq, Hkv, Lk, Lcap, d, dt, tau, split, bk, rpv, 0.0, P, P, None, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    ({"q": None}, INVALID, "null"),
+    ({"Lcap": 4000}, INVALID, "Lcap"),
+    ({"tau": float("nan")}, INVALID, "tau"),
+    ({"Hq": 24, "Hkv": 8}, UNSUPPORTED, "instantiation"),
+    ({"rpv": 3}, INVALID, "rows_per_vote"),
+    # 64 x 64 x 33 x 130 x 4 bytes of partials: beyond the 16 MiB scratch
+    ({"B": 64, "Hq": 64, "Hkv": 8, "Lk": 131073, "Lcap": 131073}, UNSUPPORTED, "static scratch"),
+    ({"B": 1, "Hq": 8, "Hkv": 8, "Lk": 1 << 24, "Lcap": 1 << 24, "split": 64}, UNSUPPORTED, "static scratch"),
+])
+def test_decode_noalloc_rejects(lib, kw, status, msg):
+    """mala_decode_noalloc checks every argument, and that the split partials
+    fit its static scratch, before it touches the device."""
+    assert dec_noalloc(lib, **kw) == status
+    assert msg in lib.mala_last_error().decode()
+
+
+def test_decode_noalloc_limit_matches_header():
+    from mass_gated_sparse_amd import _lib
+    text = open(HEADER).read()
+    m = re.search(r"#define MALA_DECODE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.DECODE_NOALLOC_SCRATCH_BYTES
