@@ -38,6 +38,8 @@
 // and no tile is kept by force.
 #include <float.h>
 
+#include <type_traits>
+
 #include "mala_kernels.hpp"
 
 namespace mala {
@@ -65,6 +67,10 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
     float scale_log2, float log2_tau, float log2_lq, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
     uint32_t* __restrict__ bits, int pbase, int seeded_grid, int rpv, float* __restrict__ tstat) {
     constexpr int D = 128, BK = 64;
+    // tiles loaded ahead: the newest-partition launch (one workgroup per CU,
+    // each walking its tiles in series) keeps four in flight; the others one
+    constexpr int NPF = PREV ? 4 : 1;
+    static_assert(NPF >= 1 && NPF <= 4, "the visit loop below is unrolled for up to four slots");
     __shared__ int vote_sm[2][4];
     __shared__ float wmax_sm[2][4][G];
     __shared__ float wsum_sm[2][4][G];
@@ -124,13 +130,16 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
         }
     }
 
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
     u32x4 kr[4];
+    // Loads are unconditional: a key past the partition (k1 > k0 always) reads
+    // the partition's last key instead, and its score is set to -inf, so its
+    // probability is 0.  Without branches around them the compiler can count
+    // the loads in flight and wait for exactly the tile it needs.
     auto load_k = [&](int t) {
-        const int key = k0 + t * BK + skey;
+        const int key = min(k0 + t * BK + skey, k1 - 1);
         const bf16_t* src = kc + kvbase + long(key) * D + 32 * quarter;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kr[c] = key < k1 ? *reinterpret_cast<const u32x4*>(src + 8 * c) : z4;
+        for (int c = 0; c < 4; ++c) kr[c] = *reinterpret_cast<const u32x4*>(src + 8 * c);
     };
 
     // statistics of vote group tid (threads 0 .. nvg-1), at unit (bg*nvg + tid, p)
@@ -140,24 +149,38 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
     if (STATS && bits && tid < nvg)
         for (int w = ((nt - 1) >> 5) + 1; w < words; ++w) bits[sidx * words + w] = 0u;
 
-    u32x4 vn[4] = {z4, z4, z4, z4};  // PREV: V of the next tile to visit
-    auto load_v = [&](int t, u32x4* dst) {
+    auto load_v = [&](int t, u32x4* dst) {  // (clamped like load_k: a key past k1 has probability 0)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int vk = k0 + t * BK + 16 * wave + 4 * i + ksub;
-            dst[i] = vk < k1 ? *reinterpret_cast<const u32x4*>(vc + kvbase + long(vk) * D + 8 * dch) : z4;
+            const int vk = min(k0 + t * BK + 16 * wave + 4 * i + ksub, k1 - 1);
+            dst[i] = *reinterpret_cast<const u32x4*>(vc + kvbase + long(vk) * D + 8 * dch);
         }
     };
-    load_k(nt - 1);
-    if (PREV) load_v(nt - 1, vn);
-    for (int t = nt - 1; t >= 0; --t) {
+    // Tiles in flight: K (and, with PREV, V) of the next NPF tiles to visit sit
+    // in a register ring; tile t's buffers are slot (nt-1-t) % NPF.
+    u32x4 kring[NPF][4], vring[NPF][4];
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {  // (a partition shorter than NPF tiles reads tile 0 again)
+        load_k(max(nt - 1 - i, 0));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kring[i][c] = kr[c];
+        if (PREV) load_v(max(nt - 1 - i, 0), vring[i]);
+    }
+    // One tile; SL = (nt-1-t) % NPF is a compile-time constant, so the ring
+    // stays in registers.
+    auto tile = [&](auto slot_tag, int t) {
+        constexpr int SL = decltype(slot_tag)::value;
         const int par = t & 1;
-        u32x4 kcur[4] = {kr[0], kr[1], kr[2], kr[3]};
-        u32x4 vcur[4] = {vn[0], vn[1], vn[2], vn[3]};
-        if (t > 0) {
-            load_k(t - 1);
-            if (PREV) load_v(t - 1, vn);
-        }
+        u32x4 kcur[4] = {kring[SL][0], kring[SL][1], kring[SL][2], kring[SL][3]};
+        u32x4 vcur[4] = {vring[SL][0], vring[SL][1], vring[SL][2], vring[SL][3]};
+        // refill the slot with the tile NPF visits later; near the end of the
+        // partition that tile does not exist and tile 0 is read again (unused),
+        // so every step issues the same loads and no branch hides them from the
+        // wait counting
+        load_k(max(t - NPF, 0));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kring[SL][c] = kr[c];
+        if (PREV) load_v(max(t - NPF, 0), vring[SL]);
         const int key = k0 + t * BK + skey;
         const bool kvalid = key < k1;
         float s[G];
@@ -238,7 +261,7 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
                 word = 0;
             }
         }
-        if (rk == 0) continue;
+        if (rk == 0) return;
 
         // V loads for this tile (consumed after the normalizer update)
         u32x4 vr[4];
@@ -299,6 +322,22 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
         // (no barrier here: the next tile writes the other parity's buffers, and
         // this parity's again only after the next tile's own barrier, which
         // every thread reaches after its reads here)
+    };
+    for (int t = nt - 1; t >= 0;) {
+        tile(std::integral_constant<int, 0>{}, t);
+        if (--t < 0) break;
+        if constexpr (NPF > 1) {
+            tile(std::integral_constant<int, (NPF > 1 ? 1 : 0)>{}, t);
+            if (--t < 0) break;
+        }
+        if constexpr (NPF > 2) {
+            tile(std::integral_constant<int, (NPF > 2 ? 2 : 0)>{}, t);
+            if (--t < 0) break;
+        }
+        if constexpr (NPF > 3) {
+            tile(std::integral_constant<int, (NPF > 3 ? 3 : 0)>{}, t);
+            if (--t < 0) break;
+        }
     }
 
     // sum the 16 key subsets of every d chunk, write the partial state
@@ -326,16 +365,28 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
 __global__ __launch_bounds__(128) void decode_combine_d128(const float* __restrict__ part, bf16_t* __restrict__ o,
                                                            float* __restrict__ lse, int nsplit) {
     constexpr int D = 128;
+    __shared__ float wmax[2];
     const long bh = blockIdx.x;
     const int dd = threadIdx.x;
     const float* src = part + bh * nsplit * (D + 2);
+    // M = max over the partitions, the threads splitting the partitions (their
+    // loads are independent, so they are all in flight together)
     float M = -INFINITY;
-    for (int p = 0; p < nsplit; ++p) M = fmaxf(M, src[p * (D + 2)]);
+    for (int p = dd; p < nsplit; p += 128) M = fmaxf(M, src[p * (D + 2)]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    if ((dd & 63) == 0) wmax[dd >> 6] = M;
+    __syncthreads();
+    M = fmaxf(wmax[0], wmax[1]);
+    // weighted sums in partition order; unrolled so several partitions' loads
+    // are in flight at once
     float lam = 0.f, x = 0.f;
+#pragma unroll 8
     for (int p = 0; p < nsplit; ++p) {
-        const float w = fast_exp2(src[p * (D + 2)] - M);
-        lam = fmaf(src[p * (D + 2) + 1], w, lam);
-        x = fmaf(src[p * (D + 2) + 2 + dd], w, x);
+        const float* sp = src + p * (D + 2);
+        const float w = fast_exp2(sp[0] - M);
+        lam = fmaf(sp[1], w, lam);
+        x = fmaf(sp[2 + dd], w, x);
     }
     o[bh * D + dd] = f32_to_bf16(x / lam);
     if (lse && dd == 0) lse[bh] = (M + fast_log2(lam)) * kLn2;
