@@ -546,7 +546,20 @@ def micro(torch):
     n16 = (8 << 30) // 16
     buf = torch.empty(n16 * 4, dtype=torch.int32, device="cuda").fill_(1)
     t = timed(lambda: lib.ubench_hbm(vp(buf.data_ptr()), ctypes.c_long(n16), vp(out.data_ptr()), cus * 16, st))
-    res["hbm_read_gbs"] = n16 * 16 / t / 1e9
+    res["hbm_read_gbs_one_load_per_thread"] = n16 * 16 / t / 1e9
+    # several independent loads in flight per thread; the best of a small sweep
+    # of loads per thread and workgroups per CU is the streaming ceiling
+    sweep = {}
+    for unroll in (4, 8):
+        for per_cu in (4, 8, 16):
+            blocks = cus * per_cu
+            if n16 % (unroll * blocks * 256) or blocks * 256 > out.numel():
+                continue
+            t = timed(lambda: lib.ubench_hbm_unroll(vp(buf.data_ptr()), ctypes.c_long(n16), vp(out.data_ptr()),
+                                                    blocks, unroll, st))
+            sweep[f"unroll{unroll}_wg{per_cu}_per_cu"] = n16 * 16 / t / 1e9
+    res["hbm_read_sweep_gbs"] = sweep
+    res["hbm_read_gbs"] = max([res["hbm_read_gbs_one_load_per_thread"], *sweep.values()])
     return res
 
 

@@ -80,6 +80,23 @@ __global__ __launch_bounds__(256) void ub_hbm(const u32x4* __restrict__ src, lon
     out[blockIdx.x * blockDim.x + threadIdx.x] = x;
 }
 
+// Streaming read with U independent 16-byte loads in flight per thread: each
+// thread reads vectors i, i + S, ..., i + (U-1) S of a chunk (S = threads in
+// the grid), then moves U*S on; n must be a multiple of U*S.
+template <int U>
+__global__ __launch_bounds__(256) void ub_hbm_unroll(const u32x4* __restrict__ src, long n, uint32_t* __restrict__ out) {
+    const long S = long(gridDim.x) * blockDim.x;
+    uint32_t x = 0;
+    for (long base = long(blockIdx.x) * blockDim.x + threadIdx.x; base < n; base += U * S) {
+        u32x4 y[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) y[u] = __builtin_nontemporal_load(src + base + u * S);
+#pragma unroll
+        for (int u = 0; u < U; ++u) x ^= y[u][0] ^ y[u][1] ^ y[u][2] ^ y[u][3];
+    }
+    out[blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
 // 8 independent chains of x = exp2(-x) per thread: one v_exp_f32 per step
 // (the negation is a source modifier); x stays in (0.5, 1).
 __global__ __launch_bounds__(256) void ub_exp(const uint32_t* __restrict__ seed, float* __restrict__ out, int iters) {
@@ -117,6 +134,19 @@ int ubench_exp(const void* seed, void* out, int blocks, int iters, void* stream)
                        iters);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
+// unroll 4 or 8; n16 must be a multiple of unroll * blocks * 256
+int ubench_hbm_unroll(const void* src, long n16, void* out, int blocks, int unroll, void* stream) {
+    if (unroll == 4)
+        hipLaunchKernelGGL(ub_hbm_unroll<4>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, n16,
+                           (uint32_t*)out);
+    else if (unroll == 8)
+        hipLaunchKernelGGL(ub_hbm_unroll<8>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, n16,
+                           (uint32_t*)out);
+    else
+        return int(hipErrorInvalidValue);
+    return int(hipGetLastError());
+}
+
 int ubench_hbm(const void* src, long n16, void* out, int blocks, void* stream) {
     hipLaunchKernelGGL(ub_hbm, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src, n16,
                        (uint32_t*)out);
