@@ -823,6 +823,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        // Raised wave priority over each MFMA cluster: the SIMD's arbiter then
+        // lets a wave that has reached its products issue them back to back
+        // while the other wave on the SIMD does its exp and packing work.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < 8; ++s) sacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(qa) + qoff[s]), kf[s], sacc);
         if (diag) {  // keys past the row -> -inf: no probability
@@ -840,6 +844,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         for (int s = 0; s < 8; ++s)
             pacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(oa) + qoff[s]),
                           *reinterpret_cast<const u32x4*>(lds_ptr(va) + qoff[s]), pacc);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         // P = exp(s - lse) (zero where masked; lse2 = +inf on rows past L),
         // kept only as bf16 B operands: step hf holds registers 8hf .. 8hf+7.
@@ -855,11 +860,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         }
         __builtin_amdgcn_sched_barrier(0);
         // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
                 dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         // dS = P (dP - D), P taken from its bf16 operand copy
         u32x4 dsf[2];
@@ -874,11 +881,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         }
         __builtin_amdgcn_sched_barrier(0);
         // dK^T (d x keys) += Q^T dS
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
                 dkacc[db] = mfma32(tr_operand_at(qa + 256 * (16 * hf), troff[db]), dsf[hf], dkacc[db]);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // prologue: V of the pair (segments 4w .. 4w+3, rows 16w .. 16w+15); the
