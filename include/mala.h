@@ -43,7 +43,8 @@
  *
  * Supported shapes (anything else returns MALA_ERR_UNSUPPORTED)
  *  - prefill (fwd/bwd): H % Hkv == 0 (else MALA_ERR_INVALID_ARG); L >= 1
- *      (ragged L allowed);
+ *      (ragged L allowed), L*d < 2^31 (Lcap*d for chunked prefill) and
+ *      B*H*L*d < 2^40;
  *      MALA_BF16 with d = 128 and tile {128, 64} (grouped K/V heads allowed);
  *      MALA_F32  with d = 64  and tile {64, 64} (H == Hkv only).
  *  - decode: Hq % Hkv == 0 (else MALA_ERR_INVALID_ARG) with G = Hq/Hkv one of

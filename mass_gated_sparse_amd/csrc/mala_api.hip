@@ -68,6 +68,8 @@ mala_status check_prefill(const void* q, const void* k, const void* v, int B, in
         return fail(MALA_ERR_UNSUPPORTED, "unsupported prefill instantiation dtype=%d d=%d tile=%dx%d", int(dt), d,
                     tile.bq, tile.bk);
     if ((long)B * H * L * d >= (1L << 40)) return fail(MALA_ERR_UNSUPPORTED, "tensor too large");
+    // element offsets within one head are 32-bit in the kernels
+    if ((long)L * d >= (1L << 31)) return fail(MALA_ERR_UNSUPPORTED, "sequence too long (L*d >= 2^31)");
     return MALA_OK;
 }
 
@@ -131,6 +133,7 @@ mala_status mala_fwd_chunk(const void* q, const void* kcache, const void* vcache
     if ((long)P + Lq > Lcap) return fail(MALA_ERR_INVALID_ARG, "P + Lq (%ld) exceeds Lcap (%d)", (long)P + Lq, Lcap);
     if (dtype != MALA_BF16) return fail(MALA_ERR_UNSUPPORTED, "chunked prefill needs bf16");
     if ((long)B * Hkv * Lcap * d >= (1L << 40)) return fail(MALA_ERR_UNSUPPORTED, "cache too large");
+    if ((long)Lcap * d >= (1L << 31)) return fail(MALA_ERR_UNSUPPORTED, "sequence too long (Lcap*d >= 2^31)");
     mala::FwdArgs a{};
     a.q = q; a.k = kcache; a.v = vcache; a.o = o; a.lse = lse;
     a.B = B; a.H = H; a.Hkv = Hkv; a.L = Lq; a.d = d;

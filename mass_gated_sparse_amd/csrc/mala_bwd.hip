@@ -662,12 +662,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
     float scale_log2, const uint32_t* __restrict__ dbits, uint32_t* __restrict__ aux_bits) {
     using namespace bwdk;
     constexpr int HB = 64, KP = 2 * BK;  // rows per half block, keys per workgroup
-    // hbuf[0..3]: Q and dO halves of two work units (hbuf[0], hbuf[1] and
-    // hbuf[2], hbuf[3]); reused at the end for the cross-wave reduction.
-    __shared__ __attribute__((aligned(1024))) uint8_t hbuf[4][HB * 256];
+    // hbuf[2b], hbuf[2b+1]: Q and dO halves of the unit in buffer b (three
+    // buffers: the unit being loaded, the current one and the one the lagging
+    // waves finish); reused at the end for the cross-wave reduction.
+    __shared__ __attribute__((aligned(1024))) uint8_t hbuf[6][HB * 256];
     __shared__ __attribute__((aligned(1024))) uint8_t vtile[KP * 256];
-    __shared__ __attribute__((aligned(16))) float stA[2][HB];  // lse2, D of the half's rows
-    __shared__ __attribute__((aligned(16))) float stB[2][HB];
+    __shared__ __attribute__((aligned(16))) float stb[3][2][HB];  // lse2, D of the half's rows, per buffer
 
     const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it stay scalar
@@ -806,21 +806,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         return qn;
     };
 
-    // One unit: half h of block qb, computed from (qs, os, st).  Only the
-    // diagonal block needs a visibility mask (keys past the row, including
-    // keys past L); in its first half the second tile's keys lie past every
-    // row, so those waves skip it.
-    auto unit = [&](auto diag_tag, int bh, int qb, int h, int fl, const uint8_t* qs, const uint8_t* os,
-                    const float (*st)[HB]) {
-        constexpr bool diag = decltype(diag_tag)::value;
-        if (aux_bits && tid == 0 && h == 0)  // the tiles this pass visits (parity statistics)
-            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + w0], ((fl & 1) ? bit0 : 0u) | ((fl & 2) ? bit1 : 0u));
-        if (!((fl >> tt) & 1)) return;        // this wave's tile is skipped for the block
-        if (diag && h == 0 && kq >= 2) return;  // every key past every row of the half
-        const int r0 = qb * BQ + HB * h;
+    // One unit is half h of block qb.  Its front part computes S and dP, its
+    // back part P, dS and the dV, dK products.  Only the diagonal block needs
+    // a visibility mask (keys past the row, including keys past L); in its
+    // first half the second tile's keys lie past every row, so those waves
+    // skip it.
+    //
+    // Waves w and w+4 share a SIMD.  If both ran the same part at the same
+    // time, the SIMD would alternate between both waves issuing MFMAs and both
+    // doing exp and packing work.  So the waves of the second tile run half a
+    // unit behind: between two barriers a wave of the first tile computes the
+    // front and back of unit n, while its SIMD partner computes the back of
+    // unit n-1 (its P and dS work beside the first wave's S and dP MFMAs) and
+    // then the front of unit n.  Units therefore live in three buffers: the one
+    // being loaded, the current one and the one the lagging waves finish.
+    f32x16 sacc, pacc;  // S and dP of a unit between its front and its back
+    auto front = [&](bool diag, int r0, const uint8_t* qs, const uint8_t* os) {
         const uint32_t qa = lds_addr_of(qs), oa = lds_addr_of(os);
         // S (32 rows x 32 keys) = Q K^T; register r holds row 32rh + 8(r/4) + 4hl + r%4, key j
-        f32x16 sacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
         // Raised wave priority over each MFMA cluster: the SIMD's arbiter then
@@ -837,7 +840,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         }
         __builtin_amdgcn_sched_barrier(0);
         // dP (32 rows x 32 keys) = dO V^T
-        f32x16 pacc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
 #pragma unroll
@@ -846,9 +848,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
                           *reinterpret_cast<const u32x4*>(lds_ptr(va) + qoff[s]), pacc);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
+    };
+    // back part, in three steps: P from S, dS from dP and P (both into bf16
+    // operand registers), and the dV, dK products
+    u32x4 pf[2], dsf[2];
+    auto p_step = [&](const float (*st)[HB]) {
         // P = exp(s - lse) (zero where masked; lse2 = +inf on rows past L),
         // kept only as bf16 B operands: step hf holds registers 8hf .. 8hf+7.
-        u32x4 pf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[0][32 * rh + 8 * g + 4 * hl]);
@@ -859,17 +865,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
             pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
-        __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto ds_step = [&](const float (*st)[HB]) {
         // dS = P (dP - D), P taken from its bf16 operand copy
-        u32x4 dsf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[1][32 * rh + 8 * g + 4 * hl]);
@@ -880,7 +878,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
             dsf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
         }
         __builtin_amdgcn_sched_barrier(0);
+    };
+    auto dv_step = [&](const uint8_t* os) {
+        // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
+        const uint32_t oa = lds_addr_of(os);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto dk_step = [&](const uint8_t* qs) {
         // dK^T (d x keys) += Q^T dS
+        const uint32_t qa = lds_addr_of(qs);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -888,10 +901,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
             for (int hf = 0; hf < 2; ++hf)
                 dkacc[db] = mfma32(tr_operand_at(qa + 256 * (16 * hf), troff[db]), dsf[hf], dkacc[db]);
         __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // prologue: V of the pair (segments 4w .. 4w+3, rows 16w .. 16w+15); the
-    // first unit into buffers 0, 1
+    // first unit into buffer 0
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int rt = 16 * wave + 4 * it + (lane >> 4);
@@ -910,38 +924,72 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         stats_load(bkv * G + ih, qb * BQ);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
-    stats_store(stA);
+    stats_store(stb[0]);
     lds_barrier();
-    // Each unit is computed from one buffer pair while the next streams into
-    // the other.  A head's diagonal block, if kept, is its first block.
-    bool odd = false;
-    auto advance = [&](auto diag_tag) {
+    // Between two barriers: the next unit streams into buffer nb while the
+    // current unit (buffer cb) and the lagging waves' previous unit (buffer
+    // pb) are computed.  A head's diagonal block, if kept, is its first block.
+    auto run = [&](auto lag_tag) {
+    constexpr bool lag = decltype(lag_tag)::value;
+    int cb = 0, pb = 0;
+    bool pvalid = false, pact = false;  // a previous unit exists; this wave computes its back
+    while (ih < G || pvalid) {
+        const bool cvalid = ih < G;
         const int bh = bkv * G + ih, qcur = qb, hcur = h, fcur = fl;
-        if (h == 0 && qb * BQ + HB < L) {
-            h = 1;  // second half of the same block
+        const int nb = cb == 2 ? 0 : cb + 1;
+        bool more = false;
+        if (cvalid) {
+            if (h == 0 && qb * BQ + HB < L) {
+                h = 1;  // second half of the same block
+            } else {
+                qb = next_item(qb);
+                h = 0;
+                if (ih < G) fl = flags_of(qb);
+            }
+            more = ih < G;
+            if (more) {
+                const int r0n = qb * BQ + HB * h;
+                stats_load(bkv * G + ih, r0n);
+                half_async(q, hbuf[2 * nb], bkv * G + ih, r0n);
+                half_async(dout, hbuf[2 * nb + 1], bkv * G + ih, r0n);
+            }
+            if (aux_bits && tid == 0 && hcur == 0)  // the tiles this pass visits (parity statistics)
+                atomicOr(&aux_bits[(long(bh) * nqb + qcur) * words + w0],
+                         ((fcur & 1) ? bit0 : 0u) | ((fcur & 2) ? bit1 : 0u));
+        }
+        const bool diag = qcur == qb0;
+        // this wave's tile is kept for the block, and some key of it is visible
+        const bool cact = cvalid && ((fcur >> tt) & 1) && !(diag && hcur == 0 && kq >= 2);
+        if constexpr (!lag) {
+            if (cact) {
+                front(diag, qcur * BQ + HB * hcur, hbuf[2 * cb], hbuf[2 * cb + 1]);
+                p_step(stb[cb]);
+                dv_step(hbuf[2 * cb + 1]);
+                ds_step(stb[cb]);
+                dk_step(hbuf[2 * cb]);
+            }
         } else {
-            qb = next_item(qb);
-            h = 0;
-            if (ih < G) fl = flags_of(qb);
+            if (pact) {
+                dv_step(hbuf[2 * pb + 1]);
+                dk_step(hbuf[2 * pb]);
+            }
+            if (cact) {
+                front(diag, qcur * BQ + HB * hcur, hbuf[2 * cb], hbuf[2 * cb + 1]);
+                p_step(stb[cb]);
+                ds_step(stb[cb]);
+            }
         }
-        const bool more = ih < G;
-        if (more) {
-            const int r0n = qb * BQ + HB * h;
-            stats_load(bkv * G + ih, r0n);
-            half_async(q, odd ? hbuf[0] : hbuf[2], bkv * G + ih, r0n);
-            half_async(dout, odd ? hbuf[1] : hbuf[3], bkv * G + ih, r0n);
-        }
-        unit(diag_tag, bh, qcur, hcur, fcur, odd ? hbuf[2] : hbuf[0], odd ? hbuf[3] : hbuf[1], odd ? stB : stA);
-        if (more) stats_store(odd ? stA : stB);
+        if (more) stats_store(stb[nb]);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffers landed
-        lds_barrier();                       // next buffers complete; every wave is done with these
-        odd = !odd;
-    };
-    while (ih < G) {
-        const int hcur = ih;
-        while (ih == hcur && qb == qb0) advance(std::true_type{});  // at most its two halves
-        while (ih == hcur) advance(std::false_type{});
+        lds_barrier();  // next buffers complete; every wave is done with the oldest
+        pvalid = cvalid;
+        pact = cact;
+        pb = cb;
+        cb = nb;
     }
+    };
+    if (tt == 0) run(std::false_type{});
+    else run(std::true_type{});
 
     // Sum the two row groups.  Accumulators hold dK^T, dV^T: lane = key,
     // register 4g + x of block db = d 32db + 8g + 4hl + x.  Waves of row group
@@ -967,7 +1015,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
                     u32x2 w;
                     w[0] = pack_bf16x2((acc[db][4 * g] + x[0]) * mul, (acc[db][4 * g + 1] + x[1]) * mul);
                     w[1] = pack_bf16x2((acc[db][4 * g + 2] + x[2]) * mul, (acc[db][4 * g + 3] + x[3]) * mul);
-                    *reinterpret_cast<u32x2*>(out + kvoff + long(key) * D + 32 * db + 8 * g + 4 * hl) = w;
+                    // 32-bit element offset within the head (key < L): nothing
+                    // per lane stays live from the K loads to here
+                    *reinterpret_cast<u32x2*>(out + kvoff + uint32_t(key * D + 32 * db + 8 * g + 4 * hl)) = w;
                 }
         }
         lds_barrier();

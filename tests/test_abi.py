@@ -98,6 +98,7 @@ def fwd(lib, q=P, B=1, H=2, Hkv=2, L=256, d=128, dt=0, tau=1.0, tile=(128, 64), 
     ({"tile": (64, 64)}, UNSUPPORTED, "instantiation"),
     ({"dt": 1}, UNSUPPORTED, "instantiation"),  # f32 path is d=64 only
     ({"B": 1 << 12, "H": 1 << 12, "Hkv": 1 << 12, "L": 1 << 10}, UNSUPPORTED, "too large"),
+    ({"L": 1 << 24}, UNSUPPORTED, "too long"),
 ])
 def test_fwd_rejects(lib, kw, status, msg):
     assert fwd(lib, **kw) == status
@@ -120,6 +121,7 @@ def fwd_chunk(lib, q=P, B=1, H=4, Hkv=2, Lq=256, Poff=1000, Lcap=2048, d=128, dt
     ({"H": 4, "Hkv": 3}, INVALID, "multiple"),
     ({"dt": 1, "d": 64, "tile": (64, 64), "H": 2, "Hkv": 2}, UNSUPPORTED, "bf16"),
     ({"d": 64}, UNSUPPORTED, "instantiation"),
+    ({"Lcap": 1 << 24}, UNSUPPORTED, "too long"),
 ])
 def test_fwd_chunk_rejects(lib, kw, status, msg):
     assert fwd_chunk(lib, **kw) == status
