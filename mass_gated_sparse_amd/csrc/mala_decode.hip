@@ -129,6 +129,18 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
             ltest[r] = sp[1];
         }
     }
+    // Each row's test threshold in the raw dot-product domain,
+    // (m2 + log2 l + log2 tau - log2 Lq) / c with l the test normalizer, kept
+    // in registers and recomputed only when the row's state changes (after a
+    // tile its vote group keeps); an empty state keeps any visible key.
+    const float inv_scale_log2 = 1.f / scale_log2;
+    float thr[G];
+    auto set_thr = [&](int r) {
+        const float lz = SEED ? ltest[r] : lsum[r];
+        thr[r] = (lz == 0.f) ? -FLT_MAX : (m2[r] + fast_log2(lz) + log2_tau - log2_lq) * inv_scale_log2;
+    };
+#pragma unroll
+    for (int r = 0; r < G; ++r) set_thr(r);
 
     u32x4 kr[4];
     // Loads are unconditional: a key past the partition (k1 > k0 always) reads
@@ -215,9 +227,7 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
             uint32_t vm = 0;  // rows of this wave's keys that vote keep
 #pragma unroll
             for (int r = 0; r < G; ++r) {
-                const float lz = SEED ? ltest[r] : lsum[r];
-                const float thr = (lz == 0.f) ? -FLT_MAX : (m2[r] + fast_log2(lz) + log2_tau - log2_lq) / scale_log2;
-                if (mx[r] >= thr) vm |= 1u << r;
+                if (mx[r] >= thr[r]) vm |= 1u << r;
             }
             if (lane == 0) {
                 vote_sm[par][wave] = int(vm);
@@ -300,6 +310,7 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
             const float tsum = (wsum_sm[par][0][r] + wsum_sm[par][1][r]) + (wsum_sm[par][2][r] + wsum_sm[par][3][r]);
             lsum[r] = lsum[r] * alpha[r] + tsum;
             if (SEED) ltest[r] = ltest[r] * alpha[r] + tsum;
+            if (GATED && ((rk >> r) & 1u)) set_thr(r);
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[r][c] *= alpha[r];
         }
