@@ -124,6 +124,7 @@ def main():
 
     from mass_gated_sparse_amd import ops
     from synth import WORKLOADS, decode_inputs, prefill_inputs
+    from synth import sharpness
 
     wx, wd = WORKLOADS["train128k"], WORKLOADS["decode128k"]
     t0 = time.time()
@@ -161,7 +162,12 @@ def main():
         ops.decode_into(qd, kc, vc, Lk, od, lsed, tau, ws_d, split, wd.bk, stats=std)
         dkp, dlg = int(std["kept"].sum()), int(std["legal"].sum())
         torch.cuda.synchronize()
-        return fk, bk_, dkp, dlg
+        # per (sequence, head): its sharpness multiplier c_h and kept fractions
+        per_head = [{"b": b_, "h": h_, "c_h": sharpness(wx, b_, h_),
+                     "fwd": int(st["kept"][b_, h_].sum()) / legal_tiles(L, *tile),
+                     "bwd": int(stb["kept"][b_, h_].sum()) / legal_tiles(L, *tile)}
+                    for b_ in range(B) for h_ in range(H)]
+        return fk, bk_, dkp, dlg, per_head
 
     n_legal = B * H * legal_tiles(L, *tile)
 
@@ -193,7 +199,7 @@ def main():
     dense_dec = 4.0 * Bd * Hq * Lk * d
     dense_step = dense_fwd + dense_bwd + dense_dec
 
-    fk, bk_, dkp, dlg = stats_pass(args.tau)
+    fk, bk_, dkp, dlg, per_head = stats_pass(args.tau)
     log(f"tau={args.tau}: fwd kept {fk}/{n_legal}, bwd kept {bk_}/{n_legal}, decode kept {dkp}/{dlg}")
     wall, ms = run(args.tau, args.steps, args.warmup)
     log(f"tau={args.tau}: step {wall:.2f} ms  fwd {ms['fwd']:.2f}  bwd {ms['bwd']:.2f} (dK/dV {ms['dkdv']:.2f}, "
@@ -292,6 +298,7 @@ def main():
         "bwd_dense_tflops": dense_bwd / (ms["bwd"] * 1e-3) / 1e12,
         "decode_dense_tflops": dense_dec / (ms["dec"] * 1e-3) / 1e12,
         "kept_frac": {"fwd": fk / n_legal, "bwd": bk_ / n_legal, "decode": dkp / dlg},
+        "kept_frac_per_head": per_head,
         "tau0": out_tau0,
         "qk_rate": extra["qk_rate"] if extra else None,
         "vote_overhead": extra["vote_overhead"] if extra else None,
