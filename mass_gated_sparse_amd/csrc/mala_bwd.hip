@@ -637,8 +637,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_tile_bf16_d128(
 // Pair layout.  One workgroup of 8 waves per pair of 64-key tiles (128 keys, tiles 2u and
 // 2u+1): wave w owns keys 32kq .. +31 of the pair, kq = 2(w>>2) + (w&1) (so
 // tile 2u + w/4), and rows 32((w>>1)&1) .. +31 of every 64-row half of a
-// query block; waves w and w+4 share a SIMD.  K of the wave's keys is held in registers (B operand of
-// S = Q K^T); the V tiles of the pair sit in LDS (B operand of dP = dO V^T).
+// query block; waves w and w+4 share a SIMD.  The K and V tiles of the pair
+// sit in LDS (B operands of S = Q K^T and dP = dO V^T); keys past L read key
+// L-1 there, and the diagonal block's mask gives them no probability.
+//
+// Operand reads.  With the accumulators and the per-row state a wave is at
+// the 256-register limit, and left to itself the compiler issues each LDS
+// operand read just before its product, so every product waits out the LDS
+// latency.  The products of a unit therefore run from explicit rings: the
+// two operands of S and dP three products ahead, the transposed operands of
+// dV and dK three ahead, with a scheduling fence after each product so the
+// order stays; the rows' lse is read two products before P needs it.  K
+// sits in LDS (not in registers) to make room for the rings.
 //
 // Decisions.  The dQ pass runs first and tests every tile against the final
 // lse; its decision bits reach this pass through the backward's workspace.
@@ -662,12 +672,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
     float scale_log2, const uint32_t* __restrict__ dbits, uint32_t* __restrict__ aux_bits) {
     using namespace bwdk;
     constexpr int HB = 64, KP = 2 * BK;  // rows per half block, keys per workgroup
-    // hbuf[2b], hbuf[2b+1]: Q and dO halves of the unit in buffer b (three
-    // buffers: the unit being loaded, the current one and the one the lagging
-    // waves finish); reused at the end for the cross-wave reduction.
-    __shared__ __attribute__((aligned(1024))) uint8_t hbuf[6][HB * 256];
+    // hbuf[0..3]: Q and dO halves of two work units (hbuf[0], hbuf[1] and
+    // hbuf[2], hbuf[3]); reused at the end for the cross-wave reduction.
+    __shared__ __attribute__((aligned(1024))) uint8_t hbuf[4][HB * 256];
     __shared__ __attribute__((aligned(1024))) uint8_t vtile[KP * 256];
-    __shared__ __attribute__((aligned(16))) float stb[3][2][HB];  // lse2, D of the half's rows, per buffer
+    __shared__ __attribute__((aligned(1024))) uint8_t ktile[KP * 256];
+    __shared__ __attribute__((aligned(16))) float stA[2][HB];  // lse2, D of the half's rows
+    __shared__ __attribute__((aligned(16))) float stB[2][HB];
 
     const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, j = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it stay scalar
@@ -681,13 +692,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
     const bool kvalid = key < L;
     const int qb0 = u;  // the pair's diagonal block: the first query block that sees it
     const bool t1 = 2 * u + 1 < (L + BK - 1) / BK;  // the pair's second tile exists
-    const u32x4 z4 = {0u, 0u, 0u, 0u};
 
-    // K of this wave's 32 keys as B operands (lane = key, 8 contiguous d)
-    u32x4 kf[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-        kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(k + kvoff + long(key) * D + 16 * s + 8 * hl) : z4;
     f32x16 dvacc[4], dkacc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -745,6 +750,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
     };
     // this wave's 32 keys of V, addressed with the Q-half offsets
     const uint32_t va = lds_addr_of(vtile) + 8192 * kq - 8192 * rh;
+    const uint32_t ka = lds_addr_of(ktile) + 8192 * kq - 8192 * rh;
 
     // Work units are (query head of the group, kept query block, half),
     // head by head.  Kept blocks of one head come 64 at a time: bit i of km0
@@ -806,32 +812,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         return qn;
     };
 
-    // One unit is half h of block qb.  Its front part computes S and dP, its
-    // back part P, dS and the dV, dK products.  Only the diagonal block needs
-    // a visibility mask (keys past the row, including keys past L); in its
-    // first half the second tile's keys lie past every row, so those waves
-    // skip it.
-    //
-    // Waves w and w+4 share a SIMD.  If both ran the same part at the same
-    // time, the SIMD would alternate between both waves issuing MFMAs and both
-    // doing exp and packing work.  So the waves of the second tile run half a
-    // unit behind: between two barriers a wave of the first tile computes the
-    // front and back of unit n, while its SIMD partner computes the back of
-    // unit n-1 (its P and dS work beside the first wave's S and dP MFMAs) and
-    // then the front of unit n.  Units therefore live in three buffers: the one
-    // being loaded, the current one and the one the lagging waves finish.
-    f32x16 sacc, pacc;  // S and dP of a unit between its front and its back
-    auto front = [&](bool diag, int r0, const uint8_t* qs, const uint8_t* os) {
+    // One unit: half h of block qb, computed from (qs, os, st).  Only the
+    // diagonal block needs a visibility mask (keys past the row, including
+    // keys past L); in its first half the second tile's keys lie past every
+    // row, so those waves skip it.
+    auto unit = [&](auto diag_tag, int bh, int qb, int h, int fl, const uint8_t* qs, const uint8_t* os,
+                    const float (*st)[HB]) {
+        constexpr bool diag = decltype(diag_tag)::value;
+        if (aux_bits && tid == 0 && h == 0)  // the tiles this pass visits (parity statistics)
+            atomicOr(&aux_bits[(long(bh) * nqb + qb) * words + w0], ((fl & 1) ? bit0 : 0u) | ((fl & 2) ? bit1 : 0u));
+        if (!((fl >> tt) & 1)) return;        // this wave's tile is skipped for the block
+        if (diag && h == 0 && kq >= 2) return;  // every key past every row of the half
+        const int r0 = qb * BQ + HB * h;
         const uint32_t qa = lds_addr_of(qs), oa = lds_addr_of(os);
-        // S (32 rows x 32 keys) = Q K^T; register r holds row 32rh + 8(r/4) + 4hl + r%4, key j
+        // S (32 rows x 32 keys) = Q K^T and dP = dO V^T: 16 products whose two
+        // operands are read from LDS three products ahead (a ring of four),
+        // with a scheduling fence after each product so that the reads stay
+        // ahead.  Register r of S holds row 32rh + 8(r/4) + 4hl + r%4, key j.
+        f32x16 sacc, pacc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-        // Raised wave priority over each MFMA cluster: the SIMD's arbiter then
-        // lets a wave that has reached its products issue them back to back
-        // while the other wave on the SIMD does its exp and packing work.
+        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; pacc[r] = 0.f; }
+        auto rdA = [&](int i) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(lds_ptr(i < 8 ? qa : oa) + qoff[i & 7]);
+        };
+        auto rdB = [&](int i) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(lds_ptr(i < 8 ? ka : va) + qoff[i & 7]);
+        };
+        u32x4 ra[4], rb[4];
+        f32x4 lz[4];
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) sacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(qa) + qoff[s]), kf[s], sacc);
+        for (int i = 0; i < 3; ++i) { ra[i] = rdA(i); rb[i] = rdB(i); }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i + 3 < 16) { ra[(i + 3) & 3] = rdA(i + 3); rb[(i + 3) & 3] = rdB(i + 3); }
+            if (i == 14) {  // the rows' lse for P, read while the last products run
+#pragma unroll
+                for (int g = 0; g < 4; ++g) lz[g] = *reinterpret_cast<const f32x4*>(&st[0][32 * rh + 8 * g + 4 * hl]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < 8) sacc = mfma32(ra[i & 3], rb[i & 3], sacc);
+            else pacc = mfma32(ra[i & 3], rb[i & 3], pacc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
         if (diag) {  // keys past the row -> -inf: no probability
             const int lim = key - r0 - 32 * rh - 4 * hl;
 #pragma unroll
@@ -839,35 +864,40 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
                 if (8 * (r >> 2) + (r & 3) < lim) sacc[r] = -INFINITY;
         }
         __builtin_amdgcn_sched_barrier(0);
-        // dP (32 rows x 32 keys) = dO V^T
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-            pacc = mfma32(*reinterpret_cast<const u32x4*>(lds_ptr(oa) + qoff[s]),
-                          *reinterpret_cast<const u32x4*>(lds_ptr(va) + qoff[s]), pacc);
-        __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    // back part, in three steps: P from S, dS from dP and P (both into bf16
-    // operand registers), and the dV, dK products
-    u32x4 pf[2], dsf[2];
-    auto p_step = [&](const float (*st)[HB]) {
         // P = exp(s - lse) (zero where masked; lse2 = +inf on rows past L),
         // kept only as bf16 B operands: step hf holds registers 8hf .. 8hf+7.
+        u32x4 pf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const f32x4 lz = *reinterpret_cast<const f32x4*>(&st[0][32 * rh + 8 * g + 4 * hl]);
             float p[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) p[x] = fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[x]));
+            for (int x = 0; x < 4; ++x) p[x] = fast_exp2(fmaf(sacc[4 * g + x], scale_log2, -lz[g][x]));
             pf[g >> 1][2 * (g & 1)] = pack_bf16x2(p[0], p[1]);
             pf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p[2], p[3]);
         }
         __builtin_amdgcn_sched_barrier(0);
-    };
-    auto ds_step = [&](const float (*st)[HB]) {
+        // transposed-operand products: product i = (db = i / 2, hf = i % 2),
+        // A read three products ahead
+        auto tr_pipe = [&](uint32_t base, const u32x4* bop, f32x16* acc) {
+            u32x4 ta[4];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) ta[i] = tr_operand_at(base + 256 * (16 * (i & 1)), troff[i >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i + 3 < 8) ta[(i + 3) & 3] = tr_operand_at(base + 256 * (16 * ((i + 3) & 1)), troff[(i + 3) >> 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                acc[i >> 1] = mfma32(ta[i & 3], bop[i & 1], acc[i >> 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
+        __builtin_amdgcn_s_setprio(1);
+        tr_pipe(oa, pf, dvacc);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
         // dS = P (dP - D), P taken from its bf16 operand copy
+        u32x4 dsf[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 dd = *reinterpret_cast<const f32x4*>(&st[1][32 * rh + 8 * g + 4 * hl]);
@@ -878,40 +908,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
             dsf[g >> 1][2 * (g & 1) + 1] = pack_bf16x2(p2 * (pacc[4 * g + 2] - dd[2]), p3 * (pacc[4 * g + 3] - dd[3]));
         }
         __builtin_amdgcn_sched_barrier(0);
-    };
-    auto dv_step = [&](const uint8_t* os) {
-        // dV^T (d x keys) += dO^T P : A = dO^T (transposed read), B = P (lane = key)
-        const uint32_t oa = lds_addr_of(os);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                dvacc[db] = mfma32(tr_operand_at(oa + 256 * (16 * hf), troff[db]), pf[hf], dvacc[db]);
-        __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    auto dk_step = [&](const uint8_t* qs) {
         // dK^T (d x keys) += Q^T dS
-        const uint32_t qa = lds_addr_of(qs);
         __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                dkacc[db] = mfma32(tr_operand_at(qa + 256 * (16 * hf), troff[db]), dsf[hf], dkacc[db]);
+        tr_pipe(qa, dsf, dkacc);
         __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: V of the pair (segments 4w .. 4w+3, rows 16w .. 16w+15); the
-    // first unit into buffer 0
+    // prologue: K and V of the pair (segments 4w .. 4w+3, rows 16w .. 16w+15);
+    // the first unit into buffers 0, 1
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int rt = 16 * wave + 4 * it + (lane >> 4);
         const uint32_t off = uint32_t(min(rt, L - 1 - u * KP) * D + (((lane & 15) ^ rowkey(rt)) << 3)) * 2u;
         dma16s(v + kvoff + long(u) * KP * D, off,
                __builtin_amdgcn_readfirstlane(lds_addr_of(vtile) + 4096 * wave + 1024 * it));
+        dma16s(k + kvoff + long(u) * KP * D, off,
+               __builtin_amdgcn_readfirstlane(lds_addr_of(ktile) + 4096 * wave + 1024 * it));
     }
     open_head();
     int qb = kept_from(qb0);
@@ -924,72 +936,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
         stats_load(bkv * G + ih, qb * BQ);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);
-    stats_store(stb[0]);
+    stats_store(stA);
     lds_barrier();
-    // Between two barriers: the next unit streams into buffer nb while the
-    // current unit (buffer cb) and the lagging waves' previous unit (buffer
-    // pb) are computed.  A head's diagonal block, if kept, is its first block.
-    auto run = [&](auto lag_tag) {
-    constexpr bool lag = decltype(lag_tag)::value;
-    int cb = 0, pb = 0;
-    bool pvalid = false, pact = false;  // a previous unit exists; this wave computes its back
-    while (ih < G || pvalid) {
-        const bool cvalid = ih < G;
+    // Each unit is computed from one buffer pair while the next streams into
+    // the other.  A head's diagonal block, if kept, is its first block.
+    bool odd = false;
+    auto advance = [&](auto diag_tag) {
         const int bh = bkv * G + ih, qcur = qb, hcur = h, fcur = fl;
-        const int nb = cb == 2 ? 0 : cb + 1;
-        bool more = false;
-        if (cvalid) {
-            if (h == 0 && qb * BQ + HB < L) {
-                h = 1;  // second half of the same block
-            } else {
-                qb = next_item(qb);
-                h = 0;
-                if (ih < G) fl = flags_of(qb);
-            }
-            more = ih < G;
-            if (more) {
-                const int r0n = qb * BQ + HB * h;
-                stats_load(bkv * G + ih, r0n);
-                half_async(q, hbuf[2 * nb], bkv * G + ih, r0n);
-                half_async(dout, hbuf[2 * nb + 1], bkv * G + ih, r0n);
-            }
-            if (aux_bits && tid == 0 && hcur == 0)  // the tiles this pass visits (parity statistics)
-                atomicOr(&aux_bits[(long(bh) * nqb + qcur) * words + w0],
-                         ((fcur & 1) ? bit0 : 0u) | ((fcur & 2) ? bit1 : 0u));
-        }
-        const bool diag = qcur == qb0;
-        // this wave's tile is kept for the block, and some key of it is visible
-        const bool cact = cvalid && ((fcur >> tt) & 1) && !(diag && hcur == 0 && kq >= 2);
-        if constexpr (!lag) {
-            if (cact) {
-                front(diag, qcur * BQ + HB * hcur, hbuf[2 * cb], hbuf[2 * cb + 1]);
-                p_step(stb[cb]);
-                dv_step(hbuf[2 * cb + 1]);
-                ds_step(stb[cb]);
-                dk_step(hbuf[2 * cb]);
-            }
+        if (h == 0 && qb * BQ + HB < L) {
+            h = 1;  // second half of the same block
         } else {
-            if (pact) {
-                dv_step(hbuf[2 * pb + 1]);
-                dk_step(hbuf[2 * pb]);
-            }
-            if (cact) {
-                front(diag, qcur * BQ + HB * hcur, hbuf[2 * cb], hbuf[2 * cb + 1]);
-                p_step(stb[cb]);
-                ds_step(stb[cb]);
-            }
+            qb = next_item(qb);
+            h = 0;
+            if (ih < G) fl = flags_of(qb);
         }
-        if (more) stats_store(stb[nb]);
+        const bool more = ih < G;
+        if (more) {
+            const int r0n = qb * BQ + HB * h;
+            stats_load(bkv * G + ih, r0n);
+            half_async(q, odd ? hbuf[0] : hbuf[2], bkv * G + ih, r0n);
+            half_async(dout, odd ? hbuf[1] : hbuf[3], bkv * G + ih, r0n);
+        }
+        unit(diag_tag, bh, qcur, hcur, fcur, odd ? hbuf[2] : hbuf[0], odd ? hbuf[3] : hbuf[1], odd ? stB : stA);
+        if (more) stats_store(odd ? stA : stB);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's loads into the next buffers landed
-        lds_barrier();  // next buffers complete; every wave is done with the oldest
-        pvalid = cvalid;
-        pact = cact;
-        pb = cb;
-        cb = nb;
-    }
+        lds_barrier();                       // next buffers complete; every wave is done with these
+        odd = !odd;
     };
-    if (tt == 0) run(std::false_type{});
-    else run(std::true_type{});
+    while (ih < G) {
+        const int hcur = ih;
+        while (ih == hcur && qb == qb0) advance(std::true_type{});  // at most its two halves
+        while (ih == hcur) advance(std::false_type{});
+    }
 
     // Sum the two row groups.  Accumulators hold dK^T, dV^T: lane = key,
     // register 4g + x of block db = d 32db + 8g + 4hl + x.  Waves of row group
@@ -1016,7 +994,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_pair_bf16_d128(
                     w[0] = pack_bf16x2((acc[db][4 * g] + x[0]) * mul, (acc[db][4 * g + 1] + x[1]) * mul);
                     w[1] = pack_bf16x2((acc[db][4 * g + 2] + x[2]) * mul, (acc[db][4 * g + 3] + x[3]) * mul);
                     // 32-bit element offset within the head (key < L): nothing
-                    // per lane stays live from the K loads to here
+                    // per lane stays live from the start to here
                     *reinterpret_cast<u32x2*>(out + kvoff + uint32_t(key * D + 32 * db + 8 * g + 4 * hl)) = w;
                 }
         }
