@@ -107,29 +107,49 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
     for (int s = 0; s < 8; ++s) koff[s] = swz(j, 2 * s + hl);
     int voff[4][2];
     tr_offsets(lane, voff);
+    // The 16 products run from a register ring: the K operand of product i
+    // (key block i & 1, step i >> 1) is read three products ahead, with a
+    // scheduling fence after each product so that the reads stay ahead.
     auto scores = [&](const uint8_t* kt, f32x16* sacc) {
         const uint32_t kb0 = lds_addr_of(kt);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        auto rd = [&](int i) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(lds_ptr(kb0 + 8192 * (i & 1)) + koff[i >> 1]);
+        };
+        u32x4 ring[4];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(kb0 + 8192 * kb) + koff[s]);
-                sacc[kb] = mfma32(a, qf[s], sacc[kb]);
-            }
+        for (int i = 0; i < 3; ++i) ring[i] = rd(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i + 3 < 16) ring[(i + 3) & 3] = rd(i + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[i & 1] = mfma32(ring[i & 3], qf[i >> 1], sacc[i & 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // O^T (d x rows) += V^T (d x keys) P^T (keys x rows)
+    // product i = (db = i / 4, kb = (i / 2) % 2, hf = i % 2), its transposed
+    // V operand read three products ahead (ring, fenced as above)
     auto pv = [&](const uint8_t* vt, const u32x4 (*pf)[2]) {
         const uint32_t vb = lds_addr_of(vt);
+        auto rd = [&](int i) -> u32x4 {
+            return tr_operand_at(vb + 256 * (32 * ((i >> 1) & 1) + 16 * (i & 1)), voff[i >> 2]);
+        };
+        u32x4 ring[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int i = 0; i < 3; ++i) ring[i] = rd(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-                    oacc[db] = mfma32(tr_operand_at(vb + 256 * (32 * kb + 16 * hf), voff[db]), pf[kb][hf], oacc[db]);
+        for (int i = 0; i < 16; ++i) {
+            if (i + 3 < 16) ring[(i + 3) & 3] = rd(i + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            oacc[i >> 2] = mfma32(ring[i & 3], pf[(i >> 1) & 1][i & 1], oacc[i >> 2]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     int nkept = 0;
