@@ -113,17 +113,28 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
     int troff[4][2];
     tr_offsets(lane, troff);
 
-    // S^T (keys x rows) of a tile: A = K rows from LDS, B = Q (registers)
+    // S^T (keys x rows) of a tile: A = K rows from LDS, B = Q (registers).
+    // The 16 products run from a register ring: the K operand of product i
+    // (key block i & 1, step i >> 1) is read three products ahead, with a
+    // scheduling fence after each product so that the reads stay ahead.
     auto scores = [&](uint32_t kb0, f32x16* sacc) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        auto rd = [&](int i) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(lds_ptr(kb0 + 8192 * (i & 1)) + koff[i >> 1]);
+        };
+        u32x4 ring[4];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(kb0 + 8192 * kb) + koff[s]);
-                sacc[kb] = mfma32(a, qf[s], sacc[kb]);
-            }
+        for (int i = 0; i < 3; ++i) ring[i] = rd(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i + 3 < 16) ring[(i + 3) & 3] = rd(i + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc[i & 1] = mfma32(ring[i & 3], qf[i >> 1], sacc[i & 1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     // Scores of a tile at or past tdiag: keys past the row or past L become
@@ -252,10 +263,21 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
                 f32x16 pacc;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+                {  // V operands from a ring, three products ahead (as for the scores)
+                    auto rd = [&](int s) -> u32x4 {
+                        return *reinterpret_cast<const u32x4*>(lds_ptr(vta + 8192 * kb) + koff[s]);
+                    };
+                    u32x4 ring[4];
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(lds_ptr(vta + 8192 * kb) + koff[s]);
-                    pacc = mfma32(a, of[s], pacc);
+                    for (int s = 0; s < 3; ++s) ring[s] = rd(s);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        if (s + 3 < 8) ring[(s + 3) & 3] = rd(s + 3);
+                        __builtin_amdgcn_sched_barrier(0);
+                        pacc = mfma32(ring[s & 3], of[s], pacc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
@@ -266,13 +288,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
                         pk[kb][hf][e] = pack_bf16x2(__uint_as_float(w << 16) * (pacc[r0] - Di),
                                                     __uint_as_float(w & 0xffff0000u) * (pacc[r0 + 1] - Di));
                     }
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf)
-                        gacc[db] = mfma32(tr_operand_at(ks0 + 256 * (32 * kb + 16 * hf), troff[db]), pk[kb][hf],
-                                          gacc[db]);
                 __builtin_amdgcn_sched_barrier(0);
+                {  // transposed K operands from a ring: product i = (db = i / 2, hf = i % 2)
+                    auto rd = [&](int i) -> u32x4 {
+                        return tr_operand_at(ks0 + 256 * (32 * kb + 16 * (i & 1)), troff[i >> 1]);
+                    };
+                    u32x4 ring[4];
+#pragma unroll
+                    for (int i = 0; i < 3; ++i) ring[i] = rd(i);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if (i + 3 < 8) ring[(i + 3) & 3] = rd(i + 3);
+                        __builtin_amdgcn_sched_barrier(0);
+                        gacc[i >> 1] = mfma32(ring[i & 3], pk[kb][i & 1], gacc[i >> 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
             }
         }
         // decisions: handed to the dK/dV pass (dbits), and to the caller's stats
