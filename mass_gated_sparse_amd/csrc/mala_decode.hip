@@ -50,6 +50,41 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// Cross-lane steps that stay off the LDS pipe.  DPP moves within a row of 16
+// lanes: quad_perm [1,0,3,2] and [2,3,0,1] give lane i the value of lane i^1
+// and i^2; row_half_mirror gives it lane 7-i of its 8-lane half (the other
+// quad), row_mirror lane 15-i (the other half).  On values that are uniform
+// within quads (within 8-lane halves) the two mirrors pair the same values as
+// xor 4 (xor 8).  Every lane holds its result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// A value uniform within each 16-lane row, combined over the four rows as
+// op(op(row 0, row 1), op(row 2, row 3)) -- the grouping of the xor-16 then
+// xor-32 butterfly, so the result is the same bit for bit.  The row swaps
+// (v_permlane16_swap / v_permlane32_swap with both operands x) leave the two
+// rows of each pair in the two results.
+__device__ __forceinline__ void row_pairs(float x, float& a, float& b, bool wide) {
+    const auto s = wide ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                        : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(s[0]);
+    b = __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float rows_max(float x) {
+    float a, b;
+    row_pairs(x, a, b, false);
+    row_pairs(fmaxf(a, b), a, b, true);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    float a, b;
+    row_pairs(x, a, b, false);
+    row_pairs(a + b, a, b, true);
+    return a + b;
+}
+
 // SEED: this launch covers the older partitions of a seeded decode and reads
 // partition 0's final state from `part` (written by the previous launch).
 // PREV: V tiles are fetched one tile ahead together with K, whatever the
@@ -207,8 +242,8 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
                 a = dot2(qx[2], kcur[c][2], a);
                 a = dot2(qx[3], kcur[c][3], a);
             }
-            a += __shfl_xor(a, 1, 64);
-            a += __shfl_xor(a, 2, 64);
+            a += dpp_f<kDppXor1>(a);  // the key's four d-quarters
+            a += dpp_f<kDppXor2>(a);
             s[r] = kvalid ? a : -INFINITY;
         }
 
@@ -218,9 +253,9 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
 #pragma unroll
         for (int r = 0; r < G; ++r) {
             float x = s[r];
-#pragma unroll
-            for (int m = 4; m <= 32; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-            mx[r] = x;
+            x = fmaxf(x, dpp_f<kDppHalfMirror>(x));  // (x is uniform within quads)
+            x = fmaxf(x, dpp_f<kDppMirror>(x));
+            mx[r] = rows_max(x);
         }
         uint32_t rk = (1u << G) - 1u;  // rows whose vote group keeps the tile
         if (GATED) {
@@ -298,9 +333,10 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
             alpha[r] = rkeep ? fast_exp2(m2[r] - mn) : 1.f;
             m2[r] = mn;
             const float pv = rkeep ? fast_exp2(fmaf(s[r], scale_log2, -mn)) : 0.f;  // invalid key (-inf): 0
-            float ps = (quarter == 0) ? pv : 0.f;
-#pragma unroll
-            for (int m = 4; m <= 32; m <<= 1) ps += __shfl_xor(ps, m, 64);
+            // the wave's sum over its 16 keys (pv is uniform within quads)
+            float ps = pv + dpp_f<kDppHalfMirror>(pv);
+            ps += dpp_f<kDppMirror>(ps);
+            ps = rows_sum(ps);
             if (quarter == 0) p_sm[par][r][skey] = pv;
             if (lane == 0) wsum_sm[par][wave][r] = ps;
         }
@@ -311,8 +347,10 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
             lsum[r] = lsum[r] * alpha[r] + tsum;
             if (SEED) ltest[r] = ltest[r] * alpha[r] + tsum;
             if (GATED && ((rk >> r) & 1u)) set_thr(r);
+            if (alpha[r] != 1.f) {  // (exact: most tiles move no row's maximum)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[r][c] *= alpha[r];
+                for (int c = 0; c < 8; ++c) acc[r][c] *= alpha[r];
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
