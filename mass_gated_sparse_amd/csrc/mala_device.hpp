@@ -58,6 +58,19 @@ __device__ __forceinline__ void balanced_item(int i, int BH, int period, int& ra
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// x combined with the value of lane i^32, in every lane: op(x[i % 32], x[i % 32 + 32]).
+// v_permlane32_swap with both operands x leaves the low half in the first
+// result and the high half in the second, so no LDS traffic is involved; the
+// operations are commutative, so every lane gets the xor-32 butterfly's value.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
 // Workgroup barrier that orders LDS only: waits for this wave's LDS operations,

@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
         float alpha = 1.f;
         if (keep) {
             // statistics (no V needed); P_t = exp2(s*c - m) kept in place
-            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            mx = max_halves(mx);
             const float mn = fmaxf(m2, mx * scale_log2);
             const float mref = (mn == -INFINITY) ? 0.f : mn;
             float lpart = 0.f;
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(const bf16_t* __restrict
                     sc[kb][r] = p;
                     lpart += p;
                 }
-            lpart += shfl_xor_f(lpart, 32);
+            lpart = sum_halves(lpart);
             alpha = fast_exp2(m2 - mref);
             lsum = lsum * alpha + lpart;
             m2 = mn;
