@@ -212,15 +212,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
         // V tile that step consumed).
         __builtin_amdgcn_s_waitcnt(0x0f70);
         lds_barrier();  // vote flags of tile t and K(t-1) visible; previous V and K(t+1) reads done
+        if (t >= 2) tile_dma(kh, ks2, t - 2);  // (independent of the vote: issued before its flags are read)
         int vflags = 1;
         if (GATED) vflags = vote_sm[t & 1][0] | vote_sm[t & 1][1] | vote_sm[t & 1][2] | vote_sm[t & 1][3];
         const bool keep = vflags != 0;
+        if (keep) tile_dma(vh, vta, t);
         if (STATS && tstat && tid == 0)  // tau = 0 runs no test: NaN
             tstat[(long(bh) * nqb + qb) * ntk + t] =
                 GATED ? fmaxf(fmaxf(tstat_sm[t & 1][0], tstat_sm[t & 1][1]), fmaxf(tstat_sm[t & 1][2], tstat_sm[t & 1][3]))
                       : NAN;
-        if (keep) tile_dma(vh, vta, t);
-        if (t >= 2) tile_dma(kh, ks2, t - 2);
         // P = exp(s - lse) (zero on invisible entries) as bf16 B operands; step
         // (kb, hf) holds score registers 8hf .. 8hf+7 of key block kb
         u32x4 pk[2][2];
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_d128(
             }
         }
         if (keep) {
-            // V(t) was issued just before K(t-2); wait for both
+            // K(t-2) and V(t) were issued at the start of the step; wait for both
             __builtin_amdgcn_s_waitcnt(0x0f70);
             lds_barrier();  // V(t) visible
             __builtin_amdgcn_sched_barrier(0);
