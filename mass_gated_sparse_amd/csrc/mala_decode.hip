@@ -218,15 +218,12 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
     auto tile = [&](auto slot_tag, int t) {
         constexpr int SL = decltype(slot_tag)::value;
         const int par = t & 1;
-        u32x4 kcur[4] = {kring[SL][0], kring[SL][1], kring[SL][2], kring[SL][3]};
         u32x4 vcur[4] = {vring[SL][0], vring[SL][1], vring[SL][2], vring[SL][3]};
-        // refill the slot with the tile NPF visits later; near the end of the
+        // refill the V slot with the tile NPF visits later (its K slot is
+        // refilled once the scores have read it); near the end of the
         // partition that tile does not exist and tile 0 is read again (unused),
         // so every step issues the same loads and no branch hides them from the
         // wait counting
-        load_k(max(t - NPF, 0));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kring[SL][c] = kr[c];
         if (PREV) load_v(max(t - NPF, 0), vring[SL]);
         const int key = k0 + t * BK + skey;
         const bool kvalid = key < k1;
@@ -237,15 +234,18 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const u32x4 qx = *reinterpret_cast<const u32x4*>(&q_sm[r][16 * quarter + 4 * c]);
-                a = dot2(qx[0], kcur[c][0], a);
-                a = dot2(qx[1], kcur[c][1], a);
-                a = dot2(qx[2], kcur[c][2], a);
-                a = dot2(qx[3], kcur[c][3], a);
+                a = dot2(qx[0], kring[SL][c][0], a);
+                a = dot2(qx[1], kring[SL][c][1], a);
+                a = dot2(qx[2], kring[SL][c][2], a);
+                a = dot2(qx[3], kring[SL][c][3], a);
             }
             a += dpp_f<kDppXor1>(a);  // the key's four d-quarters
             a += dpp_f<kDppXor2>(a);
             s[r] = kvalid ? a : -INFINITY;
         }
+        load_k(max(t - NPF, 0));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kring[SL][c] = kr[c];
 
         // per-row maximum over the wave's keys (wave-uniform): the vote tests it,
         // and a kept tile's statistics need it; both go out in one exchange
