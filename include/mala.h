@@ -194,7 +194,14 @@ mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o,
                      void* dq, void* dk, void* dv, mala_stats* stats,
                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mala_decode needs for these sizes (0 for invalid sizes). */
+/*
+ * Workspace bytes mala_decode and mala_decode_seeded need for these sizes (0
+ * for invalid sizes): the partition states, B*Hq*nsplit*(d+2) floats with
+ * nsplit = ceil(Lk/split_keys), rounded up to 256 bytes; when nsplit > 1 and
+ * split_keys/64 <= 256, plus the states of the newest partition's 64-key
+ * tiles, B*Hq*(split_keys/64)*(d+2) floats rounded up to 256 bytes (used by
+ * mala_decode_seeded only; mala_decode needs the first part).
+ */
 size_t mala_decode_workspace_size(int B, int Hq, int Hkv, int Lk, int d, int split_keys);
 
 /*
@@ -239,9 +246,12 @@ mala_status mala_decode(const void* q, const void* kcache, const void* vcache,
  * first visited tile is kept), exactly as a mala_decode partition.  Every
  * older partition is tested against partition 0's final normalizer plus its
  * own kept keys, and keeps nothing by force; its output state holds only its
- * own kept keys, and the partitions' states are merged exactly.  Two kernel
- * launches: partition 0, then the older partitions (tau = 0: one launch,
- * every tile kept).  Statistics as for mala_decode with nsplit = ceil(Lk /
+ * own kept keys, and the partitions' states are merged exactly.  Partition
+ * 0 runs first: with older partitions (and tps <= 256) as the states of its
+ * tiles, formed in parallel, followed by a replay of its walk over them (the
+ * same test and merge, so the same decisions up to floating-point rounding
+ * of the merge order); otherwise tile by tile.  The older partitions follow
+ * (tau = 0: one launch, every tile kept).  Statistics as for mala_decode with nsplit = ceil(Lk /
  * split_keys) partitions in this order; bit t of partition p = its t-th tile
  * from the oldest.  events[0] is recorded before the first launch and
  * events[1] after the merge.

@@ -212,10 +212,23 @@ mala_status mala_bwd(const void* q, const void* k, const void* v, const void* o,
     return hip_status(e, "mala_bwd launch");
 }
 
+// Partition states of a decode: [B, Hq, nsplit, d + 2] floats.
+static size_t decode_part_bytes(int B, int Hq, long nsplit, int d) {
+    return align256(size_t(B) * Hq * nsplit * (d + 2) * sizeof(float));
+}
+// Tile states of a seeded decode's newest partition, when it is replayed from
+// them (more than one partition, at most kSeedScanMaxTiles 64-key tiles in
+// one): [B, Hq, split_keys / 64, d + 2] floats after the partition states.
+static size_t decode_tile_bytes(int B, int Hq, long nsplit, int d, int split_keys) {
+    const long tps = split_keys / 64;
+    if (nsplit < 2 || split_keys % 64 || tps > mala::kSeedScanMaxTiles) return 0;
+    return align256(size_t(B) * Hq * tps * (d + 2) * sizeof(float));
+}
+
 size_t mala_decode_workspace_size(int B, int Hq, int Hkv, int Lk, int d, int split_keys) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lk <= 0 || d <= 0 || split_keys <= 0) return 0;
     const long nsplit = cdiv(Lk, split_keys);
-    return align256(size_t(B) * Hq * nsplit * (d + 2) * sizeof(float));
+    return decode_part_bytes(B, Hq, nsplit, d) + decode_tile_bytes(B, Hq, nsplit, d, split_keys);
 }
 
 // Address of `scratch` on the current device, looked up once per device
@@ -267,7 +280,12 @@ static mala_status decode_call(const char* name, bool seeded, const void* q, con
     if (rows_per_vote == 0) rows_per_vote = G;
     if (rows_per_vote < 0 || G % rows_per_vote)
         return fail(MALA_ERR_INVALID_ARG, "rows_per_vote (%d) must divide Hq/Hkv (%d)", rows_per_vote, G);
-    const size_t need = mala_decode_workspace_size(B, Hq, Hkv, Lk, d, split_keys);
+    // a plain decode needs the partition states only; a seeded one also the
+    // tile states of its newest partition
+    const long nsplit = cdiv(Lk, split_keys);
+    const size_t part_bytes = decode_part_bytes(B, Hq, nsplit, d);
+    const size_t tile_bytes = seeded ? decode_tile_bytes(B, Hq, nsplit, d, split_keys) : 0;
+    const size_t need = part_bytes + tile_bytes;
     if (use_scratch) {
         if (need > size_t(MALA_DECODE_NOALLOC_SCRATCH_BYTES))
             return fail(MALA_ERR_UNSUPPORTED,
@@ -286,6 +304,7 @@ static mala_status decode_call(const char* name, bool seeded, const void* q, con
     mala::DecArgs a{};
     a.q = q; a.kc = kcache; a.vc = vcache; a.o = o; a.lse = lse;
     a.part = static_cast<float*>(workspace);
+    a.tpart = tile_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes) : nullptr;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = G; a.Lk = Lk; a.Lcap = Lcap; a.d = d;
     a.split_keys = split_keys; a.bk = bk;
     // plain: ceil(Lk/split) partitions from key 0; seeded: ceil(ntiles/tps) partitions counted back from

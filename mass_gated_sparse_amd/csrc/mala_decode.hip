@@ -30,12 +30,20 @@
 // Partitions.  Plain: partition p holds keys [p*S, min((p+1)*S, Lk)).
 // Seeded: tiles stay the 64-key tiles counted from key 0, but partition p
 // holds the S/64 tiles ending S/64*p tiles before the newest tile (partition
-// 0 is the newest; the oldest may be short).  A seeded decode runs in two
-// launches: partition 0 from an empty state, then every older partition with
+// 0 is the newest; the oldest may be short).  A seeded decode runs
+// partition 0 from an empty state first, then every older partition with
 // partition 0's final (m2, l) added to its test normalizer (the normalizer
 // established on the most recent keys, extended across partitions).  Its own
 // output state still starts empty, so the exact merge counts no key twice,
 // and no tile is kept by force.
+//
+// Partition 0 of a seeded decode with older partitions is not walked tile by
+// tile: its tiles' states (m_t, l_t, acc_t) are formed in parallel, each from
+// an empty state (the split kernel, ungated, one tile per partition), and
+// decode_seed_scan_d128 then visits them newest first, tests each against
+// the running state (m2 + log2 l + log2 tau - log2 Lq against the tile's
+// c*max s, the split kernel's test) and merges the kept ones.  The same
+// decisions and the same state, up to the rounding of the merge order.
 #include <float.h>
 
 #include <type_traits>
@@ -410,6 +418,106 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
     }
 }
 
+// Newest partition of a seeded decode from the states of its tiles (tile
+// partition p = tile tps-1-p of the partition, each formed from an empty
+// state): one workgroup of 512 threads per (sequence, K/V head).  Lane r < G
+// of the first wave replays row r's walk over the tiles, newest first: a vote
+// group (rpv consecutive rows) keeps a tile iff one of its rows has
+// c*max s >= m2 + log2 l + log2 tau - log2 Lq (any visible key while l = 0),
+// and its rows then merge the tile's (m_t, l_t) into their state.  Every
+// thread (row mod 4, d) then sums the kept tiles' acc_t with weights
+// 2^(m_t - m_final).  Writes partition 0's (m2, l, acc) in the split kernel's
+// format, and its statistics.
+template <int G, bool STATS>
+__global__ __launch_bounds__(512) void decode_seed_scan_d128(
+    const float* __restrict__ tpart, float* __restrict__ part, int Hq, int Hkv, int nsplit, int tps, int words,
+    float log2_tau, float log2_lq, int rpv, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
+    uint32_t* __restrict__ bits, float* __restrict__ tstat) {
+    constexpr int D = 128;
+    __shared__ float mt_sm[G][kSeedScanMaxTiles], lt_sm[G][kSeedScanMaxTiles];
+    __shared__ __attribute__((aligned(16))) float w_sm[G][kSeedScanMaxTiles];  // merge weights (0: skipped)
+    __shared__ float fin_sm[2][G];
+    const int tid = threadIdx.x, bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
+    auto src = [&](int r, int p) { return tpart + ((long(b) * Hq + g * G + r) * tps + p) * (D + 2); };
+    for (int e = tid; e < G * tps; e += 512) {
+        const int r = e / tps, p = e % tps;
+        mt_sm[r][p] = src(r, p)[0];
+        lt_sm[r][p] = src(r, p)[1];
+    }
+    __syncthreads();
+    if (tid < 64) {  // the walk: lane r = row r (lanes G.. idle)
+        const int r = tid;
+        const bool live = r < G;
+        const int rc = live ? r : 0;
+        const uint64_t gmask = ((rpv >= 64 ? ~0ull : (1ull << rpv) - 1ull)) << (r / rpv * rpv);
+        const bool lead = live && r % rpv == 0;  // keeps its group's statistics
+        const long sidx = (long(bg) * (G / rpv) + r / rpv) * nsplit;  // partition 0 (lead lanes)
+        float m2 = -INFINITY, l = 0.f;
+        int nkept = 0;
+        uint32_t word = 0;
+        for (int p = 0; p < tps; ++p) {
+            const int t = tps - 1 - p;
+            const float mt = mt_sm[rc][p];
+            const float base = m2 + fast_log2(l) + log2_tau - log2_lq;
+            const bool v = live && ((l == 0.f) ? (mt != -INFINITY) : (mt >= base));
+            const bool keep = (__ballot(v) & gmask) != 0ull;
+            if (STATS) {
+                float dl = !live || mt == -INFINITY ? -INFINITY : (l == 0.f) ? INFINITY : mt - base;
+                for (int m = 1; m < rpv; m <<= 1) dl = fmaxf(dl, __shfl_xor(dl, m, 64));
+                if (lead) {
+                    nkept += keep;
+                    if (keep) word |= 1u << (t & 31);
+                    if (bits && (t & 31) == 0) {
+                        bits[sidx * words + (t >> 5)] = word;
+                        word = 0;
+                    }
+                    if (tstat) tstat[sidx * tps + t] = dl;
+                }
+            }
+            if (live) {
+                if (keep) {
+                    const float mn = fmaxf(m2, mt);
+                    l = l * fast_exp2(m2 - mn) + lt_sm[rc][p] * fast_exp2(mt - mn);
+                    m2 = mn;
+                }
+                w_sm[r][p] = keep ? 1.f : 0.f;
+            }
+        }
+        if (live) {
+            fin_sm[0][r] = m2;
+            fin_sm[1][r] = l;
+        }
+        if (STATS && lead) {
+            if (kept) kept[sidx] = nkept;
+            if (legal) legal[sidx] = tps;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * tps; e += 512) {
+        const int r = e / tps, p = e % tps;
+        w_sm[r][p] = w_sm[r][p] != 0.f ? fast_exp2(mt_sm[r][p] - fin_sm[0][r]) : 0.f;
+    }
+    __syncthreads();
+    const int dd = tid & 127;
+    for (int r = tid >> 7; r < G; r += 4) {
+        float x = 0.f;
+        // 32 tiles' loads in flight at a time; a skipped tile weighs 0
+        for (int p0 = 0; p0 < tps; p0 += 32) {
+            float a32[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) a32[i] = src(r, min(p0 + i, tps - 1))[2 + dd];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) x = fmaf(a32[i], p0 + i < tps ? w_sm[r][min(p0 + i, tps - 1)] : 0.f, x);
+        }
+        float* dst = part + ((long(b) * Hq + g * G + r) * nsplit) * (D + 2);
+        dst[2 + dd] = x;
+        if (dd == 0) {
+            dst[0] = fin_sm[0][r];
+            dst[1] = fin_sm[1][r];
+        }
+    }
+}
+
 // Exact merge of the partition states of every (sequence, query head).
 __global__ __launch_bounds__(128) void decode_combine_d128(const float* __restrict__ part, bf16_t* __restrict__ o,
                                                            float* __restrict__ lse, int nsplit) {
@@ -455,8 +563,21 @@ static void launch_decode_gs(const DecArgs& a, hipStream_t s) {
         launch_decode_one<G, false, ST, false>(a, s, a.nsplit, 0);
     } else if (!a.seeded) {
         launch_decode_one<G, true, ST, false>(a, s, a.nsplit, 0);
+    } else if (a.nsplit > 1 && a.tps <= kSeedScanMaxTiles && a.tpart) {
+        // partition 0: its tiles' states in parallel (one tile per
+        // partition of the tile workspace, ungated), then the replayed walk;
+        // then the older partitions, which read its final state
+        DecArgs t = a;
+        t.part = a.tpart;
+        t.nsplit = a.tps;
+        t.tps = 1;
+        launch_decode_one<G, false, false, false>(t, s, a.tps, 0);
+        hipLaunchKernelGGL((decode_seed_scan_d128<G, ST>), dim3(a.B * a.Hkv), dim3(512), 0, s, a.tpart, a.part,
+                           a.Hq, a.Hkv, a.nsplit, a.tps, a.words, a.log2_tau, a.log2_lq, a.rpv, a.kept, a.legal,
+                           a.bits, a.tstat);
+        launch_decode_one<G, true, ST, true>(a, s, a.nsplit - 1, 1);
     } else {
-        // partition 0 first; the older partitions read its final state
+        // partition 0 walked tile by tile; the older partitions read its final state
         launch_decode_one<G, true, ST, false, true>(a, s, 1, 0);
         if (a.nsplit > 1) launch_decode_one<G, true, ST, true>(a, s, a.nsplit - 1, 1);
     }

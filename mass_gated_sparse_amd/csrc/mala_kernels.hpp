@@ -46,6 +46,7 @@ struct DecArgs {
     void* o;
     float* lse;
     float* part;  // [B, Hq, nsplit, d + 2] fp32 partial states (m2, l, acc[d])
+    float* tpart;  // seeded: [B, Hq, tps, d + 2] states of partition 0's tiles (or null)
     int B, Hq, Hkv, G, Lk, Lcap, d;
     int split_keys, bk, nsplit, tps, words;
     float scale_log2, log2_tau, log2_lq;
@@ -67,5 +68,8 @@ hipError_t launch_simple_bwd_f32(const BwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecArgs& a, hipStream_t s);
+// Largest partition (in tiles) whose seeded newest-partition walk is replayed
+// from per-tile states; longer ones are walked tile by tile.
+constexpr int kSeedScanMaxTiles = 256;
 
 }  // namespace mala
