@@ -103,7 +103,9 @@ __device__ __forceinline__ float rows_sum(float x) {
 // live in LDS) give the HBM stream enough independent tiles in flight; the
 // PREV launch runs one workgroup per (sequence, KV head) and keeps the
 // registers its extra V prefetch needs instead.
-template <int G, bool GATED, bool STATS, bool SEED, bool PREV>
+// ONE: every partition is a single tile (the tile states of a seeded decode's
+// newest partition): its V is requested with its K, and nothing is refilled.
+template <int G, bool GATED, bool STATS, bool SEED, bool PREV, bool ONE = false>
 __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     float* __restrict__ part, int Hq, int Hkv, int Lk, int Lcap, int split_keys, int nsplit, int tps, int words,
@@ -113,6 +115,7 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
     // tiles loaded ahead: the newest-partition launch (one workgroup per CU,
     // each walking its tiles in series) keeps four in flight; the others one
     constexpr int NPF = PREV ? 4 : 1;
+    constexpr bool VPF = PREV || ONE;  // V requested together with K
     static_assert(NPF >= 1 && NPF <= 4, "the visit loop below is unrolled for up to four slots");
     __shared__ int vote_sm[2][4];
     __shared__ float wmax_sm[2][4][G];
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
         load_k(max(nt - 1 - i, 0));
 #pragma unroll
         for (int c = 0; c < 4; ++c) kring[i][c] = kr[c];
-        if (PREV) load_v(max(nt - 1 - i, 0), vring[i]);
+        if (VPF) load_v(max(nt - 1 - i, 0), vring[i]);
     }
     // One tile; SL = (nt-1-t) % NPF is a compile-time constant, so the ring
     // stays in registers.
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
         // partition that tile does not exist and tile 0 is read again (unused),
         // so every step issues the same loads and no branch hides them from the
         // wait counting
-        if (PREV) load_v(max(t - NPF, 0), vring[SL]);
+        if (PREV && !ONE) load_v(max(t - NPF, 0), vring[SL]);
         const int key = k0 + t * BK + skey;
         const bool kvalid = key < k1;
         float s[G];
@@ -251,9 +254,11 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
             a += dpp_f<kDppXor2>(a);
             s[r] = kvalid ? a : -INFINITY;
         }
-        load_k(max(t - NPF, 0));
+        if (!ONE) {
+            load_k(max(t - NPF, 0));
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kring[SL][c] = kr[c];
+            for (int c = 0; c < 4; ++c) kring[SL][c] = kr[c];
+        }
 
         // per-row maximum over the wave's keys (wave-uniform): the vote tests it,
         // and a kept tile's statistics need it; both go out in one exchange
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
 
         // V loads for this tile (consumed after the normalizer update)
         u32x4 vr[4];
-        if (PREV) {
+        if (VPF) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) vr[i] = vcur[i];
         } else {
@@ -549,9 +554,9 @@ __global__ __launch_bounds__(128) void decode_combine_d128(const float* __restri
     if (lse && dd == 0) lse[bh] = (M + fast_log2(lam)) * kLn2;
 }
 
-template <int G, bool GT, bool ST, bool SD, bool PV = false>
+template <int G, bool GT, bool ST, bool SD, bool PV = false, bool ONE = false>
 static void launch_decode_one(const DecArgs& a, hipStream_t s, int nparts, int pbase) {
-    hipLaunchKernelGGL((decode_split_bf16_d128<G, GT, ST, SD, PV>), dim3(nparts, a.B * a.Hkv), dim3(256), 0, s,
+    hipLaunchKernelGGL((decode_split_bf16_d128<G, GT, ST, SD, PV, ONE>), dim3(nparts, a.B * a.Hkv), dim3(256), 0, s,
                        (const bf16_t*)a.q, (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.part, a.Hq, a.Hkv, a.Lk,
                        a.Lcap, a.split_keys, a.nsplit, a.tps, a.words, a.scale_log2, a.log2_tau, a.log2_lq, a.kept,
                        a.legal, a.bits, pbase, a.seeded ? 1 : 0, a.rpv, a.tstat);
@@ -571,7 +576,7 @@ static void launch_decode_gs(const DecArgs& a, hipStream_t s) {
         t.part = a.tpart;
         t.nsplit = a.tps;
         t.tps = 1;
-        launch_decode_one<G, false, false, false>(t, s, a.tps, 0);
+        launch_decode_one<G, false, false, false, false, true>(t, s, a.tps, 0);
         hipLaunchKernelGGL((decode_seed_scan_d128<G, ST>), dim3(a.B * a.Hkv), dim3(512), 0, s, a.tpart, a.part,
                            a.Hq, a.Hkv, a.nsplit, a.tps, a.words, a.log2_tau, a.log2_lq, a.rpv, a.kept, a.legal,
                            a.bits, a.tstat);
