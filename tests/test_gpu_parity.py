@@ -357,12 +357,15 @@ def seeded_legal(Lk, split, bk=64):
 
 
 @pytest.mark.parametrize("Lk,split,Lcap", [(3000, 1024, None), (4097, 4096, 4200), (1536, 512, None),
-                                           (5000, 512, 5003), (64, 4096, None), (1, 64, 100), (20000, 4096, None)])
+                                           (5000, 512, 5003), (64, 4096, None), (1, 64, 100), (20000, 4096, None),
+                                           (40000, 16384, None), (70000, 32768, None)])
 @pytest.mark.parametrize("tau", [0.0, 1.0, 16.0, math.inf])
 def test_decode_seeded_bf16(ops, Lk, split, Lcap, tau):
     """mala_decode_seeded against the oracle's seeded decode: decisions per
     partition (partition 0 the newest), O and lse; with one partition it is
-    mala_decode bit for bit."""
+    mala_decode bit for bit.  Newest partitions of up to 256 tiles are
+    replayed from tile states (40000 / 16384: 256 tiles), longer ones walked
+    tile by tile (70000 / 32768: 512 tiles)."""
     w, x = _decode_case(Lk, (0, 1), Lcap)
     q, kc, vc = _dev_tensors(x, "bf16", ("q", "k", "v"))
     o, lse, st = ops.decode(q, kc, vc, Lk, tau, split_keys=split, bk=64, stats=True, seeded=True)
