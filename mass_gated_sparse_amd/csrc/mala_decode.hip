@@ -8,22 +8,17 @@
 // kept.  Savings and limitations paragraphs: the KV cache is read in full for
 // QK; a skipped tile saves its V read, so decode is bound by cache traffic.
 //
-// One workgroup (4 waves) per (sequence, KV head, partition).  The G query
-// heads sharing the KV head are the rows of the workgroup; they share every
-// K/V tile load.  Votes run over groups of rpv consecutive rows (rpv = G: the
-// whole group, so a skipped tile really saves the V bytes; rpv = 1: one vote
-// per query head).  A tile is kept for a vote group iff one of its rows votes
+// One wave per (sequence, KV head, partition).  The G query heads sharing
+// the KV head are the rows of the wave's products; they share every K/V tile
+// load.  Votes run over groups of rpv consecutive rows (rpv = G: the whole
+// group, so a skipped tile really saves the V bytes; rpv = 1: one vote per
+// query head).  A tile is kept for a vote group iff one of its rows votes
 // keep; only that group's rows update their state, and V is read iff some
-// group keeps the tile.  The kernel is
-// HBM-bound: K tiles are prefetched one tile ahead into registers; V is read
-// only for kept tiles.
-//
-// Thread mapping.  Scores: thread t handles key t/4 of the tile and a
-// 32-element quarter of d (four 16-byte loads), bf16 dot2 products in fp32,
-// summed over the 4 quarters with lane shuffles; the query quarters are read
-// from LDS (every thread of a quarter reads the same addresses).  PV: thread t handles an
-// 8-element d chunk (t%16) of keys 16*wave + 4*i + (t/16)%4, i = 0..3; its
-// fp32 accumulators are summed over the 16 key subsets once per partition.
+// group keeps the tile.  The kernel is HBM-bound: K of the next tile is
+// requested as soon as the current scores are formed; V is read only for
+// kept tiles.  Scores and PV are bf16 MFMAs with fp32 accumulation (the
+// probabilities enter PV rounded to bf16, the normalizer sums them in fp32);
+// the lane mapping is described at the kernel.
 // Partial states (m2 = running max of s*log2(e), l, acc[d]) are written per
 // (sequence, query head, partition) and merged exactly by the combine kernel.
 //
@@ -52,28 +47,12 @@
 
 namespace mala {
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-// Cross-lane steps that stay off the LDS pipe.  DPP moves within a row of 16
-// lanes: quad_perm [1,0,3,2] and [2,3,0,1] give lane i the value of lane i^1
-// and i^2; row_half_mirror gives it lane 7-i of its 8-lane half (the other
-// quad), row_mirror lane 15-i (the other half).  On values that are uniform
-// within quads (within 8-lane halves) the two mirrors pair the same values as
-// xor 4 (xor 8).  Every lane holds its result.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-// A value uniform within each 16-lane row, combined over the four rows as
-// op(op(row 0, row 1), op(row 2, row 3)) -- the grouping of the xor-16 then
-// xor-32 butterfly, so the result is the same bit for bit.  The row swaps
+// Cross-lane steps that stay off the LDS pipe: a lane's value combined with
+// those of the lanes at the same position in the other three 16-lane rows,
+// as op(op(row 0, row 1), op(row 2, row 3)).  The row swaps
 // (v_permlane16_swap / v_permlane32_swap with both operands x) leave the two
-// rows of each pair in the two results.
+// rows of each pair in the two results; the operations commute, so all four
+// lanes hold the same bits.
 __device__ __forceinline__ void row_pairs(float x, float& a, float& b, bool wide) {
     const auto s = wide ? __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false)
                         : __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -93,38 +72,42 @@ __device__ __forceinline__ float rows_sum(float x) {
     return a + b;
 }
 
+// One wave per (partition, sequence, KV head) runs every step of a tile.
+// The scores and the PV product are 16x16x32 bf16 MFMAs in which lane
+// column n = lane % 16 is query row n (rows past G are zero and never
+// written), so a row's state (m2, l, its test threshold) lives in the four
+// lanes n, n+16, n+32, n+48 and needs no exchange between waves:
+//  - scores S^T (16 keys x 16 rows per chunk, four chunks a tile): A = the
+//    chunk's K (lane (key n, g4 = lane/16) holds d 32c+8g4 .. +8 of its key
+//    for product c), B = Q^T (lane (row n, g4) the same d of its row); lane
+//    (row n, g4) gets keys 16*chunk + 4*g4 + i, i = 0..3;
+//  - the tile's row maximum is a max over a lane's 16 scores and the four
+//    lanes of the row (row swaps); the vote is one ballot;
+//  - PV as O^T (d x rows) += V^T P^T over two 32-key products: B = P^T
+//    (lane (row n, g4) holds keys 32h + 16(j/4) + 4*g4 + j%4, j = 0..7: the
+//    lane's own probabilities of chunks 2h and 2h+1, rounded to bf16), A =
+//    V^T with d = 8m + db for product db and lane (m = n, g4): the lane reads
+//    d 8n .. 8n+8 of those eight keys (16 bytes each, a key's 256 bytes over
+//    16 lanes) and pairs keys with byte permutes; lane (row n, g4) then holds
+//    O[n][32*g4 + 8r + db] in register r of accumulator db, so the rescale by
+//    the row's alpha is lane-local too.
+// K of the next tile is requested as soon as the scores have read the
+// current one; V after the vote, only for a kept tile.  At two waves per
+// SIMD each wave has up to 32 KiB of K and V in flight, which keeps the HBM
+// queue full; the arithmetic of a tile is a few hundred cycles.
 // SEED: this launch covers the older partitions of a seeded decode and reads
 // partition 0's final state from `part` (written by the previous launch).
-// PREV: V tiles are fetched one tile ahead together with K, whatever the
-// vote decides.  Used for the newest partition alone (one workgroup per
-// sequence and KV head, keeping nearly every tile): there the V load would
-// otherwise add a memory latency per tile to a short, serial launch.
-// Occupancy: four workgroups per CU (at most 128 VGPRs, so the query rows
-// live in LDS) give the HBM stream enough independent tiles in flight; the
-// PREV launch runs one workgroup per (sequence, KV head) and keeps the
-// registers its extra V prefetch needs instead.
-// ONE: every partition is a single tile (the tile states of a seeded decode's
-// newest partition): its V is requested with its K, and nothing is refilled.
-template <int G, bool GATED, bool STATS, bool SEED, bool PREV, bool ONE = false>
-__global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
-    float* __restrict__ part, int Hq, int Hkv, int Lk, int Lcap, int split_keys, int nsplit, int tps, int words,
+// VPF: V of the next tile is requested once the current PV has read its
+// registers, whatever the vote decides (the tile states of a seeded decode's
+// newest partition, one tile each, and its walk when that runs tile by tile).
+template <bool GATED, bool STATS, bool SEED, bool VPF>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_bf16_d128(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kcache, const bf16_t* __restrict__ vcache,
+    float* __restrict__ part, int Hq, int Hkv, int G, int Lk, int Lcap, int split_keys, int nsplit, int tps, int words,
     float scale_log2, float log2_tau, float log2_lq, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
     uint32_t* __restrict__ bits, int pbase, int seeded_grid, int rpv, float* __restrict__ tstat) {
     constexpr int D = 128, BK = 64;
-    // tiles loaded ahead: the newest-partition launch (one workgroup per CU,
-    // each walking its tiles in series) keeps four in flight; the others one
-    constexpr int NPF = PREV ? 4 : 1;
-    constexpr bool VPF = PREV || ONE;  // V requested together with K
-    static_assert(NPF >= 1 && NPF <= 4, "the visit loop below is unrolled for up to four slots");
-    __shared__ int vote_sm[2][4];
-    __shared__ float wmax_sm[2][4][G];
-    __shared__ float wsum_sm[2][4][G];
-    __shared__ float p_sm[2][G][BK];
-    __shared__ float red_sm[G][16][D + 4];
-    __shared__ __attribute__((aligned(16))) uint32_t q_sm[G][D / 2];  // the G query rows (bf16 pairs)
-
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lane = threadIdx.x, n = lane & 15, g4 = lane >> 4;
     const int p = int(blockIdx.x) + pbase;
     const int bg = blockIdx.y;  // b * Hkv + g
     const int b = bg / Hkv, g = bg % Hkv;
@@ -141,177 +124,119 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
         k1 = min(k0 + split_keys, Lk);
     }
     const int nt = (k1 - k0 + BK - 1) / BK;
-    // vote groups: row r belongs to group r / rpv; gm[r] = bits of its group's rows
-    const int nvg = G / rpv;
-    uint32_t gm[G];
-#pragma unroll
-    for (int r = 0; r < G; ++r) gm[r] = ((1u << rpv) - 1u) << (r / rpv * rpv);
+    const bool live = n < G;  // lane column n is query row n
+    const long qrow = long(b) * Hq + g * G + (live ? n : 0);
 
-    // score mapping
-    const int skey = tid >> 2, quarter = tid & 3;
-    if (tid < G * 16) {  // 16-byte pieces of the G rows
-        const int r = tid >> 4, c = tid & 15;
-        *reinterpret_cast<u32x4*>(&q_sm[r][4 * c]) =
-            *reinterpret_cast<const u32x4*>(q + (long(b) * Hq + g * G + r) * D + 8 * c);
+    u32x4 qf[4];  // Q^T operands; rows past G are zero
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        qf[c] = u32x4{0u, 0u, 0u, 0u};
+        if (live) qf[c] = *reinterpret_cast<const u32x4*>(q + qrow * D + 32 * c + 8 * g4);
     }
-    __syncthreads();
-    // PV mapping
-    const int dch = tid & 15, ksub = (tid >> 4) & 3;
-    float acc[G][8];
-#pragma unroll
-    for (int r = 0; r < G; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
-    // (m2, lsum): this partition's own state; ltest: the normalizer the test
-    // uses, which also holds the seed (the same as lsum without one)
-    float m2[G], lsum[G], ltest[G];
-#pragma unroll
-    for (int r = 0; r < G; ++r) { m2[r] = -INFINITY; lsum[r] = 0.f; ltest[r] = 0.f; }
-    if (SEED) {
-#pragma unroll
-        for (int r = 0; r < G; ++r) {
-            const float* sp = part + (long(b) * Hq + g * G + r) * nsplit * (D + 2);  // partition 0
-            m2[r] = sp[0];
-            ltest[r] = sp[1];
-        }
-    }
-    // Each row's test threshold in the raw dot-product domain,
-    // (m2 + log2 l + log2 tau - log2 Lq) / c with l the test normalizer, kept
-    // in registers and recomputed only when the row's state changes (after a
-    // tile its vote group keeps); an empty state keeps any visible key.
-    const float inv_scale_log2 = 1.f / scale_log2;
-    float thr[G];
-    auto set_thr = [&](int r) {
-        const float lz = SEED ? ltest[r] : lsum[r];
-        thr[r] = (lz == 0.f) ? -FLT_MAX : (m2[r] + fast_log2(lz) + log2_tau - log2_lq) * inv_scale_log2;
-    };
-#pragma unroll
-    for (int r = 0; r < G; ++r) set_thr(r);
 
-    u32x4 kr[4];
-    // Loads are unconditional: a key past the partition (k1 > k0 always) reads
-    // the partition's last key instead, and its score is set to -inf, so its
-    // probability is 0.  Without branches around them the compiler can count
-    // the loads in flight and wait for exactly the tile it needs.
+    // Loads are clamped: a key past the partition (k1 > k0 always) reads the
+    // partition's last key instead; its score is set to -inf, so its
+    // probability is 0.
+    u32x4 kf[4][4];  // [chunk][product]
     auto load_k = [&](int t) {
-        const int key = min(k0 + t * BK + skey, k1 - 1);
-        const bf16_t* src = kc + kvbase + long(key) * D + 32 * quarter;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kr[c] = *reinterpret_cast<const u32x4*>(src + 8 * c);
+        for (int ch = 0; ch < 4; ++ch) {
+            const int key = min(k0 + t * BK + 16 * ch + n, k1 - 1);
+            const bf16_t* src = kcache + kvbase + long(key) * D + 8 * g4;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) kf[ch][c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+        }
+    };
+    u32x4 vf[2][8];  // [product h][key j]
+    auto load_v = [&](int t) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int key = min(k0 + t * BK + 32 * h + 16 * (j >> 2) + 4 * g4 + (j & 3), k1 - 1);
+                vf[h][j] = *reinterpret_cast<const u32x4*>(vcache + kvbase + long(key) * D + 8 * n);
+            }
     };
 
-    // statistics of vote group tid (threads 0 .. nvg-1), at unit (bg*nvg + tid, p)
-    const long sidx = (long(bg) * nvg + tid) * nsplit + p;
+    // (m2, lsum): this partition's own state of row n; ltest: the normalizer
+    // the test uses, which also holds the seed (the same as lsum without one)
+    float m2 = -INFINITY, lsum = 0.f, ltest = 0.f;
+    if (SEED && live) {
+        const float* sp = part + qrow * nsplit * (D + 2);  // partition 0
+        m2 = sp[0];
+        ltest = sp[1];
+    }
+    // The row's test threshold in the raw dot-product domain,
+    // (m2 + log2 l + log2 tau - log2 Lq) / c with l the test normalizer,
+    // recomputed only after a tile its vote group keeps; an empty state keeps
+    // any visible key.
+    const float inv_scale_log2 = 1.f / scale_log2;
+    auto thr_of = [&]() {
+        const float lz = SEED ? ltest : lsum;
+        return (lz == 0.f) ? -FLT_MAX : (m2 + fast_log2(lz) + log2_tau - log2_lq) * inv_scale_log2;
+    };
+    float thr = thr_of();
+
+    // statistics of vote group n / rpv: kept by lane n = its first row (g4 = 0)
+    const int nvg = G / rpv;
+    const bool lead = g4 == 0 && live && n % rpv == 0;
+    const long sidx = (long(bg) * nvg + n / rpv) * nsplit + p;
     int nkept = 0;
     uint32_t word = 0;
-    if (STATS && bits && tid < nvg)
+    if (STATS && bits && lead)
         for (int w = ((nt - 1) >> 5) + 1; w < words; ++w) bits[sidx * words + w] = 0u;
 
-    auto load_v = [&](int t, u32x4* dst) {  // (clamped like load_k: a key past k1 has probability 0)
+    f32x4 acc[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int vk = min(k0 + t * BK + 16 * wave + 4 * i + ksub, k1 - 1);
-            dst[i] = *reinterpret_cast<const u32x4*>(vc + kvbase + long(vk) * D + 8 * dch);
-        }
-    };
-    // Tiles in flight: K (and, with PREV, V) of the next NPF tiles to visit sit
-    // in a register ring; tile t's buffers are slot (nt-1-t) % NPF.
-    u32x4 kring[NPF][4], vring[NPF][4];
-#pragma unroll
-    for (int i = 0; i < NPF; ++i) {  // (a partition shorter than NPF tiles reads tile 0 again)
-        load_k(max(nt - 1 - i, 0));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kring[i][c] = kr[c];
-        if (VPF) load_v(max(nt - 1 - i, 0), vring[i]);
-    }
-    // One tile; SL = (nt-1-t) % NPF is a compile-time constant, so the ring
-    // stays in registers.
-    auto tile = [&](auto slot_tag, int t) {
-        constexpr int SL = decltype(slot_tag)::value;
-        const int par = t & 1;
-        u32x4 vcur[4] = {vring[SL][0], vring[SL][1], vring[SL][2], vring[SL][3]};
-        // refill the V slot with the tile NPF visits later (its K slot is
-        // refilled once the scores have read it); near the end of the
-        // partition that tile does not exist and tile 0 is read again (unused),
-        // so every step issues the same loads and no branch hides them from the
-        // wait counting
-        if (PREV && !ONE) load_v(max(t - NPF, 0), vring[SL]);
-        const int key = k0 + t * BK + skey;
-        const bool kvalid = key < k1;
-        float s[G];
-#pragma unroll
-        for (int r = 0; r < G; ++r) {
-            float a = 0.f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const u32x4 qx = *reinterpret_cast<const u32x4*>(&q_sm[r][16 * quarter + 4 * c]);
-                a = dot2(qx[0], kring[SL][c][0], a);
-                a = dot2(qx[1], kring[SL][c][1], a);
-                a = dot2(qx[2], kring[SL][c][2], a);
-                a = dot2(qx[3], kring[SL][c][3], a);
-            }
-            a += dpp_f<kDppXor1>(a);  // the key's four d-quarters
-            a += dpp_f<kDppXor2>(a);
-            s[r] = kvalid ? a : -INFINITY;
-        }
-        if (!ONE) {
-            load_k(max(t - NPF, 0));
-#pragma unroll
-            for (int c = 0; c < 4; ++c) kring[SL][c] = kr[c];
-        }
+    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-        // per-row maximum over the wave's keys (wave-uniform): the vote tests it,
-        // and a kept tile's statistics need it; both go out in one exchange
-        float mx[G];
+    load_k(nt - 1);
+    if (VPF) load_v(nt - 1);
+    for (int t = nt - 1; t >= 0; --t) {
+        f32x4 s[4];
 #pragma unroll
-        for (int r = 0; r < G; ++r) {
-            float x = s[r];
-            x = fmaxf(x, dpp_f<kDppHalfMirror>(x));  // (x is uniform within quads)
-            x = fmaxf(x, dpp_f<kDppMirror>(x));
-            mx[r] = rows_max(x);
+        for (int ch = 0; ch < 4; ++ch) {
+            s[ch] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s[ch] = mfma16(kf[ch][c], qf[c], s[ch]);
         }
+        if (t > 0) load_k(t - 1);  // into the registers the products have read
+        if (k0 + t * BK + BK > k1) {  // the partition's newest tile may be partial
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (k0 + t * BK + 16 * ch + 4 * g4 + i >= k1) s[ch][i] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+        for (int ch = 1; ch < 4; ++ch) mx = fmaxf(mx, fmaxf(fmaxf(s[ch][0], s[ch][1]), fmaxf(s[ch][2], s[ch][3])));
+        mx = rows_max(mx);  // the row's maximum over the tile (raw dot product)
+
         uint32_t rk = (1u << G) - 1u;  // rows whose vote group keeps the tile
         if (GATED) {
-            uint32_t vm = 0;  // rows of this wave's keys that vote keep
-#pragma unroll
-            for (int r = 0; r < G; ++r) {
-                if (mx[r] >= thr[r]) vm |= 1u << r;
-            }
-            if (lane == 0) {
-                vote_sm[par][wave] = int(vm);
-#pragma unroll
-                for (int r = 0; r < G; ++r) wmax_sm[par][wave][r] = mx[r];
-            }
-            __syncthreads();
-            const uint32_t rv = uint32_t(vote_sm[par][0] | vote_sm[par][1] | vote_sm[par][2] | vote_sm[par][3]);
+            const uint32_t vm = uint32_t(__ballot(live && mx >= thr)) & 0xffffu;
             rk = 0;
-#pragma unroll
-            for (int r = 0; r < G; ++r)
-                if (rv & gm[r]) rk |= 1u << r;
-            if (STATS && tstat && tid < nvg) {
+            for (int r0 = 0; r0 < G; r0 += rpv) {
+                const uint32_t gmk = ((1u << rpv) - 1u) << r0;
+                if (vm & gmk) rk |= gmk;
+            }
+            if (STATS && tstat) {
                 // log2 of the vote group's test statistic: the largest margin
                 // c*max_j s_rj - (m2 + log2 l + log2 tau - log2 Lq) of its rows,
                 // from the state the vote used (+inf for an empty state)
-                float dl = -INFINITY;
-#pragma unroll
-                for (int r = 0; r < G; ++r) {
-                    if (r / rpv != tid) continue;
-                    const float tm = fmaxf(fmaxf(wmax_sm[par][0][r], wmax_sm[par][1][r]),
-                                           fmaxf(wmax_sm[par][2][r], wmax_sm[par][3][r]));
-                    const float lz = SEED ? ltest[r] : lsum[r];
-                    float dr;
-                    if (tm == -INFINITY) dr = -INFINITY;
-                    else if (lz == 0.f) dr = INFINITY;
-                    else dr = tm * scale_log2 - (m2[r] + fast_log2(lz) + log2_tau - log2_lq);
-                    dl = fmaxf(dl, dr);
-                }
-                tstat[sidx * tps + t] = dl;
+                const float lz = SEED ? ltest : lsum;
+                float dr = (!live || mx == -INFINITY) ? -INFINITY
+                           : (lz == 0.f)              ? INFINITY
+                                                      : mx * scale_log2 - (m2 + fast_log2(lz) + log2_tau - log2_lq);
+                for (int m = 1; m < rpv; m <<= 1) dr = fmaxf(dr, __shfl_xor(dr, m, 64));
+                if (lead) tstat[sidx * tps + t] = dr;
             }
-        } else if (STATS && tstat && tid < nvg) {
+        } else if (STATS && tstat && lead) {
             tstat[sidx * tps + t] = NAN;  // tau = 0 runs no test
         }
-        if (STATS && tid < nvg) {
-            const bool gk = (rk >> (tid * rpv)) & 1u;
+        if (STATS && lead) {
+            const bool gk = (rk >> n) & 1u;
             nkept += gk;
             if (gk) word |= 1u << (t & 31);
             if (bits && (t & 31) == 0) {
@@ -319,105 +244,64 @@ __global__ __launch_bounds__(256, PREV ? 1 : 4) void decode_split_bf16_d128(
                 word = 0;
             }
         }
-        if (rk == 0) return;
-
-        // V loads for this tile (consumed after the normalizer update)
-        u32x4 vr[4];
-        if (VPF) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vr[i] = vcur[i];
-        } else {
-            load_v(t, vr);
-        }
-        if (!GATED) {  // (gated: the maxima went out with the vote)
-            if (lane == 0)
-#pragma unroll
-                for (int r = 0; r < G; ++r) wmax_sm[par][wave][r] = mx[r];
-            __syncthreads();
-        }
-        float alpha[G];
-#pragma unroll
-        for (int r = 0; r < G; ++r) {
+        if (rk != 0) {
+            if (!VPF) load_v(t);
             // a row whose group skips the tile keeps its state: alpha = 1, no probability
-            const bool rkeep = (rk >> r) & 1u;
-            const float tm = fmaxf(fmaxf(wmax_sm[par][0][r], wmax_sm[par][1][r]),
-                                   fmaxf(wmax_sm[par][2][r], wmax_sm[par][3][r]));
-            const float mn = rkeep ? fmaxf(m2[r], tm * scale_log2) : m2[r];  // kept: finite (a valid key)
-            alpha[r] = rkeep ? fast_exp2(m2[r] - mn) : 1.f;
-            m2[r] = mn;
-            const float pv = rkeep ? fast_exp2(fmaf(s[r], scale_log2, -mn)) : 0.f;  // invalid key (-inf): 0
-            // the wave's sum over its 16 keys (pv is uniform within quads)
-            float ps = pv + dpp_f<kDppHalfMirror>(pv);
-            ps += dpp_f<kDppMirror>(ps);
+            const bool rkeep = (rk >> n) & 1u;
+            const float mn = rkeep ? fmaxf(m2, mx * scale_log2) : m2;  // kept: finite (a valid key)
+            const float alpha = rkeep ? fast_exp2(m2 - mn) : 1.f;
+            m2 = mn;
+            float ps = 0.f;
+            u32x4 pb[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ch = 2 * h + (e >> 1), i0 = 2 * (e & 1);
+                    const float p0 = rkeep ? fast_exp2(fmaf(s[ch][i0], scale_log2, -mn)) : 0.f;  // -inf: 0
+                    const float p1 = rkeep ? fast_exp2(fmaf(s[ch][i0 + 1], scale_log2, -mn)) : 0.f;
+                    ps += p0 + p1;
+                    pb[h][e] = pack_bf16x2(p0, p1);
+                }
             ps = rows_sum(ps);
-            if (quarter == 0) p_sm[par][r][skey] = pv;
-            if (lane == 0) wsum_sm[par][wave][r] = ps;
-        }
-        __syncthreads();
+            lsum = lsum * alpha + ps;
+            if (SEED) ltest = ltest * alpha + ps;
+            if (GATED && rkeep) thr = thr_of();
+            if (alpha != 1.f) {  // (exact: most tiles move no row's maximum)
 #pragma unroll
-        for (int r = 0; r < G; ++r) {
-            const float tsum = (wsum_sm[par][0][r] + wsum_sm[par][1][r]) + (wsum_sm[par][2][r] + wsum_sm[par][3][r]);
-            lsum[r] = lsum[r] * alpha[r] + tsum;
-            if (SEED) ltest[r] = ltest[r] * alpha[r] + tsum;
-            if (GATED && ((rk >> r) & 1u)) set_thr(r);
-            if (alpha[r] != 1.f) {  // (exact: most tiles move no row's maximum)
+                for (int db = 0; db < 8; ++db)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[r][c] *= alpha[r];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kk = 16 * wave + 4 * i + ksub;
-            float vf[8];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                vf[2 * c] = __uint_as_float(vr[i][c] << 16);
-                vf[2 * c + 1] = __uint_as_float(vr[i][c] & 0xffff0000u);
+                    for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
             }
 #pragma unroll
-            for (int r = 0; r < G; ++r) {
-                const float pw = p_sm[par][r][kk];
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[r][c] = fmaf(pw, vf[c], acc[r][c]);
-            }
+                for (int db = 0; db < 8; ++db) {
+                    u32x4 a;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t x = vf[h][2 * e][db >> 1], y = vf[h][2 * e + 1][db >> 1];
+                        a[e] = (db & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+                    }
+                    acc[db] = mfma16(a, pb[h], acc[db]);
+                }
         }
-        // (no barrier here: the next tile writes the other parity's buffers, and
-        // this parity's again only after the next tile's own barrier, which
-        // every thread reaches after its reads here)
-    };
-    for (int t = nt - 1; t >= 0;) {
-        tile(std::integral_constant<int, 0>{}, t);
-        if (--t < 0) break;
-        if constexpr (NPF > 1) {
-            tile(std::integral_constant<int, (NPF > 1 ? 1 : 0)>{}, t);
-            if (--t < 0) break;
-        }
-        if constexpr (NPF > 2) {
-            tile(std::integral_constant<int, (NPF > 2 ? 2 : 0)>{}, t);
-            if (--t < 0) break;
-        }
-        if constexpr (NPF > 3) {
-            tile(std::integral_constant<int, (NPF > 3 ? 3 : 0)>{}, t);
-            if (--t < 0) break;
-        }
+        if (VPF && t > 0) load_v(t - 1);
     }
 
-    // sum the 16 key subsets of every d chunk, write the partial state
+    if (live) {
+        float* dst = part + (qrow * nsplit + p) * (D + 2);
+        if (g4 == 0) {
+            dst[0] = m2;
+            dst[1] = lsum;
+        }
 #pragma unroll
-    for (int r = 0; r < G; ++r)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) red_sm[r][4 * wave + ksub][8 * dch + c] = acc[r][c];
-    __syncthreads();
-    for (int e = tid; e < G * D; e += 256) {
-        const int r = e / D, dd = e % D;
-        float x = 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) x += red_sm[r][u][dd];
-        float* dst = part + ((long(b) * Hq + g * G + r) * nsplit + p) * (D + 2);
-        dst[2 + dd] = x;
-        if (dd == 0) { dst[0] = m2[r]; dst[1] = lsum[r]; }
+            for (int db = 0; db < 8; db += 2)
+                *reinterpret_cast<f32x2*>(dst + 2 + 32 * g4 + 8 * r + db) = f32x2{acc[db][r], acc[db + 1][r]};
     }
-    if (STATS && tid < nvg) {
+    if (STATS && lead) {
         if (kept) kept[sidx] = nkept;
         if (legal) legal[sidx] = nt;
     }
@@ -554,10 +438,10 @@ __global__ __launch_bounds__(128) void decode_combine_d128(const float* __restri
     if (lse && dd == 0) lse[bh] = (M + fast_log2(lam)) * kLn2;
 }
 
-template <int G, bool GT, bool ST, bool SD, bool PV = false, bool ONE = false>
+template <bool GT, bool ST, bool SD, bool VPF = false>
 static void launch_decode_one(const DecArgs& a, hipStream_t s, int nparts, int pbase) {
-    hipLaunchKernelGGL((decode_split_bf16_d128<G, GT, ST, SD, PV, ONE>), dim3(nparts, a.B * a.Hkv), dim3(256), 0, s,
-                       (const bf16_t*)a.q, (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.part, a.Hq, a.Hkv, a.Lk,
+    hipLaunchKernelGGL((decode_split_bf16_d128<GT, ST, SD, VPF>), dim3(nparts, a.B * a.Hkv), dim3(64), 0, s,
+                       (const bf16_t*)a.q, (const bf16_t*)a.kc, (const bf16_t*)a.vc, a.part, a.Hq, a.Hkv, a.G, a.Lk,
                        a.Lcap, a.split_keys, a.nsplit, a.tps, a.words, a.scale_log2, a.log2_tau, a.log2_lq, a.kept,
                        a.legal, a.bits, pbase, a.seeded ? 1 : 0, a.rpv, a.tstat);
 }
@@ -565,9 +449,9 @@ static void launch_decode_one(const DecArgs& a, hipStream_t s, int nparts, int p
 template <int G, bool ST>
 static void launch_decode_gs(const DecArgs& a, hipStream_t s) {
     if (!a.gated) {
-        launch_decode_one<G, false, ST, false>(a, s, a.nsplit, 0);
+        launch_decode_one<false, ST, false>(a, s, a.nsplit, 0);
     } else if (!a.seeded) {
-        launch_decode_one<G, true, ST, false>(a, s, a.nsplit, 0);
+        launch_decode_one<true, ST, false>(a, s, a.nsplit, 0);
     } else if (a.nsplit > 1 && a.tps <= kSeedScanMaxTiles && a.tpart) {
         // partition 0: its tiles' states in parallel (one tile per
         // partition of the tile workspace, ungated), then the replayed walk;
@@ -576,15 +460,15 @@ static void launch_decode_gs(const DecArgs& a, hipStream_t s) {
         t.part = a.tpart;
         t.nsplit = a.tps;
         t.tps = 1;
-        launch_decode_one<G, false, false, false, false, true>(t, s, a.tps, 0);
+        launch_decode_one<false, false, false, true>(t, s, a.tps, 0);
         hipLaunchKernelGGL((decode_seed_scan_d128<G, ST>), dim3(a.B * a.Hkv), dim3(512), 0, s, a.tpart, a.part,
                            a.Hq, a.Hkv, a.nsplit, a.tps, a.words, a.log2_tau, a.log2_lq, a.rpv, a.kept, a.legal,
                            a.bits, a.tstat);
-        launch_decode_one<G, true, ST, true>(a, s, a.nsplit - 1, 1);
+        launch_decode_one<true, ST, true>(a, s, a.nsplit - 1, 1);
     } else {
         // partition 0 walked tile by tile; the older partitions read its final state
-        launch_decode_one<G, true, ST, false, true>(a, s, 1, 0);
-        if (a.nsplit > 1) launch_decode_one<G, true, ST, true>(a, s, a.nsplit - 1, 1);
+        launch_decode_one<true, ST, false, true>(a, s, 1, 0);
+        if (a.nsplit > 1) launch_decode_one<true, ST, true>(a, s, a.nsplit - 1, 1);
     }
 }
 

@@ -43,6 +43,14 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                    0, 0, 0);
 }
 
+// 16x16x32 bf16 MFMA: D[i][j] = C[i][j] + sum_k A[i][k] B[k][j].
+// Lane l holds A[l%16][8*(l/16) .. +8], B[8*(l/16) .. +8][l%16];
+// D register r of lane l is D[4*(l/16) + r][l%16].
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
 // Work item of workgroup i in a grid ordered by rank (i / BH) and head.  The
 // GPU deals workgroups to its 8 XCDs round-robin (i % 8), so with head =
 // i % BH every XCD would serve a fixed subset of the heads for the whole
