@@ -86,19 +86,26 @@ __device__ __forceinline__ float rows_sum(float x) {
 //  - PV as O^T (d x rows) += V^T P^T over two 32-key products: B = P^T
 //    (lane (row n, g4) holds keys 32h + 16(j/4) + 4*g4 + j%4, j = 0..7: the
 //    lane's own probabilities of chunks 2h and 2h+1, rounded to bf16), A =
-//    V^T with d = 8m + db for product db and lane (m = n, g4): the lane reads
-//    d 8n .. 8n+8 of those eight keys (16 bytes each, a key's 256 bytes over
-//    16 lanes) and pairs keys with byte permutes; lane (row n, g4) then holds
-//    O[n][32*g4 + 8r + db] in register r of accumulator db, so the rescale by
-//    the row's alpha is lane-local too.
-// K of the next tile is requested as soon as the scores have read the
-// current one; V after the vote, only for a kept tile.  At two waves per
-// SIMD each wave has up to 32 KiB of K and V in flight, which keeps the HBM
-// queue full; the arithmetic of a tile is a few hundred cycles.
+//    V^T, read from the wave's V tile in LDS by transposing reads (lane
+//    (m, g4) gets d = 16*db + m of those eight keys for product db); lane
+//    (row n, g4) then holds O[n][16*db + 4*g4 + r] in register r of
+//    accumulator db, so the rescale by the row's alpha is lane-local too.
+// Memory: K tiles go to registers two tiles ahead (a two-slot ring, tile t
+// in slot (nt-1-t) % 2); a kept tile's V goes straight to LDS (direct loads,
+// the 16-byte chunks of each 256-byte key row swizzled) right after the vote,
+// then the slot the scores have read is refilled with tile t-2, so the wait
+// for V before the PV products leaves those 16 K loads in flight.  Every
+// tile of the loop issues its 16 refill loads (past tile 0 they read a few
+// bytes of the query rows instead, unused): with no load under a branch the
+// compiler's own waits for K stay exact.  The V wait counts on those 16
+// loads being issued after the V loads and executed; the final tile of an
+// odd count refills nothing and waits for every load.  At two waves per SIMD a wave keeps 32-48 KiB
+// of K and V in flight, also through runs of skipped tiles; the arithmetic
+// of a tile is a few hundred cycles.
 // SEED: this launch covers the older partitions of a seeded decode and reads
 // partition 0's final state from `part` (written by the previous launch).
-// VPF: V of the next tile is requested once the current PV has read its
-// registers, whatever the vote decides (the tile states of a seeded decode's
+// VPF: V of the next tile is requested once the current PV has read the LDS
+// tile, whatever the vote decides (the tile states of a seeded decode's
 // newest partition, one tile each, and its walk when that runs tile by tile).
 template <bool GATED, bool STATS, bool SEED, bool VPF>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_split_bf16_d128(
@@ -107,6 +114,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     float scale_log2, float log2_tau, float log2_lq, int32_t* __restrict__ kept, int32_t* __restrict__ legal,
     uint32_t* __restrict__ bits, int pbase, int seeded_grid, int rpv, float* __restrict__ tstat) {
     constexpr int D = 128, BK = 64;
+    __shared__ __attribute__((aligned(1024))) uint8_t vsm[BK * D * 2];  // V tile: 64 swizzled rows
     const int lane = threadIdx.x, n = lane & 15, g4 = lane >> 4;
     const int p = int(blockIdx.x) + pbase;
     const int bg = blockIdx.y;  // b * Hkv + g
@@ -137,26 +145,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // Loads are clamped: a key past the partition (k1 > k0 always) reads the
     // partition's last key instead; its score is set to -inf, so its
     // probability is 0.
-    u32x4 kf[4][4];  // [chunk][product]
-    auto load_k = [&](int t) {
+    u32x4 kf[2][4][4];  // [slot][chunk][product]
+    // (t < 0: no such tile; the loads read the first 128 elements of q)
+    auto load_k = [&](auto slot_tag, int t) {
+        constexpr int SL = decltype(slot_tag)::value;
+        const int tb = k0 + t * BK;
+        const bf16_t* base = t >= 0 ? kcache + kvbase + long(tb) * D : q;
+        const int lim = t >= 0 ? k1 - 1 - tb : 0;  // last key of the partition, tile-relative
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
-            const int key = min(k0 + t * BK + 16 * ch + n, k1 - 1);
-            const bf16_t* src = kcache + kvbase + long(key) * D + 8 * g4;
+            const bf16_t* src = base + min(16 * ch + n, lim) * D + 8 * g4;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) kf[ch][c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+            for (int c = 0; c < 4; ++c) kf[SL][ch][c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
         }
     };
-    u32x4 vf[2][8];  // [product h][key j]
+    // V tile t into LDS: load i writes keys 4i .. 4i+3, lane l the chunk at
+    // swizzled position l % 16 of key 4i + l/16
+    const uint32_t vlds = lds_addr_of(vsm);
     auto load_v = [&](int t) {
+        const int tb = k0 + t * BK;
+        const int lim = k1 - 1 - tb;  // last key of the partition, tile-relative
+        const bf16_t* base = vcache + kvbase + long(tb) * D;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int key = min(k0 + t * BK + 32 * h + 16 * (j >> 2) + 4 * g4 + (j & 3), k1 - 1);
-                vf[h][j] = *reinterpret_cast<const u32x4*>(vcache + kvbase + long(key) * D + 8 * n);
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int kl = 4 * i + g4;
+            const uint32_t ch = uint32_t(n ^ rowkey(kl));
+            dma16s(base, uint32_t(min(kl, lim)) * 256u + ch * 16u, vlds + 1024u * i);
+        }
     };
+    // transposing-read offsets: lane (m = n, g4) addresses key 4*g4 + m/4
+    // (+ 32h + 16 for the second half of product h) at d = 16*db + 4*(m%4)
+    int vrd[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) vrd[db] = swz_el(4 * g4 + (n >> 2), 16 * db + 4 * (n & 3));
 
     // (m2, lsum): this partition's own state of row n; ltest: the normalizer
     // the test uses, which also holds the seed (the same as lsum without one)
@@ -190,17 +211,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
     for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    load_k(nt - 1);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    load_k(S0{}, nt - 1);
+    load_k(S1{}, nt - 2);
     if (VPF) load_v(nt - 1);
-    for (int t = nt - 1; t >= 0; --t) {
+    // LAST: the final tile after the pairs of the loop; it refills nothing
+    // (the refill would be dead code, which the compiler drops)
+    auto tile = [&](auto slot_tag, auto last_tag, int t) {
+        constexpr int SL = decltype(slot_tag)::value;
+        constexpr bool LAST = decltype(last_tag)::value;
         f32x4 s[4];
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
             s[ch] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) s[ch] = mfma16(kf[ch][c], qf[c], s[ch]);
+            for (int c = 0; c < 4; ++c) s[ch] = mfma16(kf[SL][ch][c], qf[c], s[ch]);
         }
-        if (t > 0) load_k(t - 1);  // into the registers the products have read
         if (k0 + t * BK + BK > k1) {  // the partition's newest tile may be partial
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch)
@@ -244,8 +271,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
                 word = 0;
             }
         }
+        if (!VPF && rk != 0) load_v(t);
+        if (!LAST) load_k(slot_tag, t - 2);  // into the slot the products have read
         if (rk != 0) {
-            if (!VPF) load_v(t);
             // a row whose group skips the tile keeps its state: alpha = 1, no probability
             const bool rkeep = (rk >> n) & 1u;
             const float mn = rkeep ? fmaxf(m2, mx * scale_log2) : m2;  // kept: finite (a valid key)
@@ -273,22 +301,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
                     for (int r = 0; r < 4; ++r) acc[db][r] *= alpha;
             }
+            // V(t) has landed once at most the K refill's 16 loads (issued after
+            // it) are pending
+            if (LAST) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int db = 0; db < 8; ++db) {
-                    u32x4 a;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t x = vf[h][2 * e][db >> 1], y = vf[h][2 * e + 1][db >> 1];
-                        a[e] = (db & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-                    }
-                    acc[db] = mfma16(a, pb[h], acc[db]);
+                    const u32x2 lo = tr16(vsm, vrd[db] + 8192 * h);
+                    const u32x2 hi = tr16(vsm, vrd[db] + 8192 * h + 4096);
+                    acc[db] = mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[h], acc[db]);
                 }
         }
-        if (VPF && t > 0) load_v(t - 1);
+        if (VPF && t > 0) load_v(t - 1);  // (the products above have read the LDS tile)
+    };
+    using MID = std::false_type;
+    using LAST = std::true_type;
+    int t = nt - 1;
+    for (; t >= 1; t -= 2) {
+        tile(S0{}, MID{}, t);
+        tile(S1{}, MID{}, t - 1);
     }
-
+    if (t == 0) tile(S0{}, LAST{}, 0);
     if (live) {
         float* dst = part + (qrow * nsplit + p) * (D + 2);
         if (g4 == 0) {
@@ -296,10 +331,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
             dst[1] = lsum;
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int db = 0; db < 8; db += 2)
-                *reinterpret_cast<f32x2*>(dst + 2 + 32 * g4 + 8 * r + db) = f32x2{acc[db][r], acc[db + 1][r]};
+        for (int db = 0; db < 8; ++db) {
+            *reinterpret_cast<f32x2*>(dst + 2 + 16 * db + 4 * g4) = f32x2{acc[db][0], acc[db][1]};
+            *reinterpret_cast<f32x2*>(dst + 4 + 16 * db + 4 * g4) = f32x2{acc[db][2], acc[db][3]};
+        }
     }
     if (STATS && lead) {
         if (kept) kept[sidx] = nkept;
