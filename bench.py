@@ -238,7 +238,7 @@ def main():
                               "fwd_vs_tau0": ms_vote["fwd"] / out_tau0["fwd_ms"] if out_tau0 else None,
                               "dq_vs_tau0": ms_vote["dq"] / out_tau0["dq_ms"] if out_tau0 else None,
                               "dkdv_vs_tau0": ms_vote["dkdv"] / out_tau0["dkdv_ms"] if out_tau0 else None,
-                              "note": "every tile voted on and kept; ratio to the ungated (tau=0) kernels"},
+                              "note": "every tile voted on and kept; ratio to the tau=0 kernels (ungated dQ and dK/dV; the tau=0 forward without statistics runs the gated kernel, whose thresholds are then -inf)"},
         }
         log(f"tau=inf fwd {ms_inf['fwd']:.2f} ms (QK rate {extra['qk_rate']['tflops']:.0f} TFLOP/s); "
             f"tau=1e-30 fwd {ms_vote['fwd']:.2f} dQ {ms_vote['dq']:.2f} dK/dV {ms_vote['dkdv']:.2f}")
