@@ -196,7 +196,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
         const float lz = SEED ? ltest : lsum;
         return (lz == 0.f) ? -FLT_MAX : (m2 + fast_log2(lz) + log2_tau - log2_lq) * inv_scale_log2;
     };
-    float thr = thr_of();
 
     // statistics of vote group n / rpv: kept by lane n = its first row (g4 = 0)
     const int nvg = G / rpv;
@@ -216,6 +215,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     load_k(S0{}, nt - 1);
     load_k(S1{}, nt - 2);
     if (VPF) load_v(nt - 1);
+    float thr = thr_of();  // (after the first requests: a seed load's latency overlaps them)
     // LAST: the final tile after the pairs of the loop; it refills nothing
     // (the refill would be dead code, which the compiler drops)
     auto tile = [&](auto slot_tag, auto last_tag, int t) {
