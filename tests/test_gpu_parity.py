@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import WORKLOADS, prefill_inputs, decode_inputs, to_f64
+from synth import WORKLOADS, prefill_inputs, decode_inputs, round_to, to_f64
 from tests.parity import (BAND, TOL_GRAD, TOL_O, TOL_TSTAT, bf16_to_f64, bwd_decision_check, check_rows,
                           chunk_legal_mask, decision_report, legal_mask, rel_l2, tstat_report)
 
@@ -391,6 +391,41 @@ def test_decode_seeded_bf16(ops, Lk, split, Lcap, tau):
         o2, lse2 = ops.decode(q, kc, vc, Lk, tau, split_keys=split, bk=64)
         torch.cuda.synchronize()
         assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("seeded", [False, True])
+@pytest.mark.parametrize("tau", [0.0, 1.0])
+def test_decode_lone_tile_dominates(ops, seeded, tau):
+    """A partition of a single tile whose key carries nearly all of every
+    row's softmax mass: plain decode's last partition holds only the newest
+    key (Lk = 4097, split 4096), a seeded decode's oldest partition only
+    tile 0 (the query is aligned with key 0 there).  Its V must reach the
+    output: O and lse against the oracle, and O close to that key's V row."""
+    rng = np.random.default_rng(20261204)
+    B, Hq, Hkv, Lk, d, split = 2, 8, 2, 4097, 128, 4096
+    G = Hq // Hkv
+    k = rng.standard_normal((B, Hkv, Lk, d))
+    v = rng.standard_normal((B, Hkv, Lk, d))
+    j = 0 if seeded else Lk - 1
+    q = 2.0 * np.repeat(k[:, :, j, :], G, axis=1) + 0.1 * rng.standard_normal((B, Hq, d))
+    x = {"q": round_to(q, "bf16"), "k": round_to(k, "bf16"), "v": round_to(v, "bf16")}
+    qd, kd, vd = _dev_tensors(x, "bf16", ("q", "k", "v"))
+    o, lse, st = ops.decode(qd, kd, vd, Lk, tau, split_keys=split, bk=64, stats=True, seeded=seeded)
+    torch.cuda.synchronize()
+    qf, kf, vf = (to_f64(x[n], "bf16") for n in ("q", "k", "v"))
+    if seeded:
+        nsplit, tps = oracle.seeded_decode_shapes(Lk, split, 64)
+        gk = ops.bits_to_keep(st["keep_bits"], tps)
+        oo, ol, ok, oT = oracle.decode_seeded(qf, kf, vf, Lk, tau, split, 64, replay=gk[:, :, None], band=BAND)
+    else:
+        gk = ops.bits_to_keep(st["keep_bits"], split // 64)
+        oo, ol, ok, oT = oracle.decode(qf, kf, vf, Lk, tau, split, 64, replay=gk[:, :, None], band=BAND)
+    og = bf16_to_f64(o)
+    assert rel_l2(og, oo) <= TOL_O
+    assert float(np.abs(lse.cpu().numpy() - ol).max()) <= 1e-3
+    check_rows("o_decode", og, oo, f"lone tile seeded={seeded} tau={tau}")
+    vj = np.repeat(vf[:, :, j, :], G, axis=1)  # the dominant key's V row, per query head
+    assert rel_l2(og, vj) <= 0.05
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (16, 2)])
