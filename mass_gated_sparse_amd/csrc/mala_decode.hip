@@ -14,9 +14,8 @@
 // group, so a skipped tile really saves the V bytes; rpv = 1: one vote per
 // query head).  A tile is kept for a vote group iff one of its rows votes
 // keep; only that group's rows update their state, and V is read iff some
-// group keeps the tile.  The kernel is HBM-bound: K of the next tile is
-// requested as soon as the current scores are formed; V is read only for
-// kept tiles.  Scores and PV are bf16 MFMAs with fp32 accumulation (the
+// group keeps the tile.  The kernel is HBM-bound: K is requested two tiles
+// ahead; V is read only for kept tiles.  Scores and PV are bf16 MFMAs with fp32 accumulation (the
 // probabilities enter PV rounded to bf16, the normalizer sums them in fp32);
 // the lane mapping is described at the kernel.
 // Partial states (m2 = running max of s*log2(e), l, acc[d]) are written per
@@ -99,9 +98,9 @@ __device__ __forceinline__ float rows_sum(float x) {
 // bytes of the query rows instead, unused): with no load under a branch the
 // compiler's own waits for K stay exact.  The V wait counts on those 16
 // loads being issued after the V loads and executed; the final tile of an
-// odd count refills nothing and waits for every load.  At two waves per SIMD a wave keeps 32-48 KiB
-// of K and V in flight, also through runs of skipped tiles; the arithmetic
-// of a tile is a few hundred cycles.
+// odd count refills nothing and waits for every load.  At two waves per
+// SIMD a wave keeps 32-48 KiB of K and V in flight, also through runs of
+// skipped tiles; the arithmetic of a tile is a few hundred cycles.
 // SEED: this launch covers the older partitions of a seeded decode and reads
 // partition 0's final state from `part` (written by the previous launch).
 // VPF: V of the next tile is requested once the current PV has read the LDS
