@@ -399,11 +399,13 @@ def summarize_counters(name, workload, tau, *dirs):
         passes.append(sorted(counters))
         for (disp, cn), v in per.items():
             vals[names[disp]][cn].append(v)
+    from synth import WORKLOADS
+    op = "decode" if WORKLOADS[workload].kind == "decode" else "<fwd|bwd>"
     lines = [f"# Hardware counters per dispatch: {workload}, tau={tau}", "",
              "Commands (from the repository root, on one MI355X; one rocprofv3 pass per counter set):", ""]
     for cs in dict.fromkeys(tuple(c) for c in passes):
         lines.append(f"    cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {' '.join(cs)} --output-format csv "
-                     f"-d <dir> -o run -- python3 <repo>/bench.py --profile-op <fwd|bwd> "
+                     f"-d <dir> -o run -- python3 <repo>/bench.py --profile-op {op} "
                      f"--workload {workload} --tau {tau} --iters 1")
     lines += ["", "Derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES); LDS active = "
               "SQ_LDS_IDX_ACTIVE / SQ_BUSY_CU_CYCLES; waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES; LDS waits = "
